@@ -1,0 +1,113 @@
+/* CPU oracle for the Mamba-2 mixer layer: plain fp64 loops.
+ *
+ * TEST INFRASTRUCTURE ONLY. This code is the slow, obviously correct definition
+ * that the HIP path is checked against. Only the tests, the smoke check and the
+ * bench's CPU-baseline leg may load it; the product path never does. It shares
+ * no code, header, table or helper with the HIP library.
+ *
+ * What it computes: the per-frame decode step of one Mamba-2 mixer layer of the
+ * hybrid Mamba-2/attention backbone (page "NemotronLabs VoiceChat 11B: GPTQ
+ * 3-bit LLM, MLX", introduction: Nemotron-Nano-9B-v2, Mamba-2 and attention;
+ * page "NemotronLabs VoiceChat" (SGLang-Omni cookbook), introduction: one
+ * token per 80 ms frame), and the prompt prefill (GPTQ page, "Recipe":
+ * system-prompt prefill before streaming) as that many recurrent steps.
+ * The pages print no equation of the mixer; the steps are:
+ *   1. zxbcdt = W_in u                         (in_proj, no bias)
+ *   2. split [z | xBC | dt_raw]
+ *   3. causal depthwise conv (width d_conv) over xBC with bias, then SiLU;
+ *      the cache holds the last d_conv-1 raw inputs, oldest first
+ *   4. split the conv output into x (head-major), B and C (group-major)
+ *   5. dt = softplus(dt_raw + dt_bias), A = -exp(A_log), dA = exp(dt A)
+ *   6. S[h][p][n] = dA S[h][p][n] + dt x[h][p] B[g][n],  g = h / (H/G)
+ *   7. y[h][p] = sum_n S[h][p][n] C[g][n] + D[h] x[h][p]    (updated S)
+ *   8. v = y * SiLU(z)
+ *   9. per group of norm_group channels: yn = v / sqrt(mean(v^2) + eps) * norm_w
+ *  10. out = W_out yn  (optionally y = u + out: residual stack)
+ * A second, independent definition of steps 5-7 over a sequence, the
+ * materialised quadratic (attention-like) form, is orc_ssd_quadratic.
+ *
+ * Parity pins live in tests/test_oracle_pins.py.
+ */
+#ifndef M2_ORACLE_H
+#define M2_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_W_F32 = 0, ORC_W_BF16 = 1, ORC_W_INT8G = 2 };
+
+typedef struct {
+  int32_t d_model, n_heads, head_dim, d_state, n_groups, d_conv;
+  int32_t norm_group;          /* channels per RMS group (> 0) */
+  double norm_eps;
+  int32_t wtype;               /* ORC_W_* */
+  int32_t q_group;             /* K-group of the int8 scales */
+  double q_gamma_in, q_gamma_out;
+} orc_cfg;
+
+typedef struct {
+  const void *w_in;            /* [d_in_proj][d_model]: float, bf16 bits (uint16) or int8 */
+  const uint16_t *s_in;        /* fp16 bits [d_in_proj][d_model/q_group] (int8 only) */
+  const void *w_out;           /* [d_model][d_inner] */
+  const uint16_t *s_out;       /* fp16 bits [d_model][d_inner/q_group] (int8 only) */
+  const float *conv_w;         /* [conv_dim][d_conv], tap d_conv-1 = newest */
+  const float *conv_b;         /* [conv_dim] */
+  const float *dt_bias, *A_log, *D;   /* [n_heads] */
+  const float *norm_w;         /* [d_inner] */
+} orc_weights;
+
+/* Optional intermediates of the last token processed, all [batch][...] doubles. */
+typedef struct {
+  double *zxbcdt;              /* [B][d_in_proj] */
+  double *xconv;               /* [B][conv_dim] conv + SiLU output */
+  double *dt;                  /* [B][n_heads] softplus output */
+  double *y;                   /* [B][d_inner] SSM readout incl. D x */
+  double *v;                   /* [B][d_inner] gated */
+  double *yn;                  /* [B][d_inner] normalised */
+  double *out;                 /* [B][d_model] out_proj result (before residual) */
+} orc_trace;
+
+/* One token for `batch` sessions. ssm [n_slots][H][P][N], conv [n_slots][d_conv-1][conv_dim]
+ * are updated in place for the slots named by slot_ids (NULL: session b uses slot b).
+ * x, y: [batch][d_model]. residual != 0 gives y = x + out. Returns 0, or -1 on bad arguments. */
+int orc_step(const orc_cfg *cfg, const orc_weights *w, double *ssm, double *conv, int32_t n_slots,
+             const double *x, double *y, int32_t batch, const int32_t *slot_ids, int32_t residual,
+             orc_trace *trace);
+
+/* Prompt prefill as `seqlen` recurrent steps: x, y [batch][seqlen][d_model]. */
+int orc_prefill(const orc_cfg *cfg, const orc_weights *w, double *ssm, double *conv, int32_t n_slots,
+                const double *x, double *y, int32_t batch, int32_t seqlen, const int32_t *slot_ids,
+                int32_t residual);
+
+/* Steps 5-7 alone, token by token over T tokens (the same code orc_step uses).
+ * x [T][H][P], Bm and Cm [T][G][N], dt [T][H] (already softplus'd), A [H] (negative),
+ * D [H]; S [H][P][N] is updated in place; y [T][H][P]. */
+void orc_ssd_recurrent(int32_t T, int32_t H, int32_t P, int32_t N, int32_t G, const double *x,
+                       const double *Bm, const double *Cm, const double *dt, const double *A,
+                       const double *D, double *S, double *y);
+
+/* The same map as a materialised quadratic form:
+ *   cs_t = sum_{r<=t} dt_r A
+ *   y_t  = sum_{s<=t} (C_t . B_s) exp(cs_t - cs_s) dt_s x_s + exp(cs_t) C_t S0 + D x_t
+ *   S_T  = exp(cs_{T-1}) S0 + sum_s exp(cs_{T-1} - cs_s) dt_s x_s (x) B_s
+ * S0 [H][P][N] is read; S_final [H][P][N] written (may be NULL). */
+void orc_ssd_quadratic(int32_t T, int32_t H, int32_t P, int32_t N, int32_t G, const double *x,
+                       const double *Bm, const double *Cm, const double *dt, const double *A,
+                       const double *D, const double *S0, double *y, double *S_final);
+
+/* Helpers exposed so tests can pin them: element decoders and scalar functions. */
+double orc_bf16_to_double(uint16_t h);
+double orc_fp16_to_double(uint16_t h);
+double orc_softplus(double x);
+double orc_silu(double x);
+
+/* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
+int orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
