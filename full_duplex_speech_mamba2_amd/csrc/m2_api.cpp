@@ -1,0 +1,232 @@
+// C-ABI layer of libm2.so: argument validation, handles and dispatch.
+// Every check runs on the host before anything is enqueued; the operation and
+// its sources are described in include/m2.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "m2_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return M2_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int gcd(int a, int b) {
+  while (b) {
+    int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+int check_config(const m2_config *c) {
+  if (!c) return fail(M2_ERR_NULL, "config is NULL");
+  if (c->d_model <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->d_state <= 0 || c->n_groups <= 0)
+    return fail(M2_ERR_SHAPE, "dimensions must be positive");
+  if (c->d_conv < 2 || c->d_conv > 8) return fail(M2_ERR_SHAPE, "d_conv %d outside [2, 8]", c->d_conv);
+  if (c->n_heads % c->n_groups)
+    return fail(M2_ERR_SHAPE, "n_heads %d is not a multiple of n_groups %d", c->n_heads, c->n_groups);
+  if (c->d_model % 16) return fail(M2_ERR_SHAPE, "d_model %d is not a multiple of 16", c->d_model);
+  const long d_inner = (long)c->n_heads * c->head_dim;
+  if (d_inner % 16) return fail(M2_ERR_SHAPE, "d_inner %ld is not a multiple of 16", d_inner);
+  const int N = c->d_state;
+  if (N < 4 || N > 256 || (N & (N - 1)))
+    return fail(M2_ERR_SHAPE, "d_state %d must be a power of two in [4, 256]", N);
+  const long ng = c->norm_group > 0 ? c->norm_group : d_inner / c->n_groups;
+  if (c->norm_group < 0 || ng <= 0 || d_inner % ng)
+    return fail(M2_ERR_SHAPE, "norm_group %d does not divide d_inner %ld", c->norm_group, d_inner);
+  if (!(c->norm_eps >= 0.0f)) return fail(M2_ERR_SHAPE, "norm_eps must be >= 0");
+  if (d_inner / ng > 4096) return fail(M2_ERR_UNSUPPORTED, "more than 4096 RMS groups");
+  if (c->wtype != M2_W_F32 && c->wtype != M2_W_BF16 && c->wtype != M2_W_INT8G)
+    return fail(M2_ERR_DTYPE, "unknown wtype %d", c->wtype);
+  if (c->wtype == M2_W_INT8G) {
+    if (c->q_group <= 0 || c->q_group % 16)
+      return fail(M2_ERR_SHAPE, "q_group %d must be a positive multiple of 16", c->q_group);
+    if (c->d_model % c->q_group || d_inner % c->q_group)
+      return fail(M2_ERR_SHAPE, "q_group %d does not divide d_model %d and d_inner %ld", c->q_group,
+                  c->d_model, d_inner);
+  }
+  const long conv_dim = d_inner + 2L * c->n_groups * N;
+  const long d_in_proj = 2 * d_inner + 2L * c->n_groups * N + c->n_heads;
+  if (d_in_proj > (1L << 30) / 1 || conv_dim > (1L << 28))
+    return fail(M2_ERR_SHAPE, "layer too large");
+  return M2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int m2_abi_version(void) { return M2_ABI_VERSION; }
+
+const char *m2_last_error(void) { return g_err; }
+
+int m2_layer_create(const m2_config *cfg, const m2_weights *w, m2_layer *out) {
+  if (!out) return fail(M2_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!w) return fail(M2_ERR_NULL, "weights struct is NULL");
+  const void *req[] = {w->w_in, w->w_out, w->conv_w, w->conv_b, w->dt_bias, w->A_log, w->D, w->norm_w};
+  const char *names[] = {"w_in", "w_out", "conv_w", "conv_b", "dt_bias", "A_log", "D", "norm_w"};
+  for (int i = 0; i < 8; ++i)
+    if (!req[i]) return fail(M2_ERR_NULL, "weight pointer %s is NULL", names[i]);
+  if (cfg->wtype == M2_W_INT8G && (!w->s_in || !w->s_out))
+    return fail(M2_ERR_NULL, "int8 weights need s_in and s_out");
+  if (!aligned16(w->w_in) || !aligned16(w->w_out))
+    return fail(M2_ERR_ALIGN, "w_in and w_out must be 16-byte aligned");
+  if (cfg->wtype == M2_W_INT8G && (!aligned16(w->s_in) || !aligned16(w->s_out)))
+    return fail(M2_ERR_ALIGN, "s_in and s_out must be 16-byte aligned");
+  for (int i = 2; i < 8; ++i)
+    if (reinterpret_cast<uintptr_t>(req[i]) & 3u)
+      return fail(M2_ERR_ALIGN, "%s must be 4-byte aligned", names[i]);
+
+  m2_layer_s *L = new (std::nothrow) m2_layer_s();
+  if (!L) return fail(M2_ERR_SHAPE, "out of host memory");
+  L->cfg = *cfg;
+  L->w = *w;
+  L->d_inner = cfg->n_heads * cfg->head_dim;
+  L->conv_dim = L->d_inner + 2 * cfg->n_groups * cfg->d_state;
+  L->d_in_proj = 2 * L->d_inner + 2 * cfg->n_groups * cfg->d_state + cfg->n_heads;
+  L->zx_stride = (L->d_in_proj + 3) & ~3;
+  L->hpg = cfg->n_heads / cfg->n_groups;
+  L->ng = cfg->norm_group > 0 ? cfg->norm_group : L->d_inner / cfg->n_groups;
+  L->cfg.norm_group = L->ng;
+  L->n_norm = L->d_inner / L->ng;
+  // SSD workgroup row range: the largest divisor of gcd(head_dim, ng) not above 32,
+  // so a workgroup's channels never straddle an RMS group.
+  const int gg = gcd(cfg->head_dim, L->ng);
+  int pr = 1;
+  for (int d = 1; d <= 32 && d <= gg; ++d)
+    if (gg % d == 0) pr = d;
+  L->prange = pr;
+  L->psplit = cfg->head_dim / pr;
+  L->n_partials = L->d_inner / pr;
+  *out = L;
+  return ok();
+}
+
+void m2_layer_destroy(m2_layer layer) { delete layer; }
+
+int m2_state_sizes(const m2_config *cfg, int32_t n_slots, size_t *ssm_bytes, size_t *conv_bytes) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (n_slots <= 0) return fail(M2_ERR_SHAPE, "n_slots must be positive");
+  if (!ssm_bytes || !conv_bytes) return fail(M2_ERR_NULL, "size outputs are NULL");
+  const size_t d_inner = (size_t)cfg->n_heads * cfg->head_dim;
+  const size_t conv_dim = d_inner + 2 * (size_t)cfg->n_groups * cfg->d_state;
+  *ssm_bytes = (size_t)n_slots * d_inner * cfg->d_state * sizeof(float);
+  *conv_bytes = (size_t)n_slots * (cfg->d_conv - 1) * conv_dim * sizeof(float);
+  return ok();
+}
+
+int m2_state_create(m2_layer layer, int32_t n_slots, float *ssm, float *conv, m2_state *out) {
+  if (!out) return fail(M2_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  if (!layer) return fail(M2_ERR_NULL, "layer is NULL");
+  if (n_slots <= 0) return fail(M2_ERR_SHAPE, "n_slots must be positive");
+  if (!ssm || !conv) return fail(M2_ERR_NULL, "ssm and conv buffers are required");
+  if (!aligned16(ssm) || !aligned16(conv)) return fail(M2_ERR_ALIGN, "state buffers must be 16-byte aligned");
+  m2_state_s *S = new (std::nothrow) m2_state_s();
+  if (!S) return fail(M2_ERR_SHAPE, "out of host memory");
+  S->layer = layer;
+  S->n_slots = n_slots;
+  S->ssm = ssm;
+  S->conv = conv;
+  *out = S;
+  return ok();
+}
+
+void m2_state_destroy(m2_state st) { delete st; }
+
+int m2_state_zero(m2_state st, const int32_t *slot_ids, int32_t n, void *stream) {
+  if (!st) return fail(M2_ERR_NULL, "state is NULL");
+  if (slot_ids && n <= 0) return fail(M2_ERR_SHAPE, "n must be positive");
+  if (slot_ids && n > st->n_slots) return fail(M2_ERR_SLOT, "n %d exceeds n_slots %d", n, st->n_slots);
+  hipError_t e = m2d::launch_state_zero(*st, slot_ids, slot_ids ? n : st->n_slots,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(M2_ERR_HIP, "state zero launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t m2_step_workspace(m2_layer layer, int32_t batch) {
+  if (!layer || batch <= 0) return 0;
+  return m2d::step_ws_layout(*layer, batch, nullptr).bytes;
+}
+
+int m2_step(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
+            const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  if (!layer || !st) return fail(M2_ERR_NULL, "layer or state is NULL");
+  if (st->layer != layer) {
+    const m2_config &a = st->layer->cfg, &b = layer->cfg;
+    if (a.n_heads != b.n_heads || a.head_dim != b.head_dim || a.d_state != b.d_state ||
+        a.n_groups != b.n_groups || a.d_conv != b.d_conv)
+      return fail(M2_ERR_SHAPE, "state was created for a layer of another shape");
+  }
+  if (!x || !y) return fail(M2_ERR_NULL, "x and y are required");
+  if (!aligned16(x) || !aligned16(y)) return fail(M2_ERR_ALIGN, "x and y must be 16-byte aligned");
+  if (batch <= 0) return fail(M2_ERR_SHAPE, "batch must be positive");
+  if (batch > st->n_slots) return fail(M2_ERR_SLOT, "batch %d exceeds n_slots %d", batch, st->n_slots);
+  if (flags & ~M2_RESIDUAL) return fail(M2_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (!(flags & M2_RESIDUAL) && x == y)
+    return fail(M2_ERR_SHAPE, "y may alias x only with M2_RESIDUAL");
+  const size_t need = m2_step_workspace(layer, batch);
+  if (!ws || ws_bytes < need)
+    return fail(M2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(M2_ERR_ALIGN, "workspace must be 16-byte aligned");
+  m2d::StepWs W = m2d::step_ws_layout(*layer, batch, ws);
+  hipError_t e = m2d::launch_step(*layer, *st, x, y, batch, slot_ids, flags, W,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(M2_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk) {
+  if (!layer || batch <= 0 || seqlen <= 0 || chunk < 16 || chunk > 256 || chunk % 16) return 0;
+  return m2d::prefill_ws_bytes(*layer, batch, seqlen, chunk);
+}
+
+int m2_prefill(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch, int32_t seqlen,
+               int32_t chunk, const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes,
+               void *stream) {
+  if (!layer || !st) return fail(M2_ERR_NULL, "layer or state is NULL");
+  if (!x || !y) return fail(M2_ERR_NULL, "x and y are required");
+  if (!aligned16(x) || !aligned16(y)) return fail(M2_ERR_ALIGN, "x and y must be 16-byte aligned");
+  if (batch <= 0 || seqlen <= 0) return fail(M2_ERR_SHAPE, "batch and seqlen must be positive");
+  if (chunk < 16 || chunk > 256 || chunk % 16)
+    return fail(M2_ERR_SHAPE, "chunk %d must be a multiple of 16 in [16, 256]", chunk);
+  if (batch > st->n_slots) return fail(M2_ERR_SLOT, "batch %d exceeds n_slots %d", batch, st->n_slots);
+  if (flags & ~M2_RESIDUAL) return fail(M2_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (!(flags & M2_RESIDUAL) && x == y)
+    return fail(M2_ERR_SHAPE, "y may alias x only with M2_RESIDUAL");
+  if ((long)batch * seqlen > (1L << 24)) return fail(M2_ERR_SHAPE, "batch * seqlen too large");
+  const size_t need = m2_prefill_workspace(layer, batch, seqlen, chunk);
+  if (need == 0) return fail(M2_ERR_UNSUPPORTED, "prefill is not available for this layer");
+  if (!ws || ws_bytes < need)
+    return fail(M2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(M2_ERR_ALIGN, "workspace must be 16-byte aligned");
+  hipError_t e = m2d::launch_prefill(*layer, *st, x, y, batch, seqlen, chunk, slot_ids, flags, ws,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(M2_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

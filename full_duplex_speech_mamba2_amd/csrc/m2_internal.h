@@ -1,0 +1,57 @@
+// Internal declarations shared by the C-ABI layer (m2_api.cpp) and the HIP
+// kernels (decode.hip, prefill.hip) of libm2.so. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "m2.h"
+
+struct m2_layer_s {
+  m2_config cfg;
+  m2_weights w;
+  // derived sizes
+  int d_inner;      // H * P
+  int conv_dim;     // d_inner + 2 G N
+  int d_in_proj;    // 2 d_inner + 2 G N + H
+  int zx_stride;    // d_in_proj rounded up to 4 floats (workspace row stride)
+  int hpg;          // heads per B/C group
+  int ng;           // channels per RMS group
+  int n_norm;       // RMS groups: d_inner / ng
+  int prange;       // head_dim rows per SSD workgroup (divides head_dim and ng)
+  int psplit;       // head_dim / prange
+  int n_partials;   // d_inner / prange sum-of-squares partials per session
+};
+
+struct m2_state_s {
+  const m2_layer_s *layer;
+  int n_slots;
+  float *ssm;       // [n_slots][H][P][N]
+  float *conv;      // [n_slots][d_conv-1][conv_dim]
+};
+
+namespace m2d {
+
+// Workspace carve-up of one decode step for `batch` sessions.
+struct StepWs {
+  float *zx;        // [B][d_in_proj]: z raw | conv+SiLU(x|B|C) | softplus dt
+  float *v;         // [B][d_inner]: gated SSD output
+  float *ss;        // [B][n_partials]: sums of squares of v per partial range
+  size_t bytes;
+};
+StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base);
+
+hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x, float *y, int batch,
+                       const int32_t *slots, int flags, const StepWs &ws, hipStream_t stream);
+
+hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, hipStream_t stream);
+
+// Prefill
+size_t prefill_ws_bytes(const m2_layer_s &L, int batch, int seqlen, int chunk);
+hipError_t launch_prefill(const m2_layer_s &L, const m2_state_s &S, const float *x, float *y, int batch,
+                          int seqlen, int chunk, const int32_t *slots, int flags, void *ws,
+                          hipStream_t stream);
+
+}  // namespace m2d

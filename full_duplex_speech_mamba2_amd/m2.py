@@ -1,0 +1,222 @@
+"""Thin ctypes binding of libm2.so (argument marshalling only).
+
+Every step of the layer runs in the HIP library; this module only moves
+arguments across the C ABI declared in include/m2.h. PyTorch supplies device
+memory (tensors) and the stream (torch's current stream). torch is imported
+before the library is loaded so that the process maps a single HIP runtime
+(torch's bundled libamdhip64.so.7 satisfies libm2.so's dependency).
+
+Importing this module raises ImportError if libm2.so has not been built: there
+is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libm2.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libm2.so is not built (python -m full_duplex_speech_mamba2_amd.build)")
+
+_lib = C.CDLL(LIB_PATH)
+
+M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIGN = 0, -1, -2, -3, -4
+M2_ERR_WORKSPACE, M2_ERR_SLOT, M2_ERR_UNSUPPORTED, M2_ERR_HIP = -5, -6, -7, -8
+M2_RESIDUAL = 1
+WTYPE = {"f32": 0, "bf16": 1, "int8g": 2}
+
+
+class Config(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("n_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("d_state", C.c_int32), ("n_groups", C.c_int32), ("d_conv", C.c_int32),
+                ("norm_group", C.c_int32), ("norm_eps", C.c_float), ("wtype", C.c_int32),
+                ("q_group", C.c_int32), ("q_gamma_in", C.c_float), ("q_gamma_out", C.c_float)]
+
+
+class Weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("w_in", "s_in", "w_out", "s_out", "conv_w", "conv_b",
+                                          "dt_bias", "A_log", "D", "norm_w")]
+
+
+_P = C.c_void_p
+_i32 = C.c_int32
+_lib.m2_abi_version.restype = C.c_int
+_lib.m2_last_error.restype = C.c_char_p
+_lib.m2_layer_create.argtypes = [_P, _P, _P]
+_lib.m2_layer_destroy.argtypes = [_P]
+_lib.m2_layer_destroy.restype = None
+_lib.m2_state_sizes.argtypes = [_P, _i32, _P, _P]
+_lib.m2_state_create.argtypes = [_P, _i32, _P, _P, _P]
+_lib.m2_state_destroy.argtypes = [_P]
+_lib.m2_state_destroy.restype = None
+_lib.m2_state_zero.argtypes = [_P, _P, _i32, _P]
+_lib.m2_step_workspace.argtypes = [_P, _i32]
+_lib.m2_step_workspace.restype = C.c_size_t
+_lib.m2_step.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P]
+_lib.m2_prefill_workspace.argtypes = [_P, _i32, _i32, _i32]
+_lib.m2_prefill_workspace.restype = C.c_size_t
+_lib.m2_prefill.argtypes = [_P, _P, _P, _P, _i32, _i32, _i32, _P, _i32, _P, C.c_size_t, _P]
+for _f in ("m2_layer_create", "m2_state_sizes", "m2_state_create", "m2_state_zero", "m2_step",
+           "m2_prefill"):
+    getattr(_lib, _f).restype = C.c_int
+
+
+class M2Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("m2 status %d: %s" % (status, msg))
+        self.status = status
+
+
+def _check(rc: int):
+    if rc != M2_OK:
+        raise M2Error(rc, _lib.m2_last_error().decode())
+
+
+def lib():
+    return _lib
+
+
+def abi_version() -> int:
+    return _lib.m2_abi_version()
+
+
+def config_from_dims(dims) -> Config:
+    return Config(dims.d_model, dims.n_heads, dims.head_dim, dims.d_state, dims.n_groups, dims.d_conv,
+                  dims.norm_group, float(dims.norm_eps), WTYPE[dims.wtype], dims.q_group,
+                  float(dims.q_gamma_in), float(dims.q_gamma_out))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
+
+
+def to_device(a, device="cuda") -> Optional[torch.Tensor]:
+    """numpy (float32, uint16 bf16 bits, int8, float16) or tensor -> contiguous device tensor."""
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        return a.to(device).contiguous()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+class Layer:
+    """A mixer layer handle over device copies of its weights (the handle borrows them)."""
+
+    def __init__(self, dims, weights: Dict[str, object], device="cuda"):
+        self.dims = dims
+        self.device = torch.device(device)
+        self.tensors = {k: to_device(v, self.device) for k, v in weights.items()}
+        self.cfg = config_from_dims(dims)
+        self.wstruct = Weights(*[_ptr(self.tensors.get(k)) for k in
+                                 ("w_in", "s_in", "w_out", "s_out", "conv_w", "conv_b", "dt_bias",
+                                  "A_log", "D", "norm_w")])
+        h = C.c_void_p()
+        _check(_lib.m2_layer_create(C.byref(self.cfg), C.byref(self.wstruct), C.byref(h)))
+        self.handle = h
+        self._ws: Dict[tuple, torch.Tensor] = {}
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            _lib.m2_layer_destroy(h)
+            self.handle = None
+
+    def step_workspace_bytes(self, batch: int) -> int:
+        return int(_lib.m2_step_workspace(self.handle, batch))
+
+    def prefill_workspace_bytes(self, batch: int, seqlen: int, chunk: int) -> int:
+        return int(_lib.m2_prefill_workspace(self.handle, batch, seqlen, chunk))
+
+    def workspace(self, kind: str, *args) -> torch.Tensor:
+        """A cached device workspace for step(batch) or prefill(batch, seqlen, chunk)."""
+        key = (kind,) + tuple(args)
+        ws = self._ws.get(key)
+        if ws is None:
+            n = self.step_workspace_bytes(*args) if kind == "step" else self.prefill_workspace_bytes(*args)
+            if n == 0:
+                raise M2Error(M2_ERR_UNSUPPORTED, "no workspace size for %s%s" % (kind, args))
+            ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+            self._ws[key] = ws
+        return ws
+
+
+class State:
+    """Per-layer session state: ssm [n_slots][H][P][N] and conv [n_slots][d_conv-1][conv_dim], fp32."""
+
+    def __init__(self, layer: Layer, n_slots: int, ssm: Optional[torch.Tensor] = None,
+                 conv: Optional[torch.Tensor] = None):
+        d = layer.dims
+        self.layer = layer
+        self.n_slots = n_slots
+        self.ssm = ssm if ssm is not None else torch.zeros(
+            (n_slots, d.n_heads, d.head_dim, d.d_state), dtype=torch.float32, device=layer.device)
+        self.conv = conv if conv is not None else torch.zeros(
+            (n_slots, d.d_conv - 1, d.conv_dim), dtype=torch.float32, device=layer.device)
+        for t in (self.ssm, self.conv):
+            if t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError("state tensors must be contiguous float32")
+        h = C.c_void_p()
+        _check(_lib.m2_state_create(layer.handle, n_slots, _ptr(self.ssm), _ptr(self.conv), C.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            _lib.m2_state_destroy(h)
+            self.handle = None
+
+    def zero(self, slot_ids: Optional[torch.Tensor] = None, stream=None):
+        n = 0 if slot_ids is None else int(slot_ids.numel())
+        _check(_lib.m2_state_zero(self.handle, _ptr(slot_ids), n, _stream(stream)))
+
+
+def _act(t: torch.Tensor, shape) -> torch.Tensor:
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError("expected a contiguous float32 tensor of shape %s, got %s %s"
+                         % (tuple(shape), t.dtype, tuple(t.shape)))
+    return t
+
+
+def step(layer: Layer, state: State, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+         slot_ids: Optional[torch.Tensor] = None, residual: bool = False,
+         ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode token for x.shape[0] sessions; returns y [B][d_model]."""
+    B = x.shape[0]
+    _act(x, (B, layer.dims.d_model))
+    if y is None:
+        y = torch.empty_like(x)
+    _act(y, x.shape)
+    if ws is None:
+        ws = layer.workspace("step", B)
+    _check(_lib.m2_step(layer.handle, state.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids),
+                        M2_RESIDUAL if residual else 0, _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def prefill(layer: Layer, state: State, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+            chunk: int = 256, slot_ids: Optional[torch.Tensor] = None, residual: bool = False,
+            ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Chunked prefill of x [B][T][d_model]; returns y [B][T][d_model]."""
+    B, T = x.shape[0], x.shape[1]
+    _act(x, (B, T, layer.dims.d_model))
+    if y is None:
+        y = torch.empty_like(x)
+    _act(y, x.shape)
+    if ws is None:
+        ws = layer.workspace("prefill", B, T, chunk)
+    _check(_lib.m2_prefill(layer.handle, state.handle, _ptr(x), _ptr(y), B, T, chunk, _ptr(slot_ids),
+                           M2_RESIDUAL if residual else 0, _ptr(ws), ws.numel(), _stream(stream)))
+    return y

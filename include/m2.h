@@ -1,0 +1,156 @@
+/* m2.h: C ABI of libm2.so, the MI355X (gfx950) Mamba-2 mixer layer.
+ *
+ * The operation is one Mamba-2 mixer layer of the hybrid Mamba-2/attention LLM
+ * backbone of a full-duplex speech model (page "NemotronLabs VoiceChat 11B:
+ * GPTQ 3-bit LLM, MLX", introduction: Nemotron-Nano-9B-v2, a hybrid of Mamba-2
+ * and attention with 56 layers; page "NVIDIA NemotronLabs VoiceChat 11B: The
+ * First Open Full-Duplex Voice Model with Tool Calling", "Key design
+ * decisions" 2: Mamba keeps inference linear in the length of the streamed
+ * 80 ms frames). Two entry points:
+ *   m2_step     one token per session per 80 ms frame (page "NemotronLabs
+ *               VoiceChat", SGLang-Omni cookbook, introduction: the thinker
+ *               emits one token per frame; "Request parameters": one token per
+ *               80 ms of input);
+ *   m2_prefill  a whole prompt, before streaming starts (GPTQ page, "Recipe":
+ *               system-prompt prefill, then the user's speech; cookbook "Known
+ *               limitations": the system-prompt region is walked before frame 0).
+ * The pages print no equation of the mixer. The layer computes, per token:
+ *   zxbcdt = W_in u, split [z | x | B | C | dt_raw] (x head-major, B and C
+ *   group-major); causal depthwise conv (width d_conv, bias, SiLU) over x|B|C
+ *   with a cache of the last d_conv-1 raw inputs; dt = softplus(dt_raw+dt_bias);
+ *   A = -exp(A_log); S = exp(dt A) S + dt x B^T; y = C.S + D x; v = y*SiLU(z);
+ *   grouped RMSNorm with weight; out = W_out yn; optionally y = u + out.
+ *
+ * Memory: every pointer passed to these calls is a DEVICE pointer owned by
+ * the caller, except the m2_config / m2_weights structs themselves and the
+ * size outputs, which are host memory. Handles borrow pointers; no call frees
+ * caller memory. Float activations, states and small parameters are fp32.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = default stream).
+ * m2_step, m2_prefill and m2_state_zero only enqueue kernels: they never
+ * allocate, never synchronise and never enqueue a memset, so they can be
+ * captured into a HIP graph.
+ *
+ * Errors: every argument check runs on the host before anything is enqueued.
+ * On failure a call returns a negative m2_status, enqueues nothing, and
+ * m2_last_error() (thread-local) describes the failure. A failed launch
+ * returns M2_ERR_HIP. Device-side faults surface at the caller's next
+ * synchronisation. Slot ids live in device memory and cannot be checked on the
+ * host: a session whose slot id is outside [0, n_slots) gets NaN outputs and
+ * touches no state; slot ids within one call must be distinct (not checked).
+ */
+#ifndef M2_H
+#define M2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define M2_ABI_VERSION 1
+
+typedef enum {
+  M2_OK = 0,
+  M2_ERR_NULL = -1,         /* a required pointer or handle is NULL */
+  M2_ERR_SHAPE = -2,        /* dimensions inconsistent or unsupported */
+  M2_ERR_DTYPE = -3,        /* unknown weight type */
+  M2_ERR_ALIGN = -4,        /* a device pointer is not 16-byte aligned */
+  M2_ERR_WORKSPACE = -5,    /* ws_bytes smaller than the *_workspace size, or ws NULL */
+  M2_ERR_SLOT = -6,         /* batch larger than the state's slot count */
+  M2_ERR_UNSUPPORTED = -7,  /* valid but not implemented combination */
+  M2_ERR_HIP = -8           /* HIP runtime error (message carries the HIP error string) */
+} m2_status;
+
+/* Storage of the two projection matrices. */
+typedef enum {
+  M2_W_F32 = 0,             /* float32 */
+  M2_W_BF16 = 1,            /* bfloat16 */
+  M2_W_INT8G = 2            /* int8, symmetric, one fp16 scale per (row, q_group columns) */
+} m2_wtype;
+
+/* flags */
+enum { M2_RESIDUAL = 1 };   /* y = x + mixer(x); y may alias x */
+
+typedef struct {
+  int32_t d_model;          /* model width (K of in_proj); multiple of 16 */
+  int32_t n_heads;          /* H */
+  int32_t head_dim;         /* P; d_inner = H * P */
+  int32_t d_state;          /* N */
+  int32_t n_groups;         /* G: B/C groups; H % G == 0; head h uses group h / (H/G) */
+  int32_t d_conv;           /* causal conv width, 2..8 */
+  int32_t norm_group;       /* channels per RMS group; 0 means d_inner / n_groups */
+  float norm_eps;           /* RMSNorm epsilon */
+  int32_t wtype;            /* m2_wtype */
+  int32_t q_group;          /* columns per int8 scale (M2_W_INT8G); multiple of 16 */
+  float q_gamma_in;         /* per-tensor multiplier applied to int8 in_proj results (1 = none) */
+  float q_gamma_out;        /* per-tensor multiplier applied to int8 out_proj results */
+} m2_config;
+
+/* Layer parameters, all device pointers, 16-byte aligned, row-major. */
+typedef struct {
+  const void *w_in;         /* [d_in_proj][d_model], d_in_proj = 2 d_inner + 2 G N + H;
+                               rows [z: d_inner | x: d_inner | B: G N | C: G N | dt: H] */
+  const void *s_in;         /* fp16 [d_in_proj][d_model / q_group] (int8 only, else NULL) */
+  const void *w_out;        /* [d_model][d_inner] */
+  const void *s_out;        /* fp16 [d_model][d_inner / q_group] (int8 only, else NULL) */
+  const float *conv_w;      /* [conv_dim][d_conv], conv_dim = d_inner + 2 G N; tap d_conv-1 = newest */
+  const float *conv_b;      /* [conv_dim] */
+  const float *dt_bias;     /* [H] */
+  const float *A_log;       /* [H]: A = -exp(A_log) */
+  const float *D;           /* [H] */
+  const float *norm_w;      /* [d_inner] */
+} m2_weights;
+
+typedef struct m2_layer_s *m2_layer;  /* borrows the m2_weights pointers; immutable */
+typedef struct m2_state_s *m2_state;  /* borrows the ssm and conv buffers */
+
+/* Version of this ABI (M2_ABI_VERSION). */
+int m2_abi_version(void);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *m2_last_error(void);
+
+/* Validate cfg and w and create a layer handle (host memory only; no HIP call). */
+int m2_layer_create(const m2_config *cfg, const m2_weights *w, m2_layer *out);
+void m2_layer_destroy(m2_layer layer);
+
+/* Bytes of the per-layer state buffers for n_slots sessions:
+ *   ssm  fp32 [n_slots][H][P][N]           (N contiguous)
+ *   conv fp32 [n_slots][d_conv-1][conv_dim] (oldest raw input first) */
+int m2_state_sizes(const m2_config *cfg, int32_t n_slots, size_t *ssm_bytes, size_t *conv_bytes);
+
+/* Wrap caller-owned ssm / conv buffers (sizes from m2_state_sizes) as a state handle. */
+int m2_state_create(m2_layer layer, int32_t n_slots, float *ssm, float *conv, m2_state *out);
+void m2_state_destroy(m2_state st);
+
+/* Zero the state and conv cache of the n slots listed in slot_ids (device int32[n]);
+ * slot_ids == NULL zeroes every slot (n ignored). Session rollover. */
+int m2_state_zero(m2_state st, const int32_t *slot_ids, int32_t n, void *stream);
+
+/* Workspace bytes m2_step needs for `batch` sessions. */
+size_t m2_step_workspace(m2_layer layer, int32_t batch);
+
+/* One decode step for `batch` sessions: x, y fp32 [batch][d_model]; session b
+ * uses state slot slot_ids[b] (device int32[batch]) or slot b if slot_ids is
+ * NULL. Updates those slots' ssm and conv state in place. flags: M2_RESIDUAL.
+ * ws: device workspace of at least m2_step_workspace(layer, batch) bytes. */
+int m2_step(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
+            const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes m2_prefill needs. */
+size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk);
+
+/* Prefill `seqlen` tokens for `batch` sessions with the chunked SSD scan
+ * (chunk tokens per chunk, a multiple of 16 in [16, 256]; the last chunk may be
+ * partial). x, y fp32 [batch][seqlen][d_model]. Starts from each slot's current
+ * state and conv cache and leaves them as seqlen calls of m2_step would. */
+int m2_prefill(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
+               int32_t seqlen, int32_t chunk, const int32_t *slot_ids, int32_t flags, void *ws,
+               size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -69,8 +69,10 @@ static void dequant_row(const orc_cfg *c, const void *w, const uint16_t *s, int6
   } else {
     const int8_t *p = (const int8_t *)w + row * K;
     const int64_t ng = K / c->q_group;
-    for (int64_t k = 0; k < K; ++k)
-      dst[k] = (double)p[k] * orc_fp16_to_double(s[row * ng + k / c->q_group]) * gamma;
+    for (int64_t j = 0; j < ng; ++j) {            /* one scale per q_group columns */
+      const double sj = orc_fp16_to_double(s[row * ng + j]);
+      for (int64_t k = j * c->q_group; k < (j + 1) * c->q_group; ++k) dst[k] = (double)p[k] * sj * gamma;
+    }
   }
 }
 

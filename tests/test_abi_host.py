@@ -1,0 +1,130 @@
+"""Host-side checks of libm2.so that need no GPU: the library loads, exports every
+function include/m2.h declares, and rejects bad arguments with the documented
+status before anything is enqueued (so no call below reaches the device)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+m2 = pytest.importorskip("full_duplex_speech_mamba2_amd.m2",
+                         reason="libm2.so not built (run __graft_entry__.build())")
+from full_duplex_speech_mamba2_amd import synth  # noqa: E402
+
+FAKE = 0x10000   # a 16-byte aligned non-null address; validation never dereferences it
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "m2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(m2_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "m2_step" in names and "m2_prefill" in names and len(names) >= 12
+    lib = C.CDLL(m2.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_single_hip_runtime_mapped():
+    maps = open("/proc/self/maps").read()
+    runtimes = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(runtimes) == 1, runtimes
+
+
+def test_abi_version():
+    assert m2.abi_version() == 1
+
+
+def fake_weights(int8=False):
+    w = m2.Weights(*([FAKE] * 10))
+    if not int8:
+        w.s_in = None
+        w.s_out = None
+    return w
+
+
+def create(dims, w=None):
+    cfg = m2.config_from_dims(dims)
+    h = C.c_void_p()
+    rc = m2.lib().m2_layer_create(C.byref(cfg), C.byref(w or fake_weights(dims.wtype == "int8g")), C.byref(h))
+    return rc, h
+
+
+GOOD = synth.MixerDims(d_model=256, n_heads=8, head_dim=32, d_state=16, n_groups=2, wtype="bf16")
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(n_heads=6, n_groups=4), m2.M2_ERR_SHAPE),          # H % G != 0
+    (dict(d_model=264), m2.M2_ERR_SHAPE),                    # d_model not a multiple of 16
+    (dict(d_state=24), m2.M2_ERR_SHAPE),                     # N not a power of two
+    (dict(d_conv=1), m2.M2_ERR_SHAPE),
+    (dict(norm_group=100), m2.M2_ERR_SHAPE),                 # does not divide d_inner
+    (dict(wtype="int8g", q_group=100), m2.M2_ERR_SHAPE),     # not a multiple of 16
+    (dict(wtype="int8g", q_group=48), m2.M2_ERR_SHAPE),      # does not divide K
+])
+def test_layer_create_rejects_bad_configs(bad, status):
+    rc, h = create(GOOD.replace(**bad))
+    assert rc == status and not h.value
+    assert m2.lib().m2_last_error()
+
+
+def test_layer_create_rejects_nulls_alignment_and_dtype():
+    w = fake_weights()
+    w.w_out = None
+    assert create(GOOD, w)[0] == m2.M2_ERR_NULL
+    w = fake_weights()
+    w.w_in = FAKE + 8
+    assert create(GOOD, w)[0] == m2.M2_ERR_ALIGN
+    assert create(GOOD.replace(wtype="int8g"), fake_weights(False))[0] == m2.M2_ERR_NULL
+    cfg = m2.config_from_dims(GOOD)
+    cfg.wtype = 9
+    h = C.c_void_p()
+    assert m2.lib().m2_layer_create(C.byref(cfg), C.byref(fake_weights()), C.byref(h)) == m2.M2_ERR_DTYPE
+
+
+def test_state_sizes_and_workspace():
+    cfg = m2.config_from_dims(synth.NINE_B)
+    a, b = C.c_size_t(), C.c_size_t()
+    assert m2.lib().m2_state_sizes(C.byref(cfg), 32, C.byref(a), C.byref(b)) == 0
+    assert a.value == 32 * 128 * 80 * 128 * 4
+    assert b.value == 32 * 3 * 12288 * 4
+    rc, h = create(synth.NINE_B)
+    assert rc == 0
+    ws1 = m2.lib().m2_step_workspace(h, 1)
+    ws32 = m2.lib().m2_step_workspace(h, 32)
+    assert ws1 >= 4 * (22656 + 10240) and ws32 >= 32 * 4 * (22656 + 10240)
+    assert m2.lib().m2_step_workspace(h, 0) == 0
+    m2.lib().m2_layer_destroy(h)
+
+
+def test_step_rejects_bad_calls_without_launching():
+    L = m2.lib()
+    rc, h = create(GOOD)
+    assert rc == 0
+    st = C.c_void_p()
+    assert L.m2_state_create(h, 2, FAKE, FAKE, C.byref(st)) == 0
+    need = L.m2_step_workspace(h, 2)
+    assert L.m2_step(None, st, FAKE, FAKE * 2, 1, None, 0, FAKE, need, None) == m2.M2_ERR_NULL
+    assert L.m2_step(h, st, None, FAKE * 2, 1, None, 0, FAKE, need, None) == m2.M2_ERR_NULL
+    assert L.m2_step(h, st, FAKE, FAKE * 2, 3, None, 0, FAKE, need, None) == m2.M2_ERR_SLOT
+    assert L.m2_step(h, st, FAKE, FAKE * 2, 0, None, 0, FAKE, need, None) == m2.M2_ERR_SHAPE
+    assert L.m2_step(h, st, FAKE, FAKE * 2, 2, None, 0, FAKE, need - 1, None) == m2.M2_ERR_WORKSPACE
+    assert L.m2_step(h, st, FAKE, FAKE * 2, 2, None, 0, None, need, None) == m2.M2_ERR_WORKSPACE
+    assert L.m2_step(h, st, FAKE + 4, FAKE * 2, 2, None, 0, FAKE, need, None) == m2.M2_ERR_ALIGN
+    assert L.m2_step(h, st, FAKE, FAKE, 2, None, 0, FAKE, need, None) == m2.M2_ERR_SHAPE   # alias w/o residual
+    assert L.m2_step(h, st, FAKE, FAKE * 2, 2, None, 4, FAKE, need, None) == m2.M2_ERR_UNSUPPORTED
+    assert L.m2_step(h, st, FAKE, FAKE * 2, 2, None, 0, FAKE, 1, None) == m2.M2_ERR_WORKSPACE
+    assert b"workspace" in L.m2_last_error()
+    pw = L.m2_prefill_workspace(h, 2, 100, 64)
+    assert L.m2_prefill(h, st, FAKE, FAKE * 2, 2, 100, 40, None, 0, FAKE, pw, None) == m2.M2_ERR_SHAPE
+    assert L.m2_prefill(h, st, FAKE, FAKE * 2, 2, 100, 512, None, 0, FAKE, pw, None) == m2.M2_ERR_SHAPE
+    assert L.m2_prefill(h, st, FAKE, FAKE * 2, 3, 100, 64, None, 0, FAKE, pw, None) == m2.M2_ERR_SLOT
+    assert L.m2_state_zero(None, None, 0, None) == m2.M2_ERR_NULL
+    assert L.m2_state_zero(st, FAKE, 3, None) == m2.M2_ERR_SLOT
+    L.m2_state_destroy(st)
+    L.m2_layer_destroy(h)

@@ -1,0 +1,139 @@
+"""Parity of the HIP decode step (m2_step through the C ABI) with the fp64 oracle."""
+import numpy as np
+import pytest
+
+from full_duplex_speech_mamba2_amd import synth
+from parity import (TOL_OUT, TOL_STATE, e_conv, e_out, e_state, gpu_decode, oracle_decode)
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(tag, eo, es, ec):
+    print("[parity] %s e_out=%.3e e_state=%.3e e_conv=%.3e" % (tag, eo, es, ec), flush=True)
+
+
+def _check(tag, dims, w, xs, ssm0, conv0, slot_ids=None, residual=False, sessions=None):
+    yg, sg, cg = gpu_decode(dims, w, xs, ssm0, conv0, slot_ids=slot_ids, residual=residual)
+    yo, so, co = oracle_decode(dims, w, xs, ssm0, conv0, slot_ids=slot_ids, residual=residual,
+                               sessions=sessions)
+    if sessions is not None:
+        used = np.asarray(sessions) if slot_ids is None else np.asarray(slot_ids)[sessions]
+        yg = yg[:, sessions]
+    else:
+        used = np.arange(xs.shape[1]) if slot_ids is None else np.asarray(slot_ids)
+    eo, es, ec = e_out(yg, yo), e_state(sg[used], so[used]), e_conv(cg[used], co[used])
+    _report(tag, eo, es, ec)
+    assert eo <= TOL_OUT and es <= TOL_STATE and ec <= TOL_STATE
+    return yg, sg, cg
+
+
+def test_tiny_fp32_16_steps():
+    wl = synth.workload(0)
+    w = synth.make_layer_weights(wl.dims, wl.weight_seed)
+    xs = synth.make_inputs(wl.dims, wl.seed, wl.steps, wl.batch)
+    ssm0, conv0 = synth.make_state(wl.dims, wl.seed, wl.batch, wl.state_var)
+    _check("tiny", wl.dims, w, xs, ssm0, conv0)
+
+
+RAGGED = synth.MixerDims(d_model=272, n_heads=6, head_dim=24, d_state=32, n_groups=2, d_conv=4)
+
+
+@pytest.mark.parametrize("wtype", ["f32", "bf16", "int8g"])
+@pytest.mark.parametrize("variant", ["plain", "slots_residual", "norm_all", "conv2", "conv5_n64"])
+def test_ragged_shapes(wtype, variant):
+    dims = RAGGED.replace(wtype=wtype, q_group=16, q_gamma_in=0.0625, q_gamma_out=0.1)
+    B, slots, n_slots, residual, steps = 3, None, 3, False, 9
+    if variant == "slots_residual":
+        n_slots, slots, residual = 5, np.array([4, 0, 2], np.int32), True
+    elif variant == "norm_all":
+        dims = dims.replace(norm_group=dims.d_inner)
+    elif variant == "conv2":
+        dims = dims.replace(d_conv=2, norm_group=48)
+    elif variant == "conv5_n64":
+        dims = dims.replace(d_conv=5, d_state=64, n_groups=3, norm_group=24)
+    w = synth.make_layer_weights(dims, 31)
+    xs = synth.make_inputs(dims, 32, steps, B)
+    ssm0, conv0 = synth.make_state(dims, 33, n_slots, 0.1)
+    _check("ragged-%s-%s" % (wtype, variant), dims, w, xs, ssm0, conv0, slot_ids=slots, residual=residual)
+
+
+@pytest.mark.parametrize("batch", [1, 2, 5, 8, 17])
+def test_batch_sizes_bf16(batch):
+    dims = synth.MixerDims(d_model=512, n_heads=16, head_dim=32, d_state=64, n_groups=4, wtype="bf16")
+    w = synth.make_layer_weights(dims, 41)
+    xs = synth.make_inputs(dims, 42, 5, batch)
+    ssm0, conv0 = synth.make_state(dims, 43, batch, 0.1)
+    _check("batch%d" % batch, dims, w, xs, ssm0, conv0)
+
+
+def test_dt_zero_keeps_state_and_A_to_minus_inf_resets_it():
+    import torch
+    from full_duplex_speech_mamba2_amd import m2
+    dims = synth.MixerDims(d_model=256, n_heads=8, head_dim=32, d_state=16, n_groups=2, wtype="bf16")
+    w = synth.make_layer_weights(dims, 51)
+    w["dt_bias"] = np.full(dims.n_heads, -1e4, np.float32)       # softplus underflows to 0
+    ssm0, conv0 = synth.make_state(dims, 52, 1, 0.1)
+    lay = m2.Layer(dims, w)
+    st = m2.State(lay, 1, torch.from_numpy(ssm0).cuda(), torch.from_numpy(conv0).cuda())
+    x = torch.from_numpy(synth.make_inputs(dims, 53, 1, 1)[0]).cuda()
+    m2.step(lay, st, x)
+    torch.cuda.synchronize()
+    assert np.array_equal(st.ssm.cpu().numpy(), ssm0)             # bitwise unchanged
+
+    w2 = synth.make_layer_weights(dims, 51)
+    w2["A_log"] = np.full(dims.n_heads, np.log(1e30), np.float32)  # exp(dt A) = 0
+    lay2 = m2.Layer(dims, w2)
+    st2 = m2.State(lay2, 1, torch.from_numpy(ssm0).cuda(), torch.from_numpy(conv0).cuda())
+    m2.step(lay2, st2, x)
+    torch.cuda.synchronize()
+    lo = __import__("oracle").Layer(dims, w2)
+    so, co = lo.new_state(1, ssm0, conv0)
+    _, tr = lo.step(so, co, x.cpu().numpy().astype(np.float64), trace=True)
+    # the reset state is dt x B^T: no trace of the random initial state remains
+    assert e_state(st2.ssm.cpu().numpy(), so) <= 1e-5
+
+
+def test_run_twice_bitwise_equal():
+    dims = synth.MixerDims(d_model=512, n_heads=16, head_dim=32, d_state=64, n_groups=4, wtype="bf16")
+    w = synth.make_layer_weights(dims, 61)
+    xs = synth.make_inputs(dims, 62, 4, 6)
+    ssm0, conv0 = synth.make_state(dims, 63, 6, 0.1)
+    a = gpu_decode(dims, w, xs, ssm0, conv0)
+    b = gpu_decode(dims, w, xs, ssm0, conv0)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_out_of_range_slot_gives_nan_and_touches_nothing():
+    import torch
+    from full_duplex_speech_mamba2_amd import m2
+    dims = synth.MixerDims(d_model=256, n_heads=8, head_dim=32, d_state=16, n_groups=2, wtype="bf16")
+    w = synth.make_layer_weights(dims, 71)
+    ssm0, conv0 = synth.make_state(dims, 72, 2, 0.1)
+    lay = m2.Layer(dims, w)
+    st = m2.State(lay, 2, torch.from_numpy(ssm0).cuda(), torch.from_numpy(conv0).cuda())
+    x = torch.from_numpy(synth.make_inputs(dims, 73, 1, 2)[0]).cuda()
+    y = m2.step(lay, st, x, slot_ids=torch.tensor([1, 7], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    assert np.all(np.isfinite(yh[0])) and np.all(np.isnan(yh[1]))
+    assert np.array_equal(st.ssm.cpu().numpy()[0], ssm0[0])
+    assert np.array_equal(st.conv.cpu().numpy()[0], conv0[0])
+
+
+def test_state_zero_selected_slots():
+    import torch
+    from full_duplex_speech_mamba2_amd import m2
+    dims = synth.MixerDims(d_model=256, n_heads=8, head_dim=32, d_state=16, n_groups=2, wtype="bf16")
+    w = synth.make_layer_weights(dims, 81)
+    ssm0, conv0 = synth.make_state(dims, 82, 4, 0.1)
+    lay = m2.Layer(dims, w)
+    st = m2.State(lay, 4, torch.from_numpy(ssm0).cuda(), torch.from_numpy(conv0).cuda())
+    st.zero(torch.tensor([2, 0], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    s, c = st.ssm.cpu().numpy(), st.conv.cpu().numpy()
+    assert np.all(s[[0, 2]] == 0) and np.all(c[[0, 2]] == 0)
+    assert np.array_equal(s[[1, 3]], ssm0[[1, 3]]) and np.array_equal(c[[1, 3]], conv0[[1, 3]])
+    st.zero()
+    torch.cuda.synchronize()
+    assert not st.ssm.any() and not st.conv.any()
