@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Decode throughput of the 9B-shaped Mamba-2 mixer layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+
+One step = one m2_step call: in_proj GEMV (+conv, dt), SSD state update and
+readout (+gate), RMSNorm + out_proj GEMV, for every session of the batch, on
+seeded synthetic inputs already resident in HBM. The default workload is the
+single-session decode of a 9B-shaped layer (d_model 4480, 128 heads x 80,
+d_state 128, 8 groups, bf16 weights, fp32 state), 750 frames of 80 ms.
+
+The layer's weights are held in `--copies` identical device copies used in
+turn (default 2, 590 MB), so the 256 MB last-level cache cannot serve a step
+from the previous step's weights, as in a real stack where every other layer's
+weights stream through in between.
+
+Prints one JSON line. Besides steps/s it reports the step's algorithmic HBM
+bytes and bandwidth, per-kernel durations measured with HIP events on the
+stream the kernels run on, the dominant kernel's roofline, a parity check of
+the first steps against the CPU oracle, and that oracle's own speed on a
+bounded sample (cpu_baseline: a baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "Mamba-2 decode steps/s + achieved HBM GB/s (% peak), 9B-shaped layer"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", type=int, default=1, help="decode workload index (1, 2 or 3)")
+    ap.add_argument("--copies", type=int, default=2, help="identical weight copies used in turn")
+    ap.add_argument("--no-graph", action="store_true", help="time plain launches only")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity")
+    ap.add_argument("--prof-steps", type=int, default=200, help="steps of the per-kernel event pass")
+    return ap.parse_args()
+
+
+def wbytes(dims):
+    return {"f32": 4, "bf16": 2, "int8g": 1}[dims.wtype]
+
+
+def kernel_bytes(dims, B):
+    """Algorithmic HBM bytes per launch of each decode kernel, and of the whole step."""
+    d = dims
+    f = 4
+    sc_in = d.d_in_proj * (d.d_model // d.q_group) * 2 if d.wtype == "int8g" else 0
+    sc_out = d.d_model * (d.d_inner // d.q_group) * 2 if d.wtype == "int8g" else 0
+    w_in = d.d_in_proj * d.d_model * wbytes(d) + sc_in
+    w_out = d.d_model * d.d_inner * wbytes(d) + sc_out
+    state = 2 * B * d.n_heads * d.head_dim * d.d_state * f
+    cache = 2 * B * (d.d_conv - 1) * d.conv_dim * f
+    conv_par = d.conv_dim * (d.d_conv + 1) * f
+    head_par = 3 * d.n_heads * f
+    zx = B * d.d_in_proj * f
+    v = B * d.d_inner * f
+    io = B * d.d_model * f
+    gemv_in = w_in + io + zx + cache + conv_par + d.n_heads * f
+    ssd = state + B * (2 * d.d_inner + 2 * d.n_groups * d.d_state + d.n_heads) * f + 2 * d.n_heads * f + v
+    gemv_out = w_out + v + d.d_inner * f + io
+    step = w_in + w_out + state + cache + conv_par + head_par + d.d_inner * f + 2 * io
+    return {"gemv_in": gemv_in, "ssd_step": ssd, "gemv_out": gemv_out, "step": step}
+
+
+def traffic_for(kernel_name, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on the
+    current kernel source (the summary stores the source hash); else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel_name, workload))
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+            return None
+        return float(rec["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from full_duplex_speech_mamba2_amd import m2, synth
+
+    wl = synth.workload(args.config)
+    if wl.prefill or wl.layers != 1:
+        print("bench.py times single-layer decode workloads (1 or 2)", file=sys.stderr)
+        sys.exit(2)
+    dims, B = wl.dims, wl.batch
+    dev = torch.device("cuda:0")
+    print("[bench] workload %s: generating inputs" % wl.name, file=sys.stderr, flush=True)
+    w = synth.make_layer_weights(dims, wl.weight_seed)
+    xs_np = synth.make_inputs(dims, wl.seed, wl.steps, B)
+    ssm0, conv0 = synth.make_state(dims, wl.seed, B, wl.state_var)
+
+    layers = [m2.Layer(dims, w, dev) for _ in range(max(1, args.copies))]
+    st = m2.State(layers[0], B, torch.from_numpy(ssm0).to(dev), torch.from_numpy(conv0).to(dev))
+    xs = torch.from_numpy(xs_np).to(dev)
+    ys = torch.empty_like(xs)
+    ws = layers[0].workspace("step", B)
+    nx = xs.shape[0]
+    nl = len(layers)
+
+    def run(t0, n):
+        for t in range(t0, t0 + n):
+            m2.step(layers[t % nl], st, xs[t % nx], ys[t % nx], ws=ws)
+
+    torch.cuda.synchronize()
+    run(0, args.warmup)
+    torch.cuda.synchronize()
+
+    # timed region 1: plain launches on torch's current stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    run(args.warmup, args.steps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / args.steps
+
+    # timed region 2: the same steps captured once into a HIP graph and replayed
+    ms_graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                run(0, args.steps)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()                      # warm replay
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / args.steps
+        del g
+
+    ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
+    steps_per_s = 1000.0 / ms
+    kb = kernel_bytes(dims, B)
+
+    # per-kernel durations: HIP events recorded between the step's kernels on the same stream
+    kp = max(10, args.prof_steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(kp)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for t in range(kp):
+        m2.step_timed(layers[t % nl], st, xs[t % nx], ys[t % nx], evs[t], ws=ws)
+    torch.cuda.synchronize()
+    names = ["gemv_in", "ssd_step", "gemv_out"]
+    dur_us = {n: 1000.0 * float(np.mean([evs[t][i].elapsed_time(evs[t][i + 1]) for t in range(kp)]))
+              for i, n in enumerate(names)}
+    dom = max(names, key=lambda n: kb[n])
+    achieved = kb[dom] / (dur_us[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_for(dom, wl.name),
+                "algorithmic_bytes": kb[dom], "avg_duration_us": round(dur_us[dom], 2)}
+
+    out = {
+        "metric": METRIC, "value": round(steps_per_s, 1), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "d_model": dims.d_model, "n_heads": dims.n_heads,
+                   "head_dim": dims.head_dim, "d_state": dims.d_state, "n_groups": dims.n_groups,
+                   "d_conv": dims.d_conv, "batch": B, "weight_dtype": dims.wtype,
+                   "state_dtype": "f32", "weight_copies": nl,
+                   "timing": "graph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"},
+        "achieved_GBps": round(kb["step"] * steps_per_s / 1e9, 1),
+        "hbm_peak_frac": round(kb["step"] * steps_per_s / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_algorithmic_bytes": kb["step"],
+        "session_tokens_per_s": round(B * steps_per_s, 1),
+        "ms_per_step_eager": round(ms_eager, 5),
+        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
+        "kernel_us": {n: round(v, 2) for n, v in dur_us.items()},
+        "roofline": roofline,
+        "cpu_baseline": None,
+        "parity": None,
+    }
+
+    if not args.no_cpu:
+        out["cpu_baseline"], out["parity"] = cpu_baseline_and_parity(args, wl, w, xs_np, ssm0, conv0)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_and_parity(args, wl, w, xs_np, ssm0, conv0):
+    """Time the oracle on the first steps of the workload (bounded by --cpu-seconds) and compare
+    the GPU path's outputs for those steps, from the same initial state, with it."""
+    import numpy as np
+    import torch
+    import oracle
+    from full_duplex_speech_mamba2_amd import m2
+    from full_duplex_speech_mamba2_amd.synth import workload  # noqa: F401
+
+    dims, B = wl.dims, wl.batch
+    lay = oracle.Layer(dims, w)
+    so, co = lay.new_state(B, ssm0, conv0)
+    ys_o = []
+    t0 = time.perf_counter()
+    n = 0
+    while n < xs_np.shape[0] and (n < 2 or time.perf_counter() - t0 < args.cpu_seconds):
+        ys_o.append(lay.step(so, co, xs_np[n]))
+        n += 1
+    wall = time.perf_counter() - t0
+    base = {"value": round(n / wall, 3), "unit": "steps/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "first %d decode steps of %s (batch %d), fp64 C oracle, %.1f s wall"
+                      % (n, wl.name, B, wall)}
+
+    gl = m2.Layer(dims, w)
+    gs = m2.State(gl, B, torch.from_numpy(ssm0).cuda(), torch.from_numpy(conv0).cuda())
+    xd = torch.from_numpy(xs_np[:n]).cuda()
+    yd = torch.empty_like(xd)
+    for t in range(n):
+        m2.step(gl, gs, xd[t], yd[t])
+    torch.cuda.synchronize()
+    yg = yd.cpu().numpy().astype(np.float64)
+    yo = np.array(ys_o)
+    e_out = float(np.max(np.max(np.abs(yg - yo), axis=-1) / np.max(np.abs(yo), axis=-1)))
+    sg = gs.ssm.cpu().numpy().astype(np.float64)
+    floor = 1e-6 * float(np.max(np.abs(so)))
+    e_state = float(np.max(np.max(np.abs(sg - so), axis=(-2, -1)) /
+                           np.maximum(np.max(np.abs(so), axis=(-2, -1)), floor)))
+    return base, {"steps": n, "e_out": e_out, "e_state": e_state, "tol_out": 2e-3, "tol_state": 1e-3,
+                  "ok": bool(e_out <= 2e-3 and e_state <= 1e-3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -402,8 +402,14 @@ StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base) {
 }
 
 hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x, float *y, int batch,
-                       const int32_t *slots, int flags, const StepWs &ws, hipStream_t stream) {
+                       const int32_t *slots, int flags, const StepWs &ws, hipStream_t stream,
+                       hipEvent_t const *events) {
   const m2_config &c = L.cfg;
+  auto mark = [&](int i) -> hipError_t {
+    return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return e;
   // 1. in_proj + conv + dt
   GemvArgs gi{};
   gi.W = L.w.w_in;
@@ -425,7 +431,8 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   gi.conv_cache = S.conv;
   gi.slots = slots;
   gi.n_slots = S.n_slots;
-  hipError_t e = dispatch_wt<PRO_PLAIN, EPI_INPROJ, 1>(c.wtype, gi, stream);
+  e = dispatch_wt<PRO_PLAIN, EPI_INPROJ, 1>(c.wtype, gi, stream);
+  if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return e;
 
   // 2. SSD update + readout + gate + sums of squares
@@ -451,6 +458,7 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   sa.n_slots = S.n_slots;
   hipLaunchKernelGGL(ssd_step_kernel, dim3(c.n_heads * L.psplit, batch), dim3(kThreads), 0, stream, sa);
   e = hipGetLastError();
+  if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return e;
 
   // 3. RMSNorm + out_proj (+ residual)
@@ -474,7 +482,9 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   go.resid = (flags & M2_RESIDUAL) ? x : nullptr;
   go.slots = slots;
   go.n_slots = S.n_slots;
-  return dispatch_wt<PRO_NORM, EPI_OUT, 4>(c.wtype, go, stream);
+  e = dispatch_wt<PRO_NORM, EPI_OUT, 4>(c.wtype, go, stream);
+  if (e == hipSuccess) e = mark(3);
+  return e;
 }
 
 hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, hipStream_t stream) {

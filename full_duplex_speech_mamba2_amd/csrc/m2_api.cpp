@@ -172,8 +172,9 @@ size_t m2_step_workspace(m2_layer layer, int32_t batch) {
   return m2d::step_ws_layout(*layer, batch, nullptr).bytes;
 }
 
-int m2_step(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
-            const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream) {
+static int step_impl(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
+                     const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream,
+                     void *const *events) {
   if (!layer || !st) return fail(M2_ERR_NULL, "layer or state is NULL");
   if (st->layer != layer) {
     const m2_config &a = st->layer->cfg, &b = layer->cfg;
@@ -194,9 +195,21 @@ int m2_step(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch
   if (!aligned16(ws)) return fail(M2_ERR_ALIGN, "workspace must be 16-byte aligned");
   m2d::StepWs W = m2d::step_ws_layout(*layer, batch, ws);
   hipError_t e = m2d::launch_step(*layer, *st, x, y, batch, slot_ids, flags, W,
-                                  static_cast<hipStream_t>(stream));
+                                  static_cast<hipStream_t>(stream),
+                                  reinterpret_cast<hipEvent_t const *>(events));
   if (e != hipSuccess) return fail(M2_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+int m2_step(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
+            const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  return step_impl(layer, st, x, y, batch, slot_ids, flags, ws, ws_bytes, stream, nullptr);
+}
+
+int m2_step_timed(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
+                  const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream,
+                  void *const *events) {
+  return step_impl(layer, st, x, y, batch, slot_ids, flags, ws, ws_bytes, stream, events);
 }
 
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk) {

@@ -44,7 +44,8 @@ struct StepWs {
 StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base);
 
 hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x, float *y, int batch,
-                       const int32_t *slots, int flags, const StepWs &ws, hipStream_t stream);
+                       const int32_t *slots, int flags, const StepWs &ws, hipStream_t stream,
+                       hipEvent_t const *events = nullptr);
 
 hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, hipStream_t stream);
 

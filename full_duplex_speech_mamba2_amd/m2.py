@@ -57,11 +57,12 @@ _lib.m2_state_zero.argtypes = [_P, _P, _i32, _P]
 _lib.m2_step_workspace.argtypes = [_P, _i32]
 _lib.m2_step_workspace.restype = C.c_size_t
 _lib.m2_step.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P]
+_lib.m2_step_timed.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P, _P]
 _lib.m2_prefill_workspace.argtypes = [_P, _i32, _i32, _i32]
 _lib.m2_prefill_workspace.restype = C.c_size_t
 _lib.m2_prefill.argtypes = [_P, _P, _P, _P, _i32, _i32, _i32, _P, _i32, _P, C.c_size_t, _P]
 for _f in ("m2_layer_create", "m2_state_sizes", "m2_state_create", "m2_state_zero", "m2_step",
-           "m2_prefill"):
+           "m2_step_timed", "m2_prefill"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -203,6 +204,22 @@ def step(layer: Layer, state: State, x: torch.Tensor, y: Optional[torch.Tensor] 
         ws = layer.workspace("step", B)
     _check(_lib.m2_step(layer.handle, state.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids),
                         M2_RESIDUAL if residual else 0, _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def step_timed(layer: Layer, state: State, x: torch.Tensor, y: torch.Tensor, events,
+               slot_ids: Optional[torch.Tensor] = None, residual: bool = False,
+               ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """step() that records the four torch.cuda.Event objects in `events` around its three
+    kernels (each event must have been recorded once so that its HIP event exists)."""
+    B = x.shape[0]
+    _act(x, (B, layer.dims.d_model))
+    _act(y, x.shape)
+    if ws is None:
+        ws = layer.workspace("step", B)
+    ev = (C.c_void_p * 4)(*[e.cuda_event for e in events])
+    _check(_lib.m2_step_timed(layer.handle, state.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids),
+                              M2_RESIDUAL if residual else 0, _ptr(ws), ws.numel(), _stream(stream), ev))
     return y
 
 
