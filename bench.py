@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity")
     ap.add_argument("--prof-steps", type=int, default=200, help="steps of the per-kernel event pass")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run 3 device-to-device copies of MIB MiB (the known-size kernel that "
+                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -73,7 +76,37 @@ def kernel_bytes(dims, B):
     ssd = state + B * (2 * d.d_inner + 2 * d.n_groups * d.d_state + d.n_heads) * f + 2 * d.n_heads * f + v
     gemv_out = w_out + v + d.d_inner * f + io
     step = w_in + w_out + state + cache + conv_par + head_par + d.d_inner * f + 2 * io
-    return {"gemv_in": gemv_in, "ssd_step": ssd, "gemv_out": gemv_out, "step": step}
+    return {"gemv_in": gemv_in, "ssd_step": ssd, "gemv_out": gemv_out, "ssd_out": ssd + gemv_out,
+            "step": step}
+
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def hip_runtime():
+    """The HIP runtime torch has already mapped (same soname), for event timing."""
+    import ctypes as C
+    hip = C.CDLL("libamdhip64.so.7")
+    hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+    hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+    hip.hipEventDestroy.argtypes = [C.c_void_p]
+    return hip
+
+
+def hip_event(hip):
+    import ctypes as C
+    e = C.c_void_p()
+    if hip.hipEventCreateWithFlags(C.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+        raise RuntimeError("hipEventCreateWithFlags failed")
+    return e.value
+
+
+def hip_elapsed_ms(hip, a, b):
+    import ctypes as C
+    ms = C.c_float()
+    if hip.hipEventElapsedTime(C.byref(ms), a, b) != 0:
+        raise RuntimeError("hipEventElapsedTime failed")
+    return ms.value
 
 
 def traffic_for(kernel_name, workload):
@@ -110,6 +143,14 @@ def main():
         sys.exit(2)
     dims, B = wl.dims, wl.batch
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print("[bench] workload %s: generating inputs" % wl.name, file=sys.stderr, flush=True)
     w = synth.make_layer_weights(dims, wl.weight_seed)
     xs_np = synth.make_inputs(dims, wl.seed, wl.steps, B)
@@ -163,19 +204,22 @@ def main():
     steps_per_s = 1000.0 / ms
     kb = kernel_bytes(dims, B)
 
-    # per-kernel durations: HIP events recorded between the step's kernels on the same stream
+    # per-kernel durations: HIP events recorded between the step's kernels on the stream they
+    # run on; created without the system-scope fence so that a marker costs little
     kp = max(10, args.prof_steps)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(kp)]
-    for row in evs:
-        for e in row:
-            e.record()
+    hip = hip_runtime()
+    evs = [[hip_event(hip) for _ in range(4)] for _ in range(kp)]
     torch.cuda.synchronize()
     for t in range(kp):
         m2.step_timed(layers[t % nl], st, xs[t % nx], ys[t % nx], evs[t], ws=ws)
     torch.cuda.synchronize()
-    names = ["gemv_in", "ssd_step", "gemv_out"]
-    dur_us = {n: 1000.0 * float(np.mean([evs[t][i].elapsed_time(evs[t][i + 1]) for t in range(kp)]))
+    names = (["gemv_in", "ssd_step", "gemv_out"] if layers[0].step_kernel_count(B) == 3
+             else ["gemv_in", "ssd_out"])
+    dur_us = {n: 1000.0 * float(np.mean([hip_elapsed_ms(hip, evs[t][i], evs[t][i + 1]) for t in range(kp)]))
               for i, n in enumerate(names)}
+    for row in evs:
+        for e in row:
+            hip.hipEventDestroy(e)
     dom = max(names, key=lambda n: kb[n])
     achieved = kb[dom] / (dur_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,

@@ -6,9 +6,10 @@
 //             dt rows, the raw value for the z rows.
 //   ssd_step  per (session, head, row range): S = exp(dt A) S + dt x B^T and
 //             y = C.S + D x on the state tile held in registers (one read, one
-//             write), then v = y SiLU(z) and per-range sums of squares.
-//   gemv_out  RMS factors from the sums of squares, yn = v r norm_w staged into
-//             LDS, then out = W_out yn (+ residual).
+//             write), then v = y SiLU(z), written as v * norm_w, and per-range
+//             sums of squares of v.
+//   gemv_out  RMS factors from the sums of squares, yn = (v norm_w) r staged
+//             into LDS, then out = W_out yn (+ residual).
 //
 // The operation follows the Mamba-2 layer the backbone of the pages uses (page
 // "NemotronLabs VoiceChat 11B: GPTQ 3-bit LLM, MLX", introduction; page
@@ -17,6 +18,13 @@
 // matrices from HBM (GPTQ page, introduction: the LLM step is limited by
 // memory bandwidth), so the GEMVs are built around full 16-byte coalesced loads
 // with several loads in flight per lane; the rest is small.
+//
+// Two GEMV shapes:
+//   gemv_wave   batch <= 2: one wave per weight row, so every load instruction
+//               reads 1 KB of one row; the activations of the batch are staged
+//               whole into LDS after the first weight loads have been issued.
+//   gemv_tiled  any batch: 16-lane row groups, K split inside the workgroup,
+//               activations staged in K tiles for tiles of 4 sessions.
 #include <hip/hip_fp16.h>
 
 #include "m2_internal.h"
@@ -24,8 +32,11 @@
 namespace m2d {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
-constexpr int kLdsFloatsPerBatch = 12288;   // activation tile budget: 48 KB at batch tile 1
+constexpr int kNormF4PerThread = 5;          // gemv_wave out_proj: float4 activations held per thread (K <= 10240 at 512 threads)
+constexpr int kLdsFloatsPerBatch = 12288;   // tiled kernel: activation tile budget (48 KB at 1 session)
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -43,10 +54,15 @@ template <> struct WTraits<M2_W_F32> { static constexpr int EPC = 4; static cons
 template <> struct WTraits<M2_W_BF16> { static constexpr int EPC = 8; static constexpr int ESZ = 2; };
 template <> struct WTraits<M2_W_INT8G> { static constexpr int EPC = 16; static constexpr int ESZ = 1; };
 
-// Dot product of one 16-byte weight chunk with EPC consecutive fp32 activations.
-template <int WT> __device__ __forceinline__ float chunk_dot(const uint4 &w, const float *a);
+template <int NT> __device__ __forceinline__ u32x4 wload(const u32x4 *p) {
+  if (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
 
-template <> __device__ __forceinline__ float chunk_dot<M2_W_F32>(const uint4 &w, const float *a) {
+// Dot product of one 16-byte weight chunk with EPC consecutive fp32 activations.
+template <int WT> __device__ __forceinline__ float chunk_dot(const u32x4 &w, const float *a);
+
+template <> __device__ __forceinline__ float chunk_dot<M2_W_F32>(const u32x4 &w, const float *a) {
   const float4 x = *reinterpret_cast<const float4 *>(a);
   float s = __uint_as_float(w.x) * x.x;
   s = fmaf(__uint_as_float(w.y), x.y, s);
@@ -55,7 +71,7 @@ template <> __device__ __forceinline__ float chunk_dot<M2_W_F32>(const uint4 &w,
   return s;
 }
 
-template <> __device__ __forceinline__ float chunk_dot<M2_W_BF16>(const uint4 &w, const float *a) {
+template <> __device__ __forceinline__ float chunk_dot<M2_W_BF16>(const u32x4 &w, const float *a) {
   const float4 x0 = *reinterpret_cast<const float4 *>(a);
   const float4 x1 = *reinterpret_cast<const float4 *>(a + 4);
   float s = bf16_lo(w.x) * x0.x;
@@ -69,7 +85,7 @@ template <> __device__ __forceinline__ float chunk_dot<M2_W_BF16>(const uint4 &w
   return s;
 }
 
-template <> __device__ __forceinline__ float chunk_dot<M2_W_INT8G>(const uint4 &w, const float *a) {
+template <> __device__ __forceinline__ float chunk_dot<M2_W_INT8G>(const u32x4 &w, const float *a) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   float s = 0.0f;
 #pragma unroll
@@ -89,14 +105,14 @@ enum { EPI_INPROJ = 0, EPI_OUT = 1 };
 struct GemvArgs {
   const void *W;          // [rows][K]
   const __half *S;        // int8 scales [rows][K / q_group]
-  int rows, K, q_group;
+  int rows, K;
+  int q_shift;            // log2(q_group / EPC): chunk index -> scale column (int8 only)
   float gamma;
-  const float *act;       // [B][K]
-  int B, KT;              // sessions, activation K tile
-  // RMSNorm prologue (gemv_out)
+  const float *act;       // [B][K]: x (in_proj) or v * norm_w (out_proj)
+  int B, KT;              // sessions, activation K tile (tiled kernel)
+  // RMSNorm prologue (out_proj)
   const float *ss;        // [B][n_partials]
-  const float *norm_w;    // [K]
-  int ng, prange, n_partials, n_norm;
+  int ng, n_partials, n_norm;
   float eps;
   // in_proj epilogue
   float *zx;              // [B][zx_stride]
@@ -110,11 +126,257 @@ struct GemvArgs {
   int n_slots;
 };
 
-// One workgroup computes RPW = 16/KS rows for a tile of BT sessions. Threads
-// form 16 groups of 16 lanes; group (ks, r) covers row r over the ks-th share
-// of each K tile, lanes striding over 16-byte weight chunks, U chunks in flight.
+// ---------------------------------------------------------------------------
+struct SsdArgs {
+  const float *zx;        // [B][zx_stride]
+  int zx_stride, d_inner, conv_dim, H, P, N, G, hpg;
+  float *ssm;             // [n_slots][H][P][N]
+  const float *A_log, *D, *norm_w;
+  float *vw;              // [B][d_inner]: v * norm_w
+  float *ss;              // [B][n_partials]
+  int prange, psplit, n_partials;
+  const int32_t *slots;
+  int n_slots;
+};
+
+// Per-row epilogue inputs, loaded when the row starts so that their latency
+// overlaps the weight stream: conv history, taps and bias (x|B|C rows), dt bias
+// (dt rows), residual (out_proj).
+struct EpiIn {
+  float hist[7];
+  float w[8];
+  float bias;
+  float resid;
+  int slot;
+  bool sok;
+};
+
+template <int EPI>
+__device__ __forceinline__ EpiIn epilogue_prefetch(const GemvArgs &a, int row, int b) {
+  EpiIn e;
+  e.slot = a.slots ? a.slots[b] : b;
+  e.sok = e.slot >= 0 && e.slot < a.n_slots;
+  e.bias = 0.0f;
+  e.resid = 0.0f;
+  if (EPI == EPI_INPROJ) {
+    if (row >= a.d_inner && row < a.d_inner + a.conv_dim) {
+      const int c = row - a.d_inner;
+      const float *cc = a.conv_cache + (size_t)(e.sok ? e.slot : 0) * (a.d_conv - 1) * a.conv_dim + c;
+      const float *w = a.conv_w + (size_t)c * a.d_conv;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k < a.d_conv) e.w[k] = w[k];
+#pragma unroll
+      for (int k = 0; k < 7; ++k)
+        if (k < a.d_conv - 1) e.hist[k] = e.sok ? cc[(size_t)k * a.conv_dim] : 0.0f;
+      e.bias = a.conv_b[c];
+    } else if (row >= a.d_inner + a.conv_dim) {
+      e.bias = a.dt_bias[row - a.d_inner - a.conv_dim];
+    }
+  } else if (a.resid) {
+    e.resid = a.resid[(size_t)b * a.rows + row];
+  }
+  return e;
+}
+
+// Per-row result -> outputs. in_proj: z raw, conv + SiLU with cache shift, or
+// softplus(dt + bias). out_proj: gamma, residual add.
+template <int EPI>
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs &a, int row, int b, float val, const EpiIn &e) {
+  val *= a.gamma;
+  const float qnan = __builtin_nanf("");
+  if (EPI == EPI_INPROJ) {
+    float out = val;
+    if (row >= a.d_inner && row < a.d_inner + a.conv_dim) {
+      const int c = row - a.d_inner;
+      if (!e.sok) {
+        out = qnan;
+      } else {
+        float *cc = a.conv_cache + (size_t)e.slot * (a.d_conv - 1) * a.conv_dim + c;
+        float s = e.bias;
+#pragma unroll
+        for (int k = 0; k < 7; ++k)
+          if (k < a.d_conv - 1) s = fmaf(e.w[k], e.hist[k], s);
+        float wl = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k == a.d_conv - 1) wl = e.w[k];
+        s = fmaf(wl, val, s);
+#pragma unroll
+        for (int k = 0; k < 6; ++k)
+          if (k + 1 < a.d_conv - 1) cc[(size_t)k * a.conv_dim] = e.hist[k + 1];
+        cc[(size_t)(a.d_conv - 2) * a.conv_dim] = val;
+        out = silu(s);
+      }
+    } else if (row >= a.d_inner + a.conv_dim) {
+      out = softplus(val + e.bias);
+    }
+    a.zx[(size_t)b * a.zx_stride + row] = out;
+  } else {
+    a.y[(size_t)b * a.rows + row] = e.sok ? val + e.resid : qnan;
+  }
+}
+
+// RMS factors r[bb][j] = 1/sqrt(mean_j(v^2) + eps) for sessions b0 .. b0+nb-1,
+// summing each group's partials in a fixed order. Uses LDS part[n_partials].
+__device__ __forceinline__ void rms_factors(const GemvArgs &a, int b0, int nb, float *part, float *rn,
+                                            int tid, int nthreads) {
+  const int per = a.n_partials / a.n_norm;
+  for (int bb = 0; bb < nb; ++bb) {
+    for (int p = tid; p < a.n_partials; p += nthreads) part[p] = a.ss[(size_t)(b0 + bb) * a.n_partials + p];
+    __syncthreads();
+    for (int j = tid; j < a.n_norm; j += nthreads) {
+      float s = 0.0f;
+      for (int q = 0; q < per; ++q) s += part[j * per + q];
+      rn[bb * a.n_norm + j] = 1.0f / sqrtf(s / (float)a.ng + a.eps);
+    }
+    __syncthreads();
+  }
+}
+
+// out_proj activation staging in one memory trip: each thread loads its float4s
+// of v * norm_w and one sum-of-squares partial per session together, the RMS
+// factors are formed in LDS, then the float4s are scaled by their group's factor.
+// LDS: act [BT][K] | part [n_partials] | rn [BT][n_norm]. K/4 <= TPB * kNormF4PerThread.
+template <int BT, int TPB>
+__device__ __forceinline__ void stage_norm_act(const GemvArgs &a, float *lds, int tid) {
+  const int K = a.K;
+  const int nb = min(BT, a.B);
+  float *act_s = lds;
+  float *part = lds + BT * K;
+  float *rn = part + a.n_partials;
+  constexpr int MAXF = kNormF4PerThread;
+  const int nf = K / 4;
+  float pv[BT];
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb) {
+    pv[bb] = (bb < nb && tid < a.n_partials) ? a.ss[(size_t)bb * a.n_partials + tid] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXF; ++i) {
+      const int f = tid + TPB * i;
+      if (f < nf)
+        reinterpret_cast<float4 *>(act_s + bb * K)[f] =
+            bb < nb ? reinterpret_cast<const float4 *>(a.act + (size_t)bb * K)[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  const int per = a.n_partials / a.n_norm;
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb) {
+    if (tid < a.n_partials) part[tid] = pv[bb];
+    __syncthreads();
+    if (tid < a.n_norm) {
+      float sum = 0.0f;
+      for (int q = 0; q < per; ++q) sum += part[tid * per + q];
+      rn[bb * a.n_norm + tid] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
+    }
+    __syncthreads();
+  }
+  // each thread rescales the float4s it staged
+  const int ng4 = a.ng / 4;
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb)
+#pragma unroll
+    for (int i = 0; i < MAXF; ++i) {
+      const int f = tid + TPB * i;
+      if (f < nf) {
+        const float r = bb < nb ? rn[bb * a.n_norm + f / ng4] : 0.0f;
+        float4 *p4 = reinterpret_cast<float4 *>(act_s + bb * K) + f;
+        const float4 x = *p4;
+        *p4 = make_float4(x.x * r, x.y * r, x.z * r, x.w * r);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gemv_wave: one wave per row, whole-K activations of BT (= batch) sessions in LDS.
+// LDS: act [BT][K] | part [n_partials] | rn [BT][n_norm]
+template <int WT, int BT, int TPB, int U, int NT, int PRO, int EPI>
+__global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
+  extern __shared__ float lds[];
+  constexpr int WPB = TPB / 64;
+  constexpr int EPC = WTraits<WT>::EPC;
+  constexpr int ESZ = WTraits<WT>::ESZ;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int row = blockIdx.x * WPB + (tid >> 6);
+  const bool row_ok = row < a.rows;
+  const int nb = min(BT, a.B);
+  const int K = a.K;
+  const int NC = K / EPC;
+  const u32x4 *wr = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.W) +
+                                                    (size_t)(row_ok ? row : 0) * K * ESZ);
+  const __half *srow = a.S + (size_t)(row_ok ? row : 0) * (NC >> a.q_shift);
+
+  // weights do not depend on the activations: put the first U loads in flight first
+  u32x4 w[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = lane + 64 * u;
+    w[u] = (row_ok && c < NC) ? wload<NT>(wr + c) : u32x4{0u, 0u, 0u, 0u};
+  }
+  EpiIn epi{};
+  if (row_ok && lane < nb) epi = epilogue_prefetch<EPI>(a, row, lane);
+
+  float *act_s = lds;
+  if (PRO == PRO_NORM) {
+    stage_norm_act<BT, TPB>(a, lds, tid);
+  } else {
+#pragma unroll
+    for (int bb = 0; bb < BT; ++bb)
+      for (int i = tid * 4; i < K; i += TPB * 4) {
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (bb < nb) v = *reinterpret_cast<const float4 *>(a.act + (size_t)bb * K + i);
+        *reinterpret_cast<float4 *>(act_s + bb * K + i) = v;
+      }
+  }
+  __syncthreads();
+
+  float acc[BT];
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb) acc[bb] = 0.0f;
+  if (row_ok) {
+    for (int cb = lane;;) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = cb + 64 * u;
+        if (c < NC) {
+          float sc = 1.0f;
+          if (WT == M2_W_INT8G) sc = __half2float(srow[c >> a.q_shift]);
+#pragma unroll
+          for (int bb = 0; bb < BT; ++bb) {
+            const float d = chunk_dot<WT>(w[u], act_s + bb * K + c * EPC);
+            acc[bb] = WT == M2_W_INT8G ? fmaf(sc, d, acc[bb]) : acc[bb] + d;
+          }
+        }
+      }
+      cb += 64 * U;
+      if (cb >= NC) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = cb + 64 * u;
+        w[u] = c < NC ? wload<NT>(wr + c) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc[bb] += __shfl_xor(acc[bb], off, 64);
+  }
+  if (!row_ok || lane >= nb) return;
+  float val = 0.0f;
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb)
+    if (lane == bb) val = acc[bb];
+  gemv_epilogue<EPI>(a, row, lane, val, epi);
+}
+
+// ---------------------------------------------------------------------------
+// gemv_tiled: one workgroup computes RPW = 16/KS rows for a tile of BT sessions.
+// Threads form 16 groups of 16 lanes; group (ks, r) covers row r over the ks-th
+// share of each K tile, lanes striding over 16-byte chunks, U chunks in flight.
+// LDS: act [BT][KT] | part [n_partials] | rn [BT][n_norm] | red [16][BT]
 template <int WT, int BT, int KS, int PRO, int EPI, int U>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
   extern __shared__ float lds[];
   constexpr int RPW = 16 / KS;
   constexpr int EPC = WTraits<WT>::EPC;
@@ -125,58 +387,63 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
   const bool row_ok = row < a.rows;
   const int b0 = blockIdx.y * BT;
   const int nb = min(BT, a.B - b0);
-  float *act_s = lds;                       // [BT][KT]
-  float *rn_s = lds + BT * a.KT;            // [BT][n_norm]
-  float *red_s = rn_s + (PRO == PRO_NORM ? BT * a.n_norm : 0);   // [16][BT]
+  float *act_s = lds;
+  float *part = lds + BT * a.KT;
+  float *rn = part + (PRO == PRO_NORM ? a.n_partials : 0);
+  float *red_s = rn + (PRO == PRO_NORM ? BT * a.n_norm : 0);
 
-  if (PRO == PRO_NORM) {
-    const int per = a.ng / a.prange;
-    for (int i = tid; i < nb * a.n_norm; i += kThreads) {
-      const int bb = i / a.n_norm, j = i - bb * a.n_norm;
-      const float *p = a.ss + (size_t)(b0 + bb) * a.n_partials + (size_t)j * per;
-      float s = 0.0f;
-      for (int q = 0; q < per; ++q) s += p[q];
-      rn_s[bb * a.n_norm + j] = 1.0f / sqrtf(s / (float)a.ng + a.eps);
-    }
-    __syncthreads();
-  }
+  if (PRO == PRO_NORM) rms_factors(a, b0, nb, part, rn, tid, kThreads);
 
   float acc[BT];
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) acc[bb] = 0.0f;
 
-  const int ngrp = a.K / a.q_group;
+  const __half *srow = a.S + (size_t)(row_ok ? row : 0) * ((a.K / EPC) >> a.q_shift);
   for (int kt = 0; kt < a.K; kt += a.KT) {
     const int klen = min(a.KT, a.K - kt);
-    for (int i = tid; i < BT * klen; i += kThreads) {
-      const int bb = i / klen, k = i - bb * klen;
-      float v = 0.0f;
-      if (bb < nb) {
-        v = a.act[(size_t)(b0 + bb) * a.K + kt + k];
-        if (PRO == PRO_NORM) v *= rn_s[bb * a.n_norm + (kt + k) / a.ng] * a.norm_w[kt + k];
+    // stage act[b0 .. b0+BT)[kt .. kt+klen) (times the RMS factor for out_proj); klen % 4 == 0
+#pragma unroll
+    for (int bb = 0; bb < BT; ++bb) {
+      if (PRO == PRO_NORM) {
+        const int j0 = kt / a.ng, j1 = (kt + klen - 1) / a.ng;
+        for (int j = j0; j <= j1; ++j) {
+          const int lo = max(kt, j * a.ng), hi = min(kt + klen, (j + 1) * a.ng);
+          const float r = bb < nb ? rn[bb * a.n_norm + j] : 0.0f;
+          for (int i = lo + tid * 4; i < hi; i += kThreads * 4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (bb < nb) v = *reinterpret_cast<const float4 *>(a.act + (size_t)(b0 + bb) * a.K + i);
+            *reinterpret_cast<float4 *>(act_s + bb * a.KT + (i - kt)) = make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+          }
+        }
+      } else {
+        for (int i = tid * 4; i < klen; i += kThreads * 4) {
+          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (bb < nb) v = *reinterpret_cast<const float4 *>(a.act + (size_t)(b0 + bb) * a.K + kt + i);
+          *reinterpret_cast<float4 *>(act_s + bb * a.KT + i) = v;
+        }
       }
-      act_s[bb * a.KT + k] = v;
     }
     __syncthreads();
     if (row_ok) {
       const int nch = klen / EPC;
       const int per = (nch + KS - 1) / KS;
       const int c0 = ks * per, c1 = min(nch, c0 + per);
-      const uint4 *wrow =
-          reinterpret_cast<const uint4 *>(static_cast<const char *>(a.W) + ((size_t)row * a.K + kt) * ESZ);
+      const int cbase = kt / EPC;
+      const u32x4 *wrow =
+          reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.W) + ((size_t)row * a.K + kt) * ESZ);
       for (int cb = c0 + lane; cb < c1; cb += 16 * U) {
-        uint4 wv[U];
+        u32x4 wv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = cb + 16 * u;
-          wv[u] = c < c1 ? wrow[c] : make_uint4(0, 0, 0, 0);
+          wv[u] = c < c1 ? wrow[c] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = cb + 16 * u;
           if (c < c1) {
             float sc = 1.0f;
-            if (WT == M2_W_INT8G) sc = __half2float(a.S[(size_t)row * ngrp + (kt + c * EPC) / a.q_group]);
+            if (WT == M2_W_INT8G) sc = __half2float(srow[(cbase + c) >> a.q_shift]);
 #pragma unroll
             for (int bb = 0; bb < BT; ++bb) {
               const float d = chunk_dot<WT>(wv[u], act_s + bb * a.KT + c * EPC);
@@ -189,7 +456,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     __syncthreads();
   }
 
-  // reduce over the 16 lanes of the group (every lane ends with the total)
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) {
 #pragma unroll
@@ -209,62 +475,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     }
   }
   if (ks != 0 || !row_ok || lane >= nb) return;
-
-  const int b = b0 + lane;
-  val *= a.gamma;
-  const int slot = a.slots ? a.slots[b] : b;
-  const bool sok = slot >= 0 && slot < a.n_slots;
-  const float qnan = __builtin_nanf("");
-  if (EPI == EPI_INPROJ) {
-    float out = val;
-    if (row >= a.d_inner && row < a.d_inner + a.conv_dim) {
-      const int c = row - a.d_inner;
-      if (!sok) {
-        out = qnan;
-      } else {
-        float *cc = a.conv_cache + (size_t)slot * (a.d_conv - 1) * a.conv_dim + c;
-        const float *w = a.conv_w + (size_t)c * a.d_conv;
-        float hist[8];
-        float s = a.conv_b[c];
-        for (int k = 0; k < a.d_conv - 1; ++k) {
-          hist[k] = cc[(size_t)k * a.conv_dim];
-          s = fmaf(w[k], hist[k], s);
-        }
-        s = fmaf(w[a.d_conv - 1], val, s);
-        for (int k = 0; k + 1 < a.d_conv - 1; ++k) cc[(size_t)k * a.conv_dim] = hist[k + 1];
-        cc[(size_t)(a.d_conv - 2) * a.conv_dim] = val;
-        out = silu(s);
-      }
-    } else if (row >= a.d_inner + a.conv_dim) {
-      out = softplus(val + a.dt_bias[row - a.d_inner - a.conv_dim]);
-    }
-    a.zx[(size_t)b * a.zx_stride + row] = out;
-  } else {
-    float out = val + (a.resid ? a.resid[(size_t)b * a.rows + row] : 0.0f);
-    a.y[(size_t)b * a.rows + row] = sok ? out : qnan;
-  }
+  gemv_epilogue<EPI>(a, row, b0 + lane, val, epilogue_prefetch<EPI>(a, row, b0 + lane));
 }
 
-struct SsdArgs {
-  const float *zx;        // [B][zx_stride]
-  int zx_stride, d_inner, conv_dim, H, P, N, G, hpg;
-  float *ssm;             // [n_slots][H][P][N]
-  const float *A_log, *D;
-  float *v;               // [B][d_inner]
-  float *ss;              // [B][n_partials]
-  int prange, psplit, n_partials;
-  const int32_t *slots;
-  int n_slots;
-};
+// ---------------------------------------------------------------------------
 
-constexpr int kSsdMaxInst = 8;   // float4 row-slices per lane: prange <= 32 rows
-
-// One workgroup = (session b, head h, rows [ps*prange, (ps+1)*prange)). A row of
-// the state (N floats) is read by N/4 lanes as float4; every slice of the tile
-// is loaded before any is used, updated in registers and written once.
-__global__ __launch_bounds__(kThreads) void ssd_step_kernel(SsdArgs a) {
-  const int h = blockIdx.x / a.psplit, ps = blockIdx.x - h * a.psplit, b = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// One SSD work item = (session b, head h, rows [ps*prange, (ps+1)*prange)),
+// done by the NW waves of a workgroup. A state row (N floats) is read by N/4
+// lanes as float4; every slice of the tile is loaded before any is used,
+// updated in registers and written once. wsum: LDS float[NW]. Must be called by
+// every thread of the workgroup.
+template <int NW, int MAXI>
+__device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b, int wave, int lane,
+                                         float *wsum) {
   const int g = h / a.hpg;
   const int lpr = a.N >> 2;                 // lanes per state row
   const int rpi = 64 / lpr;                 // rows per wave instruction
@@ -273,60 +496,70 @@ __global__ __launch_bounds__(kThreads) void ssd_step_kernel(SsdArgs a) {
   const float *zb = a.zx + (size_t)b * a.zx_stride;
   const int slot = a.slots ? a.slots[b] : b;
   const bool sok = slot >= 0 && slot < a.n_slots;
+  float4 *S = reinterpret_cast<float4 *>(a.ssm + ((size_t)(sok ? slot : 0) * a.H + h) * a.P * a.N);
+
+  float4 st[MAXI];
+  int prow[MAXI];
+#pragma unroll
+  for (int k = 0; k < MAXI; ++k) {
+    const int i = wave + NW * k;
+    const int pl = i * rpi + r_in;
+    prow[k] = (i < n_inst && pl < a.prange) ? ps * a.prange + pl : -1;
+    st[k] = (sok && prow[k] >= 0) ? S[(size_t)prow[k] * lpr + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const float dt = zb[a.d_inner + a.conv_dim + h];
   const float dA = expf(-expf(a.A_log[h]) * dt);
   const float Dh = a.D[h];
   const float4 Bq = reinterpret_cast<const float4 *>(zb + 2 * a.d_inner + (size_t)g * a.N)[q];
   const float4 Cq = reinterpret_cast<const float4 *>(zb + 2 * a.d_inner + (size_t)(a.G + g) * a.N)[q];
-  float4 *S = reinterpret_cast<float4 *>(a.ssm + ((size_t)(sok ? slot : 0) * a.H + h) * a.P * a.N);
-
-  float4 st[kSsdMaxInst];
-  int prow[kSsdMaxInst];
-#pragma unroll
-  for (int k = 0; k < kSsdMaxInst; ++k) {
-    const int i = wave + 4 * k;
-    const int pl = i * rpi + r_in;
-    prow[k] = (i < n_inst && pl < a.prange) ? ps * a.prange + pl : -1;
-    st[k] = (sok && prow[k] >= 0) ? S[(size_t)prow[k] * lpr + q] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   float ssacc = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kSsdMaxInst; ++k) {
-    if (wave + 4 * k >= n_inst) break;      // uniform across the wave
+  for (int k = 0; k < MAXI; ++k) {
+    if (wave + NW * k >= n_inst) break;     // uniform across the wave
     const int p = prow[k];
     const float xp = p >= 0 ? zb[a.d_inner + h * a.P + p] : 0.0f;
     const float dtx = dt * xp;
-    float4 s = st[k];
-    s.x = fmaf(dA, s.x, dtx * Bq.x);
-    s.y = fmaf(dA, s.y, dtx * Bq.y);
-    s.z = fmaf(dA, s.z, dtx * Bq.z);
-    s.w = fmaf(dA, s.w, dtx * Bq.w);
-    st[k] = s;
-    float r = s.x * Cq.x;
-    r = fmaf(s.y, Cq.y, r);
-    r = fmaf(s.z, Cq.z, r);
-    r = fmaf(s.w, Cq.w, r);
+    float4 sv = st[k];
+    sv.x = fmaf(dA, sv.x, dtx * Bq.x);
+    sv.y = fmaf(dA, sv.y, dtx * Bq.y);
+    sv.z = fmaf(dA, sv.z, dtx * Bq.z);
+    sv.w = fmaf(dA, sv.w, dtx * Bq.w);
+    st[k] = sv;
+    float r = sv.x * Cq.x;
+    r = fmaf(sv.y, Cq.y, r);
+    r = fmaf(sv.z, Cq.z, r);
+    r = fmaf(sv.w, Cq.w, r);
     for (int off = lpr >> 1; off >= 1; off >>= 1) r += __shfl_xor(r, off, 64);
     if (q == 0 && p >= 0) {
+      const int ch = h * a.P + p;
       const float yv = fmaf(Dh, xp, r);
-      float vv = yv * silu(zb[h * a.P + p]);
+      float vv = yv * silu(zb[ch]);
       if (!sok) vv = __builtin_nanf("");
-      a.v[(size_t)b * a.d_inner + h * a.P + p] = vv;
+      a.vw[(size_t)b * a.d_inner + ch] = vv * a.norm_w[ch];
       ssacc = fmaf(vv, vv, ssacc);
     }
   }
   if (sok) {
 #pragma unroll
-    for (int k = 0; k < kSsdMaxInst; ++k)
+    for (int k = 0; k < MAXI; ++k)
       if (prow[k] >= 0) S[(size_t)prow[k] * lpr + q] = st[k];
   }
-  // sum of squares of this workgroup's rows, in a fixed order
+  // sum of squares of this item's rows, in a fixed order
   for (int off = 32; off >= 1; off >>= 1) ssacc += __shfl_xor(ssacc, off, 64);
-  __shared__ float wsum[4];
   if (lane == 0) wsum[wave] = ssacc;
   __syncthreads();
-  if (threadIdx.x == 0)
-    a.ss[(size_t)b * a.n_partials + (h * a.P + ps * a.prange) / a.prange] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  if (wave == 0 && lane == 0) {
+    float t = 0.0f;
+    for (int i = 0; i < NW; ++i) t += wsum[i];
+    a.ss[(size_t)b * a.n_partials + (h * a.P + ps * a.prange) / a.prange] = t;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads) void ssd_step_kernel(SsdArgs a) {
+  __shared__ float wsum[4];
+  const int h = blockIdx.x / a.psplit, ps = blockIdx.x - h * a.psplit;
+  ssd_item<4, 8>(a, h, ps, blockIdx.y, threadIdx.x >> 6, threadIdx.x & 63, wsum);
 }
 
 __global__ void state_zero_kernel(float *ssm, float *conv, size_t ssm_per, size_t conv_per,
@@ -343,44 +576,93 @@ __global__ void state_zero_kernel(float *ssm, float *conv, size_t ssm_per, size_
   }
 }
 
+// ---------------------------------------------------------------------------
+// launch helpers
+
+template <typename F>
+hipError_t allow_lds(F *kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+constexpr size_t kWaveLdsMax = 96 * 1024;
+
+size_t wave_lds_bytes(const GemvArgs &a, int BT, int PRO) {
+  return sizeof(float) * ((size_t)BT * a.K + (PRO == PRO_NORM ? (size_t)a.n_partials + (size_t)BT * a.n_norm : 0));
+}
+
+template <int WT, int BT, int TPB, int U, int NT, int PRO, int EPI>
+hipError_t launch_wave(const GemvArgs &a, hipStream_t stream) {
+  constexpr int WPB = TPB / 64;
+  const size_t lds = wave_lds_bytes(a, BT, PRO);
+  auto *k = gemv_wave_kernel<WT, BT, TPB, U, NT, PRO, EPI>;
+  hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3((a.rows + WPB - 1) / WPB), dim3(TPB), lds, stream, a);
+  return hipGetLastError();
+}
+
 template <int WT, int BT, int KS, int PRO, int EPI, int U>
-hipError_t launch_gemv(const GemvArgs &a, hipStream_t stream) {
+hipError_t launch_tiled(const GemvArgs &a, hipStream_t stream) {
   constexpr int RPW = 16 / KS;
   dim3 grid((a.rows + RPW - 1) / RPW, (a.B + BT - 1) / BT);
-  size_t lds = sizeof(float) * ((size_t)BT * a.KT + (PRO == PRO_NORM ? (size_t)BT * a.n_norm : 0) + 16 * BT);
-  hipLaunchKernelGGL((gemv_kernel<WT, BT, KS, PRO, EPI, U>), grid, dim3(kThreads), lds, stream, a);
+  const size_t lds = sizeof(float) * ((size_t)BT * a.KT +
+                                      (PRO == PRO_NORM ? (size_t)a.n_partials + (size_t)BT * a.n_norm : 0) +
+                                      16 * BT);
+  auto *k = gemv_tiled_kernel<WT, BT, KS, PRO, EPI, U>;
+  hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, grid, dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
 int pick_kt(int K, int BT) {
-  int kt = (kLdsFloatsPerBatch / BT) & ~255;
+  const int kt = (kLdsFloatsPerBatch / BT) & ~255;
   return K <= kt ? K : kt;
 }
 
-template <int WT, int PRO, int EPI, int KS>
+// in_proj: U=4 nontemporal loads; out_proj: U=8 cached loads (measured best on gfx950)
+template <int WT, int PRO, int EPI>
 hipError_t dispatch_bt(GemvArgs a, hipStream_t stream) {
+  constexpr int KS = EPI == EPI_INPROJ ? 1 : 4;
+  const bool regs_ok = PRO != PRO_NORM || (a.K / 4 <= 512 * kNormF4PerThread && a.n_partials <= 512 && a.n_norm <= 512);
+  if (a.B <= 2 && regs_ok && wave_lds_bytes(a, a.B, PRO) <= kWaveLdsMax) {
+    if (EPI == EPI_INPROJ) {
+      if (a.B == 1) return launch_wave<WT, 1, 512, 4, 1, PRO, EPI>(a, stream);
+      return launch_wave<WT, 2, 512, 4, 1, PRO, EPI>(a, stream);
+    }
+    if (a.B == 1) return launch_wave<WT, 1, 512, 8, 0, PRO, EPI>(a, stream);
+    return launch_wave<WT, 2, 512, 8, 0, PRO, EPI>(a, stream);
+  }
   if (a.B >= 4) {
     a.KT = pick_kt(a.K, 4);
-    return launch_gemv<WT, 4, KS, PRO, EPI, 8>(a, stream);
+    return launch_tiled<WT, 4, KS, PRO, EPI, 8>(a, stream);
   }
   if (a.B >= 2) {
     a.KT = pick_kt(a.K, 2);
-    return launch_gemv<WT, 2, KS, PRO, EPI, 8>(a, stream);
+    return launch_tiled<WT, 2, KS, PRO, EPI, 8>(a, stream);
   }
   a.KT = pick_kt(a.K, 1);
-  return launch_gemv<WT, 1, KS, PRO, EPI, 8>(a, stream);
+  return launch_tiled<WT, 1, KS, PRO, EPI, 8>(a, stream);
 }
 
-template <int PRO, int EPI, int KS>
+template <int PRO, int EPI>
 hipError_t dispatch_wt(int wtype, const GemvArgs &a, hipStream_t stream) {
   switch (wtype) {
-    case M2_W_F32: return dispatch_bt<M2_W_F32, PRO, EPI, KS>(a, stream);
-    case M2_W_BF16: return dispatch_bt<M2_W_BF16, PRO, EPI, KS>(a, stream);
-    default: return dispatch_bt<M2_W_INT8G, PRO, EPI, KS>(a, stream);
+    case M2_W_F32: return dispatch_bt<M2_W_F32, PRO, EPI>(a, stream);
+    case M2_W_BF16: return dispatch_bt<M2_W_BF16, PRO, EPI>(a, stream);
+    default: return dispatch_bt<M2_W_INT8G, PRO, EPI>(a, stream);
   }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int log2i(int v) {
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
 
 }  // namespace
 
@@ -408,6 +690,8 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   auto mark = [&](int i) -> hipError_t {
     return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess;
   };
+  const int epc = c.wtype == M2_W_F32 ? 4 : c.wtype == M2_W_BF16 ? 8 : 16;
+  const int q_shift = c.wtype == M2_W_INT8G ? log2i(c.q_group / epc) : 30;
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
   // 1. in_proj + conv + dt
@@ -416,7 +700,7 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   gi.S = static_cast<const __half *>(L.w.s_in);
   gi.rows = L.d_in_proj;
   gi.K = c.d_model;
-  gi.q_group = c.wtype == M2_W_INT8G ? c.q_group : c.d_model;
+  gi.q_shift = q_shift;
   gi.gamma = c.wtype == M2_W_INT8G ? c.q_gamma_in : 1.0f;
   gi.act = x;
   gi.B = batch;
@@ -431,7 +715,7 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   gi.conv_cache = S.conv;
   gi.slots = slots;
   gi.n_slots = S.n_slots;
-  e = dispatch_wt<PRO_PLAIN, EPI_INPROJ, 1>(c.wtype, gi, stream);
+  e = dispatch_wt<PRO_PLAIN, EPI_INPROJ>(c.wtype, gi, stream);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return e;
 
@@ -449,17 +733,14 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   sa.ssm = S.ssm;
   sa.A_log = L.w.A_log;
   sa.D = L.w.D;
-  sa.v = ws.v;
+  sa.norm_w = L.w.norm_w;
+  sa.vw = ws.v;
   sa.ss = ws.ss;
   sa.prange = L.prange;
   sa.psplit = L.psplit;
   sa.n_partials = L.n_partials;
   sa.slots = slots;
   sa.n_slots = S.n_slots;
-  hipLaunchKernelGGL(ssd_step_kernel, dim3(c.n_heads * L.psplit, batch), dim3(kThreads), 0, stream, sa);
-  e = hipGetLastError();
-  if (e == hipSuccess) e = mark(2);
-  if (e != hipSuccess) return e;
 
   // 3. RMSNorm + out_proj (+ residual)
   GemvArgs go{};
@@ -467,14 +748,12 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   go.S = static_cast<const __half *>(L.w.s_out);
   go.rows = c.d_model;
   go.K = L.d_inner;
-  go.q_group = c.wtype == M2_W_INT8G ? c.q_group : L.d_inner;
+  go.q_shift = q_shift;
   go.gamma = c.wtype == M2_W_INT8G ? c.q_gamma_out : 1.0f;
   go.act = ws.v;
   go.B = batch;
   go.ss = ws.ss;
-  go.norm_w = L.w.norm_w;
   go.ng = L.ng;
-  go.prange = L.prange;
   go.n_partials = L.n_partials;
   go.n_norm = L.n_norm;
   go.eps = c.norm_eps;
@@ -482,10 +761,15 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   go.resid = (flags & M2_RESIDUAL) ? x : nullptr;
   go.slots = slots;
   go.n_slots = S.n_slots;
-  e = dispatch_wt<PRO_NORM, EPI_OUT, 4>(c.wtype, go, stream);
+  hipLaunchKernelGGL(ssd_step_kernel, dim3(c.n_heads * L.psplit, batch), dim3(kThreads), 0, stream, sa);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = mark(2);
+  if (e != hipSuccess) return e;
+  e = dispatch_wt<PRO_NORM, EPI_OUT>(c.wtype, go, stream);
   if (e == hipSuccess) e = mark(3);
   return e;
 }
+
 
 hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, hipStream_t stream) {
   const m2_layer_s &L = *S.layer;

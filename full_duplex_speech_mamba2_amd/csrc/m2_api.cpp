@@ -53,13 +53,14 @@ int check_config(const m2_config *c) {
   const long ng = c->norm_group > 0 ? c->norm_group : d_inner / c->n_groups;
   if (c->norm_group < 0 || ng <= 0 || d_inner % ng)
     return fail(M2_ERR_SHAPE, "norm_group %d does not divide d_inner %ld", c->norm_group, d_inner);
+  if (ng % 4) return fail(M2_ERR_SHAPE, "channels per RMS group (%ld) must be a multiple of 4", ng);
   if (!(c->norm_eps >= 0.0f)) return fail(M2_ERR_SHAPE, "norm_eps must be >= 0");
   if (d_inner / ng > 4096) return fail(M2_ERR_UNSUPPORTED, "more than 4096 RMS groups");
   if (c->wtype != M2_W_F32 && c->wtype != M2_W_BF16 && c->wtype != M2_W_INT8G)
     return fail(M2_ERR_DTYPE, "unknown wtype %d", c->wtype);
   if (c->wtype == M2_W_INT8G) {
-    if (c->q_group <= 0 || c->q_group % 16)
-      return fail(M2_ERR_SHAPE, "q_group %d must be a positive multiple of 16", c->q_group);
+    if (c->q_group < 16 || (c->q_group & (c->q_group - 1)))
+      return fail(M2_ERR_SHAPE, "q_group %d must be a power of two >= 16", c->q_group);
     if (c->d_model % c->q_group || d_inner % c->q_group)
       return fail(M2_ERR_SHAPE, "q_group %d does not divide d_model %d and d_inner %ld", c->q_group,
                   c->d_model, d_inner);
@@ -210,6 +211,11 @@ int m2_step_timed(m2_layer layer, m2_state st, const float *x, float *y, int32_t
                   const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream,
                   void *const *events) {
   return step_impl(layer, st, x, y, batch, slot_ids, flags, ws, ws_bytes, stream, events);
+}
+
+int m2_step_kernel_count(m2_layer layer, int32_t batch) {
+  if (!layer || batch <= 0) return 0;
+  return m2d::kStepKernels;
 }
 
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk) {

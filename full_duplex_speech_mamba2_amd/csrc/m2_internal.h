@@ -47,6 +47,9 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
                        const int32_t *slots, int flags, const StepWs &ws, hipStream_t stream,
                        hipEvent_t const *events = nullptr);
 
+// Kernels one decode step launches (in_proj; SSD; out_proj).
+constexpr int kStepKernels = 3;
+
 hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, hipStream_t stream);
 
 // Prefill

@@ -58,6 +58,8 @@ _lib.m2_step_workspace.argtypes = [_P, _i32]
 _lib.m2_step_workspace.restype = C.c_size_t
 _lib.m2_step.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P]
 _lib.m2_step_timed.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P, _P]
+_lib.m2_step_kernel_count.argtypes = [_P, _i32]
+_lib.m2_step_kernel_count.restype = C.c_int
 _lib.m2_prefill_workspace.argtypes = [_P, _i32, _i32, _i32]
 _lib.m2_prefill_workspace.restype = C.c_size_t
 _lib.m2_prefill.argtypes = [_P, _P, _P, _P, _i32, _i32, _i32, _P, _i32, _P, C.c_size_t, _P]
@@ -138,6 +140,9 @@ class Layer:
     def step_workspace_bytes(self, batch: int) -> int:
         return int(_lib.m2_step_workspace(self.handle, batch))
 
+    def step_kernel_count(self, batch: int) -> int:
+        return int(_lib.m2_step_kernel_count(self.handle, batch))
+
     def prefill_workspace_bytes(self, batch: int, seqlen: int, chunk: int) -> int:
         return int(_lib.m2_prefill_workspace(self.handle, batch, seqlen, chunk))
 
@@ -210,14 +215,15 @@ def step(layer: Layer, state: State, x: torch.Tensor, y: Optional[torch.Tensor] 
 def step_timed(layer: Layer, state: State, x: torch.Tensor, y: torch.Tensor, events,
                slot_ids: Optional[torch.Tensor] = None, residual: bool = False,
                ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """step() that records the four torch.cuda.Event objects in `events` around its three
-    kernels (each event must have been recorded once so that its HIP event exists)."""
+    """step() that records the four events in `events` around its three kernels. Each is a
+    raw hipEvent_t handle (int) or a torch.cuda.Event that has been recorded once (so that
+    its HIP event exists)."""
     B = x.shape[0]
     _act(x, (B, layer.dims.d_model))
     _act(y, x.shape)
     if ws is None:
         ws = layer.workspace("step", B)
-    ev = (C.c_void_p * 4)(*[e.cuda_event for e in events])
+    ev = (C.c_void_p * 4)(*[getattr(e, "cuda_event", e) for e in events])
     _check(_lib.m2_step_timed(layer.handle, state.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids),
                               M2_RESIDUAL if residual else 0, _ptr(ws), ws.numel(), _stream(stream), ev))
     return y

@@ -80,10 +80,10 @@ typedef struct {
   int32_t d_state;          /* N */
   int32_t n_groups;         /* G: B/C groups; H % G == 0; head h uses group h / (H/G) */
   int32_t d_conv;           /* causal conv width, 2..8 */
-  int32_t norm_group;       /* channels per RMS group; 0 means d_inner / n_groups */
+  int32_t norm_group;       /* channels per RMS group (multiple of 4); 0 means d_inner / n_groups */
   float norm_eps;           /* RMSNorm epsilon */
   int32_t wtype;            /* m2_wtype */
-  int32_t q_group;          /* columns per int8 scale (M2_W_INT8G); multiple of 16 */
+  int32_t q_group;          /* columns per int8 scale (M2_W_INT8G); power of two >= 16 */
   float q_gamma_in;         /* per-tensor multiplier applied to int8 in_proj results (1 = none) */
   float q_gamma_out;        /* per-tensor multiplier applied to int8 out_proj results */
 } m2_config;
@@ -146,6 +146,11 @@ int m2_step(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch
 int m2_step_timed(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
                   const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream,
                   void *const *events);
+
+/* Number of kernels one m2_step of `batch` sessions launches (currently 3: in_proj;
+ * SSD; out_proj), i.e. the intervals m2_step_timed's events delimit. Returns 0 for
+ * a NULL layer or batch <= 0. */
+int m2_step_kernel_count(m2_layer layer, int32_t batch);
 
 /* Workspace bytes m2_prefill needs. */
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk);
