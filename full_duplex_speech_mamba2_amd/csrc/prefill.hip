@@ -1,13 +1,795 @@
-// Chunked SSD prefill (not yet available: m2_prefill reports M2_ERR_UNSUPPORTED).
+// Chunked prefill of the Mamba-2 mixer layer on gfx950.
+//
+// A prompt of T tokens per session is processed in one pass before streaming
+// starts (page "NemotronLabs VoiceChat 11B: GPTQ 3-bit LLM, MLX", "Recipe":
+// system-prompt prefill, then the user's speech; page "NemotronLabs VoiceChat"
+// of the SGLang-Omni cookbook, "Known limitations": the system-prompt region is
+// walked before frame 0). The result equals T decode steps; the chunked form
+// only reorders the arithmetic of the SSD recurrence
+//     S_t = exp(dt_t A) S_{t-1} + dt_t x_t B_t^T,   y_t = C_t . S_t + D x_t
+// into, per chunk of Q tokens with cs_t = sum_{r<=t in chunk} dt_r A:
+//     y_t   = sum_{s<=t} (C_t.B_s) exp(cs_t - cs_s) dt_s x_s      (intra-chunk, MFMA)
+//           + exp(cs_t) C_t . H_{c-1}                             (entering state, MFMA)
+//           + D x_t
+//     S_c   = sum_s exp(cs_end - cs_s) dt_s x_s B_s^T             (chunk state, MFMA)
+//     H_c   = exp(cs_end) H_{c-1} + S_c                           (sequential over chunks)
+//
+// Kernels, in stream order:
+//   gemm (in_proj)   ZX[BT][d_in_proj] = X W_in^T: bf16 MFMA 32x32x16, fp32 activations
+//                    split into bf16 hi + lo so that bf16 weights multiply exactly
+//   conv_dt          causal conv + SiLU over T (halo from the conv cache), softplus dt
+//   cb               per (session, chunk, group): C B^T tiles (f32 MFMA 16x16x4), s-tile <= t-tile
+//   chunk_state      per (session, chunk, head): cumsum of dt A, S_c
+//   state_pass       per (session, head): H_c recurrence; entering states; final state -> slot
+//   chunk_out        per (session, chunk, head): y, gate, v * norm_w, per-head sum of squares
+//   rms              RMS factor per (token, norm group)
+//   gemm (out_proj)  Y = (v norm_w r) W_out^T (+ residual), same GEMM with a row-group scale on A
+//   cache_update     conv cache <- last d_conv-1 raw inputs (mixing with the old cache if T is short)
+// Weights stored as fp32 or int8 use a fp32 VALU GEMM instead of the MFMA GEMM.
+#include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
+
 #include "m2_internal.h"
 
 namespace m2d {
+namespace {
 
-size_t prefill_ws_bytes(const m2_layer_s &, int, int, int) { return 0; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-hipError_t launch_prefill(const m2_layer_s &, const m2_state_s &, const float *, float *, int, int, int,
-                          const int32_t *, int, void *, hipStream_t) {
-  return hipErrorNotSupported;
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
+__device__ __forceinline__ float softplus(float a) { return a > 20.0f ? a : log1pf(expf(a)); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ unsigned short bf16_rne(float f) {
+  const unsigned u = __float_as_uint(f);
+  return (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_to_f(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
+
+// ---------------------------------------------------------------------------
+// MFMA GEMM: C[M][N] = A[M][K] W[N][K]^T (+ R), A fp32 (optionally scaled by
+// rs[m][k / ng]), W bf16. Block tile 128 x 128 x 32, 4 waves in 2 x 2, each wave
+// 64 x 64 = 2 x 2 MFMA 32x32x16 tiles, two MFMAs (hi, lo) per tile and k-step.
+// LDS rows padded to 40 bf16 (80 B). Global loads of the next K tile are held in
+// registers while the current tile is multiplied out of LDS.
+
+constexpr int GBM = 128, GBN = 128, GBK = 32, GLD = 40;
+
+struct GemmArgs {
+  const float *A;
+  int lda;
+  const unsigned short *W;   // bf16 [N][K]
+  float *C;
+  int ldc;
+  const float *R;            // residual [M][ldr] or null
+  int ldr;
+  const float *rs;           // row-group scale [M][n_rs] or null
+  int n_rs, ng;
+  int M, N, K;
+};
+
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ unsigned short sAh[2][GBM * GLD];
+  __shared__ unsigned short sAl[2][GBM * GLD];
+  __shared__ unsigned short sW[2][GBN * GLD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
+  // loader mapping: row = tid / 2, 16 consecutive k per thread
+  const int lr = tid >> 1, lk = (tid & 1) * 16;
+  const int am = m0 + lr, wnr = n0 + lr;
+  const bool a_ok = am < g.M, w_ok = wnr < g.N;
+  const float *arow = g.A + (size_t)(a_ok ? am : 0) * g.lda;
+  const unsigned short *wrow = g.W + (size_t)(w_ok ? wnr : 0) * g.K;
+
+  float4 ra[4];
+  u32x4 rw[2];
+  auto load_tile = [&](int k0) {
+    const int kb = k0 + lk;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = kb + 4 * q;
+      if (a_ok && k + 3 < g.K) {
+        ra[q] = *reinterpret_cast<const float4 *>(arow + k);
+      } else {
+        float t[4];
+        for (int e = 0; e < 4; ++e) t[e] = (a_ok && k + e < g.K) ? arow[k + e] : 0.0f;
+        ra[q] = make_float4(t[0], t[1], t[2], t[3]);
+      }
+      if (g.rs) {
+        // scale per (row, norm group); a group never splits a float4 (ng % 4 == 0)
+        const float s = (a_ok && k < g.K) ? g.rs[(size_t)am * g.n_rs + k / g.ng] : 0.0f;
+        ra[q].x *= s; ra[q].y *= s; ra[q].z *= s; ra[q].w *= s;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int k = kb + 8 * q;
+      if (w_ok && k + 7 < g.K) {
+        rw[q] = *reinterpret_cast<const u32x4 *>(wrow + k);
+      } else {
+        unsigned short t[8];
+        for (int e = 0; e < 8; ++e) t[e] = (w_ok && k + e < g.K) ? wrow[k + e] : (unsigned short)0;
+        rw[q] = u32x4{t[0] | ((unsigned)t[1] << 16), t[2] | ((unsigned)t[3] << 16),
+                      t[4] | ((unsigned)t[5] << 16), t[6] | ((unsigned)t[7] << 16)};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    unsigned short hi[16], lo[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float v[4] = {ra[q].x, ra[q].y, ra[q].z, ra[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned short h = bf16_rne(v[e]);
+        hi[4 * q + e] = h;
+        lo[4 * q + e] = bf16_rne(v[e] - bf16_to_f(h));
+      }
+    }
+    u32x4 *ph = reinterpret_cast<u32x4 *>(&sAh[buf][lr * GLD + lk]);
+    u32x4 *pl = reinterpret_cast<u32x4 *>(&sAl[buf][lr * GLD + lk]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      ph[q] = u32x4{hi[8 * q] | ((unsigned)hi[8 * q + 1] << 16), hi[8 * q + 2] | ((unsigned)hi[8 * q + 3] << 16),
+                    hi[8 * q + 4] | ((unsigned)hi[8 * q + 5] << 16), hi[8 * q + 6] | ((unsigned)hi[8 * q + 7] << 16)};
+      pl[q] = u32x4{lo[8 * q] | ((unsigned)lo[8 * q + 1] << 16), lo[8 * q + 2] | ((unsigned)lo[8 * q + 3] << 16),
+                    lo[8 * q + 4] | ((unsigned)lo[8 * q + 5] << 16), lo[8 * q + 6] | ((unsigned)lo[8 * q + 7] << 16)};
+    }
+    u32x4 *pw = reinterpret_cast<u32x4 *>(&sW[buf][lr * GLD + lk]);
+    pw[0] = rw[0];
+    pw[1] = rw[1];
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  const int nk = (g.K + GBK - 1) / GBK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load_tile((kt + 1) * GBK);
+#pragma unroll
+    for (int ks = 0; ks < GBK; ks += 16) {
+      const int kofs = ks + (lane >> 5) * 8;
+      bf16x8 ah[2], al[2], bw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + (lane & 31);
+        ah[i] = *reinterpret_cast<const bf16x8 *>(&sAh[buf][r * GLD + kofs]);
+        al[i] = *reinterpret_cast<const bf16x8 *>(&sAl[buf][r * GLD + kofs]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = wn * 64 + j * 32 + (lane & 31);
+        bw[j] = *reinterpret_cast<const bf16x8 *>(&sW[buf][r * GLD + kofs]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    if (kt + 1 < nk) {
+      store_tile(buf ^ 1);
+    }
+    __syncthreads();
+  }
+  // epilogue: lane l, reg r -> row (r/4)*8 + (l/32)*4 + r%4, col l%32 of each 32 x 32 tile
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (row < g.M) {
+          float v = acc[i][j][r];
+          if (g.R) v += g.R[(size_t)row * g.ldr + col];
+          g.C[(size_t)row * g.ldc + col] = v;
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 VALU GEMM for weights stored as fp32 or int8 (and any shape): 64 x 64
+// tiles, 256 threads, 4 x 4 outputs per thread, K tiles of 16 in LDS.
+struct GemmValuArgs {
+  const float *A;
+  int lda;
+  const void *W;             // [N][K] fp32, bf16 or int8
+  const __half *S;           // int8 scales [N][K / q_group]
+  int wtype, q_group;
+  float gamma;
+  float *C;
+  int ldc;
+  const float *R;
+  int ldr;
+  const float *rs;
+  int n_rs, ng;
+  int M, N, K;
+};
+
+__device__ __forceinline__ float weight_at(const GemmValuArgs &g, int n, int k) {
+  if (g.wtype == M2_W_F32) return static_cast<const float *>(g.W)[(size_t)n * g.K + k];
+  if (g.wtype == M2_W_BF16) return bf16_to_f(static_cast<const unsigned short *>(g.W)[(size_t)n * g.K + k]);
+  const float q = (float)static_cast<const int8_t *>(g.W)[(size_t)n * g.K + k];
+  return q * __half2float(g.S[(size_t)n * (g.K / g.q_group) + k / g.q_group]);
+}
+
+__global__ __launch_bounds__(256) void gemm_valu_kernel(GemmValuArgs g) {
+  __shared__ float sA[16][65];
+  __shared__ float sB[16][65];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < g.K; k0 += 16) {
+    for (int i = tid; i < 64 * 16; i += 256) {
+      const int r = i >> 4, k = i & 15;
+      const int m = m0 + r, n = n0 + r, kk = k0 + k;
+      float a = 0.0f, b = 0.0f;
+      if (m < g.M && kk < g.K) {
+        a = g.A[(size_t)m * g.lda + kk];
+        if (g.rs) a *= g.rs[(size_t)m * g.n_rs + kk / g.ng];
+      }
+      if (n < g.N && kk < g.K) b = weight_at(g, n, kk);
+      sA[k][r] = a;
+      sB[k][r] = b;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = sA[k][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = sB[k][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+      if (m < g.M && n < g.N) {
+        float v = acc[i][j] * g.gamma;
+        if (g.R) v += g.R[(size_t)m * g.ldr + n];
+        g.C[(size_t)m * g.ldc + n] = v;
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+struct ScanArgs {
+  int B, T, Q, nch;                 // sessions, tokens, chunk length, chunks
+  int H, P, N, G, hpg;
+  int d_inner, conv_dim, d_conv, zx_stride;
+  const float *zx;                  // [B*T][zx_stride]: z | raw x|B|C | raw dt (in_proj output)
+  float *xc;                        // [B*T][conv_dim]: conv + SiLU
+  float *dt;                        // [B*T][H]: softplus(dt_raw + bias)
+  float *cs;                        // [B*T][H]: cumsum of dt A within the chunk
+  float *cse;                       // [B][nch][H]: chunk-end cumsum
+  float *sc;                        // [B][nch][H][P][N]: chunk states, then entering states
+  float *cbt;                       // [B][nch][G][npair][64][4]: C B^T tiles
+  float *vw;                        // [B*T][d_inner]: v * norm_w
+  float *ssh;                       // [B*T][H]: per-head sum of squares of v
+  float *rn;                        // [B*T][n_norm]
+  int n_norm, ng;
+  float eps;
+  const float *conv_w, *conv_b, *dt_bias, *A_log, *D, *norm_w;
+  float *ssm;                       // [n_slots][H][P][N]
+  float *conv;                      // [n_slots][d_conv-1][conv_dim]
+  const int32_t *slots;
+  int n_slots;
+};
+
+__device__ __forceinline__ int slot_of(const ScanArgs &a, int b, bool &ok) {
+  const int s = a.slots ? a.slots[b] : b;
+  ok = s >= 0 && s < a.n_slots;
+  return ok ? s : 0;
+}
+
+// conv over T with the cache as left halo, SiLU; softplus dt. One thread per (token, channel).
+__global__ void conv_dt_kernel(ScanArgs a) {
+  const int nc = a.conv_dim + a.H;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)a.B * a.T * nc) return;
+  const int c = (int)(idx % nc);
+  const size_t bt = idx / nc;
+  const int t = (int)(bt % a.T), b = (int)(bt / a.T);
+  const float *zrow = a.zx + bt * a.zx_stride;
+  bool ok;
+  const int slot = slot_of(a, b, ok);
+  if (c < a.conv_dim) {
+    float s = a.conv_b[c];
+    for (int k = 0; k < a.d_conv; ++k) {
+      const int tau = t - (a.d_conv - 1) + k;
+      float in;
+      if (tau >= 0) in = a.zx[((size_t)b * a.T + tau) * a.zx_stride + a.d_inner + c];
+      else in = a.conv[((size_t)slot * (a.d_conv - 1) + (a.d_conv - 1 + tau)) * a.conv_dim + c];
+      s = fmaf(a.conv_w[(size_t)c * a.d_conv + k], in, s);
+    }
+    a.xc[bt * a.conv_dim + c] = ok ? silu(s) : __builtin_nanf("");
+  } else {
+    const int h = c - a.conv_dim;
+    a.dt[bt * a.H + h] = softplus(zrow[a.d_inner + a.conv_dim + h] + a.dt_bias[h]);
+  }
+}
+
+__device__ __forceinline__ int npairs(int nt) { return nt * (nt + 1) / 2; }
+// tile pair (si <= ti) -> index, row-major over ti
+__device__ __forceinline__ int pair_index(int si, int ti) { return ti * (ti + 1) / 2 + si; }
+
+// C B^T tiles for one (session, chunk, group): CBT[s][t] = sum_n B_s[n] C_t[n] for
+// 16 x 16 tiles with s-tile <= t-tile, stored in MFMA accumulator order
+// (lane l, reg r -> s = 16 si + 4 (l/16) + r, t = 16 ti + l % 16).
+__global__ __launch_bounds__(256) void cb_kernel(ScanArgs a) {
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = c * a.Q;
+  const int Qc = min(a.Q, a.T - t0);
+  const int nt = (Qc + 15) / 16, np = npairs(a.Q / 16);
+  const size_t rowbase = (size_t)b * a.T + t0;
+  const int boff = a.d_inner + g * a.N, coff = a.d_inner + a.G * a.N + g * a.N;
+  float *out = a.cbt + (((size_t)b * a.nch + c) * a.G + g) * (size_t)np * 256;
+  for (int pi = wave; pi < npairs(nt); pi += 4) {
+    int ti = 0;
+    while (pair_index(0, ti + 1) <= pi) ++ti;
+    const int si = pi - pair_index(0, ti);
+    const int s = 16 * si + (lane & 15), t = 16 * ti + (lane & 15);
+    const bool s_ok = s < Qc, t_ok = t < Qc;
+    const float *bs = a.xc + (rowbase + (s_ok ? s : 0)) * a.conv_dim + boff;
+    const float *ct = a.xc + (rowbase + (t_ok ? t : 0)) * a.conv_dim + coff;
+    f32x4 acc = {};
+    for (int k0 = 0; k0 < a.N; k0 += 4) {
+      const int n = k0 + (lane >> 4);
+      const float av = s_ok ? bs[n] : 0.0f;   // A (s x n): lane -> s = l%16, n = k0 + l/16
+      const float bv = t_ok ? ct[n] : 0.0f;   // B (n x t): lane -> n = k0 + l/16, t = l%16
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+    }
+    reinterpret_cast<f32x4 *>(out)[(size_t)pi * 64 + lane] = acc;
+  }
+}
+
+// Per (session, chunk, head): cs (inclusive cumsum of dt A), chunk-end cumsum, and
+// the chunk state S_c[p][n] = sum_s exp(cs_end - cs_s) dt_s x_s[p] B_s[n].
+// LDS: xs [Q][P + 4] (x of the head), w [Q], cs [Q].
+__global__ __launch_bounds__(256) void chunk_state_kernel(ScanArgs a) {
+  extern __shared__ float lds[];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = h / a.hpg;
+  const int t0 = c * a.Q;
+  const int Qc = min(a.Q, a.T - t0);
+  const int PP = a.P + 4;
+  float *xs = lds;
+  float *ws = xs + (size_t)a.Q * PP;
+  float *css = ws + a.Q;
+  const size_t rowbase = (size_t)b * a.T + t0;
+  const float A = -expf(a.A_log[h]);
+  // inclusive scan of dt A over the chunk (Hillis-Steele in LDS)
+  for (int s = tid; s < a.Q; s += 256) css[s] = s < Qc ? a.dt[(rowbase + s) * a.H + h] * A : 0.0f;
+  __syncthreads();
+  for (int off = 1; off < a.Q; off <<= 1) {
+    float v[4];
+    int n = 0;
+    for (int s = tid; s < a.Q; s += 256) v[n++] = s >= off ? css[s - off] : 0.0f;
+    __syncthreads();
+    n = 0;
+    for (int s = tid; s < a.Q; s += 256) css[s] += v[n++];
+    __syncthreads();
+  }
+  const float cend = css[Qc - 1];
+  for (int s = tid; s < a.Q; s += 256) {
+    float w = 0.0f;
+    if (s < Qc) {
+      a.cs[(rowbase + s) * a.H + h] = css[s];
+      w = expf(cend - css[s]) * a.dt[(rowbase + s) * a.H + h];
+    }
+    ws[s] = w;
+  }
+  if (tid == 0) a.cse[((size_t)b * a.nch + c) * a.H + h] = cend;
+  for (int i = tid; i < a.Q * a.P; i += 256) {
+    const int s = i / a.P, p = i - s * a.P;
+    xs[s * PP + p] = s < Qc ? a.xc[(rowbase + s) * a.conv_dim + h * a.P + p] : 0.0f;
+  }
+  __syncthreads();
+  // S_c tiles (p-tile i, n-tile j): A (p x s) = x_s[p] w_s from LDS, B (s x n) = B_s[n];
+  // the k index of lane group q4 = l/16 at step kk is s = s0 + 4 q4 + kk
+  const int nP = a.P / 16, nN = a.N / 16;
+  const int boff = a.d_inner + g * a.N;
+  float *out = a.sc + (((size_t)b * a.nch + c) * a.H + h) * (size_t)a.P * a.N;
+  for (int j = wave; j < nN; j += 4) {
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{};
+    const int n = 16 * j + (lane & 15);
+    for (int s0 = 0; s0 < Qc; s0 += 16) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int s = s0 + 4 * (lane >> 4) + kk;
+        const float bv = s < Qc ? a.xc[(rowbase + s) * a.conv_dim + boff + n] : 0.0f;
+        const float w = ws[s];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nP) {
+            const float av = xs[s * PP + 16 * i + (lane & 15)] * w;
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[i], 0, 0, 0);
+          }
+      }
+    }
+    // lane l, reg r -> p = 16 i + 4 (l/16) + r, n = 16 j + l % 16
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nP)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[(size_t)(16 * i + 4 * (lane >> 4) + r) * a.N + n] = acc[i][r];
+  }
+}
+
+// Per (session, head, state element): H_c = exp(cs_end_c) H_{c-1} + S_c over the
+// chunks; sc[c] is overwritten with the state entering chunk c; the final state
+// goes to the session's slot.
+__global__ void state_pass_kernel(ScanArgs a) {
+  const size_t PN = (size_t)a.P * a.N;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)a.B * a.H * PN) return;
+  const size_t e = idx % PN;
+  const int h = (int)((idx / PN) % a.H), b = (int)(idx / PN / a.H);
+  bool ok;
+  const int slot = slot_of(a, b, ok);
+  float *st = a.ssm + ((size_t)slot * a.H + h) * PN + e;
+  float Hs = *st;
+  for (int c = 0; c < a.nch; ++c) {
+    float *p = a.sc + (((size_t)b * a.nch + c) * a.H + h) * PN + e;
+    const float S = *p;
+    *p = Hs;
+    Hs = fmaf(expf(a.cse[((size_t)b * a.nch + c) * a.H + h]), Hs, S);
+  }
+  if (ok) *st = Hs;
+}
+
+// Per (session, chunk, head): y = intra-chunk + entering-state terms + D x, the
+// gate, v * norm_w and per-token sums of squares of v over the head. Computed as
+// y^T tiles (p x t): lane l, reg r -> p = 16 i + 4 (l/16) + r, t = 16 ti + l % 16.
+// LDS: xs [Q][P + 4], hs [P][N + 4] (entering state), cs [Q], dt [Q].
+__global__ __launch_bounds__(256) void chunk_out_kernel(ScanArgs a) {
+  extern __shared__ float lds[];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = h / a.hpg;
+  const int t0 = c * a.Q;
+  const int Qc = min(a.Q, a.T - t0);
+  const int PP = a.P + 4, NN = a.N + 4;
+  float *xs = lds;
+  float *hs = xs + (size_t)a.Q * PP;
+  float *css = hs + (size_t)a.P * NN;
+  float *dts = css + a.Q;
+  const size_t rowbase = (size_t)b * a.T + t0;
+  for (int i = tid; i < a.Q * a.P; i += 256) {
+    const int s = i / a.P, p = i - s * a.P;
+    xs[s * PP + p] = s < Qc ? a.xc[(rowbase + s) * a.conv_dim + h * a.P + p] : 0.0f;
+  }
+  const float *hsrc = a.sc + (((size_t)b * a.nch + c) * a.H + h) * (size_t)a.P * a.N;
+  for (int i = tid; i < a.P * a.N; i += 256) {
+    const int p = i / a.N, n = i - p * a.N;
+    hs[p * NN + n] = hsrc[i];
+  }
+  for (int s = tid; s < a.Q; s += 256) {
+    css[s] = s < Qc ? a.cs[(rowbase + s) * a.H + h] : 0.0f;
+    dts[s] = s < Qc ? a.dt[(rowbase + s) * a.H + h] : 0.0f;
+  }
+  __syncthreads();
+  const int nP = a.P / 16;
+  const int nt = (Qc + 15) / 16, np = npairs(a.Q / 16);
+  const float *cbt = a.cbt + (((size_t)b * a.nch + c) * a.G + g) * (size_t)np * 256;
+  const int coff = a.d_inner + a.G * a.N + g * a.N;
+  const float Dh = a.D[h];
+  for (int ti = wave; ti < nt; ti += 4) {
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{};
+    const int t = 16 * ti + (lane & 15);
+    const bool t_ok = t < Qc;
+    const float cst = t_ok ? css[t] : 0.0f;
+    // intra-chunk: B (s x t) = CB^T[s][t] exp(cs_t - cs_s) dt_s for s <= t, from the tile registers
+    for (int si = 0; si <= ti; ++si) {
+      f32x4 m = reinterpret_cast<const f32x4 *>(cbt)[(size_t)pair_index(si, ti) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = 16 * si + 4 * (lane >> 4) + r;
+        m[r] = (t_ok && s <= t) ? m[r] * expf(cst - css[s]) * dts[s] : 0.0f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int s = 16 * si + 4 * (lane >> 4) + kk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nP) {
+            const float av = xs[s * PP + 16 * i + (lane & 15)];   // A (p x s) = x_s[p]
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, m[kk], acc[i], 0, 0, 0);
+          }
+      }
+    }
+    // entering state: A (p x n) = H[p][n], B (n x t) = C_t[n] exp(cs_t)
+    const float ecs = t_ok ? expf(cst) : 0.0f;
+    const float *ct = a.xc + (rowbase + (t_ok ? t : 0)) * a.conv_dim + coff;
+    for (int k0 = 0; k0 < a.N; k0 += 4) {
+      const int n = k0 + (lane >> 4);
+      const float bv = ct[n] * ecs;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < nP) {
+          const float av = hs[(16 * i + (lane & 15)) * NN + n];
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[i], 0, 0, 0);
+        }
+    }
+    // epilogue
+    float ssq = 0.0f;
+    const size_t row = rowbase + (t_ok ? t : 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nP)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p = 16 * i + 4 * (lane >> 4) + r;
+          const int ch = h * a.P + p;
+          const float y = fmaf(Dh, xs[(t_ok ? t : 0) * PP + p], acc[i][r]);
+          const float v = y * silu(a.zx[row * a.zx_stride + ch]);
+          if (t_ok) a.vw[row * a.d_inner + ch] = v * a.norm_w[ch];
+          ssq = fmaf(v, v, ssq);
+        }
+    ssq += __shfl_xor(ssq, 16, 64);
+    ssq += __shfl_xor(ssq, 32, 64);
+    if (t_ok && lane < 16) a.ssh[row * a.H + h] = ssq;
+  }
+}
+
+// RMS factor per (token, norm group) from per-head sums of squares (ng % P == 0).
+__global__ void rms_kernel(ScanArgs a) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)a.B * a.T * a.n_norm) return;
+  const int j = (int)(idx % a.n_norm);
+  const size_t bt = idx / a.n_norm;
+  const int hg = a.ng / a.P;
+  float s = 0.0f;
+  for (int q = 0; q < hg; ++q) s += a.ssh[bt * a.H + j * hg + q];
+  a.rn[bt * a.n_norm + j] = 1.0f / sqrtf(s / (float)a.ng + a.eps);
+}
+
+// conv cache <- the last d_conv-1 raw inputs; one thread per (session, channel) so
+// every old value is read before any is overwritten.
+__global__ void cache_update_kernel(ScanArgs a) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.B * a.conv_dim) return;
+  const int c = idx % a.conv_dim, b = idx / a.conv_dim;
+  bool ok;
+  const int slot = slot_of(a, b, ok);
+  if (!ok) return;
+  const int K1 = a.d_conv - 1;
+  float *cc = a.conv + (size_t)slot * K1 * a.conv_dim + c;
+  float nv[8];
+  for (int k = 0; k < K1; ++k) {
+    const int tau = a.T - K1 + k;           // position of the k-th newest-but-(K1-1-k) input
+    nv[k] = tau >= 0 ? a.zx[((size_t)b * a.T + tau) * a.zx_stride + a.d_inner + c]
+                     : cc[(size_t)(K1 + tau) * a.conv_dim];
+  }
+  for (int k = 0; k < K1; ++k) cc[(size_t)k * a.conv_dim] = nv[k];
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct PrefillWs {
+  float *zx, *xc, *dt, *cs, *cse, *sc, *cbt, *vw, *ssh, *rn;
+  size_t bytes;
+};
+
+PrefillWs prefill_layout(const m2_layer_s &L, int B, int T, int Q, void *base) {
+  const size_t BT = (size_t)B * T;
+  const int nch = (T + Q - 1) / Q;
+  const int nt = Q / 16;
+  const size_t sizes[10] = {
+      BT * L.zx_stride, BT * L.conv_dim, BT * L.cfg.n_heads, BT * L.cfg.n_heads,
+      (size_t)B * nch * L.cfg.n_heads,
+      (size_t)B * nch * L.cfg.n_heads * L.cfg.head_dim * L.cfg.d_state,
+      (size_t)B * nch * L.cfg.n_groups * (size_t)(nt * (nt + 1) / 2) * 256,
+      BT * L.d_inner, BT * L.cfg.n_heads, BT * L.n_norm};
+  PrefillWs w{};
+  float **ptrs[10] = {&w.zx, &w.xc, &w.dt, &w.cs, &w.cse, &w.sc, &w.cbt, &w.vw, &w.ssh, &w.rn};
+  size_t off = 0;
+  for (int i = 0; i < 10; ++i) {
+    *ptrs[i] = base ? reinterpret_cast<float *>(static_cast<char *>(base) + off) : nullptr;
+    off += align256(sizes[i] * sizeof(float));
+  }
+  w.bytes = off;
+  return w;
+}
+
+bool prefill_supported(const m2_layer_s &L) {
+  return L.cfg.head_dim % 16 == 0 && L.cfg.head_dim <= 128 && L.cfg.d_state % 16 == 0 &&
+         L.ng % L.cfg.head_dim == 0;
+}
+
+size_t scan_lds_state(const m2_layer_s &L, int Q) {
+  return sizeof(float) * ((size_t)Q * (L.cfg.head_dim + 4) + 2 * (size_t)Q);
+}
+size_t scan_lds_out(const m2_layer_s &L, int Q) {
+  return sizeof(float) *
+         ((size_t)Q * (L.cfg.head_dim + 4) + (size_t)L.cfg.head_dim * (L.cfg.d_state + 4) + 2 * (size_t)Q);
+}
+
+template <typename F>
+hipError_t allow_lds(F *kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+hipError_t run_gemm(const m2_layer_s &L, bool in_proj, const float *A, int lda, float *C, int ldc,
+                    const float *R, int ldr, const float *rs, int M, hipStream_t stream) {
+  const m2_config &c = L.cfg;
+  const int N = in_proj ? L.d_in_proj : c.d_model;
+  const int K = in_proj ? c.d_model : L.d_inner;
+  if (c.wtype == M2_W_BF16) {
+    GemmArgs g{};
+    g.A = A;
+    g.lda = lda;
+    g.W = static_cast<const unsigned short *>(in_proj ? L.w.w_in : L.w.w_out);
+    g.C = C;
+    g.ldc = ldc;
+    g.R = R;
+    g.ldr = ldr;
+    g.rs = rs;
+    g.n_rs = L.n_norm;
+    g.ng = L.ng;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((N + GBN - 1) / GBN, (M + GBM - 1) / GBM), dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
+  GemmValuArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.W = in_proj ? L.w.w_in : L.w.w_out;
+  g.S = static_cast<const __half *>(in_proj ? L.w.s_in : L.w.s_out);
+  g.wtype = c.wtype;
+  g.q_group = c.wtype == M2_W_INT8G ? c.q_group : K;
+  g.gamma = c.wtype == M2_W_INT8G ? (in_proj ? c.q_gamma_in : c.q_gamma_out) : 1.0f;
+  g.C = C;
+  g.ldc = ldc;
+  g.R = R;
+  g.ldr = ldr;
+  g.rs = rs;
+  g.n_rs = L.n_norm;
+  g.ng = L.ng;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  hipLaunchKernelGGL(gemm_valu_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t prefill_ws_bytes(const m2_layer_s &L, int batch, int seqlen, int chunk) {
+  if (!prefill_supported(L)) return 0;
+  return prefill_layout(L, batch, seqlen, chunk, nullptr).bytes;
+}
+
+hipError_t launch_prefill(const m2_layer_s &L, const m2_state_s &S, const float *x, float *y, int batch,
+                          int seqlen, int chunk, const int32_t *slots, int flags, void *ws_base,
+                          hipStream_t stream) {
+  const m2_config &c = L.cfg;
+  const int B = batch, T = seqlen, Q = chunk;
+  const int M = B * T;
+  PrefillWs ws = prefill_layout(L, B, T, Q, ws_base);
+  ScanArgs a{};
+  a.B = B;
+  a.T = T;
+  a.Q = Q;
+  a.nch = (T + Q - 1) / Q;
+  a.H = c.n_heads;
+  a.P = c.head_dim;
+  a.N = c.d_state;
+  a.G = c.n_groups;
+  a.hpg = L.hpg;
+  a.d_inner = L.d_inner;
+  a.conv_dim = L.conv_dim;
+  a.d_conv = c.d_conv;
+  a.zx_stride = L.zx_stride;
+  a.zx = ws.zx;
+  a.xc = ws.xc;
+  a.dt = ws.dt;
+  a.cs = ws.cs;
+  a.cse = ws.cse;
+  a.sc = ws.sc;
+  a.cbt = ws.cbt;
+  a.vw = ws.vw;
+  a.ssh = ws.ssh;
+  a.rn = ws.rn;
+  a.n_norm = L.n_norm;
+  a.ng = L.ng;
+  a.eps = c.norm_eps;
+  a.conv_w = L.w.conv_w;
+  a.conv_b = L.w.conv_b;
+  a.dt_bias = L.w.dt_bias;
+  a.A_log = L.w.A_log;
+  a.D = L.w.D;
+  a.norm_w = L.w.norm_w;
+  a.ssm = S.ssm;
+  a.conv = S.conv;
+  a.slots = slots;
+  a.n_slots = S.n_slots;
+
+  // 1. in_proj
+  hipError_t e = run_gemm(L, true, x, c.d_model, ws.zx, L.zx_stride, nullptr, 0, nullptr, M, stream);
+  if (e != hipSuccess) return e;
+  // 2. conv + dt
+  {
+    const size_t n = (size_t)M * (L.conv_dim + c.n_heads);
+    hipLaunchKernelGGL(conv_dt_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 3. C B^T tiles
+  hipLaunchKernelGGL(cb_kernel, dim3(a.nch, c.n_groups, B), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 4. chunk states
+  {
+    const size_t lds = scan_lds_state(L, Q);
+    if ((e = allow_lds(chunk_state_kernel, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_state_kernel, dim3(a.nch, c.n_heads, B), dim3(256), lds, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 5. inter-chunk pass (reads the slots' states, writes the final ones)
+  {
+    const size_t n = (size_t)B * c.n_heads * c.head_dim * c.d_state;
+    hipLaunchKernelGGL(state_pass_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 6. chunk outputs, gate, sums of squares
+  {
+    const size_t lds = scan_lds_out(L, Q);
+    if ((e = allow_lds(chunk_out_kernel, lds)) != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_out_kernel, dim3(a.nch, c.n_heads, B), dim3(256), lds, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 7. RMS factors
+  {
+    const size_t n = (size_t)M * L.n_norm;
+    hipLaunchKernelGGL(rms_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 8. out_proj (+ residual)
+  e = run_gemm(L, false, ws.vw, L.d_inner, y, c.d_model, (flags & M2_RESIDUAL) ? x : nullptr, c.d_model, ws.rn, M,
+               stream);
+  if (e != hipSuccess) return e;
+  // 9. conv cache
+  {
+    const int n = B * L.conv_dim;
+    hipLaunchKernelGGL(cache_update_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace m2d
