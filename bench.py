@@ -138,8 +138,8 @@ def main():
     from full_duplex_speech_mamba2_amd import m2, synth
 
     wl = synth.workload(args.config)
-    if wl.prefill or wl.layers != 1:
-        print("bench.py times single-layer decode workloads (1 or 2)", file=sys.stderr)
+    if wl.layers != 1:
+        print("bench.py times single-layer workloads (configs 1, 2 and 4)", file=sys.stderr)
         sys.exit(2)
     dims, B = wl.dims, wl.batch
     dev = torch.device("cuda:0")
@@ -158,6 +158,9 @@ def main():
 
     layers = [m2.Layer(dims, w, dev) for _ in range(max(1, args.copies))]
     st = m2.State(layers[0], B, torch.from_numpy(ssm0).to(dev), torch.from_numpy(conv0).to(dev))
+    prefill_rec = None
+    if wl.prefill:
+        prefill_rec = time_prefill(args, wl, layers[0], st, dev)
     xs = torch.from_numpy(xs_np).to(dev)
     ys = torch.empty_like(xs)
     ws = layers[0].workspace("step", B)
@@ -248,10 +251,55 @@ def main():
         "cpu_baseline": None,
         "parity": None,
     }
+    if prefill_rec is not None:
+        out["prefill"] = prefill_rec
 
     if not args.no_cpu:
         out["cpu_baseline"], out["parity"] = cpu_baseline_and_parity(args, wl, w, xs_np, ssm0, conv0)
     print(json.dumps(out), flush=True)
+
+
+def prefill_flops(dims, B, T, Q):
+    """Algorithmic flops of one prefill: the two projections and the chunked scan."""
+    d = dims
+    proj = 2.0 * B * T * (d.d_in_proj * d.d_model + d.d_model * d.d_inner)
+    nch = -(-T // Q)
+    cb = 2.0 * B * nch * d.n_groups * Q * Q * d.d_state
+    diag = 2.0 * B * nch * d.n_heads * (Q * (Q + 1) / 2) * d.head_dim
+    states = 2.0 * B * nch * d.n_heads * Q * d.head_dim * d.d_state
+    off = 2.0 * B * nch * d.n_heads * Q * d.d_state * d.head_dim
+    return proj, cb + diag + states + off
+
+
+def time_prefill(args, wl, layer, st, dev):
+    """Time m2_prefill of the workload's prompt from a zero state (events around each call)."""
+    import numpy as np
+    import torch
+    from full_duplex_speech_mamba2_amd import m2, synth
+    dims, B, T, Q = wl.dims, wl.batch, wl.prefill, wl.chunk
+    x = torch.from_numpy(synth.make_prompt(dims, wl.seed, B, T)).to(dev)
+    y = torch.empty_like(x)
+    ws = layer.workspace("prefill", B, T, Q)
+    times = []
+    for it in range(5):
+        st.zero()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        m2.prefill(layer, st, x, y, chunk=Q, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if it >= 2:
+            times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    proj, scan = prefill_flops(dims, B, T, Q)
+    executed = 2 * proj + scan          # hi/lo activations: two MFMAs per projection product
+    return {"batch": B, "seqlen": T, "chunk": Q, "ms": round(ms, 4),
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "algorithmic_tflop": round((proj + scan) / 1e12, 4),
+            "algorithmic_tflops_per_s": round((proj + scan) / (ms * 1e-3) / 1e12, 2),
+            "executed_tflops_per_s": round(executed / (ms * 1e-3) / 1e12, 2),
+            "mfma_bf16_peak_tflops": 2500.0,
+            "workspace_bytes": int(ws.numel())}
 
 
 def cpu_baseline_and_parity(args, wl, w, xs_np, ssm0, conv0):

@@ -372,34 +372,37 @@ __global__ __launch_bounds__(256) void cb_kernel(ScanArgs a) {
 
 // Per (session, chunk, head): cs (inclusive cumsum of dt A), chunk-end cumsum, and
 // the chunk state S_c[p][n] = sum_s exp(cs_end - cs_s) dt_s x_s[p] B_s[n].
-// LDS: xs [Q][P + 4] (x of the head), w [Q], cs [Q].
-__global__ __launch_bounds__(256) void chunk_state_kernel(ScanArgs a) {
+// One wave per 16-row p-tile (P/16 waves); B of the chunk is staged in LDS and x is
+// read from global one k-step ahead. LDS: bs [Q][N + 4], w [Q], cs [Q].
+template <int NT>
+__global__ __launch_bounds__(512) void chunk_state_kernel(ScanArgs a) {
   extern __shared__ float lds[];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nthr = blockDim.x;
   const int g = h / a.hpg;
   const int t0 = c * a.Q;
   const int Qc = min(a.Q, a.T - t0);
-  const int PP = a.P + 4;
-  float *xs = lds;
-  float *ws = xs + (size_t)a.Q * PP;
+  const int NN = a.N + 4;
+  float *bs = lds;
+  float *ws = bs + (size_t)a.Q * NN;
   float *css = ws + a.Q;
   const size_t rowbase = (size_t)b * a.T + t0;
   const float A = -expf(a.A_log[h]);
-  // inclusive scan of dt A over the chunk (Hillis-Steele in LDS)
-  for (int s = tid; s < a.Q; s += 256) css[s] = s < Qc ? a.dt[(rowbase + s) * a.H + h] * A : 0.0f;
+  // inclusive scan of dt A over the chunk (Hillis-Steele in LDS); Q <= 4 * nthr
+  for (int s = tid; s < a.Q; s += nthr) css[s] = s < Qc ? a.dt[(rowbase + s) * a.H + h] * A : 0.0f;
   __syncthreads();
   for (int off = 1; off < a.Q; off <<= 1) {
     float v[4];
     int n = 0;
-    for (int s = tid; s < a.Q; s += 256) v[n++] = s >= off ? css[s - off] : 0.0f;
+    for (int s = tid; s < a.Q; s += nthr) v[n++] = s >= off ? css[s - off] : 0.0f;
     __syncthreads();
     n = 0;
-    for (int s = tid; s < a.Q; s += 256) css[s] += v[n++];
+    for (int s = tid; s < a.Q; s += nthr) css[s] += v[n++];
     __syncthreads();
   }
   const float cend = css[Qc - 1];
-  for (int s = tid; s < a.Q; s += 256) {
+  for (int s = tid; s < a.Q; s += nthr) {
     float w = 0.0f;
     if (s < Qc) {
       a.cs[(rowbase + s) * a.H + h] = css[s];
@@ -408,42 +411,51 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(ScanArgs a) {
     ws[s] = w;
   }
   if (tid == 0) a.cse[((size_t)b * a.nch + c) * a.H + h] = cend;
-  for (int i = tid; i < a.Q * a.P; i += 256) {
-    const int s = i / a.P, p = i - s * a.P;
-    xs[s * PP + p] = s < Qc ? a.xc[(rowbase + s) * a.conv_dim + h * a.P + p] : 0.0f;
+  const int boff = a.d_inner + g * a.N;
+  const int n4 = a.N / 4;
+  for (int i = tid; i < a.Q * n4; i += nthr) {
+    const int s = i / n4, q = i - s * n4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s < Qc) v = *reinterpret_cast<const float4 *>(a.xc + (rowbase + s) * a.conv_dim + boff + 4 * q);
+    *reinterpret_cast<float4 *>(bs + s * NN + 4 * q) = v;
   }
   __syncthreads();
-  // S_c tiles (p-tile i, n-tile j): A (p x s) = x_s[p] w_s from LDS, B (s x n) = B_s[n];
-  // the k index of lane group q4 = l/16 at step kk is s = s0 + 4 q4 + kk
-  const int nP = a.P / 16, nN = a.N / 16;
-  const int boff = a.d_inner + g * a.N;
-  float *out = a.sc + (((size_t)b * a.nch + c) * a.H + h) * (size_t)a.P * a.N;
-  for (int j = wave; j < nN; j += 4) {
-    f32x4 acc[8];
+  // wave = p-tile i; k index of lane group l/16 at step kk of block s0 is s = s0 + 4 (l/16) + kk
+  const int p = 16 * wave + (lane & 15);
+  const float *xcol = a.xc + rowbase * a.conv_dim + h * a.P + p;
+  f32x4 acc[NT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = f32x4{};
-    const int n = 16 * j + (lane & 15);
-    for (int s0 = 0; s0 < Qc; s0 += 16) {
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{};
+  float xa[4], xn[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int s = s0 + 4 * (lane >> 4) + kk;
-        const float bv = s < Qc ? a.xc[(rowbase + s) * a.conv_dim + boff + n] : 0.0f;
-        const float w = ws[s];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (i < nP) {
-            const float av = xs[s * PP + 16 * i + (lane & 15)] * w;
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[i], 0, 0, 0);
-          }
-      }
-    }
-    // lane l, reg r -> p = 16 i + 4 (l/16) + r, n = 16 j + l % 16
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < nP)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) out[(size_t)(16 * i + 4 * (lane >> 4) + r) * a.N + n] = acc[i][r];
+  for (int kk = 0; kk < 4; ++kk) {
+    const int s = 4 * (lane >> 4) + kk;
+    xa[kk] = s < Qc ? xcol[(size_t)s * a.conv_dim] : 0.0f;
   }
+  for (int s0 = 0; s0 < Qc; s0 += 16) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int s = s0 + 16 + 4 * (lane >> 4) + kk;
+      xn[kk] = s < Qc ? xcol[(size_t)s * a.conv_dim] : 0.0f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int s = s0 + 4 * (lane >> 4) + kk;
+      const float av = xa[kk] * ws[s];
+      const float *brow = bs + s * NN + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, brow[16 * j], acc[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) xa[kk] = xn[kk];
+  }
+  // lane l, reg r -> p = 16 wave + 4 (l/16) + r, n = 16 j + l % 16
+  float *out = a.sc + (((size_t)b * a.nch + c) * a.H + h) * (size_t)a.P * a.N;
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        out[(size_t)(16 * wave + 4 * (lane >> 4) + r) * a.N + 16 * j + (lane & 15)] = acc[j][r];
 }
 
 // Per (session, head, state element): H_c = exp(cs_end_c) H_{c-1} + S_c over the
@@ -471,7 +483,9 @@ __global__ void state_pass_kernel(ScanArgs a) {
 // Per (session, chunk, head): y = intra-chunk + entering-state terms + D x, the
 // gate, v * norm_w and per-token sums of squares of v over the head. Computed as
 // y^T tiles (p x t): lane l, reg r -> p = 16 i + 4 (l/16) + r, t = 16 ti + l % 16.
-// LDS: xs [Q][P + 4], hs [P][N + 4] (entering state), cs [Q], dt [Q].
+// Operands held in LDS: xs [Q][P + 4], hs [P][N + 4] (entering state); the C.B^T
+// tiles and C rows come from global memory one step ahead of their use.
+template <int NP>
 __global__ __launch_bounds__(256) void chunk_out_kernel(ScanArgs a) {
   extern __shared__ float lds[];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -485,35 +499,43 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(ScanArgs a) {
   float *css = hs + (size_t)a.P * NN;
   float *dts = css + a.Q;
   const size_t rowbase = (size_t)b * a.T + t0;
-  for (int i = tid; i < a.Q * a.P; i += 256) {
-    const int s = i / a.P, p = i - s * a.P;
-    xs[s * PP + p] = s < Qc ? a.xc[(rowbase + s) * a.conv_dim + h * a.P + p] : 0.0f;
+  const int p4 = a.P / 4;
+  for (int i = tid; i < a.Q * p4; i += 256) {
+    const int s = i / p4, q = i - s * p4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s < Qc) v = *reinterpret_cast<const float4 *>(a.xc + (rowbase + s) * a.conv_dim + h * a.P + 4 * q);
+    *reinterpret_cast<float4 *>(xs + s * PP + 4 * q) = v;
   }
   const float *hsrc = a.sc + (((size_t)b * a.nch + c) * a.H + h) * (size_t)a.P * a.N;
-  for (int i = tid; i < a.P * a.N; i += 256) {
-    const int p = i / a.N, n = i - p * a.N;
-    hs[p * NN + n] = hsrc[i];
+  const int n4 = a.N / 4;
+  for (int i = tid; i < a.P * n4; i += 256) {
+    const int p = i / n4, q = i - p * n4;
+    *reinterpret_cast<float4 *>(hs + p * NN + 4 * q) = reinterpret_cast<const float4 *>(hsrc)[i];
   }
   for (int s = tid; s < a.Q; s += 256) {
     css[s] = s < Qc ? a.cs[(rowbase + s) * a.H + h] : 0.0f;
     dts[s] = s < Qc ? a.dt[(rowbase + s) * a.H + h] : 0.0f;
   }
   __syncthreads();
-  const int nP = a.P / 16;
   const int nt = (Qc + 15) / 16, np = npairs(a.Q / 16);
-  const float *cbt = a.cbt + (((size_t)b * a.nch + c) * a.G + g) * (size_t)np * 256;
+  const f32x4 *cbt = reinterpret_cast<const f32x4 *>(a.cbt + (((size_t)b * a.nch + c) * a.G + g) * (size_t)np * 256);
   const int coff = a.d_inner + a.G * a.N + g * a.N;
   const float Dh = a.D[h];
+#pragma unroll 1
   for (int ti = wave; ti < nt; ti += 4) {
-    f32x4 acc[8];
+    f32x4 acc[NP];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = f32x4{};
+    for (int i = 0; i < NP; ++i) acc[i] = f32x4{};
     const int t = 16 * ti + (lane & 15);
     const bool t_ok = t < Qc;
     const float cst = t_ok ? css[t] : 0.0f;
-    // intra-chunk: B (s x t) = CB^T[s][t] exp(cs_t - cs_s) dt_s for s <= t, from the tile registers
+    // intra-chunk: B (s x t) = CB^T[s][t] exp(cs_t - cs_s) dt_s for s <= t, straight from the
+    // tile registers; A (p x s) = x_s[p] from LDS
+    f32x4 mnext = cbt[(size_t)pair_index(0, ti) * 64 + lane];
+#pragma unroll 1
     for (int si = 0; si <= ti; ++si) {
-      f32x4 m = reinterpret_cast<const f32x4 *>(cbt)[(size_t)pair_index(si, ti) * 64 + lane];
+      f32x4 m = mnext;
+      if (si < ti) mnext = cbt[(size_t)pair_index(si + 1, ti) * 64 + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int s = 16 * si + 4 * (lane >> 4) + r;
@@ -521,41 +543,47 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(ScanArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int s = 16 * si + 4 * (lane >> 4) + kk;
+        const float *xrow = xs + (16 * si + 4 * (lane >> 4) + kk) * PP + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (i < nP) {
-            const float av = xs[s * PP + 16 * i + (lane & 15)];   // A (p x s) = x_s[p]
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, m[kk], acc[i], 0, 0, 0);
-          }
+        for (int i = 0; i < NP; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(xrow[16 * i], m[kk], acc[i], 0, 0, 0);
       }
     }
-    // entering state: A (p x n) = H[p][n], B (n x t) = C_t[n] exp(cs_t)
+    // entering state: A (p x n) = H[p][n] from LDS, B (n x t) = C_t[n] exp(cs_t), in blocks of
+    // 16 n (N % 16 == 0), the next block's C values loaded while this one is multiplied
     const float ecs = t_ok ? expf(cst) : 0.0f;
-    const float *ct = a.xc + (rowbase + (t_ok ? t : 0)) * a.conv_dim + coff;
-    for (int k0 = 0; k0 < a.N; k0 += 4) {
-      const int n = k0 + (lane >> 4);
-      const float bv = ct[n] * ecs;
+    const float *ct = a.xc + (rowbase + (t_ok ? t : 0)) * a.conv_dim + coff + (lane >> 4);
+    float cv[4], cn[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < nP) {
-          const float av = hs[(16 * i + (lane & 15)) * NN + n];
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[i], 0, 0, 0);
-        }
+    for (int q = 0; q < 4; ++q) cv[q] = ct[4 * q];
+#pragma unroll 1
+    for (int n0 = 0; n0 < a.N; n0 += 16) {
+      const bool more = n0 + 16 < a.N;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cn[q] = more ? ct[n0 + 16 + 4 * q] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float *hrow = hs + (lane & 15) * NN + n0 + 4 * q + (lane >> 4);
+        const float bv = cv[q] * ecs;
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(hrow[16 * i * NN], bv, acc[i], 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cv[q] = cn[q];
     }
     // epilogue
     float ssq = 0.0f;
     const size_t row = rowbase + (t_ok ? t : 0);
+    const float *zrow = a.zx + row * a.zx_stride + h * a.P;
+    const float *xrow = xs + (t_ok ? t : 0) * PP;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < nP)
+    for (int i = 0; i < NP; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; ++r) {
           const int p = 16 * i + 4 * (lane >> 4) + r;
-          const int ch = h * a.P + p;
-          const float y = fmaf(Dh, xs[(t_ok ? t : 0) * PP + p], acc[i][r]);
-          const float v = y * silu(a.zx[row * a.zx_stride + ch]);
-          if (t_ok) a.vw[row * a.d_inner + ch] = v * a.norm_w[ch];
+          const float y = fmaf(Dh, xrow[p], acc[i][r]);
+          const float v = y * silu(zrow[p]);
+          if (t_ok) a.vw[row * a.d_inner + h * a.P + p] = v * a.norm_w[h * a.P + p];
           ssq = fmaf(v, v, ssq);
         }
     ssq += __shfl_xor(ssq, 16, 64);
@@ -626,11 +654,11 @@ PrefillWs prefill_layout(const m2_layer_s &L, int B, int T, int Q, void *base) {
 
 bool prefill_supported(const m2_layer_s &L) {
   return L.cfg.head_dim % 16 == 0 && L.cfg.head_dim <= 128 && L.cfg.d_state % 16 == 0 &&
-         L.ng % L.cfg.head_dim == 0;
+         L.cfg.d_state <= 256 && L.ng % L.cfg.head_dim == 0;
 }
 
 size_t scan_lds_state(const m2_layer_s &L, int Q) {
-  return sizeof(float) * ((size_t)Q * (L.cfg.head_dim + 4) + 2 * (size_t)Q);
+  return sizeof(float) * ((size_t)Q * (L.cfg.d_state + 4) + 2 * (size_t)Q);
 }
 size_t scan_lds_out(const m2_layer_s &L, int Q) {
   return sizeof(float) *
@@ -642,6 +670,49 @@ hipError_t allow_lds(F *kernel, size_t bytes) {
   if (bytes <= 65536) return hipSuccess;
   return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int NT>
+hipError_t launch_chunk_state_t(const ScanArgs &a, size_t lds, dim3 grid, dim3 block, hipStream_t stream) {
+  hipError_t e = allow_lds(chunk_state_kernel<NT>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_state_kernel<NT>, grid, block, lds, stream, a);
+  return hipGetLastError();
+}
+
+// n-tiles of the state: d_state / 16 in {1, 2, 4, 8, 16}
+hipError_t launch_chunk_state(int nt, const ScanArgs &a, size_t lds, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (nt) {
+    case 1: return launch_chunk_state_t<1>(a, lds, grid, block, stream);
+    case 2: return launch_chunk_state_t<2>(a, lds, grid, block, stream);
+    case 4: return launch_chunk_state_t<4>(a, lds, grid, block, stream);
+    case 8: return launch_chunk_state_t<8>(a, lds, grid, block, stream);
+    case 16: return launch_chunk_state_t<16>(a, lds, grid, block, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int NP>
+hipError_t launch_chunk_out_t(const ScanArgs &a, size_t lds, dim3 grid, hipStream_t stream) {
+  hipError_t e = allow_lds(chunk_out_kernel<NP>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_out_kernel<NP>, grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+// p-tiles of a head: head_dim / 16 in 1 .. 8
+hipError_t launch_chunk_out(int np, const ScanArgs &a, size_t lds, dim3 grid, hipStream_t stream) {
+  switch (np) {
+    case 1: return launch_chunk_out_t<1>(a, lds, grid, stream);
+    case 2: return launch_chunk_out_t<2>(a, lds, grid, stream);
+    case 3: return launch_chunk_out_t<3>(a, lds, grid, stream);
+    case 4: return launch_chunk_out_t<4>(a, lds, grid, stream);
+    case 5: return launch_chunk_out_t<5>(a, lds, grid, stream);
+    case 6: return launch_chunk_out_t<6>(a, lds, grid, stream);
+    case 7: return launch_chunk_out_t<7>(a, lds, grid, stream);
+    case 8: return launch_chunk_out_t<8>(a, lds, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t run_gemm(const m2_layer_s &L, bool in_proj, const float *A, int lda, float *C, int ldc,
@@ -756,9 +827,9 @@ hipError_t launch_prefill(const m2_layer_s &L, const m2_state_s &S, const float 
   // 4. chunk states
   {
     const size_t lds = scan_lds_state(L, Q);
-    if ((e = allow_lds(chunk_state_kernel, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_state_kernel, dim3(a.nch, c.n_heads, B), dim3(256), lds, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_chunk_state(c.d_state / 16, a, lds, dim3(a.nch, c.n_heads, B), dim3(64 * (c.head_dim / 16)),
+                                stream)) != hipSuccess)
+      return e;
   }
   // 5. inter-chunk pass (reads the slots' states, writes the final ones)
   {
@@ -769,9 +840,7 @@ hipError_t launch_prefill(const m2_layer_s &L, const m2_state_s &S, const float 
   // 6. chunk outputs, gate, sums of squares
   {
     const size_t lds = scan_lds_out(L, Q);
-    if ((e = allow_lds(chunk_out_kernel, lds)) != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_out_kernel, dim3(a.nch, c.n_heads, B), dim3(256), lds, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_chunk_out(c.head_dim / 16, a, lds, dim3(a.nch, c.n_heads, B), stream)) != hipSuccess) return e;
   }
   // 7. RMS factors
   {
