@@ -76,8 +76,7 @@ def kernel_bytes(dims, B):
     ssd = state + B * (2 * d.d_inner + 2 * d.n_groups * d.d_state + d.n_heads) * f + 2 * d.n_heads * f + v
     gemv_out = w_out + v + d.d_inner * f + io
     step = w_in + w_out + state + cache + conv_par + head_par + d.d_inner * f + 2 * io
-    return {"gemv_in": gemv_in, "ssd_step": ssd, "gemv_out": gemv_out, "ssd_out": ssd + gemv_out,
-            "step": step}
+    return {"gemv_in": gemv_in, "ssd_step": ssd, "gemv_out": gemv_out, "step": step}
 
 
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
@@ -216,8 +215,7 @@ def main():
     for t in range(kp):
         m2.step_timed(layers[t % nl], st, xs[t % nx], ys[t % nx], evs[t], ws=ws)
     torch.cuda.synchronize()
-    names = (["gemv_in", "ssd_step", "gemv_out"] if layers[0].step_kernel_count(B) == 3
-             else ["gemv_in", "ssd_out"])
+    names = ["gemv_in", "ssd_step", "gemv_out"]
     dur_us = {n: 1000.0 * float(np.mean([hip_elapsed_ms(hip, evs[t][i], evs[t][i + 1]) for t in range(kp)]))
               for i, n in enumerate(names)}
     for row in evs:

@@ -562,6 +562,188 @@ __global__ __launch_bounds__(kThreads) void ssd_step_kernel(SsdArgs a) {
   ssd_item<4, 8>(a, h, ps, blockIdx.y, threadIdx.x >> 6, threadIdx.x & 63, wsum);
 }
 
+
+// ---------------------------------------------------------------------------
+// gemv_mfma: batch >= 3 with bf16 or int8 (q_group % 32 == 0) weights. Partial
+// sums out[b][row] over one K chunk (blockIdx.y) as MFMA 16x16x32 bf16 products:
+// A = 16 weight rows x 32 k straight from HBM (one 16-byte or 8-byte load per lane
+// and k-step, a K tile of 8 steps in flight), B = 32 k x 16 sessions of the
+// activations, staged per 256-wide K tile in LDS as bf16 hi + lo (an fp32 value is
+// hi + lo to 2^-16 relative; bf16 and int8 weights are exact in bf16), two MFMAs
+// per product. gemv_mfma_reduce sums the chunks in a fixed order and applies the
+// row epilogue, so results do not depend on scheduling.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMKT = 256;          // K tile
+constexpr int kMLD = kMKT + 8;     // LDS row stride (bf16)
+
+struct MfmaArgs {
+  const void *W;
+  const __half *S;
+  int rows, K, q_group, kchunk;
+  const float *act;                // [B][K]
+  int B;
+  const float *rn;                 // optional [B][n_norm]: act[b][k] *= rn[b][k / ng]
+  int ng, n_norm;
+  float *part;                     // [KS][B][rows]
+};
+
+__device__ __forceinline__ unsigned short f2bf(float f) {
+  const unsigned u = __float_as_uint(f);
+  return (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int WT, int NBT>
+__global__ __launch_bounds__(256) void gemv_mfma_kernel(MfmaArgs a) {
+  __shared__ unsigned short xh[NBT * 16 * kMLD];
+  __shared__ unsigned short xl[NBT * 16 * kMLD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rbase = blockIdx.x * 64 + wave * 16;
+  const int arow = rbase + (lane & 15);             // A-operand row of this lane
+  const bool arow_ok = arow < a.rows;
+  const int k_begin = blockIdx.y * a.kchunk, k_end = min(a.K, k_begin + a.kchunk);
+  const int kq = (lane >> 4) * 8;                   // this lane's 8 k within a 32-wide step
+  f32x4 acc[NBT];
+#pragma unroll
+  for (int j = 0; j < NBT; ++j) acc[j] = f32x4{};
+  // int8: rows (l/16)*4 + r of the C tile carry a scale per q_group columns
+  float sc[4] = {1.f, 1.f, 1.f, 1.f};
+  const int ngrp = a.K / a.q_group;
+
+  for (int kt = k_begin; kt < k_end; kt += kMKT) {
+    const int klen = min(kMKT, k_end - kt);         // multiple of 16
+    // weights of this tile first: 8 k-steps per lane in flight
+    bf16x8 wf[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int k = kt + 32 * st + kq;
+      if (WT == M2_W_BF16) {
+        const bool ok = arow_ok && 32 * st + kq < klen;
+        wf[st] = ok ? *reinterpret_cast<const bf16x8 *>(static_cast<const unsigned short *>(a.W) + (size_t)arow * a.K + k)
+                    : bf16x8{};
+      } else {
+        const bool ok = arow_ok && 32 * st + kq < klen;
+        uint2 q = ok ? *reinterpret_cast<const uint2 *>(static_cast<const int8_t *>(a.W) + (size_t)arow * a.K + k)
+                     : make_uint2(0u, 0u);
+        bf16x8 f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const unsigned wd = e < 4 ? q.x : q.y;
+          const float v = (float)((int32_t)(wd << (24 - 8 * (e & 3))) >> 24);
+          f[e] = __builtin_bit_cast(__bf16, f2bf(v));
+        }
+        wf[st] = f;
+      }
+    }
+    // activations of the tile as bf16 hi / lo: 16 NBT sessions x 256 k (zero-filled)
+    for (int i = tid; i < NBT * 16 * (kMKT / 4); i += 256) {
+      const int b = i / (kMKT / 4), k4 = (i - b * (kMKT / 4)) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (b < a.B && k4 < klen) {
+        v = *reinterpret_cast<const float4 *>(a.act + (size_t)b * a.K + kt + k4);
+        if (a.rn) {
+          const float r = a.rn[b * a.n_norm + (kt + k4) / a.ng];
+          v.x *= r; v.y *= r; v.z *= r; v.w *= r;
+        }
+      }
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      u16x4 h, l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = f2bf(vv[e]);
+        l[e] = f2bf(vv[e] - __uint_as_float((unsigned)h[e] << 16));
+      }
+      *reinterpret_cast<u16x4 *>(&xh[b * kMLD + k4]) = h;
+      *reinterpret_cast<u16x4 *>(&xl[b * kMLD + k4]) = l;
+    }
+    __syncthreads();
+    if (WT == M2_W_BF16) {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (32 * st >= klen) break;
+#pragma unroll
+        for (int j = 0; j < NBT; ++j) {
+          const int b = 16 * j + (lane & 15);
+          const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&xh[b * kMLD + 32 * st + kq]);
+          const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&xl[b * kMLD + 32 * st + kq]);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], bh, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], bl, acc[j], 0, 0, 0);
+        }
+      }
+    } else {
+      // one scale group = q_group / 32 k-steps: products of a group gathered, then scaled
+      const int spg = a.q_group / 32;
+      f32x4 gacc[NBT];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (32 * st >= klen) break;
+        if (st % spg == 0) {
+          const int g = (kt + 32 * st) / a.q_group;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rr = rbase + (lane >> 4) * 4 + r;
+            sc[r] = rr < a.rows ? __half2float(a.S[(size_t)rr * ngrp + g]) : 0.0f;
+          }
+#pragma unroll
+          for (int j = 0; j < NBT; ++j) gacc[j] = f32x4{};
+        }
+#pragma unroll
+        for (int j = 0; j < NBT; ++j) {
+          const int b = 16 * j + (lane & 15);
+          const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&xh[b * kMLD + 32 * st + kq]);
+          const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&xl[b * kMLD + 32 * st + kq]);
+          gacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], bh, gacc[j], 0, 0, 0);
+          gacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], bl, gacc[j], 0, 0, 0);
+        }
+        if (st % spg == spg - 1 || 32 * (st + 1) >= klen) {
+#pragma unroll
+          for (int j = 0; j < NBT; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc[r], gacc[j][r], acc[j][r]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // lane l, reg r -> row rbase + (l/16)*4 + r, session 16 j + l % 16
+  float *part = a.part + (size_t)blockIdx.y * a.B * a.rows;
+#pragma unroll
+  for (int j = 0; j < NBT; ++j) {
+    const int b = 16 * j + (lane & 15);
+    if (b >= a.B) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rr = rbase + (lane >> 4) * 4 + r;
+      if (rr < a.rows) part[(size_t)b * a.rows + rr] = acc[j][r];
+    }
+  }
+}
+
+// Sum of the K-chunk partials in chunk order, then the row epilogue.
+template <int EPI>
+__global__ void gemv_mfma_reduce_kernel(GemvArgs a, const float *part, int ks) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.rows * a.B) return;
+  const int b = idx / a.rows, row = idx - b * a.rows;
+  const EpiIn e = epilogue_prefetch<EPI>(a, row, b);
+  float v = 0.0f;
+  for (int s = 0; s < ks; ++s) v += part[((size_t)s * a.B + b) * a.rows + row];
+  gemv_epilogue<EPI>(a, row, b, v, e);
+}
+
+// RMS factors of every session for the MFMA out_proj: rn[b][j].
+__global__ void rms_decode_kernel(const float *ss, int n_partials, int n_norm, int ng, float eps, float *rn, int B) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * n_norm) return;
+  const int b = idx / n_norm, j = idx - b * n_norm;
+  const int per = n_partials / n_norm;
+  float s = 0.0f;
+  for (int q = 0; q < per; ++q) s += ss[(size_t)b * n_partials + j * per + q];
+  rn[idx] = 1.0f / sqrtf(s / (float)ng + eps);
+}
+
 __global__ void state_zero_kernel(float *ssm, float *conv, size_t ssm_per, size_t conv_per,
                                   const int32_t *slots, int n, int n_slots) {
   const int i = blockIdx.y;
@@ -656,6 +838,58 @@ hipError_t dispatch_wt(int wtype, const GemvArgs &a, hipStream_t stream) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA GEMV planning: K chunks of whole 256-wide tiles, about 1280 workgroups.
+struct MfmaPlan {
+  int ks, kchunk;
+};
+
+MfmaPlan mfma_plan(int rows, int K) {
+  const int rb = (rows + 63) / 64;
+  const int ntiles = (K + kMKT - 1) / kMKT;
+  int ks = (1280 + rb - 1) / rb;
+  if (ks > ntiles) ks = ntiles;
+  if (ks < 1) ks = 1;
+  const int tiles_per = (ntiles + ks - 1) / ks;
+  MfmaPlan p;
+  p.kchunk = tiles_per * kMKT;
+  p.ks = (K + p.kchunk - 1) / p.kchunk;
+  return p;
+}
+
+template <int WT>
+hipError_t launch_mfma(const MfmaArgs &m, hipStream_t stream) {
+  dim3 grid((m.rows + 63) / 64, (m.K + m.kchunk - 1) / m.kchunk);
+  if (m.B <= 16) hipLaunchKernelGGL((gemv_mfma_kernel<WT, 1>), grid, dim3(256), 0, stream, m);
+  else hipLaunchKernelGGL((gemv_mfma_kernel<WT, 2>), grid, dim3(256), 0, stream, m);
+  return hipGetLastError();
+}
+
+// One MFMA GEMV + reduce for the arguments of a gemv_* launch.
+template <int EPI>
+hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, const float *rn, float *part,
+                         hipStream_t stream) {
+  const MfmaPlan p = mfma_plan(g.rows, g.K);
+  MfmaArgs m{};
+  m.W = g.W;
+  m.S = g.S;
+  m.rows = g.rows;
+  m.K = g.K;
+  m.q_group = c.wtype == M2_W_INT8G ? c.q_group : g.K;
+  m.kchunk = p.kchunk;
+  m.act = g.act;
+  m.B = g.B;
+  m.rn = rn;
+  m.ng = g.ng;
+  m.n_norm = g.n_norm;
+  m.part = part;
+  hipError_t e = c.wtype == M2_W_BF16 ? launch_mfma<M2_W_BF16>(m, stream) : launch_mfma<M2_W_INT8G>(m, stream);
+  if (e != hipSuccess) return e;
+  const int n = g.rows * g.B;
+  hipLaunchKernelGGL(gemv_mfma_reduce_kernel<EPI>, dim3((n + 255) / 256), dim3(256), 0, stream, g, part, p.ks);
+  return hipGetLastError();
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int log2i(int v) {
@@ -679,6 +913,14 @@ StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base) {
   off += v;
   w.ss = p ? reinterpret_cast<float *>(p + off) : nullptr;
   off += ss;
+  if (step_uses_mfma(L, batch)) {
+    const MfmaPlan pi = mfma_plan(L.d_in_proj, L.cfg.d_model), po = mfma_plan(L.cfg.d_model, L.d_inner);
+    const size_t n_in = (size_t)pi.ks * batch * L.d_in_proj, n_out = (size_t)po.ks * batch * L.cfg.d_model;
+    w.part = p ? reinterpret_cast<float *>(p + off) : nullptr;
+    off += align256(sizeof(float) * (n_in > n_out ? n_in : n_out));
+    w.rn = p ? reinterpret_cast<float *>(p + off) : nullptr;
+    off += align256(sizeof(float) * (size_t)batch * L.n_norm);
+  }
   w.bytes = off;
   return w;
 }
@@ -715,7 +957,9 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   gi.conv_cache = S.conv;
   gi.slots = slots;
   gi.n_slots = S.n_slots;
-  e = dispatch_wt<PRO_PLAIN, EPI_INPROJ>(c.wtype, gi, stream);
+  const bool mfma = step_uses_mfma(L, batch);
+  e = mfma ? run_mfma_gemv<EPI_INPROJ>(c, gi, nullptr, ws.part, stream)
+           : dispatch_wt<PRO_PLAIN, EPI_INPROJ>(c.wtype, gi, stream);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return e;
 
@@ -765,9 +1009,26 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return e;
-  e = dispatch_wt<PRO_NORM, EPI_OUT>(c.wtype, go, stream);
+  if (mfma) {
+    const int n = batch * L.n_norm;
+    hipLaunchKernelGGL(rms_decode_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, ws.ss, L.n_partials, L.n_norm,
+                       L.ng, c.norm_eps, ws.rn, batch);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = run_mfma_gemv<EPI_OUT>(c, go, ws.rn, ws.part, stream);
+  } else {
+    e = dispatch_wt<PRO_NORM, EPI_OUT>(c.wtype, go, stream);
+  }
   if (e == hipSuccess) e = mark(3);
   return e;
+}
+
+// Batches of 3..32 sessions with bf16 weights, or int8 weights whose scale groups
+// hold whole 32-wide k-steps, use the MFMA GEMVs.
+bool step_uses_mfma(const m2_layer_s &L, int batch) {
+  const m2_config &c = L.cfg;
+  if (batch < 3 || batch > 32) return false;
+  if (c.wtype == M2_W_BF16) return true;
+  return c.wtype == M2_W_INT8G && c.q_group % 32 == 0 && c.q_group <= kMKT;
 }
 
 

@@ -39,6 +39,8 @@ struct StepWs {
   float *zx;        // [B][d_in_proj]: z raw | conv+SiLU(x|B|C) | softplus dt
   float *v;         // [B][d_inner]: gated SSD output
   float *ss;        // [B][n_partials]: sums of squares of v per partial range
+  float *part;      // MFMA GEMVs: K-chunk partial sums [KS][B][rows]
+  float *rn;        // MFMA out_proj: RMS factors [B][n_norm]
   size_t bytes;
 };
 StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base);
@@ -47,8 +49,8 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
                        const int32_t *slots, int flags, const StepWs &ws, hipStream_t stream,
                        hipEvent_t const *events = nullptr);
 
-// Kernels one decode step launches (in_proj; SSD; out_proj).
-constexpr int kStepKernels = 3;
+// Whether a step of `batch` sessions runs its projections as MFMA GEMVs.
+bool step_uses_mfma(const m2_layer_s &L, int batch);
 
 hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, hipStream_t stream);
 

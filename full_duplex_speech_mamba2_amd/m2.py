@@ -58,8 +58,6 @@ _lib.m2_step_workspace.argtypes = [_P, _i32]
 _lib.m2_step_workspace.restype = C.c_size_t
 _lib.m2_step.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P]
 _lib.m2_step_timed.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P, _P]
-_lib.m2_step_kernel_count.argtypes = [_P, _i32]
-_lib.m2_step_kernel_count.restype = C.c_int
 _lib.m2_prefill_workspace.argtypes = [_P, _i32, _i32, _i32]
 _lib.m2_prefill_workspace.restype = C.c_size_t
 _lib.m2_prefill.argtypes = [_P, _P, _P, _P, _i32, _i32, _i32, _P, _i32, _P, C.c_size_t, _P]
@@ -139,9 +137,6 @@ class Layer:
 
     def step_workspace_bytes(self, batch: int) -> int:
         return int(_lib.m2_step_workspace(self.handle, batch))
-
-    def step_kernel_count(self, batch: int) -> int:
-        return int(_lib.m2_step_kernel_count(self.handle, batch))
 
     def prefill_workspace_bytes(self, batch: int, seqlen: int, chunk: int) -> int:
         return int(_lib.m2_prefill_workspace(self.handle, batch, seqlen, chunk))

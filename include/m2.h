@@ -140,17 +140,13 @@ int m2_step(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch
             const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /* m2_step that also records hipEvent_t events[0..3] on `stream`: events[0] before the
- * first kernel and events[i] after the i-th of the step's three kernels (1: in_proj +
- * conv + dt, 2: SSD update + readout + gate, 3: RMSNorm + out_proj). For per-kernel
- * timing; the events must have been created by the caller. NULL events are skipped. */
+ * step and events[i] after its i-th phase (1: in_proj + conv + dt, 2: SSD update +
+ * readout + gate, 3: RMSNorm + out_proj); a phase is one kernel, or two or three for
+ * the MFMA path of batches above 2. For per-phase timing; the events must have been
+ * created by the caller. NULL events are skipped. */
 int m2_step_timed(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
                   const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream,
                   void *const *events);
-
-/* Number of kernels one m2_step of `batch` sessions launches (currently 3: in_proj;
- * SSD; out_proj), i.e. the intervals m2_step_timed's events delimit. Returns 0 for
- * a NULL layer or batch <= 0. */
-int m2_step_kernel_count(m2_layer layer, int32_t batch);
 
 /* Workspace bytes m2_prefill needs. */
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk);

@@ -137,3 +137,28 @@ def test_state_zero_selected_slots():
     st.zero()
     torch.cuda.synchronize()
     assert not st.ssm.any() and not st.conv.any()
+
+
+MID = synth.MixerDims(d_model=512, n_heads=16, head_dim=32, d_state=64, n_groups=4, wtype="bf16")
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "int8g"])
+@pytest.mark.parametrize("batch", [3, 8, 32])
+def test_mfma_batched_gemv(wtype, batch):
+    dims = MID.replace(wtype=wtype, q_group=128, q_gamma_in=float(np.float32(1 / np.sqrt(512))),
+                       q_gamma_out=float(np.float32(1 / np.sqrt(512))))
+    w = synth.make_layer_weights(dims, 91)
+    xs = synth.make_inputs(dims, 92, 6, batch)
+    n_slots = batch + 3
+    ssm0, conv0 = synth.make_state(dims, 93, n_slots, 0.1)
+    slots = np.random.default_rng(94).permutation(n_slots)[:batch].astype(np.int32)
+    _check("mfma-%s-b%d" % (wtype, batch), dims, w, xs, ssm0, conv0, slot_ids=slots, residual=True)
+
+
+def test_mfma_ragged_rows_and_k():
+    # rows and K not multiples of the 64-row block or the 256-wide K tile
+    dims = synth.MixerDims(d_model=336, n_heads=6, head_dim=16, d_state=32, n_groups=2, wtype="bf16")
+    w = synth.make_layer_weights(dims, 95)
+    xs = synth.make_inputs(dims, 96, 4, 5)
+    ssm0, conv0 = synth.make_state(dims, 97, 5, 0.1)
+    _check("mfma-ragged", dims, w, xs, ssm0, conv0)
