@@ -1,15 +1,15 @@
 // Decode step of the Mamba-2 mixer layer on gfx950: three kernels per step.
 //
 //   gemv_in   zxbcdt = W_in u, weight-streaming GEMV (16-byte loads of W, fp32
-//             accumulate), with the per-row epilogue fused in: causal conv +
-//             SiLU and the conv-cache shift for the x|B|C rows, softplus for the
-//             dt rows, the raw value for the z rows.
-//   ssd_step  per (session, head, row range): S = exp(dt A) S + dt x B^T and
-//             y = C.S + D x on the state tile held in registers (one read, one
-//             write), then v = y SiLU(z), written as v * norm_w, and per-range
-//             sums of squares of v.
+//             accumulate); the row epilogue applies softplus to the dt rows.
+//   ssd_step  per (session, head, row range): causal conv + SiLU of the item's
+//             x channels and of its group's B and C (cache read only), then
+//             S = exp(dt A) S + dt x B^T and y = C.S + D x on the state tile held
+//             in registers (one read, one write), v = y SiLU(z), written as
+//             v * norm_w, and per-range sums of squares of v.
 //   gemv_out  RMS factors from the sums of squares, yn = (v norm_w) r staged
-//             into LDS, then out = W_out yn (+ residual).
+//             into LDS, then out = W_out yn (+ residual); the same kernel shifts
+//             the conv cache (the SSD kernel, its last reader, has finished).
 //
 // The operation follows the Mamba-2 layer the backbone of the pages uses (page
 // "NemotronLabs VoiceChat 11B: GPTQ 3-bit LLM, MLX", introduction; page
@@ -128,9 +128,12 @@ struct GemvArgs {
 
 // ---------------------------------------------------------------------------
 struct SsdArgs {
-  const float *zx;        // [B][zx_stride]
+  const float *zx;        // [B][zx_stride]: z raw | x|B|C raw (pre-conv) | dt (softplus'd)
   int zx_stride, d_inner, conv_dim, H, P, N, G, hpg;
   float *ssm;             // [n_slots][H][P][N]
+  const float *conv_cache;// [n_slots][d_conv-1][conv_dim], read only (shifted by out_proj)
+  const float *conv_w, *conv_b;
+  int d_conv;
   const float *A_log, *D, *norm_w;
   float *vw;              // [B][d_inner]: v * norm_w
   float *ss;              // [B][n_partials]
@@ -140,11 +143,8 @@ struct SsdArgs {
 };
 
 // Per-row epilogue inputs, loaded when the row starts so that their latency
-// overlaps the weight stream: conv history, taps and bias (x|B|C rows), dt bias
-// (dt rows), residual (out_proj).
+// overlaps the weight stream: dt bias (dt rows), residual (out_proj).
 struct EpiIn {
-  float hist[7];
-  float w[8];
   float bias;
   float resid;
   int slot;
@@ -159,61 +159,42 @@ __device__ __forceinline__ EpiIn epilogue_prefetch(const GemvArgs &a, int row, i
   e.bias = 0.0f;
   e.resid = 0.0f;
   if (EPI == EPI_INPROJ) {
-    if (row >= a.d_inner && row < a.d_inner + a.conv_dim) {
-      const int c = row - a.d_inner;
-      const float *cc = a.conv_cache + (size_t)(e.sok ? e.slot : 0) * (a.d_conv - 1) * a.conv_dim + c;
-      const float *w = a.conv_w + (size_t)c * a.d_conv;
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (k < a.d_conv) e.w[k] = w[k];
-#pragma unroll
-      for (int k = 0; k < 7; ++k)
-        if (k < a.d_conv - 1) e.hist[k] = e.sok ? cc[(size_t)k * a.conv_dim] : 0.0f;
-      e.bias = a.conv_b[c];
-    } else if (row >= a.d_inner + a.conv_dim) {
-      e.bias = a.dt_bias[row - a.d_inner - a.conv_dim];
-    }
+    if (row >= a.d_inner + a.conv_dim) e.bias = a.dt_bias[row - a.d_inner - a.conv_dim];
   } else if (a.resid) {
     e.resid = a.resid[(size_t)b * a.rows + row];
   }
   return e;
 }
 
-// Per-row result -> outputs. in_proj: z raw, conv + SiLU with cache shift, or
-// softplus(dt + bias). out_proj: gamma, residual add.
+// Per-row result -> outputs. in_proj: z and x|B|C raw (the causal conv is applied
+// by the SSD kernel), softplus(dt + bias) for the dt rows. out_proj: gamma,
+// residual add.
 template <int EPI>
 __device__ __forceinline__ void gemv_epilogue(const GemvArgs &a, int row, int b, float val, const EpiIn &e) {
   val *= a.gamma;
   const float qnan = __builtin_nanf("");
   if (EPI == EPI_INPROJ) {
     float out = val;
-    if (row >= a.d_inner && row < a.d_inner + a.conv_dim) {
-      const int c = row - a.d_inner;
-      if (!e.sok) {
-        out = qnan;
-      } else {
-        float *cc = a.conv_cache + (size_t)e.slot * (a.d_conv - 1) * a.conv_dim + c;
-        float s = e.bias;
-#pragma unroll
-        for (int k = 0; k < 7; ++k)
-          if (k < a.d_conv - 1) s = fmaf(e.w[k], e.hist[k], s);
-        float wl = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (k == a.d_conv - 1) wl = e.w[k];
-        s = fmaf(wl, val, s);
-#pragma unroll
-        for (int k = 0; k < 6; ++k)
-          if (k + 1 < a.d_conv - 1) cc[(size_t)k * a.conv_dim] = e.hist[k + 1];
-        cc[(size_t)(a.d_conv - 2) * a.conv_dim] = val;
-        out = silu(s);
-      }
-    } else if (row >= a.d_inner + a.conv_dim) {
-      out = softplus(val + e.bias);
-    }
-    a.zx[(size_t)b * a.zx_stride + row] = out;
+    if (row >= a.d_inner + a.conv_dim) out = softplus(val + e.bias);
+    a.zx[(size_t)b * a.zx_stride + row] = e.sok ? out : qnan;
   } else {
     a.y[(size_t)b * a.rows + row] = e.sok ? val + e.resid : qnan;
+  }
+}
+
+// The conv cache after this step: the last d_conv-1 raw inputs, oldest first.
+// Runs in the out_proj kernels, after every reader of the old cache (the SSD
+// kernel) has finished. Elements (session, channel) strided over the grid.
+__device__ __forceinline__ void conv_cache_shift(const GemvArgs &a, size_t gtid, size_t gthreads) {
+  const size_t total = (size_t)a.B * a.conv_dim;
+  for (size_t i = gtid; i < total; i += gthreads) {
+    const int b = (int)(i / a.conv_dim), c = (int)(i - (size_t)b * a.conv_dim);
+    const int slot = a.slots ? a.slots[b] : b;
+    if (slot < 0 || slot >= a.n_slots) continue;
+    float *cc = a.conv_cache + (size_t)slot * (a.d_conv - 1) * a.conv_dim + c;
+    const float raw = a.zx[(size_t)b * a.zx_stride + a.d_inner + c];
+    for (int k = 0; k + 1 < a.d_conv - 1; ++k) cc[(size_t)k * a.conv_dim] = cc[(size_t)(k + 1) * a.conv_dim];
+    cc[(size_t)(a.d_conv - 2) * a.conv_dim] = raw;
   }
 }
 
@@ -362,6 +343,8 @@ __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc[bb] += __shfl_xor(acc[bb], off, 64);
   }
+  if (EPI == EPI_OUT && a.conv_cache)
+    conv_cache_shift(a, (size_t)blockIdx.x * TPB + tid, (size_t)gridDim.x * TPB);
   if (!row_ok || lane >= nb) return;
   float val = 0.0f;
 #pragma unroll
@@ -474,6 +457,8 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
       val = s;
     }
   }
+  if (EPI == EPI_OUT && a.conv_cache && blockIdx.y == 0)
+    conv_cache_shift(a, (size_t)blockIdx.x * kThreads + tid, (size_t)gridDim.x * kThreads);
   if (ks != 0 || !row_ok || lane >= nb) return;
   gemv_epilogue<EPI>(a, row, b0 + lane, val, epilogue_prefetch<EPI>(a, row, b0 + lane));
 }
@@ -485,9 +470,48 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
 // lanes as float4; every slice of the tile is loaded before any is used,
 // updated in registers and written once. wsum: LDS float[NW]. Must be called by
 // every thread of the workgroup.
+// Causal conv + SiLU of 4 consecutive conv channels c0..c0+3 of one session
+// (cache slot `slot`): bias + sum_k w[c][k] in(t-K+1+k), the last K-1 inputs from
+// the cache, the newest the raw in_proj output.
+__device__ __forceinline__ float4 conv4(const SsdArgs &a, const float *zb, int slot, int c0) {
+  const float4 raw = *reinterpret_cast<const float4 *>(zb + a.d_inner + c0);
+  const float4 bias = *reinterpret_cast<const float4 *>(a.conv_b + c0);
+  const float *cache = a.conv_cache + (size_t)slot * (a.d_conv - 1) * a.conv_dim + c0;
+  const float r[4] = {raw.x, raw.y, raw.z, raw.w};
+  float acc[4] = {bias.x, bias.y, bias.z, bias.w};
+  if (a.d_conv == 4) {
+    const float4 *w4 = reinterpret_cast<const float4 *>(a.conv_w + (size_t)c0 * 4);
+    const float4 w[4] = {w4[0], w4[1], w4[2], w4[3]};
+    const float4 h0 = *reinterpret_cast<const float4 *>(cache);
+    const float4 h1 = *reinterpret_cast<const float4 *>(cache + a.conv_dim);
+    const float4 h2 = *reinterpret_cast<const float4 *>(cache + 2 * (size_t)a.conv_dim);
+    const float x0[4] = {h0.x, h0.y, h0.z, h0.w}, x1[4] = {h1.x, h1.y, h1.z, h1.w}, x2[4] = {h2.x, h2.y, h2.z, h2.w};
+    const float wt[4][4] = {{w[0].x, w[0].y, w[0].z, w[0].w}, {w[1].x, w[1].y, w[1].z, w[1].w},
+                            {w[2].x, w[2].y, w[2].z, w[2].w}, {w[3].x, w[3].y, w[3].z, w[3].w}};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] = fmaf(wt[e][0], x0[e], acc[e]);
+      acc[e] = fmaf(wt[e][1], x1[e], acc[e]);
+      acc[e] = fmaf(wt[e][2], x2[e], acc[e]);
+      acc[e] = fmaf(wt[e][3], r[e], acc[e]);
+    }
+  } else {
+    const float *w = a.conv_w + (size_t)c0 * a.d_conv;
+    for (int k = 0; k < a.d_conv - 1; ++k) {
+      const float4 hv = *reinterpret_cast<const float4 *>(cache + (size_t)k * a.conv_dim);
+      const float hh[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w[e * a.d_conv + k], hh[e], acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w[e * a.d_conv + a.d_conv - 1], r[e], acc[e]);
+  }
+  return make_float4(silu(acc[0]), silu(acc[1]), silu(acc[2]), silu(acc[3]));
+}
+
 template <int NW, int MAXI>
 __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b, int wave, int lane,
-                                         float *wsum) {
+                                         float *wsum, float *cx) {
   const int g = h / a.hpg;
   const int lpr = a.N >> 2;                 // lanes per state row
   const int rpi = 64 / lpr;                 // rows per wave instruction
@@ -510,14 +534,27 @@ __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b,
   const float dt = zb[a.d_inner + a.conv_dim + h];
   const float dA = expf(-expf(a.A_log[h]) * dt);
   const float Dh = a.D[h];
-  const float4 Bq = reinterpret_cast<const float4 *>(zb + 2 * a.d_inner + (size_t)g * a.N)[q];
-  const float4 Cq = reinterpret_cast<const float4 *>(zb + 2 * a.d_inner + (size_t)(a.G + g) * a.N)[q];
+  // conv outputs, each channel once per workgroup: B and C of the group and the
+  // item's x rows, one float4 of channels per thread, through LDS (cx = [B | C | x])
+  {
+    const int tid = wave * 64 + lane;
+    const int n4 = a.N / 4;
+    int c0 = -1;
+    if (tid < n4) c0 = a.d_inner + g * a.N + 4 * tid;
+    else if (tid < 2 * n4) c0 = a.d_inner + (a.G + g) * a.N + 4 * (tid - n4);
+    else if (tid < 2 * n4 + a.prange / 4) c0 = h * a.P + ps * a.prange + 4 * (tid - 2 * n4);
+    if (c0 >= 0) reinterpret_cast<float4 *>(cx)[tid] = conv4(a, zb, sok ? slot : 0, c0);
+    __syncthreads();
+  }
+  const float4 Bq = reinterpret_cast<const float4 *>(cx)[q];
+  const float4 Cq = reinterpret_cast<const float4 *>(cx + a.N)[q];
+  const float *xs = cx + 2 * a.N;
   float ssacc = 0.0f;
 #pragma unroll
   for (int k = 0; k < MAXI; ++k) {
     if (wave + NW * k >= n_inst) break;     // uniform across the wave
     const int p = prow[k];
-    const float xp = p >= 0 ? zb[a.d_inner + h * a.P + p] : 0.0f;
+    const float xp = p >= 0 ? xs[p - ps * a.prange] : 0.0f;
     const float dtx = dt * xp;
     float4 sv = st[k];
     sv.x = fmaf(dA, sv.x, dtx * Bq.x);
@@ -558,8 +595,9 @@ __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b,
 
 __global__ __launch_bounds__(kThreads) void ssd_step_kernel(SsdArgs a) {
   __shared__ float wsum[4];
+  __shared__ float cx[2 * 256 + 32];   // conv outputs: B [N] | C [N] | x rows [prange]
   const int h = blockIdx.x / a.psplit, ps = blockIdx.x - h * a.psplit;
-  ssd_item<4, 8>(a, h, ps, blockIdx.y, threadIdx.x >> 6, threadIdx.x & 63, wsum);
+  ssd_item<4, 8>(a, h, ps, blockIdx.y, threadIdx.x >> 6, threadIdx.x & 63, wsum, cx);
 }
 
 
@@ -725,6 +763,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_kernel(MfmaArgs a) {
 template <int EPI>
 __global__ void gemv_mfma_reduce_kernel(GemvArgs a, const float *part, int ks) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (EPI == EPI_OUT && a.conv_cache) conv_cache_shift(a, idx, (size_t)gridDim.x * blockDim.x);
   if (idx >= a.rows * a.B) return;
   const int b = idx / a.rows, row = idx - b * a.rows;
   const EpiIn e = epilogue_prefetch<EPI>(a, row, b);
@@ -951,10 +990,7 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   gi.d_inner = L.d_inner;
   gi.conv_dim = L.conv_dim;
   gi.d_conv = c.d_conv;
-  gi.conv_w = L.w.conv_w;
-  gi.conv_b = L.w.conv_b;
   gi.dt_bias = L.w.dt_bias;
-  gi.conv_cache = S.conv;
   gi.slots = slots;
   gi.n_slots = S.n_slots;
   const bool mfma = step_uses_mfma(L, batch);
@@ -975,6 +1011,10 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   sa.G = c.n_groups;
   sa.hpg = L.hpg;
   sa.ssm = S.ssm;
+  sa.conv_cache = S.conv;
+  sa.conv_w = L.w.conv_w;
+  sa.conv_b = L.w.conv_b;
+  sa.d_conv = c.d_conv;
   sa.A_log = L.w.A_log;
   sa.D = L.w.D;
   sa.norm_w = L.w.norm_w;
@@ -1005,6 +1045,12 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   go.resid = (flags & M2_RESIDUAL) ? x : nullptr;
   go.slots = slots;
   go.n_slots = S.n_slots;
+  go.zx = ws.zx;                 // raw x|B|C of this step, for the conv-cache shift
+  go.zx_stride = L.zx_stride;
+  go.d_inner = L.d_inner;
+  go.conv_dim = L.conv_dim;
+  go.d_conv = c.d_conv;
+  go.conv_cache = S.conv;
   hipLaunchKernelGGL(ssd_step_kernel, dim3(c.n_heads * L.psplit, batch), dim3(kThreads), 0, stream, sa);
   e = hipGetLastError();
   if (e == hipSuccess) e = mark(2);

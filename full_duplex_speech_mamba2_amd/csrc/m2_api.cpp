@@ -47,6 +47,7 @@ int check_config(const m2_config *c) {
   if (c->d_model % 16) return fail(M2_ERR_SHAPE, "d_model %d is not a multiple of 16", c->d_model);
   const long d_inner = (long)c->n_heads * c->head_dim;
   if (d_inner % 16) return fail(M2_ERR_SHAPE, "d_inner %ld is not a multiple of 16", d_inner);
+  if (c->head_dim % 4) return fail(M2_ERR_SHAPE, "head_dim %d is not a multiple of 4", c->head_dim);
   const int N = c->d_state;
   if (N < 4 || N > 256 || (N & (N - 1)))
     return fail(M2_ERR_SHAPE, "d_state %d must be a power of two in [4, 256]", N);
@@ -97,8 +98,7 @@ int m2_layer_create(const m2_config *cfg, const m2_weights *w, m2_layer *out) {
   if (cfg->wtype == M2_W_INT8G && (!aligned16(w->s_in) || !aligned16(w->s_out)))
     return fail(M2_ERR_ALIGN, "s_in and s_out must be 16-byte aligned");
   for (int i = 2; i < 8; ++i)
-    if (reinterpret_cast<uintptr_t>(req[i]) & 3u)
-      return fail(M2_ERR_ALIGN, "%s must be 4-byte aligned", names[i]);
+    if (!aligned16(req[i])) return fail(M2_ERR_ALIGN, "%s must be 16-byte aligned", names[i]);
 
   m2_layer_s *L = new (std::nothrow) m2_layer_s();
   if (!L) return fail(M2_ERR_SHAPE, "out of host memory");
@@ -112,11 +112,12 @@ int m2_layer_create(const m2_config *cfg, const m2_weights *w, m2_layer *out) {
   L->ng = cfg->norm_group > 0 ? cfg->norm_group : L->d_inner / cfg->n_groups;
   L->cfg.norm_group = L->ng;
   L->n_norm = L->d_inner / L->ng;
-  // SSD workgroup row range: the largest divisor of gcd(head_dim, ng) not above 32,
-  // so a workgroup's channels never straddle an RMS group.
+  // SSD workgroup row range: the largest multiple of 4 not above 32 that divides
+  // gcd(head_dim, ng), so a workgroup's channels never straddle an RMS group and its
+  // conv works on whole float4s (head_dim and ng are multiples of 4).
   const int gg = gcd(cfg->head_dim, L->ng);
-  int pr = 1;
-  for (int d = 1; d <= 32 && d <= gg; ++d)
+  int pr = 4;
+  for (int d = 4; d <= 32 && d <= gg; d += 4)
     if (gg % d == 0) pr = d;
   L->prange = pr;
   L->psplit = cfg->head_dim / pr;

@@ -76,7 +76,7 @@ enum { M2_RESIDUAL = 1 };   /* y = x + mixer(x); y may alias x */
 typedef struct {
   int32_t d_model;          /* model width (K of in_proj); multiple of 16 */
   int32_t n_heads;          /* H */
-  int32_t head_dim;         /* P; d_inner = H * P */
+  int32_t head_dim;         /* P (multiple of 4); d_inner = H * P */
   int32_t d_state;          /* N */
   int32_t n_groups;         /* G: B/C groups; H % G == 0; head h uses group h / (H/G) */
   int32_t d_conv;           /* causal conv width, 2..8 */
@@ -88,7 +88,7 @@ typedef struct {
   float q_gamma_out;        /* per-tensor multiplier applied to int8 out_proj results */
 } m2_config;
 
-/* Layer parameters, all device pointers, 16-byte aligned, row-major. */
+/* Layer parameters, all device pointers, each 16-byte aligned, row-major. */
 typedef struct {
   const void *w_in;         /* [d_in_proj][d_model], d_in_proj = 2 d_inner + 2 G N + H;
                                rows [z: d_inner | x: d_inner | B: G N | C: G N | dt: H] */

@@ -67,6 +67,7 @@ GOOD = synth.MixerDims(d_model=256, n_heads=8, head_dim=32, d_state=16, n_groups
     (dict(wtype="int8g", q_group=100), m2.M2_ERR_SHAPE),     # not a power of two
     (dict(wtype="int8g", q_group=8), m2.M2_ERR_SHAPE),       # below 16
     (dict(norm_group=2), m2.M2_ERR_SHAPE),                   # not a multiple of 4
+    (dict(head_dim=6, n_heads=8), m2.M2_ERR_SHAPE),           # head_dim not a multiple of 4
     (dict(wtype="int8g", q_group=512), m2.M2_ERR_SHAPE),     # does not divide d_inner
 ])
 def test_layer_create_rejects_bad_configs(bad, status):
