@@ -57,26 +57,36 @@ def wbytes(dims):
     return {"f32": 4, "bf16": 2, "int8g": 1}[dims.wtype]
 
 
+# phases of m2_step_timed (the same for both step plans of m2_step_plan)
+PHASES = ["gemv_in", "ssd_step", "gemv_out"]
+
+
 def kernel_bytes(dims, B):
-    """Algorithmic HBM bytes per launch of each decode kernel, and of the whole step."""
+    """Algorithmic HBM bytes per launch of each phase of the step (in_proj, SSD, out_proj)
+    and of the whole step: every weight, state, cache and activation byte the phase must move
+    once, nothing for re-reads."""
     d = dims
     f = 4
-    sc_in = d.d_in_proj * (d.d_model // d.q_group) * 2 if d.wtype == "int8g" else 0
-    sc_out = d.d_model * (d.d_inner // d.q_group) * 2 if d.wtype == "int8g" else 0
-    w_in = d.d_in_proj * d.d_model * wbytes(d) + sc_in
-    w_out = d.d_model * d.d_inner * wbytes(d) + sc_out
+    wb = wbytes(d)
+
+    def w_rows(rows, K):
+        return rows * K * wb + (rows * (K // d.q_group) * 2 if d.wtype == "int8g" else 0)
+
     state = 2 * B * d.n_heads * d.head_dim * d.d_state * f
-    cache = 2 * B * (d.d_conv - 1) * d.conv_dim * f
+    cache_rd = B * (d.d_conv - 1) * d.conv_dim * f
     conv_par = d.conv_dim * (d.d_conv + 1) * f
-    head_par = 3 * d.n_heads * f
-    zx = B * d.d_in_proj * f
-    v = B * d.d_inner * f
     io = B * d.d_model * f
-    gemv_in = w_in + io + zx + cache + conv_par + d.n_heads * f
-    ssd = state + B * (2 * d.d_inner + 2 * d.n_groups * d.d_state + d.n_heads) * f + 2 * d.n_heads * f + v
-    gemv_out = w_out + v + d.d_inner * f + io
-    step = w_in + w_out + state + cache + conv_par + head_par + d.d_inner * f + 2 * io
-    return {"gemv_in": gemv_in, "ssd_step": ssd, "gemv_out": gemv_out, "step": step}
+    v = B * d.d_inner * f
+    xbc_dt = B * (d.conv_dim + d.n_heads) * f
+    # the conv-cache shift (out_proj): rows 1..K-2 and the new raw inputs in, K-1 rows out
+    shift = B * ((d.d_conv - 2) + 1 + (d.d_conv - 1)) * d.conv_dim * f
+    ssd_core = state + cache_rd + conv_par + xbc_dt + 2 * d.n_heads * f
+    k = {"gemv_in": w_rows(d.d_in_proj, d.d_model) + io + B * d.d_in_proj * f + d.n_heads * f,
+         "ssd_step": ssd_core + v + v + B * d.n_heads * f + d.d_inner * f,
+         "gemv_out": w_rows(d.d_model, d.d_inner) + v + B * d.n_heads * f + io + shift}
+    k["step"] = (w_rows(d.d_in_proj, d.d_model) + w_rows(d.d_model, d.d_inner) + state + 2 * cache_rd +
+                 conv_par + 3 * d.n_heads * f + d.d_inner * f + 2 * io)
+    return k
 
 
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
@@ -204,6 +214,7 @@ def main():
 
     ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
     steps_per_s = 1000.0 / ms
+    plan = layers[0].step_plan(B)
     kb = kernel_bytes(dims, B)
 
     # per-kernel durations: HIP events recorded between the step's kernels on the stream they
@@ -215,7 +226,7 @@ def main():
     for t in range(kp):
         m2.step_timed(layers[t % nl], st, xs[t % nx], ys[t % nx], evs[t], ws=ws)
     torch.cuda.synchronize()
-    names = ["gemv_in", "ssd_step", "gemv_out"]
+    names = PHASES
     dur_us = {n: 1000.0 * float(np.mean([hip_elapsed_ms(hip, evs[t][i], evs[t][i + 1]) for t in range(kp)]))
               for i, n in enumerate(names)}
     for row in evs:
@@ -236,7 +247,7 @@ def main():
         "config": {"workload": wl.name, "d_model": dims.d_model, "n_heads": dims.n_heads,
                    "head_dim": dims.head_dim, "d_state": dims.d_state, "n_groups": dims.n_groups,
                    "d_conv": dims.d_conv, "batch": B, "weight_dtype": dims.wtype,
-                   "state_dtype": "f32", "weight_copies": nl,
+                   "state_dtype": "f32", "weight_copies": nl, "step_plan": plan,
                    "timing": "graph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"},
         "achieved_GBps": round(kb["step"] * steps_per_s / 1e9, 1),
         "hbm_peak_frac": round(kb["step"] * steps_per_s / 1e9 / HBM_PEAK_GBPS, 4),

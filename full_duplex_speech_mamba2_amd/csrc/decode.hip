@@ -524,12 +524,20 @@ __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b,
 
   float4 st[MAXI];
   int prow[MAXI];
+  float zg[MAXI], nw[MAXI];                 // gate input and norm weight of the row (lane q == 0)
 #pragma unroll
   for (int k = 0; k < MAXI; ++k) {
     const int i = wave + NW * k;
     const int pl = i * rpi + r_in;
     prow[k] = (i < n_inst && pl < a.prange) ? ps * a.prange + pl : -1;
     st[k] = (sok && prow[k] >= 0) ? S[(size_t)prow[k] * lpr + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // the epilogue's loads go out with the state's, not after the readout
+#pragma unroll
+  for (int k = 0; k < MAXI; ++k) {
+    const bool need = q == 0 && prow[k] >= 0;
+    zg[k] = need ? zb[h * a.P + prow[k]] : 0.0f;
+    nw[k] = need ? a.norm_w[h * a.P + prow[k]] : 0.0f;
   }
   const float dt = zb[a.d_inner + a.conv_dim + h];
   const float dA = expf(-expf(a.A_log[h]) * dt);
@@ -570,9 +578,9 @@ __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b,
     if (q == 0 && p >= 0) {
       const int ch = h * a.P + p;
       const float yv = fmaf(Dh, xp, r);
-      float vv = yv * silu(zb[ch]);
+      float vv = yv * silu(zg[k]);
       if (!sok) vv = __builtin_nanf("");
-      a.vw[(size_t)b * a.d_inner + ch] = vv * a.norm_w[ch];
+      a.vw[(size_t)b * a.d_inner + ch] = vv * nw[k];
       ssacc = fmaf(vv, vv, ssacc);
     }
   }
@@ -1069,13 +1077,16 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
 }
 
 // Batches of 3..32 sessions with bf16 weights, or int8 weights whose scale groups
-// hold whole 32-wide k-steps, use the MFMA GEMVs.
-bool step_uses_mfma(const m2_layer_s &L, int batch) {
+// hold whole 32-wide k-steps, run the projections as MFMA GEMVs; the rest as VALU
+// GEMVs.
+int step_plan(const m2_layer_s &L, int batch) {
   const m2_config &c = L.cfg;
-  if (batch < 3 || batch > 32) return false;
-  if (c.wtype == M2_W_BF16) return true;
-  return c.wtype == M2_W_INT8G && c.q_group % 32 == 0 && c.q_group <= kMKT;
+  if (batch < 3 || batch > 32) return kPlanValu;
+  if (c.wtype == M2_W_BF16) return kPlanMfma;
+  return c.wtype == M2_W_INT8G && c.q_group % 32 == 0 && c.q_group <= kMKT ? kPlanMfma : kPlanValu;
 }
+
+bool step_uses_mfma(const m2_layer_s &L, int batch) { return step_plan(L, batch) == kPlanMfma; }
 
 
 hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, hipStream_t stream) {

@@ -214,6 +214,11 @@ int m2_step_timed(m2_layer layer, m2_state st, const float *x, float *y, int32_t
   return step_impl(layer, st, x, y, batch, slot_ids, flags, ws, ws_bytes, stream, events);
 }
 
+int m2_step_plan(m2_layer layer, int32_t batch) {
+  if (!layer || batch <= 0) return -1;
+  return m2d::step_plan(*layer, batch);
+}
+
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk) {
   if (!layer || batch <= 0 || seqlen <= 0 || chunk < 16 || chunk > 256 || chunk % 16) return 0;
   return m2d::prefill_ws_bytes(*layer, batch, seqlen, chunk);

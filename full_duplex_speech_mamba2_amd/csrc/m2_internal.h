@@ -49,6 +49,9 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
                        const int32_t *slots, int flags, const StepWs &ws, hipStream_t stream,
                        hipEvent_t const *events = nullptr);
 
+// Kernel plan of a decode step of `batch` sessions (m2_step_plan).
+enum { kPlanValu = 0, kPlanMfma = 1 };
+int step_plan(const m2_layer_s &L, int batch);
 // Whether a step of `batch` sessions runs its projections as MFMA GEMVs.
 bool step_uses_mfma(const m2_layer_s &L, int batch);
 

@@ -58,6 +58,8 @@ _lib.m2_step_workspace.argtypes = [_P, _i32]
 _lib.m2_step_workspace.restype = C.c_size_t
 _lib.m2_step.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P]
 _lib.m2_step_timed.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P, _P]
+_lib.m2_step_plan.argtypes = [_P, _i32]
+_lib.m2_step_plan.restype = C.c_int
 _lib.m2_prefill_workspace.argtypes = [_P, _i32, _i32, _i32]
 _lib.m2_prefill_workspace.restype = C.c_size_t
 _lib.m2_prefill.argtypes = [_P, _P, _P, _P, _i32, _i32, _i32, _P, _i32, _P, C.c_size_t, _P]
@@ -137,6 +139,10 @@ class Layer:
 
     def step_workspace_bytes(self, batch: int) -> int:
         return int(_lib.m2_step_workspace(self.handle, batch))
+
+    def step_plan(self, batch: int) -> int:
+        """0: VALU GEMVs; 1: MFMA GEMVs around the SSD kernel (m2_step_plan)."""
+        return int(_lib.m2_step_plan(self.handle, batch))
 
     def prefill_workspace_bytes(self, batch: int, seqlen: int, chunk: int) -> int:
         return int(_lib.m2_prefill_workspace(self.handle, batch, seqlen, chunk))

@@ -140,13 +140,22 @@ int m2_step(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch
             const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /* m2_step that also records hipEvent_t events[0..3] on `stream`: events[0] before the
- * step and events[i] after its i-th phase (1: in_proj + conv + dt, 2: SSD update +
- * readout + gate, 3: RMSNorm + out_proj); a phase is one kernel, or two or three for
- * the MFMA path of batches above 2. For per-phase timing; the events must have been
+ * step and events[i] after its i-th phase (see m2_step_plan); a phase is one kernel,
+ * or two or three for plan 1. For per-phase timing; the events must have been
  * created by the caller. NULL events are skipped. */
 int m2_step_timed(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
                   const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream,
                   void *const *events);
+
+/* How m2_step runs `batch` sessions. Both plans have three phases, the ones
+ * m2_step_timed's events delimit: in_proj | conv + SSD update + readout + gate |
+ * RMSNorm + out_proj.
+ *   0  VALU GEMVs: one kernel per phase
+ *   1  MFMA GEMVs (batch 3..32 with bf16 weights, or int8 weights whose q_group is
+ *      a multiple of 32 up to 256): in_proj GEMV + reduction | SSD | RMS factors +
+ *      out_proj GEMV + reduction
+ * Returns -1 for a NULL layer or batch <= 0. */
+int m2_step_plan(m2_layer layer, int32_t batch);
 
 /* Workspace bytes m2_prefill needs. */
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk);

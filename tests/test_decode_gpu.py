@@ -38,13 +38,15 @@ def test_tiny_fp32_16_steps():
 RAGGED = synth.MixerDims(d_model=272, n_heads=6, head_dim=24, d_state=32, n_groups=2, d_conv=4)
 
 
+@pytest.mark.parametrize("batch", [1, 2, 3])
 @pytest.mark.parametrize("wtype", ["f32", "bf16", "int8g"])
 @pytest.mark.parametrize("variant", ["plain", "slots_residual", "norm_all", "conv2", "conv5_n64"])
-def test_ragged_shapes(wtype, variant):
+def test_ragged_shapes(wtype, variant, batch):
+    """Batches of 1 and 2 take the fused in_proj + SSD kernel, 3 the three-kernel plan."""
     dims = RAGGED.replace(wtype=wtype, q_group=16, q_gamma_in=0.0625, q_gamma_out=0.1)
-    B, slots, n_slots, residual, steps = 3, None, 3, False, 9
+    B, slots, n_slots, residual, steps = batch, None, batch, False, 9
     if variant == "slots_residual":
-        n_slots, slots, residual = 5, np.array([4, 0, 2], np.int32), True
+        n_slots, slots, residual = 5, np.array([4, 0, 2][:batch], np.int32), True
     elif variant == "norm_all":
         dims = dims.replace(norm_group=dims.d_inner)
     elif variant == "conv2":
@@ -54,7 +56,8 @@ def test_ragged_shapes(wtype, variant):
     w = synth.make_layer_weights(dims, 31)
     xs = synth.make_inputs(dims, 32, steps, B)
     ssm0, conv0 = synth.make_state(dims, 33, n_slots, 0.1)
-    _check("ragged-%s-%s" % (wtype, variant), dims, w, xs, ssm0, conv0, slot_ids=slots, residual=residual)
+    _check("ragged-%s-%s-b%d" % (wtype, variant, batch), dims, w, xs, ssm0, conv0, slot_ids=slots,
+           residual=residual)
 
 
 @pytest.mark.parametrize("batch", [1, 2, 5, 8, 17])
