@@ -11,7 +11,8 @@ each workload's sessions; the GPU test runs every session and compares the subse
 Stored per workload (float64 unless noted):
   y at sampled steps / tokens for the sampled sessions (float32),
   per-(layer, session, head) max |S| of the state and the state at 4096 sampled
-  (head, p, n) positions, the conv cache of the sampled sessions.
+  (head, p, n) positions, per-(layer, session) max |cache| of the conv cache and
+  the cache at 4096 sampled (tap, channel) positions.
 """
 import os
 import sys
@@ -37,11 +38,21 @@ def state_positions(dims, seed):
     return np.stack([h, p, n]).astype(np.int32)
 
 
-def state_record(ssm, conv, pos):
-    """ssm [S][H][P][N], conv [S][K-1][C] (sampled sessions) -> (head max, samples, conv)."""
+def conv_positions(dims, seed):
+    r = np.random.default_rng(seed)
+    k = r.integers(0, dims.d_conv - 1, N_STATE_SAMPLES)
+    c = r.integers(0, dims.conv_dim, N_STATE_SAMPLES)
+    return np.stack([k, c]).astype(np.int32)
+
+
+def state_record(ssm, conv, pos, cpos):
+    """ssm [S][H][P][N], conv [S][K-1][C] (sampled sessions) -> (head max, samples,
+    cache max, cache samples)."""
     hmax = np.max(np.abs(ssm), axis=(2, 3))
     samp = ssm[:, pos[0], pos[1], pos[2]]
-    return hmax, samp, conv.copy()
+    cmax = np.max(np.abs(conv), axis=(1, 2))
+    csamp = conv[:, cpos[0], cpos[1]]
+    return hmax, samp, cmax, csamp
 
 
 def make_stack():
@@ -63,12 +74,12 @@ def make_stack():
             ys.append(u.astype(np.float32))
         if t % 10 == 0:
             print("step %d %.1f s" % (t, time.time() - t0), flush=True)
-    pos = state_positions(d, 303)
-    recs = [state_record(s, c, pos) for s, c in states]
+    pos, cpos = state_positions(d, 303), conv_positions(d, 304)
+    recs = [state_record(s, c, pos, cpos) for s, c in states]
     np.savez_compressed(os.path.join(HERE, "stack_int8_27layers_b8_100steps.npz"),
-                        sessions=sessions, steps=steps_kept, y=np.array(ys), pos=pos,
+                        sessions=sessions, steps=steps_kept, y=np.array(ys), pos=pos, cpos=cpos,
                         hmax=np.array([r[0] for r in recs]), samples=np.array([r[1] for r in recs]),
-                        conv=np.array([r[2] for r in recs]).astype(np.float32))
+                        cmax=np.array([r[2] for r in recs]), csamples=np.array([r[3] for r in recs]))
     print("stack done %.1f s" % (time.time() - t0), flush=True)
 
 
@@ -85,21 +96,21 @@ def make_prefill():
     s, c = lay.new_state(len(sessions))
     ypf = lay.prefill(s, c, prompt)
     print("prefill %.1f s" % (time.time() - t0), flush=True)
-    pos = state_positions(d, 404)
-    after_prefill = state_record(s, c, pos)
+    pos, cpos = state_positions(d, 404), conv_positions(d, 405)
+    after_prefill = state_record(s, c, pos, cpos)
     ys = []
     for t in range(wl.steps):
         y = lay.step(s, c, xs[t])
         if t in steps_kept:
             ys.append(y.astype(np.float32))
-    after_decode = state_record(s, c, pos)
+    after_decode = state_record(s, c, pos, cpos)
     np.savez_compressed(os.path.join(HERE, "prefill2048_decode750_bf16_b4.npz"),
                         sessions=sessions, tokens=tok_kept, y_prefill=ypf[:, tok_kept].astype(np.float32),
-                        steps=steps_kept, y_decode=np.array(ys), pos=pos,
+                        steps=steps_kept, y_decode=np.array(ys), pos=pos, cpos=cpos,
                         hmax_prefill=after_prefill[0], samples_prefill=after_prefill[1],
-                        conv_prefill=after_prefill[2].astype(np.float32),
+                        cmax_prefill=after_prefill[2], csamples_prefill=after_prefill[3],
                         hmax_decode=after_decode[0], samples_decode=after_decode[1],
-                        conv_decode=after_decode[2].astype(np.float32))
+                        cmax_decode=after_decode[2], csamples_decode=after_decode[3])
     print("prefill+decode done %.1f s" % (time.time() - t0), flush=True)
 
 

@@ -1,0 +1,143 @@
+"""Parity of the HIP path with the fp64 oracle on the full-size workloads, in the
+launch configurations the bench times (m2_step / m2_prefill through the C ABI):
+
+  9B-shaped layer, bf16, 1 session, 750 steps       oracle run live on the session
+  9B-shaped layer, bf16, 32 sessions, 200 steps     oracle run live on 3 of the sessions
+  27-layer int8 (g128) residual stack, 8 sessions   oracle values stored by
+      x 100 steps                                   tests/golden/make_golden.py
+  bf16, 4 sessions, 2048-token chunked prefill      (2 sessions, sampled steps and
+      then 750 decode steps                         state positions)
+
+The tiny fp32 workload runs in test_decode_gpu.py. Sessions are independent, so
+checking a subset of them checks the batched kernels on those sessions; the
+state is compared at 4096 sampled (head, p, n) positions per layer and session
+against the oracle's per-head maximum (the normwise measure of parity.py).
+"""
+import os
+
+import numpy as np
+import pytest
+
+from full_duplex_speech_mamba2_amd import synth
+from parity import TOL_OUT, TOL_STATE, e_conv, e_out, e_state, gpu_decode, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _report(tag, **errs):
+    print("[parity] %s %s" % (tag, " ".join("%s=%.3e" % kv for kv in errs.items())), flush=True)
+
+
+def e_state_sampled(S, pos, samples, hmax):
+    """S [H][P][N] of one session (GPU), the oracle's values at pos = [h, p, n] and its
+    per-head max |S|: max over sampled positions of |S - So| / max(hmax[h], 1e-6 max hmax)."""
+    if not np.all(np.isfinite(S)):
+        return float("inf")
+    h = pos[0]
+    floor = 1e-6 * max(float(np.max(hmax)), 1e-30)
+    d = np.abs(S[pos[0], pos[1], pos[2]].astype(np.float64) - samples)
+    return float(np.max(d / np.maximum(hmax[h], floor)))
+
+
+def e_conv_sampled(C, cpos, csamples, cmax):
+    """C [K-1][conv_dim] of one session against the oracle at cpos = [k, c]."""
+    if not np.all(np.isfinite(C)):
+        return float("inf")
+    d = np.abs(C[cpos[0], cpos[1]].astype(np.float64) - csamples)
+    return float(np.max(d / max(float(cmax), 1e-30)))
+
+
+def test_9b_bf16_single_session_750_steps():
+    wl = synth.workload(1)
+    w = synth.make_layer_weights(wl.dims, wl.weight_seed)
+    xs = synth.make_inputs(wl.dims, wl.seed, wl.steps, wl.batch)
+    ssm0, conv0 = synth.make_state(wl.dims, wl.seed, wl.batch, wl.state_var)
+    yg, sg, cg = gpu_decode(wl.dims, w, xs, ssm0, conv0)
+    yo, so, co = oracle_decode(wl.dims, w, xs, ssm0, conv0)
+    eo, es, ec = e_out(yg, yo), e_state(sg, so), e_conv(cg, co)
+    _report(wl.name, e_out=eo, e_state=es, e_conv=ec)
+    assert eo <= TOL_OUT and es <= TOL_STATE and ec <= TOL_STATE
+
+
+def test_9b_bf16_32_sessions_200_steps():
+    wl = synth.workload(2)
+    w = synth.make_layer_weights(wl.dims, wl.weight_seed)
+    xs = synth.make_inputs(wl.dims, wl.seed, wl.steps, wl.batch)
+    ssm0, conv0 = synth.make_state(wl.dims, wl.seed, wl.batch, wl.state_var)
+    sessions = [0, 17, 31]
+    yg, sg, cg = gpu_decode(wl.dims, w, xs, ssm0, conv0)
+    yo, so, co = oracle_decode(wl.dims, w, xs, ssm0, conv0, sessions=sessions)
+    eo = e_out(yg[:, sessions], yo)
+    es, ec = e_state(sg[sessions], so[sessions]), e_conv(cg[sessions], co[sessions])
+    _report(wl.name, e_out=eo, e_state=es, e_conv=ec)
+    assert eo <= TOL_OUT and es <= TOL_STATE and ec <= TOL_STATE
+
+
+def test_int8_27_layer_stack_100_steps():
+    import torch
+    from full_duplex_speech_mamba2_amd import m2
+    g = np.load(os.path.join(GOLDEN, "stack_int8_27layers_b8_100steps.npz"))
+    wl = synth.workload(3)
+    d = wl.dims
+    layers, states = [], []
+    for l in range(wl.layers):
+        lay = m2.Layer(d, synth.make_layer_weights(d, wl.weight_seed, l))
+        layers.append(lay)
+        states.append(m2.State(lay, wl.batch))
+    xs = torch.from_numpy(synth.make_inputs(d, wl.seed, wl.steps, wl.batch)).cuda()
+    kept = {int(t): i for i, t in enumerate(g["steps"])}
+    sessions = g["sessions"]
+    eo = 0.0
+    for t in range(wl.steps):
+        u = xs[t].clone()
+        for lay, st in zip(layers, states):
+            m2.step(lay, st, u, u, residual=True)      # y aliases x under M2_RESIDUAL
+        if t in kept:
+            eo = max(eo, e_out(u.cpu().numpy()[sessions], g["y"][kept[t]]))
+    torch.cuda.synchronize()
+    es = ec = 0.0
+    for l, st in enumerate(states):
+        S = st.ssm.cpu().numpy()
+        C = st.conv.cpu().numpy()
+        for j, s in enumerate(sessions):
+            es = max(es, e_state_sampled(S[s], g["pos"], g["samples"][l, j], g["hmax"][l, j]))
+            ec = max(ec, e_conv_sampled(C[s], g["cpos"], g["csamples"][l, j], g["cmax"][l, j]))
+    _report(wl.name, e_out=eo, e_state=es, e_conv=ec)
+    assert eo <= TOL_OUT and es <= TOL_STATE and ec <= TOL_STATE
+
+
+def test_bf16_prefill_2048_then_750_steps():
+    import torch
+    from full_duplex_speech_mamba2_amd import m2
+    g = np.load(os.path.join(GOLDEN, "prefill2048_decode750_bf16_b4.npz"))
+    wl = synth.workload(4)
+    d = wl.dims
+    lay = m2.Layer(d, synth.make_layer_weights(d, wl.weight_seed))
+    st = m2.State(lay, wl.batch)
+    prompt = torch.from_numpy(synth.make_prompt(d, wl.seed, wl.batch, wl.prefill)).cuda()
+    sessions = g["sessions"]
+    ypf = m2.prefill(lay, st, prompt, chunk=wl.chunk)
+    torch.cuda.synchronize()
+    eo_pf = e_out(ypf.cpu().numpy()[sessions][:, g["tokens"]], g["y_prefill"])
+    S, C = st.ssm.cpu().numpy(), st.conv.cpu().numpy()
+    es_pf = max(e_state_sampled(S[s], g["pos"], g["samples_prefill"][j], g["hmax_prefill"][j])
+                for j, s in enumerate(sessions))
+    ec_pf = max(e_conv_sampled(C[s], g["cpos"], g["csamples_prefill"][j], g["cmax_prefill"][j])
+                for j, s in enumerate(sessions))
+    xs = torch.from_numpy(synth.make_inputs(d, wl.seed, wl.steps, wl.batch)).cuda()
+    ys = torch.empty_like(xs)
+    for t in range(wl.steps):
+        m2.step(lay, st, xs[t], ys[t])
+    torch.cuda.synchronize()
+    eo_dec = e_out(ys.cpu().numpy()[g["steps"]][:, sessions], g["y_decode"])
+    S, C = st.ssm.cpu().numpy(), st.conv.cpu().numpy()
+    es_dec = max(e_state_sampled(S[s], g["pos"], g["samples_decode"][j], g["hmax_decode"][j])
+                 for j, s in enumerate(sessions))
+    ec_dec = max(e_conv_sampled(C[s], g["cpos"], g["csamples_decode"][j], g["cmax_decode"][j])
+                 for j, s in enumerate(sessions))
+    _report(wl.name, e_out_prefill=eo_pf, e_state_prefill=es_pf, e_conv_prefill=ec_pf,
+            e_out_decode=eo_dec, e_state_decode=es_dec, e_conv_decode=ec_dec)
+    assert eo_pf <= TOL_OUT and es_pf <= TOL_STATE and ec_pf <= TOL_STATE
+    assert eo_dec <= TOL_OUT and es_dec <= TOL_STATE and ec_dec <= TOL_STATE
