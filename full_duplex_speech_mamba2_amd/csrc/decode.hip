@@ -465,6 +465,19 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
 
 // ---------------------------------------------------------------------------
 
+// The SSM state is read once and written once per step: stream it (nontemporal),
+// so that it neither evicts nor leaves dirty lines for the weight stream that
+// follows.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_stream(const float4 *p) {
+  const f32x4v t = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void st_stream(float4 *p, const float4 &v) {
+  const f32x4v t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<f32x4v *>(p));
+}
+
 // One SSD work item = (session b, head h, rows [ps*prange, (ps+1)*prange)),
 // done by the NW waves of a workgroup. A state row (N floats) is read by N/4
 // lanes as float4; every slice of the tile is loaded before any is used,
@@ -530,7 +543,7 @@ __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b,
     const int i = wave + NW * k;
     const int pl = i * rpi + r_in;
     prow[k] = (i < n_inst && pl < a.prange) ? ps * a.prange + pl : -1;
-    st[k] = (sok && prow[k] >= 0) ? S[(size_t)prow[k] * lpr + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    st[k] = (sok && prow[k] >= 0) ? ld_stream(S + (size_t)prow[k] * lpr + q) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // the epilogue's loads go out with the state's, not after the readout
 #pragma unroll
@@ -545,13 +558,13 @@ __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b,
   // conv outputs, each channel once per workgroup: B and C of the group and the
   // item's x rows, one float4 of channels per thread, through LDS (cx = [B | C | x])
   {
-    const int tid = wave * 64 + lane;
     const int n4 = a.N / 4;
-    int c0 = -1;
-    if (tid < n4) c0 = a.d_inner + g * a.N + 4 * tid;
-    else if (tid < 2 * n4) c0 = a.d_inner + (a.G + g) * a.N + 4 * (tid - n4);
-    else if (tid < 2 * n4 + a.prange / 4) c0 = h * a.P + ps * a.prange + 4 * (tid - 2 * n4);
-    if (c0 >= 0) reinterpret_cast<float4 *>(cx)[tid] = conv4(a, zb, sok ? slot : 0, c0);
+    for (int t = wave * 64 + lane; t < 2 * n4 + a.prange / 4; t += NW * 64) {
+      const int c0 = t < n4 ? a.d_inner + g * a.N + 4 * t
+                   : t < 2 * n4 ? a.d_inner + (a.G + g) * a.N + 4 * (t - n4)
+                   : h * a.P + ps * a.prange + 4 * (t - 2 * n4);
+      reinterpret_cast<float4 *>(cx)[t] = conv4(a, zb, sok ? slot : 0, c0);
+    }
     __syncthreads();
   }
   const float4 Bq = reinterpret_cast<const float4 *>(cx)[q];
@@ -587,7 +600,7 @@ __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b,
   if (sok) {
 #pragma unroll
     for (int k = 0; k < MAXI; ++k)
-      if (prow[k] >= 0) S[(size_t)prow[k] * lpr + q] = st[k];
+      if (prow[k] >= 0) st_stream(S + (size_t)prow[k] * lpr + q, st[k]);
   }
   // sum of squares of this item's rows, in a fixed order
   for (int off = 32; off >= 1; off >>= 1) ssacc += __shfl_xor(ssacc, off, 64);
@@ -601,29 +614,39 @@ __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b,
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kThreads) void ssd_step_kernel(SsdArgs a) {
-  __shared__ float wsum[4];
+// NW waves per item, up to MAXI state slices per wave (NW * MAXI >= the item's
+// wave instructions).
+template <int NW, int MAXI>
+__global__ __launch_bounds__(NW * 64) void ssd_step_kernel(SsdArgs a) {
+  __shared__ float wsum[NW];
   __shared__ float cx[2 * 256 + 32];   // conv outputs: B [N] | C [N] | x rows [prange]
   const int h = blockIdx.x / a.psplit, ps = blockIdx.x - h * a.psplit;
-  ssd_item<4, 8>(a, h, ps, blockIdx.y, threadIdx.x >> 6, threadIdx.x & 63, wsum, cx);
+  ssd_item<NW, MAXI>(a, h, ps, blockIdx.y, threadIdx.x >> 6, threadIdx.x & 63, wsum, cx);
 }
 
 
 // ---------------------------------------------------------------------------
-// gemv_mfma: batch >= 3 with bf16 or int8 (q_group % 32 == 0) weights. Partial
-// sums out[b][row] over one K chunk (blockIdx.y) as MFMA 16x16x32 bf16 products:
-// A = 16 weight rows x 32 k straight from HBM (one 16-byte or 8-byte load per lane
-// and k-step, a K tile of 8 steps in flight), B = 32 k x 16 sessions of the
-// activations, staged per 256-wide K tile in LDS as bf16 hi + lo (an fp32 value is
-// hi + lo to 2^-16 relative; bf16 and int8 weights are exact in bf16), two MFMAs
-// per product. gemv_mfma_reduce sums the chunks in a fixed order and applies the
-// row epilogue, so results do not depend on scheduling.
+// gemv_mfma: batch 3..32 with bf16 weights, or int8 weights with q_group 128 or
+// 256. A workgroup of 8 waves owns 128 rows (16 per wave) over one K chunk
+// (blockIdx.y) of whole 256-wide tiles and writes its partial sums
+// part[chunk][b][row]. Per 32-wide k-step: A = 16 weight rows x 32 k straight
+// from HBM (one 16- or 8-byte load per lane and step), B = 32 k x 16 sessions
+// from LDS as bf16 hi + lo (an fp32 value is hi + lo to 2^-16 relative; bf16 and
+// int8 weights are exact in bf16), two 16x16x32 bf16 MFMAs per product. The tiles
+// are software-pipelined: while one tile's MFMAs run, the next tile's weights are
+// in flight into a second register set and its activations into registers, which
+// are then converted into the second LDS buffer; one barrier per tile. With RMS
+// (out_proj) the workgroup first forms the RMS factors of the norm groups its
+// chunk covers from the sums of squares (fixed order) and scales the activations
+// by them while staging. gemv_mfma_reduce sums the chunks in a fixed order and
+// applies the row epilogue, so results do not depend on scheduling.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMKT = 256;          // K tile
 constexpr int kMLD = kMKT + 8;     // LDS row stride (bf16)
+constexpr int kMRows = 128;        // rows per workgroup (8 waves x 16)
 
 struct MfmaArgs {
   const void *W;
@@ -631,8 +654,10 @@ struct MfmaArgs {
   int rows, K, q_group, kchunk;
   const float *act;                // [B][K]
   int B;
-  const float *rn;                 // optional [B][n_norm]: act[b][k] *= rn[b][k / ng]
-  int ng, n_norm;
+  // RMS prologue (out_proj): act[b][k] *= 1/sqrt(sum_j ss[b][g*per + j] / ng + eps), g = k / ng
+  const float *ss;
+  int n_partials, n_norm, ng;
+  float eps;
   float *part;                     // [KS][B][rows]
 };
 
@@ -641,117 +666,220 @@ __device__ __forceinline__ unsigned short f2bf(float f) {
   return (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <int WT, int NBT>
-__global__ __launch_bounds__(256) void gemv_mfma_kernel(MfmaArgs a) {
-  __shared__ unsigned short xh[NBT * 16 * kMLD];
-  __shared__ unsigned short xl[NBT * 16 * kMLD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rbase = blockIdx.x * 64 + wave * 16;
-  const int arow = rbase + (lane & 15);             // A-operand row of this lane
-  const bool arow_ok = arow < a.rows;
-  const int k_begin = blockIdx.y * a.kchunk, k_end = min(a.K, k_begin + a.kchunk);
-  const int kq = (lane >> 4) * 8;                   // this lane's 8 k within a 32-wide step
-  f32x4 acc[NBT];
-#pragma unroll
-  for (int j = 0; j < NBT; ++j) acc[j] = f32x4{};
-  // int8: rows (l/16)*4 + r of the C tile carry a scale per q_group columns
-  float sc[4] = {1.f, 1.f, 1.f, 1.f};
-  const int ngrp = a.K / a.q_group;
+// Raw weights of one tile for one lane: 8 k-steps of 8 values.
+template <int WT> struct MRaw;
+template <> struct MRaw<M2_W_BF16> { bf16x8 v[8]; };
+template <> struct MRaw<M2_W_INT8G> { uint2 v[8]; };
 
-  for (int kt = k_begin; kt < k_end; kt += kMKT) {
-    const int klen = min(kMKT, k_end - kt);         // multiple of 16
-    // weights of this tile first: 8 k-steps per lane in flight
-    bf16x8 wf[8];
+template <int WT>
+__device__ __forceinline__ void mfma_load_w(const MfmaArgs &a, int arow, int kt, int klen, int kq, MRaw<WT> &w) {
+  const bool arow_ok = arow < a.rows;
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const bool ok = arow_ok && 32 * st + kq < klen;
+    const size_t off = (size_t)arow * a.K + kt + 32 * st + kq;
+    if constexpr (WT == M2_W_BF16)
+      w.v[st] = ok ? *reinterpret_cast<const bf16x8 *>(static_cast<const unsigned short *>(a.W) + off) : bf16x8{};
+    else
+      w.v[st] = ok ? *reinterpret_cast<const uint2 *>(static_cast<const int8_t *>(a.W) + off) : make_uint2(0u, 0u);
+  }
+}
+
+// int8 scales of the tile's q_group groups (at most 2) for this lane's 4 C rows.
+__device__ __forceinline__ void mfma_load_s(const MfmaArgs &a, int rbase, int lane, int kt, float (&sc)[2][4]) {
+  const int ngrp = a.K / a.q_group;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int g = (kt + q * a.q_group) / a.q_group;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rr = rbase + (lane >> 4) * 4 + r;
+      sc[q][r] = (rr < a.rows && g < ngrp && q * a.q_group < kMKT) ? __half2float(a.S[(size_t)rr * ngrp + g]) : 0.0f;
+    }
+  }
+}
+
+template <int WT> __device__ __forceinline__ bf16x8 mfma_a(const MRaw<WT> &w, int st);
+template <> __device__ __forceinline__ bf16x8 mfma_a<M2_W_BF16>(const MRaw<M2_W_BF16> &w, int st) { return w.v[st]; }
+template <> __device__ __forceinline__ bf16x8 mfma_a<M2_W_INT8G>(const MRaw<M2_W_INT8G> &w, int st) {
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const unsigned wd = e < 4 ? w.v[st].x : w.v[st].y;
+    const float v = (float)((int32_t)(wd << (24 - 8 * (e & 3))) >> 24);
+    f[e] = __builtin_bit_cast(__bf16, f2bf(v));
+  }
+  return f;
+}
+
+// Activations of one tile (NBT*16 sessions x 256 k, zero-filled) into registers.
+template <int NBT>
+__device__ __forceinline__ void mfma_load_x(const MfmaArgs &a, int kt, int klen, int tid, float4 (&xv)[NBT * 2]) {
+#pragma unroll
+  for (int q = 0; q < NBT * 2; ++q) {
+    const int i = tid + 512 * q;
+    const int b = i / (kMKT / 4), k4 = (i - b * (kMKT / 4)) * 4;
+    xv[q] = (b < a.B && k4 < klen) ? *reinterpret_cast<const float4 *>(a.act + (size_t)b * a.K + kt + k4)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// ... scaled by the RMS factors (RMS) and stored as bf16 hi / lo.
+template <int NBT, bool RMS>
+__device__ __forceinline__ void mfma_store_x(const MfmaArgs &a, int kt, int tid, const float4 (&xv)[NBT * 2],
+                                             unsigned short *xh, unsigned short *xl, const float *rn_s, int g0,
+                                             int ngc) {
+#pragma unroll
+  for (int q = 0; q < NBT * 2; ++q) {
+    const int i = tid + 512 * q;
+    const int b = i / (kMKT / 4), k4 = (i - b * (kMKT / 4)) * 4;
+    float vv[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+    if (RMS) {
+      const float r = b < a.B ? rn_s[b * ngc + (kt + k4) / a.ng - g0] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[e] *= r;
+    }
+    u16x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = f2bf(vv[e]);
+      l[e] = f2bf(vv[e] - __uint_as_float((unsigned)h[e] << 16));
+    }
+    *reinterpret_cast<u16x4 *>(&xh[b * kMLD + k4]) = h;
+    *reinterpret_cast<u16x4 *>(&xl[b * kMLD + k4]) = l;
+  }
+}
+
+// The MFMAs of one tile; each k-step's weight registers are refilled with the same
+// k-step of the next tile (kn < k_end) as soon as its MFMAs are issued, so 8 loads
+// per lane stay in flight without a second register set.
+template <int WT, int NBT>
+__device__ __forceinline__ void mfma_tile(const MfmaArgs &a, MRaw<WT> &w, const float (&sc)[2][4], int klen,
+                                          int lane, int kq, const unsigned short *xh, const unsigned short *xl,
+                                          f32x4 (&acc)[NBT], int arow, int kn, int k_end) {
+  const bool arow_ok = arow < a.rows;
+  const int nlen = min(kMKT, k_end - kn);
+  auto refill = [&](int st) {
+    if (kn < k_end) {
+      const bool ok = arow_ok && 32 * st + kq < nlen;
+      const size_t off = (size_t)arow * a.K + kn + 32 * st + kq;
+      if constexpr (WT == M2_W_BF16)
+        w.v[st] = ok ? *reinterpret_cast<const bf16x8 *>(static_cast<const unsigned short *>(a.W) + off) : bf16x8{};
+      else
+        w.v[st] = ok ? *reinterpret_cast<const uint2 *>(static_cast<const int8_t *>(a.W) + off) : make_uint2(0u, 0u);
+    }
+  };
+  if (WT == M2_W_BF16) {
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      const int k = kt + 32 * st + kq;
-      if (WT == M2_W_BF16) {
-        const bool ok = arow_ok && 32 * st + kq < klen;
-        wf[st] = ok ? *reinterpret_cast<const bf16x8 *>(static_cast<const unsigned short *>(a.W) + (size_t)arow * a.K + k)
-                    : bf16x8{};
-      } else {
-        const bool ok = arow_ok && 32 * st + kq < klen;
-        uint2 q = ok ? *reinterpret_cast<const uint2 *>(static_cast<const int8_t *>(a.W) + (size_t)arow * a.K + k)
-                     : make_uint2(0u, 0u);
-        bf16x8 f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const unsigned wd = e < 4 ? q.x : q.y;
-          const float v = (float)((int32_t)(wd << (24 - 8 * (e & 3))) >> 24);
-          f[e] = __builtin_bit_cast(__bf16, f2bf(v));
-        }
-        wf[st] = f;
-      }
-    }
-    // activations of the tile as bf16 hi / lo: 16 NBT sessions x 256 k (zero-filled)
-    for (int i = tid; i < NBT * 16 * (kMKT / 4); i += 256) {
-      const int b = i / (kMKT / 4), k4 = (i - b * (kMKT / 4)) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (b < a.B && k4 < klen) {
-        v = *reinterpret_cast<const float4 *>(a.act + (size_t)b * a.K + kt + k4);
-        if (a.rn) {
-          const float r = a.rn[b * a.n_norm + (kt + k4) / a.ng];
-          v.x *= r; v.y *= r; v.z *= r; v.w *= r;
-        }
-      }
-      const float vv[4] = {v.x, v.y, v.z, v.w};
-      u16x4 h, l;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[e] = f2bf(vv[e]);
-        l[e] = f2bf(vv[e] - __uint_as_float((unsigned)h[e] << 16));
-      }
-      *reinterpret_cast<u16x4 *>(&xh[b * kMLD + k4]) = h;
-      *reinterpret_cast<u16x4 *>(&xl[b * kMLD + k4]) = l;
-    }
-    __syncthreads();
-    if (WT == M2_W_BF16) {
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        if (32 * st >= klen) break;
+      if (32 * st < klen) {
+        const bf16x8 av = mfma_a<WT>(w, st);
 #pragma unroll
         for (int j = 0; j < NBT; ++j) {
           const int b = 16 * j + (lane & 15);
           const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&xh[b * kMLD + 32 * st + kq]);
           const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&xl[b * kMLD + 32 * st + kq]);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], bh, acc[j], 0, 0, 0);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], bl, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[j], 0, 0, 0);
         }
       }
-    } else {
-      // one scale group = q_group / 32 k-steps: products of a group gathered, then scaled
-      const int spg = a.q_group / 32;
-      f32x4 gacc[NBT];
+      refill(st);
+    }
+  } else {
+    // one scale group = q_group / 32 k-steps (4 or 8): its products gathered, then scaled
+    const int spg = a.q_group / 32;
+    f32x4 gacc[NBT];
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        if (32 * st >= klen) break;
+    for (int st = 0; st < 8; ++st) {
+      if (32 * st < klen) {
         if (st % spg == 0) {
-          const int g = (kt + 32 * st) / a.q_group;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int rr = rbase + (lane >> 4) * 4 + r;
-            sc[r] = rr < a.rows ? __half2float(a.S[(size_t)rr * ngrp + g]) : 0.0f;
-          }
 #pragma unroll
           for (int j = 0; j < NBT; ++j) gacc[j] = f32x4{};
         }
+        const bf16x8 av = mfma_a<WT>(w, st);
 #pragma unroll
         for (int j = 0; j < NBT; ++j) {
           const int b = 16 * j + (lane & 15);
           const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&xh[b * kMLD + 32 * st + kq]);
           const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&xl[b * kMLD + 32 * st + kq]);
-          gacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], bh, gacc[j], 0, 0, 0);
-          gacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[st], bl, gacc[j], 0, 0, 0);
+          gacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, gacc[j], 0, 0, 0);
+          gacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, gacc[j], 0, 0, 0);
         }
         if (st % spg == spg - 1 || 32 * (st + 1) >= klen) {
+          const int q = st / spg;
 #pragma unroll
           for (int j = 0; j < NBT; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc[r], gacc[j][r], acc[j][r]);
+            for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(q == 0 ? sc[0][r] : sc[1][r], gacc[j][r], acc[j][r]);
         }
       }
+      refill(st);
+    }
+  }
+}
+
+template <int WT, int NBT, bool RMS>
+__global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaArgs a) {
+  extern __shared__ unsigned short xs[];            // [2 buffers][hi, lo][NBT*16][kMLD], then rn
+  constexpr int XB = NBT * 16 * kMLD;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rbase = blockIdx.x * kMRows + wave * 16;
+  const int arow = rbase + (lane & 15);             // A-operand row of this lane
+  const int k_begin = blockIdx.y * a.kchunk, k_end = min(a.K, k_begin + a.kchunk);
+  const int kq = (lane >> 4) * 8;                   // this lane's 8 k within a 32-wide step
+  float *rn_s = reinterpret_cast<float *>(xs + 4 * XB);
+  const int g0 = RMS ? k_begin / a.ng : 0;
+  const int ngc = RMS ? (k_end - 1) / a.ng - g0 + 1 : 1;
+
+  MRaw<WT> w;
+  float s0[2][4] = {}, s1[2][4] = {};
+  float4 xv[NBT * 2];
+  mfma_load_w<WT>(a, arow, k_begin, min(kMKT, k_end - k_begin), kq, w);
+  if (WT == M2_W_INT8G) mfma_load_s(a, rbase, lane, k_begin, s0);
+  mfma_load_x<NBT>(a, k_begin, min(kMKT, k_end - k_begin), tid, xv);
+  if (RMS) {
+    // RMS factors of the chunk's groups: 8 lanes per (session, group), strided sums
+    // combined in a fixed order
+    const int per = a.n_partials / a.n_norm;
+    for (int base = 0; base < a.B * ngc * 8; base += 512) {
+      const int i = base + tid, pair = i >> 3, j = i & 7;
+      float sum = 0.0f;
+      if (pair < a.B * ngc) {
+        const int b = pair / ngc, g = g0 + pair % ngc;
+        for (int q = j; q < per; q += 8) sum += a.ss[(size_t)b * a.n_partials + g * per + q];
+      }
+      sum += __shfl_xor(sum, 1, 8);
+      sum += __shfl_xor(sum, 2, 8);
+      sum += __shfl_xor(sum, 4, 8);
+      if (pair < a.B * ngc && j == 0) rn_s[pair] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
     }
     __syncthreads();
+  }
+  mfma_store_x<NBT, RMS>(a, k_begin, tid, xv, xs, xs + XB, rn_s, g0, ngc);
+  __syncthreads();
+
+  f32x4 acc[NBT];
+#pragma unroll
+  for (int j = 0; j < NBT; ++j) acc[j] = f32x4{};
+  int buf = 0;
+  for (int kt = k_begin; kt < k_end; kt += kMKT) {
+    const int kn = kt + kMKT;
+    if (kn < k_end) {
+      mfma_load_x<NBT>(a, kn, min(kMKT, k_end - kn), tid, xv);
+      if (WT == M2_W_INT8G) mfma_load_s(a, rbase, lane, kn, s1);
+    }
+    mfma_tile<WT, NBT>(a, w, s0, min(kMKT, k_end - kt), lane, kq, xs + 2 * buf * XB, xs + (2 * buf + 1) * XB, acc,
+                       arow, kn, k_end);
+    if (kn >= k_end) break;
+    mfma_store_x<NBT, RMS>(a, kn, tid, xv, xs + 2 * (buf ^ 1) * XB, xs + (2 * (buf ^ 1) + 1) * XB, rn_s, g0, ngc);
+    if (WT == M2_W_INT8G) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s0[q][r] = s1[q][r];
+    }
+    __syncthreads();
+    buf ^= 1;
   }
   // lane l, reg r -> row rbase + (l/16)*4 + r, session 16 j + l % 16
   float *part = a.part + (size_t)blockIdx.y * a.B * a.rows;
@@ -778,17 +906,6 @@ __global__ void gemv_mfma_reduce_kernel(GemvArgs a, const float *part, int ks) {
   float v = 0.0f;
   for (int s = 0; s < ks; ++s) v += part[((size_t)s * a.B + b) * a.rows + row];
   gemv_epilogue<EPI>(a, row, b, v, e);
-}
-
-// RMS factors of every session for the MFMA out_proj: rn[b][j].
-__global__ void rms_decode_kernel(const float *ss, int n_partials, int n_norm, int ng, float eps, float *rn, int B) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * n_norm) return;
-  const int b = idx / n_norm, j = idx - b * n_norm;
-  const int per = n_partials / n_norm;
-  float s = 0.0f;
-  for (int q = 0; q < per; ++q) s += ss[(size_t)b * n_partials + j * per + q];
-  rn[idx] = 1.0f / sqrtf(s / (float)ng + eps);
 }
 
 __global__ void state_zero_kernel(float *ssm, float *conv, size_t ssm_per, size_t conv_per,
@@ -851,15 +968,15 @@ int pick_kt(int K, int BT) {
   return K <= kt ? K : kt;
 }
 
-// in_proj: U=4 nontemporal loads; out_proj: U=8 cached loads (measured best on gfx950)
+// in_proj: U=5 nontemporal loads; out_proj: U=8 cached loads (measured best on gfx950)
 template <int WT, int PRO, int EPI>
 hipError_t dispatch_bt(GemvArgs a, hipStream_t stream) {
   constexpr int KS = EPI == EPI_INPROJ ? 1 : 4;
   const bool regs_ok = PRO != PRO_NORM || (a.K / 4 <= 512 * kNormF4PerThread && a.n_partials <= 512 && a.n_norm <= 512);
   if (a.B <= 2 && regs_ok && wave_lds_bytes(a, a.B, PRO) <= kWaveLdsMax) {
     if (EPI == EPI_INPROJ) {
-      if (a.B == 1) return launch_wave<WT, 1, 512, 4, 1, PRO, EPI>(a, stream);
-      return launch_wave<WT, 2, 512, 4, 1, PRO, EPI>(a, stream);
+      if (a.B == 1) return launch_wave<WT, 1, 512, 5, 1, PRO, EPI>(a, stream);
+      return launch_wave<WT, 2, 512, 5, 1, PRO, EPI>(a, stream);
     }
     if (a.B == 1) return launch_wave<WT, 1, 512, 8, 0, PRO, EPI>(a, stream);
     return launch_wave<WT, 2, 512, 8, 0, PRO, EPI>(a, stream);
@@ -886,37 +1003,51 @@ hipError_t dispatch_wt(int wtype, const GemvArgs &a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA GEMV planning: K chunks of whole 256-wide tiles, about 1280 workgroups.
+// MFMA GEMV planning: 128-row workgroups over K chunks of whole 256-wide tiles, at
+// most as many workgroups as are resident at once on the 256 CUs of an MI355X (2
+// per CU), so that no second, partial round of workgroups forms a tail.
 struct MfmaPlan {
-  int ks, kchunk;
+  int ks, kchunk, nbt;
+  size_t lds;
 };
 
-MfmaPlan mfma_plan(int rows, int K) {
-  const int rb = (rows + 63) / 64;
+MfmaPlan mfma_plan(int rows, int K, int B, int ng) {
+  MfmaPlan p;
+  p.nbt = B <= 16 ? 1 : 2;
+  const int rb = (rows + kMRows - 1) / kMRows;
   const int ntiles = (K + kMKT - 1) / kMKT;
-  int ks = (1280 + rb - 1) / rb;
+  const int target = 512;                              // 2 resident workgroups per CU
+  int ks = target / rb;
   if (ks > ntiles) ks = ntiles;
   if (ks < 1) ks = 1;
   const int tiles_per = (ntiles + ks - 1) / ks;
-  MfmaPlan p;
   p.kchunk = tiles_per * kMKT;
   p.ks = (K + p.kchunk - 1) / p.kchunk;
+  const int ngc = ng > 0 ? p.kchunk / ng + 2 : 0;      // norm groups a chunk can touch
+  p.lds = 4 * sizeof(unsigned short) * (size_t)p.nbt * 16 * kMLD + sizeof(float) * (size_t)B * ngc;
   return p;
 }
 
-template <int WT>
-hipError_t launch_mfma(const MfmaArgs &m, hipStream_t stream) {
-  dim3 grid((m.rows + 63) / 64, (m.K + m.kchunk - 1) / m.kchunk);
-  if (m.B <= 16) hipLaunchKernelGGL((gemv_mfma_kernel<WT, 1>), grid, dim3(256), 0, stream, m);
-  else hipLaunchKernelGGL((gemv_mfma_kernel<WT, 2>), grid, dim3(256), 0, stream, m);
+template <int WT, int NBT, bool RMS>
+hipError_t launch_mfma_k(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
+  auto *k = gemv_mfma_kernel<WT, NBT, RMS>;
+  hipError_t e = allow_lds(k, p.lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3((m.rows + kMRows - 1) / kMRows, p.ks), dim3(512), p.lds, stream, m);
   return hipGetLastError();
 }
 
-// One MFMA GEMV + reduce for the arguments of a gemv_* launch.
+template <int WT, bool RMS>
+hipError_t launch_mfma(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
+  return p.nbt == 1 ? launch_mfma_k<WT, 1, RMS>(m, p, stream) : launch_mfma_k<WT, 2, RMS>(m, p, stream);
+}
+
+// One MFMA GEMV + reduce for the arguments of a gemv_* launch; out_proj (EPI_OUT)
+// also forms the RMS factors from g.ss.
 template <int EPI>
-hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, const float *rn, float *part,
-                         hipStream_t stream) {
-  const MfmaPlan p = mfma_plan(g.rows, g.K);
+hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, float *part, hipStream_t stream) {
+  constexpr bool RMS = EPI == EPI_OUT;
+  const MfmaPlan p = mfma_plan(g.rows, g.K, g.B, RMS ? g.ng : 0);
   MfmaArgs m{};
   m.W = g.W;
   m.S = g.S;
@@ -926,11 +1057,14 @@ hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, const float *rn,
   m.kchunk = p.kchunk;
   m.act = g.act;
   m.B = g.B;
-  m.rn = rn;
-  m.ng = g.ng;
+  m.ss = g.ss;
+  m.n_partials = g.n_partials;
   m.n_norm = g.n_norm;
+  m.ng = g.ng;
+  m.eps = g.eps;
   m.part = part;
-  hipError_t e = c.wtype == M2_W_BF16 ? launch_mfma<M2_W_BF16>(m, stream) : launch_mfma<M2_W_INT8G>(m, stream);
+  hipError_t e = c.wtype == M2_W_BF16 ? launch_mfma<M2_W_BF16, RMS>(m, p, stream)
+                                      : launch_mfma<M2_W_INT8G, RMS>(m, p, stream);
   if (e != hipSuccess) return e;
   const int n = g.rows * g.B;
   hipLaunchKernelGGL(gemv_mfma_reduce_kernel<EPI>, dim3((n + 255) / 256), dim3(256), 0, stream, g, part, p.ks);
@@ -961,15 +1095,33 @@ StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base) {
   w.ss = p ? reinterpret_cast<float *>(p + off) : nullptr;
   off += ss;
   if (step_uses_mfma(L, batch)) {
-    const MfmaPlan pi = mfma_plan(L.d_in_proj, L.cfg.d_model), po = mfma_plan(L.cfg.d_model, L.d_inner);
+    const MfmaPlan pi = mfma_plan(L.d_in_proj, L.cfg.d_model, batch, 0);
+    const MfmaPlan po = mfma_plan(L.cfg.d_model, L.d_inner, batch, L.ng);
     const size_t n_in = (size_t)pi.ks * batch * L.d_in_proj, n_out = (size_t)po.ks * batch * L.cfg.d_model;
     w.part = p ? reinterpret_cast<float *>(p + off) : nullptr;
     off += align256(sizeof(float) * (n_in > n_out ? n_in : n_out));
-    w.rn = p ? reinterpret_cast<float *>(p + off) : nullptr;
-    off += align256(sizeof(float) * (size_t)batch * L.n_norm);
   }
   w.bytes = off;
   return w;
+}
+
+// SSD item shapes (measured on gfx950): one or two sessions are latency-bound, and
+// 8 waves with at most 2 slices each finish an item soonest; larger batches are
+// bound by the state stream, where small items with few registers (many items
+// resident) move it fastest.
+hipError_t launch_ssd(const SsdArgs &sa, int items, int batch, hipStream_t stream) {
+  const int rpi = 64 / (sa.N / 4);
+  const int n_inst = (sa.prange + rpi - 1) / rpi;
+  const dim3 grid(items, batch);
+  if (batch <= 2 && n_inst <= 16)
+    hipLaunchKernelGGL((ssd_step_kernel<8, 2>), grid, dim3(512), 0, stream, sa);
+  else if (n_inst <= 10)
+    hipLaunchKernelGGL((ssd_step_kernel<2, 5>), grid, dim3(128), 0, stream, sa);
+  else if (n_inst <= 16)
+    hipLaunchKernelGGL((ssd_step_kernel<4, 4>), grid, dim3(256), 0, stream, sa);
+  else
+    hipLaunchKernelGGL((ssd_step_kernel<4, 8>), grid, dim3(256), 0, stream, sa);
+  return hipGetLastError();
 }
 
 hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x, float *y, int batch,
@@ -1002,7 +1154,7 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   gi.slots = slots;
   gi.n_slots = S.n_slots;
   const bool mfma = step_uses_mfma(L, batch);
-  e = mfma ? run_mfma_gemv<EPI_INPROJ>(c, gi, nullptr, ws.part, stream)
+  e = mfma ? run_mfma_gemv<EPI_INPROJ>(c, gi, ws.part, stream)
            : dispatch_wt<PRO_PLAIN, EPI_INPROJ>(c.wtype, gi, stream);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return e;
@@ -1059,16 +1211,11 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   go.conv_dim = L.conv_dim;
   go.d_conv = c.d_conv;
   go.conv_cache = S.conv;
-  hipLaunchKernelGGL(ssd_step_kernel, dim3(c.n_heads * L.psplit, batch), dim3(kThreads), 0, stream, sa);
-  e = hipGetLastError();
+  e = launch_ssd(sa, c.n_heads * L.psplit, batch, stream);
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return e;
   if (mfma) {
-    const int n = batch * L.n_norm;
-    hipLaunchKernelGGL(rms_decode_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, ws.ss, L.n_partials, L.n_norm,
-                       L.ng, c.norm_eps, ws.rn, batch);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = run_mfma_gemv<EPI_OUT>(c, go, ws.rn, ws.part, stream);
+    e = run_mfma_gemv<EPI_OUT>(c, go, ws.part, stream);
   } else {
     e = dispatch_wt<PRO_NORM, EPI_OUT>(c.wtype, go, stream);
   }
@@ -1076,14 +1223,13 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   return e;
 }
 
-// Batches of 3..32 sessions with bf16 weights, or int8 weights whose scale groups
-// hold whole 32-wide k-steps, run the projections as MFMA GEMVs; the rest as VALU
-// GEMVs.
+// Batches of 3..32 sessions with bf16 weights, or int8 weights in groups of 128 or
+// 256, run the projections as MFMA GEMVs; the rest as VALU GEMVs.
 int step_plan(const m2_layer_s &L, int batch) {
   const m2_config &c = L.cfg;
   if (batch < 3 || batch > 32) return kPlanValu;
   if (c.wtype == M2_W_BF16) return kPlanMfma;
-  return c.wtype == M2_W_INT8G && c.q_group % 32 == 0 && c.q_group <= kMKT ? kPlanMfma : kPlanValu;
+  return c.wtype == M2_W_INT8G && (c.q_group == 128 || c.q_group == 256) ? kPlanMfma : kPlanValu;
 }
 
 bool step_uses_mfma(const m2_layer_s &L, int batch) { return step_plan(L, batch) == kPlanMfma; }

@@ -40,7 +40,6 @@ struct StepWs {
   float *v;         // [B][d_inner]: gated SSD output
   float *ss;        // [B][n_partials]: sums of squares of v per partial range
   float *part;      // MFMA GEMVs: K-chunk partial sums [KS][B][rows]
-  float *rn;        // MFMA out_proj: RMS factors [B][n_norm]
   size_t bytes;
 };
 StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base);

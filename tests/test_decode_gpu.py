@@ -165,3 +165,16 @@ def test_mfma_ragged_rows_and_k():
     xs = synth.make_inputs(dims, 96, 4, 5)
     ssm0, conv0 = synth.make_state(dims, 97, 5, 0.1)
     _check("mfma-ragged", dims, w, xs, ssm0, conv0)
+
+
+@pytest.mark.parametrize("d_state", [4, 256])
+@pytest.mark.parametrize("batch", [1, 3])
+def test_state_size_extremes(d_state, batch):
+    """The smallest and largest d_state: one lane per state row (64 rows per wave
+    instruction) and 64 lanes per row (more conv channels than some item shapes have
+    threads)."""
+    dims = synth.MixerDims(d_model=128, n_heads=4, head_dim=8, d_state=d_state, n_groups=2, wtype="bf16")
+    w = synth.make_layer_weights(dims, 141)
+    xs = synth.make_inputs(dims, 142, 6, batch)
+    ssm0, conv0 = synth.make_state(dims, 143, batch, 0.1)
+    _check("dstate%d-b%d" % (d_state, batch), dims, w, xs, ssm0, conv0)
