@@ -57,7 +57,8 @@ __device__ __forceinline__ float bf16_to_f(unsigned short h) { return __uint_as_
 // LDS rows padded to 40 bf16 (80 B). Global loads of the next K tile are held in
 // registers while the current tile is multiplied out of LDS.
 
-constexpr int GBM = 128, GBN = 128, GBK = 32, GLD = 40;
+constexpr int GBM = 128, GBN = 256, GBK = 32, GLD = 40;
+constexpr size_t kGemmLds = sizeof(unsigned short) * 2 * (2 * GBM + GBN) * GLD;   // 80 KB
 
 struct GemmArgs {
   const float *A;
@@ -72,22 +73,28 @@ struct GemmArgs {
   int M, N, K;
 };
 
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ unsigned short sAh[2][GBM * GLD];
-  __shared__ unsigned short sAl[2][GBM * GLD];
-  __shared__ unsigned short sW[2][GBN * GLD];
+// Block tile 128 x 256, 4 waves in 2 x 2, each wave 64 x 128 = 2 x 4 MFMA 32x32x16
+// tiles: per 16-wide k-step a wave reads 2 A fragments (x hi, lo) and 4 W fragments
+// from LDS for 16 MFMAs. LDS (dynamic, 80 KB, so two workgroups per CU): double-
+// buffered A hi, A lo [128][40] and W [256][40] bf16 (rows padded to 80 B). The next
+// K tile's global loads are held in registers while the current one is multiplied.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_kernel(GemmArgs g) {
+  extern __shared__ unsigned short gsm[];
+  unsigned short *sAh = gsm;                          // [2][GBM * GLD]
+  unsigned short *sAl = gsm + 2 * GBM * GLD;          // [2][GBM * GLD]
+  unsigned short *sW = gsm + 4 * GBM * GLD;           // [2][GBN * GLD]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
-  // loader mapping: row = tid / 2, 16 consecutive k per thread
+  // A loader: row tid / 2, 16 consecutive k; W loader: row tid, all 32 k
   const int lr = tid >> 1, lk = (tid & 1) * 16;
-  const int am = m0 + lr, wnr = n0 + lr;
+  const int am = m0 + lr, wnr = n0 + tid;
   const bool a_ok = am < g.M, w_ok = wnr < g.N;
   const float *arow = g.A + (size_t)(a_ok ? am : 0) * g.lda;
   const unsigned short *wrow = g.W + (size_t)(w_ok ? wnr : 0) * g.K;
 
   float4 ra[4];
-  u32x4 rw[2];
+  u32x4 rw[4];
   auto load_tile = [&](int k0) {
     const int kb = k0 + lk;
 #pragma unroll
@@ -102,13 +109,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
       }
       if (g.rs) {
         // scale per (row, norm group); a group never splits a float4 (ng % 4 == 0)
-        const float s = (a_ok && k < g.K) ? g.rs[(size_t)am * g.n_rs + k / g.ng] : 0.0f;
-        ra[q].x *= s; ra[q].y *= s; ra[q].z *= s; ra[q].w *= s;
+        const float sc = (a_ok && k < g.K) ? g.rs[(size_t)am * g.n_rs + k / g.ng] : 0.0f;
+        ra[q].x *= sc; ra[q].y *= sc; ra[q].z *= sc; ra[q].w *= sc;
       }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int k = kb + 8 * q;
+    for (int q = 0; q < 4; ++q) {
+      const int k = k0 + 8 * q;
       if (w_ok && k + 7 < g.K) {
         rw[q] = *reinterpret_cast<const u32x4 *>(wrow + k);
       } else {
@@ -131,8 +138,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
         lo[4 * q + e] = bf16_rne(v[e] - bf16_to_f(h));
       }
     }
-    u32x4 *ph = reinterpret_cast<u32x4 *>(&sAh[buf][lr * GLD + lk]);
-    u32x4 *pl = reinterpret_cast<u32x4 *>(&sAl[buf][lr * GLD + lk]);
+    u32x4 *ph = reinterpret_cast<u32x4 *>(&sAh[buf * GBM * GLD + lr * GLD + lk]);
+    u32x4 *pl = reinterpret_cast<u32x4 *>(&sAl[buf * GBM * GLD + lr * GLD + lk]);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       ph[q] = u32x4{hi[8 * q] | ((unsigned)hi[8 * q + 1] << 16), hi[8 * q + 2] | ((unsigned)hi[8 * q + 3] << 16),
@@ -140,16 +147,16 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
       pl[q] = u32x4{lo[8 * q] | ((unsigned)lo[8 * q + 1] << 16), lo[8 * q + 2] | ((unsigned)lo[8 * q + 3] << 16),
                     lo[8 * q + 4] | ((unsigned)lo[8 * q + 5] << 16), lo[8 * q + 6] | ((unsigned)lo[8 * q + 7] << 16)};
     }
-    u32x4 *pw = reinterpret_cast<u32x4 *>(&sW[buf][lr * GLD + lk]);
-    pw[0] = rw[0];
-    pw[1] = rw[1];
+    u32x4 *pw = reinterpret_cast<u32x4 *>(&sW[buf * GBN * GLD + tid * GLD]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pw[q] = rw[q];
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   const int nk = (g.K + GBK - 1) / GBK;
   load_tile(0);
@@ -158,40 +165,39 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs g) {
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) load_tile((kt + 1) * GBK);
+    const unsigned short *bAh = sAh + buf * GBM * GLD, *bAl = sAl + buf * GBM * GLD, *bW = sW + buf * GBN * GLD;
 #pragma unroll
     for (int ks = 0; ks < GBK; ks += 16) {
       const int kofs = ks + (lane >> 5) * 8;
-      bf16x8 ah[2], al[2], bw[2];
+      bf16x8 ah[2], al[2], bw[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = wm * 64 + i * 32 + (lane & 31);
-        ah[i] = *reinterpret_cast<const bf16x8 *>(&sAh[buf][r * GLD + kofs]);
-        al[i] = *reinterpret_cast<const bf16x8 *>(&sAl[buf][r * GLD + kofs]);
+        ah[i] = *reinterpret_cast<const bf16x8 *>(&bAh[r * GLD + kofs]);
+        al[i] = *reinterpret_cast<const bf16x8 *>(&bAl[r * GLD + kofs]);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + (lane & 31);
-        bw[j] = *reinterpret_cast<const bf16x8 *>(&sW[buf][r * GLD + kofs]);
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn * 128 + j * 32 + (lane & 31);
+        bw[j] = *reinterpret_cast<const bf16x8 *>(&bW[r * GLD + kofs]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 4; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
         }
     }
-    if (kt + 1 < nk) {
-      store_tile(buf ^ 1);
-    }
+    if (kt + 1 < nk) store_tile(buf ^ 1);
     __syncthreads();
   }
   // epilogue: lane l, reg r -> row (r/4)*8 + (l/32)*4 + r%4, col l%32 of each 32 x 32 tile
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
       if (col >= g.N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -735,7 +741,10 @@ hipError_t run_gemm(const m2_layer_s &L, bool in_proj, const float *A, int lda, 
     g.M = M;
     g.N = N;
     g.K = K;
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((N + GBN - 1) / GBN, (M + GBM - 1) / GBM), dim3(256), 0, stream, g);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_bf16_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((N + GBN - 1) / GBN, (M + GBM - 1) / GBM), dim3(256), kGemmLds, stream, g);
     return hipGetLastError();
   }
   GemmValuArgs g{};
