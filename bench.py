@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", type=int, default=1, help="decode workload index (1, 2 or 3)")
+    ap.add_argument("--config", type=int, default=1,
+                    help="workload: 1 (default), 2 (32 sessions), 3 (27-layer int8 stack), 4 (prefill + 4 sessions)")
     ap.add_argument("--copies", type=int, default=2, help="identical weight copies used in turn")
     ap.add_argument("--no-graph", action="store_true", help="time plain launches only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
@@ -147,9 +148,6 @@ def main():
     from full_duplex_speech_mamba2_amd import m2, synth
 
     wl = synth.workload(args.config)
-    if wl.layers != 1:
-        print("bench.py times single-layer workloads (configs 1, 2 and 4)", file=sys.stderr)
-        sys.exit(2)
     dims, B = wl.dims, wl.batch
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
@@ -161,12 +159,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     print("[bench] workload %s: generating inputs" % wl.name, file=sys.stderr, flush=True)
-    w = synth.make_layer_weights(dims, wl.weight_seed)
     xs_np = synth.make_inputs(dims, wl.seed, wl.steps, B)
     ssm0, conv0 = synth.make_state(dims, wl.seed, B, wl.state_var)
-
-    layers = [m2.Layer(dims, w, dev) for _ in range(max(1, args.copies))]
-    st = m2.State(layers[0], B, torch.from_numpy(ssm0).to(dev), torch.from_numpy(conv0).to(dev))
+    if wl.layers == 1:
+        # one layer's weights in identical copies used in turn
+        w = synth.make_layer_weights(dims, wl.weight_seed)
+        layers = [m2.Layer(dims, w, dev) for _ in range(max(1, args.copies))]
+        states = [m2.State(layers[0], B, torch.from_numpy(ssm0).to(dev), torch.from_numpy(conv0).to(dev))]
+    else:
+        # a residual stack: every layer its own seeded weights and zero state
+        w = None
+        layers, states = [], []
+        for l in range(wl.layers):
+            layers.append(m2.Layer(dims, synth.make_layer_weights(dims, wl.weight_seed, l), dev))
+            states.append(m2.State(layers[-1], B))
+    st = states[0]
     prefill_rec = None
     if wl.prefill:
         prefill_rec = time_prefill(args, wl, layers[0], st, dev)
@@ -178,7 +185,13 @@ def main():
 
     def run(t0, n):
         for t in range(t0, t0 + n):
-            m2.step(layers[t % nl], st, xs[t % nx], ys[t % nx], ws=ws)
+            if wl.layers == 1:
+                m2.step(layers[t % nl], st, xs[t % nx], ys[t % nx], ws=ws)
+            else:
+                u = ys[t % nx]
+                u.copy_(xs[t % nx])
+                for lay, s_ in zip(layers, states):
+                    m2.step(lay, s_, u, u, residual=True, ws=ws)   # y aliases x under M2_RESIDUAL
 
     torch.cuda.synchronize()
     run(0, args.warmup)
@@ -224,7 +237,9 @@ def main():
     evs = [[hip_event(hip) for _ in range(4)] for _ in range(kp)]
     torch.cuda.synchronize()
     for t in range(kp):
-        m2.step_timed(layers[t % nl], st, xs[t % nx], ys[t % nx], evs[t], ws=ws)
+        # per-kernel times of one layer (the stack's first layer, residual as in the stack)
+        m2.step_timed(layers[t % nl] if wl.layers == 1 else layers[0], st, xs[t % nx], ys[t % nx], evs[t],
+                      residual=wl.layers > 1, ws=ws)
     torch.cuda.synchronize()
     names = PHASES
     dur_us = {n: 1000.0 * float(np.mean([hip_elapsed_ms(hip, evs[t][i], evs[t][i + 1]) for t in range(kp)]))
@@ -247,11 +262,12 @@ def main():
         "config": {"workload": wl.name, "d_model": dims.d_model, "n_heads": dims.n_heads,
                    "head_dim": dims.head_dim, "d_state": dims.d_state, "n_groups": dims.n_groups,
                    "d_conv": dims.d_conv, "batch": B, "weight_dtype": dims.wtype,
-                   "state_dtype": "f32", "weight_copies": nl, "step_plan": plan,
+                   "state_dtype": "f32", "layers": wl.layers, "weight_copies": nl if wl.layers == 1 else 1,
+                   "step_plan": plan,
                    "timing": "graph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"},
-        "achieved_GBps": round(kb["step"] * steps_per_s / 1e9, 1),
-        "hbm_peak_frac": round(kb["step"] * steps_per_s / 1e9 / HBM_PEAK_GBPS, 4),
-        "step_algorithmic_bytes": kb["step"],
+        "achieved_GBps": round(wl.layers * kb["step"] * steps_per_s / 1e9, 1),
+        "hbm_peak_frac": round(wl.layers * kb["step"] * steps_per_s / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_algorithmic_bytes": wl.layers * kb["step"],
         "session_tokens_per_s": round(B * steps_per_s, 1),
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
@@ -263,7 +279,7 @@ def main():
     if prefill_rec is not None:
         out["prefill"] = prefill_rec
 
-    if not args.no_cpu:
+    if not args.no_cpu and wl.layers == 1:
         out["cpu_baseline"], out["parity"] = cpu_baseline_and_parity(args, wl, w, xs_np, ssm0, conv0)
     print(json.dumps(out), flush=True)
 
