@@ -641,7 +641,9 @@ __global__ __launch_bounds__(NW * 64) void ssd_step_kernel(SsdArgs a) {
 // by them while staging. gemv_mfma_reduce sums the chunks in a fixed order and
 // applies the row epilogue, so results do not depend on scheduling.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMKT = 256;          // K tile
@@ -660,11 +662,6 @@ struct MfmaArgs {
   float eps;
   float *part;                     // [KS][B][rows]
 };
-
-__device__ __forceinline__ unsigned short f2bf(float f) {
-  const unsigned u = __float_as_uint(f);
-  return (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
 
 // Raw weights of one tile for one lane: 8 k-steps of 8 values.
 template <int WT> struct MRaw;
@@ -701,15 +698,16 @@ __device__ __forceinline__ void mfma_load_s(const MfmaArgs &a, int rbase, int la
 
 template <int WT> __device__ __forceinline__ bf16x8 mfma_a(const MRaw<WT> &w, int st);
 template <> __device__ __forceinline__ bf16x8 mfma_a<M2_W_BF16>(const MRaw<M2_W_BF16> &w, int st) { return w.v[st]; }
+// int8 -> bf16 is exact; the conversions vectorise to byte-select converts and packed
+// bf16 converts (1.5 instructions per value).
 template <> __device__ __forceinline__ bf16x8 mfma_a<M2_W_INT8G>(const MRaw<M2_W_INT8G> &w, int st) {
-  bf16x8 f;
+  f32x8 f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const unsigned wd = e < 4 ? w.v[st].x : w.v[st].y;
-    const float v = (float)((int32_t)(wd << (24 - 8 * (e & 3))) >> 24);
-    f[e] = __builtin_bit_cast(__bf16, f2bf(v));
+    f[e] = (float)((int32_t)(wd << (24 - 8 * (e & 3))) >> 24);
   }
-  return f;
+  return __builtin_convertvector(f, bf16x8);
 }
 
 // Activations of one tile (NBT*16 sessions x 256 k, zero-filled) into registers.
@@ -733,20 +731,16 @@ __device__ __forceinline__ void mfma_store_x(const MfmaArgs &a, int kt, int tid,
   for (int q = 0; q < NBT * 2; ++q) {
     const int i = tid + 512 * q;
     const int b = i / (kMKT / 4), k4 = (i - b * (kMKT / 4)) * 4;
-    float vv[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+    f32x4 vv = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
     if (RMS) {
       const float r = b < a.B ? rn_s[b * ngc + (kt + k4) / a.ng - g0] : 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vv[e] *= r;
+      vv *= r;
     }
-    u16x4 h, l;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h[e] = f2bf(vv[e]);
-      l[e] = f2bf(vv[e] - __uint_as_float((unsigned)h[e] << 16));
-    }
-    *reinterpret_cast<u16x4 *>(&xh[b * kMLD + k4]) = h;
-    *reinterpret_cast<u16x4 *>(&xl[b * kMLD + k4]) = l;
+    // hi = bf16(v) and lo = bf16(v - hi), both rounded to nearest even
+    const bf16x4 h = __builtin_convertvector(vv, bf16x4);
+    const bf16x4 l = __builtin_convertvector(vv - __builtin_convertvector(h, f32x4), bf16x4);
+    *reinterpret_cast<bf16x4 *>(&xh[b * kMLD + k4]) = h;
+    *reinterpret_cast<bf16x4 *>(&xl[b * kMLD + k4]) = l;
   }
 }
 

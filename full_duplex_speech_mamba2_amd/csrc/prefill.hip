@@ -37,17 +37,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + __expf(-a)); }
 __device__ __forceinline__ float softplus(float a) { return a > 20.0f ? a : log1pf(expf(a)); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs)
-__device__ __forceinline__ unsigned short bf16_rne(float f) {
-  const unsigned u = __float_as_uint(f);
-  return (unsigned short)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
 __device__ __forceinline__ float bf16_to_f(unsigned short h) { return __uint_as_float((unsigned)h << 16); }
 
 // ---------------------------------------------------------------------------
@@ -127,25 +123,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
   auto store_tile = [&](int buf) {
-    unsigned short hi[16], lo[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float v[4] = {ra[q].x, ra[q].y, ra[q].z, ra[q].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const unsigned short h = bf16_rne(v[e]);
-        hi[4 * q + e] = h;
-        lo[4 * q + e] = bf16_rne(v[e] - bf16_to_f(h));
-      }
-    }
-    u32x4 *ph = reinterpret_cast<u32x4 *>(&sAh[buf * GBM * GLD + lr * GLD + lk]);
-    u32x4 *pl = reinterpret_cast<u32x4 *>(&sAl[buf * GBM * GLD + lr * GLD + lk]);
+    // hi = bf16(v), lo = bf16(v - hi), both rounded to nearest even (packed converts)
+    bf16x8 *ph = reinterpret_cast<bf16x8 *>(&sAh[buf * GBM * GLD + lr * GLD + lk]);
+    bf16x8 *pl = reinterpret_cast<bf16x8 *>(&sAl[buf * GBM * GLD + lr * GLD + lk]);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      ph[q] = u32x4{hi[8 * q] | ((unsigned)hi[8 * q + 1] << 16), hi[8 * q + 2] | ((unsigned)hi[8 * q + 3] << 16),
-                    hi[8 * q + 4] | ((unsigned)hi[8 * q + 5] << 16), hi[8 * q + 6] | ((unsigned)hi[8 * q + 7] << 16)};
-      pl[q] = u32x4{lo[8 * q] | ((unsigned)lo[8 * q + 1] << 16), lo[8 * q + 2] | ((unsigned)lo[8 * q + 3] << 16),
-                    lo[8 * q + 4] | ((unsigned)lo[8 * q + 5] << 16), lo[8 * q + 6] | ((unsigned)lo[8 * q + 7] << 16)};
+      const f32x8 v = {ra[2 * q].x, ra[2 * q].y, ra[2 * q].z, ra[2 * q].w,
+                       ra[2 * q + 1].x, ra[2 * q + 1].y, ra[2 * q + 1].z, ra[2 * q + 1].w};
+      const bf16x8 h = __builtin_convertvector(v, bf16x8);
+      ph[q] = h;
+      pl[q] = __builtin_convertvector(v - __builtin_convertvector(h, f32x8), bf16x8);
     }
     u32x4 *pw = reinterpret_cast<u32x4 *>(&sW[buf * GBN * GLD + tid * GLD]);
 #pragma unroll

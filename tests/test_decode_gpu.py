@@ -60,8 +60,9 @@ def test_ragged_shapes(wtype, variant, batch):
            residual=residual)
 
 
-@pytest.mark.parametrize("batch", [1, 2, 5, 8, 17])
+@pytest.mark.parametrize("batch", [1, 2, 5, 8, 17, 40])
 def test_batch_sizes_bf16(batch):
+    """1-2 sessions: one-wave-per-row GEMVs; 3-32: MFMA GEMVs; 40: the tiled VALU GEMVs."""
     dims = synth.MixerDims(d_model=512, n_heads=16, head_dim=32, d_state=64, n_groups=4, wtype="bf16")
     w = synth.make_layer_weights(dims, 41)
     xs = synth.make_inputs(dims, 42, 5, batch)
