@@ -301,30 +301,64 @@ __device__ __forceinline__ int slot_of(const ScanArgs &a, int b, bool &ok) {
   return ok ? s : 0;
 }
 
-// conv over T with the cache as left halo, SiLU; softplus dt. One thread per (token, channel).
-__global__ void conv_dt_kernel(ScanArgs a) {
-  const int nc = a.conv_dim + a.H;
-  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (size_t)a.B * a.T * nc) return;
-  const int c = (int)(idx % nc);
-  const size_t bt = idx / nc;
-  const int t = (int)(bt % a.T), b = (int)(bt / a.T);
-  const float *zrow = a.zx + bt * a.zx_stride;
+// conv over T with the cache as left halo, SiLU; softplus dt. A thread owns one
+// channel of one session over a segment of kConvSeg tokens and slides a register
+// window of the last d_conv - 1 raw inputs along it, so every raw input is read once
+// (plus a d_conv - 1 halo per segment). grid: (channel blocks of conv_dim + H, B,
+// segments of T).
+constexpr int kConvSeg = 64;
+constexpr int kMaxConv = 8;
+
+__global__ __launch_bounds__(256) void conv_dt_kernel(ScanArgs a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.z * kConvSeg, t1 = min(a.T, t0 + kConvSeg);
+  if (c >= a.conv_dim + a.H) return;
   bool ok;
   const int slot = slot_of(a, b, ok);
-  if (c < a.conv_dim) {
-    float s = a.conv_b[c];
-    for (int k = 0; k < a.d_conv; ++k) {
-      const int tau = t - (a.d_conv - 1) + k;
-      float in;
-      if (tau >= 0) in = a.zx[((size_t)b * a.T + tau) * a.zx_stride + a.d_inner + c];
-      else in = a.conv[((size_t)slot * (a.d_conv - 1) + (a.d_conv - 1 + tau)) * a.conv_dim + c];
-      s = fmaf(a.conv_w[(size_t)c * a.d_conv + k], in, s);
-    }
-    a.xc[bt * a.conv_dim + c] = ok ? silu(s) : __builtin_nanf("");
-  } else {
+  const size_t row0 = (size_t)b * a.T;
+  if (c >= a.conv_dim) {
     const int h = c - a.conv_dim;
-    a.dt[bt * a.H + h] = softplus(zrow[a.d_inner + a.conv_dim + h] + a.dt_bias[h]);
+    const float bias = a.dt_bias[h];
+    for (int t = t0; t < t1; ++t)
+      a.dt[(row0 + t) * a.H + h] = softplus(a.zx[(row0 + t) * a.zx_stride + a.d_inner + a.conv_dim + h] + bias);
+    return;
+  }
+  const int K = a.d_conv;
+  float w[kMaxConv], win[kMaxConv];                 // win[k]: the input k steps before t (k = 1 .. K-1)
+#pragma unroll
+  for (int k = 0; k < kMaxConv; ++k) w[k] = k < K ? a.conv_w[(size_t)c * K + k] : 0.0f;
+  const float bias = a.conv_b[c];
+#pragma unroll
+  for (int k = 1; k < kMaxConv; ++k) {
+    float v = 0.0f;
+    if (k < K) {
+      const int tau = t0 - k;
+      v = tau >= 0 ? a.zx[(row0 + tau) * a.zx_stride + a.d_inner + c]
+                   : a.conv[((size_t)slot * (K - 1) + (K - 1 + tau)) * a.conv_dim + c];
+    }
+    win[k] = v;
+  }
+  // 8 tokens at a time: their loads are issued together
+  constexpr int TB = 8;
+  for (int tb = t0; tb < t1; tb += TB) {
+    float in[TB];
+#pragma unroll
+    for (int j = 0; j < TB; ++j)
+      in[j] = tb + j < t1 ? a.zx[(row0 + tb + j) * a.zx_stride + a.d_inner + c] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      if (tb + j >= t1) break;
+      // tap K-1 multiplies the newest input, tap K-1-k the input k steps back
+      float s = fmaf(w[K - 1], in[j], bias);
+#pragma unroll
+      for (int k = 1; k < kMaxConv; ++k)
+        if (k < K) s = fmaf(w[K - 1 - k], win[k], s);
+      a.xc[(row0 + tb + j) * a.conv_dim + c] = ok ? silu(s) : __builtin_nanf("");
+#pragma unroll
+      for (int k = kMaxConv - 1; k > 1; --k) win[k] = win[k - 1];
+      win[1] = in[j];
+    }
   }
 }
 
@@ -813,8 +847,8 @@ hipError_t launch_prefill(const m2_layer_s &L, const m2_state_s &S, const float 
   if (e != hipSuccess) return e;
   // 2. conv + dt
   {
-    const size_t n = (size_t)M * (L.conv_dim + c.n_heads);
-    hipLaunchKernelGGL(conv_dt_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+    const dim3 grid((L.conv_dim + c.n_heads + 255) / 256, batch, (seqlen + kConvSeg - 1) / kConvSeg);
+    hipLaunchKernelGGL(conv_dt_kernel, grid, dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // 3. C B^T tiles
