@@ -82,61 +82,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
-  // A loader: row tid / 2, 16 consecutive k; W loader: row tid, all 32 k
+  // A loader: row lr, 16 consecutive k from lk; W loader: row tid, all 32 k. Rows past
+  // the matrix are read from its last row (their results are never stored); K % 16 == 0,
+  // so a 16-wide (A) or 8-wide (W) group lies wholly inside or wholly past K: a group
+  // past K is read from the last group and zeroed when stored to LDS. No branches, so
+  // the next tile's loads stay in flight while the current tile is multiplied.
   const int lr = tid >> 1, lk = (tid & 1) * 16;
-  const int am = m0 + lr, wnr = n0 + tid;
-  const bool a_ok = am < g.M, w_ok = wnr < g.N;
-  const float *arow = g.A + (size_t)(a_ok ? am : 0) * g.lda;
-  const unsigned short *wrow = g.W + (size_t)(w_ok ? wnr : 0) * g.K;
+  const int am = min(m0 + lr, g.M - 1), wnr = min(n0 + tid, g.N - 1);
+  const float *arow = g.A + (size_t)am * g.lda;
+  const unsigned short *wrow = g.W + (size_t)wnr * g.K;
+  const float *rsrow = g.rs ? g.rs + (size_t)am * g.n_rs : nullptr;
 
-  float4 ra[4];
+  f32x4 ra[4];
   u32x4 rw[4];
+  float rsc = 1.0f;
   auto load_tile = [&](int k0) {
-    const int kb = k0 + lk;
+    const int ka = min(k0 + lk, g.K - 16);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = kb + 4 * q;
-      if (a_ok && k + 3 < g.K) {
-        ra[q] = *reinterpret_cast<const float4 *>(arow + k);
-      } else {
-        float t[4];
-        for (int e = 0; e < 4; ++e) t[e] = (a_ok && k + e < g.K) ? arow[k + e] : 0.0f;
-        ra[q] = make_float4(t[0], t[1], t[2], t[3]);
-      }
-      if (g.rs) {
-        // scale per (row, norm group); a group never splits a float4 (ng % 4 == 0)
-        const float sc = (a_ok && k < g.K) ? g.rs[(size_t)am * g.n_rs + k / g.ng] : 0.0f;
-        ra[q].x *= sc; ra[q].y *= sc; ra[q].z *= sc; ra[q].w *= sc;
-      }
-    }
+    for (int q = 0; q < 4; ++q) ra[q] = *reinterpret_cast<const f32x4 *>(arow + ka + 4 * q);
+    // the out_proj scale per (row, norm group): one group covers the 16 values (ng % 16 == 0)
+    if (rsrow) rsc = rsrow[ka / g.ng];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = k0 + 8 * q;
-      if (w_ok && k + 7 < g.K) {
-        rw[q] = *reinterpret_cast<const u32x4 *>(wrow + k);
-      } else {
-        unsigned short t[8];
-        for (int e = 0; e < 8; ++e) t[e] = (w_ok && k + e < g.K) ? wrow[k + e] : (unsigned short)0;
-        rw[q] = u32x4{t[0] | ((unsigned)t[1] << 16), t[2] | ((unsigned)t[3] << 16),
-                      t[4] | ((unsigned)t[5] << 16), t[6] | ((unsigned)t[7] << 16)};
-      }
-    }
+    for (int q = 0; q < 4; ++q) rw[q] = *reinterpret_cast<const u32x4 *>(wrow + min(k0 + 8 * q, g.K - 8));
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, int k0) {
     // hi = bf16(v), lo = bf16(v - hi), both rounded to nearest even (packed converts)
+    const bool a_in = k0 + lk < g.K;
     bf16x8 *ph = reinterpret_cast<bf16x8 *>(&sAh[buf * GBM * GLD + lr * GLD + lk]);
     bf16x8 *pl = reinterpret_cast<bf16x8 *>(&sAl[buf * GBM * GLD + lr * GLD + lk]);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const f32x8 v = {ra[2 * q].x, ra[2 * q].y, ra[2 * q].z, ra[2 * q].w,
-                       ra[2 * q + 1].x, ra[2 * q + 1].y, ra[2 * q + 1].z, ra[2 * q + 1].w};
+      f32x8 v = {ra[2 * q].x, ra[2 * q].y, ra[2 * q].z, ra[2 * q].w,
+                 ra[2 * q + 1].x, ra[2 * q + 1].y, ra[2 * q + 1].z, ra[2 * q + 1].w};
+      v = a_in ? v * rsc : f32x8{};
       const bf16x8 h = __builtin_convertvector(v, bf16x8);
       ph[q] = h;
       pl[q] = __builtin_convertvector(v - __builtin_convertvector(h, f32x8), bf16x8);
     }
     u32x4 *pw = reinterpret_cast<u32x4 *>(&sW[buf * GBN * GLD + tid * GLD]);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) pw[q] = rw[q];
+    for (int q = 0; q < 4; ++q) pw[q] = k0 + 8 * q < g.K ? rw[q] : u32x4{0u, 0u, 0u, 0u};
   };
 
   f32x16 acc[2][4];
@@ -147,7 +132,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int nk = (g.K + GBK - 1) / GBK;
   load_tile(0);
-  store_tile(0);
+  store_tile(0, 0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
@@ -176,7 +161,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
         }
     }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
+    if (kt + 1 < nk) store_tile(buf ^ 1, (kt + 1) * GBK);
     __syncthreads();
   }
   // epilogue: lane l, reg r -> row (r/4)*8 + (l/32)*4 + r%4, col l%32 of each 32 x 32 tile
@@ -747,7 +732,9 @@ hipError_t run_gemm(const m2_layer_s &L, bool in_proj, const float *A, int lda, 
   const m2_config &c = L.cfg;
   const int N = in_proj ? L.d_in_proj : c.d_model;
   const int K = in_proj ? c.d_model : L.d_inner;
-  if (c.wtype == M2_W_BF16) {
+  // the MFMA GEMM reads whole 16-wide groups of K (K % 16 == 0 for every layer) and one
+  // scale per group of 16 (the norm group a multiple of 16)
+  if (c.wtype == M2_W_BF16 && K % 16 == 0 && (!rs || L.ng % 16 == 0)) {
     GemmArgs g{};
     g.A = A;
     g.lda = lda;
