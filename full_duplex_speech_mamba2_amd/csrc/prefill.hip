@@ -54,6 +54,7 @@ __device__ __forceinline__ float bf16_to_f(unsigned short h) { return __uint_as_
 // registers while the current tile is multiplied out of LDS.
 
 constexpr int GBM = 128, GBN = 256, GBK = 32, GLD = 40;
+constexpr int kGemmGroupM = 4;     // row tiles per group of the tile order
 constexpr size_t kGemmLds = sizeof(unsigned short) * 2 * (2 * GBM + GBN) * GLD;   // 80 KB
 
 struct GemmArgs {
@@ -81,7 +82,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   unsigned short *sW = gsm + 4 * GBM * GLD;           // [2][GBN * GLD]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
+  // Tile order. Workgroup ids are dealt to the 8 XCDs in turn (id % 8), each XCD with its
+  // own L2: XCD x takes the x-th contiguous range of a grouped tile order, which walks
+  // groups of kGemmGroupM row tiles across all column tiles, so that the workgroups
+  // resident on one XCD at a time share the A rows and W columns they stream through L2.
+  const int nbn = (g.N + GBN - 1) / GBN, nbm = (g.M + GBM - 1) / GBM;
+  const int T = nbn * nbm, id = blockIdx.x;
+  const int xcd = id & 7, per = T >> 3, rem = T & 7;
+  const int v = xcd * per + min(xcd, rem) + (id >> 3);
+  const int gsz = kGemmGroupM * nbn, grp = v / gsz, first = grp * kGemmGroupM;
+  const int gm = min(kGemmGroupM, nbm - first), w = v - grp * gsz;
+  const int m0 = (first + w % gm) * GBM, n0 = (w / gm) * GBN;
   // A loader: row lr, 16 consecutive k from lk; W loader: row tid, all 32 k. Rows past
   // the matrix are read from its last row (their results are never stored); K % 16 == 0,
   // so a 16-wide (A) or 8-wide (W) group lies wholly inside or wholly past K: a group
@@ -492,13 +503,15 @@ __global__ void state_pass_kernel(ScanArgs a) {
   if (ok) *st = Hs;
 }
 
+constexpr int kOutThreads = 512;
+
 // Per (session, chunk, head): y = intra-chunk + entering-state terms + D x, the
 // gate, v * norm_w and per-token sums of squares of v over the head. Computed as
 // y^T tiles (p x t): lane l, reg r -> p = 16 i + 4 (l/16) + r, t = 16 ti + l % 16.
 // Operands held in LDS: xs [Q][P + 4], hs [P][N + 4] (entering state); the C.B^T
 // tiles and C rows come from global memory one step ahead of their use.
 template <int NP>
-__global__ __launch_bounds__(256) void chunk_out_kernel(ScanArgs a) {
+__global__ __launch_bounds__(kOutThreads) void chunk_out_kernel(ScanArgs a) {
   extern __shared__ float lds[];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -512,7 +525,7 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(ScanArgs a) {
   float *dts = css + a.Q;
   const size_t rowbase = (size_t)b * a.T + t0;
   const int p4 = a.P / 4;
-  for (int i = tid; i < a.Q * p4; i += 256) {
+  for (int i = tid; i < a.Q * p4; i += kOutThreads) {
     const int s = i / p4, q = i - s * p4;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (s < Qc) v = *reinterpret_cast<const float4 *>(a.xc + (rowbase + s) * a.conv_dim + h * a.P + 4 * q);
@@ -520,11 +533,11 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(ScanArgs a) {
   }
   const float *hsrc = a.sc + (((size_t)b * a.nch + c) * a.H + h) * (size_t)a.P * a.N;
   const int n4 = a.N / 4;
-  for (int i = tid; i < a.P * n4; i += 256) {
+  for (int i = tid; i < a.P * n4; i += kOutThreads) {
     const int p = i / n4, q = i - p * n4;
     *reinterpret_cast<float4 *>(hs + p * NN + 4 * q) = reinterpret_cast<const float4 *>(hsrc)[i];
   }
-  for (int s = tid; s < a.Q; s += 256) {
+  for (int s = tid; s < a.Q; s += kOutThreads) {
     css[s] = s < Qc ? a.cs[(rowbase + s) * a.H + h] : 0.0f;
     dts[s] = s < Qc ? a.dt[(rowbase + s) * a.H + h] : 0.0f;
   }
@@ -533,8 +546,12 @@ __global__ __launch_bounds__(256) void chunk_out_kernel(ScanArgs a) {
   const f32x4 *cbt = reinterpret_cast<const f32x4 *>(a.cbt + (((size_t)b * a.nch + c) * a.G + g) * (size_t)np * 256);
   const int coff = a.d_inner + a.G * a.N + g * a.N;
   const float Dh = a.D[h];
+  // 8 waves; tile rounds alternate direction (tiles w, 15 - w, 16 + w, ...), so the
+  // triangular intra-chunk work is shared evenly
 #pragma unroll 1
-  for (int ti = wave; ti < nt; ti += 4) {
+  for (int r = 0; 8 * r < nt; ++r) {
+    const int ti = (r & 1) ? 8 * r + 7 - wave : 8 * r + wave;
+    if (ti >= nt) continue;
     f32x4 acc[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) acc[i] = f32x4{};
@@ -708,7 +725,7 @@ template <int NP>
 hipError_t launch_chunk_out_t(const ScanArgs &a, size_t lds, dim3 grid, hipStream_t stream) {
   hipError_t e = allow_lds(chunk_out_kernel<NP>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chunk_out_kernel<NP>, grid, dim3(256), lds, stream, a);
+  hipLaunchKernelGGL(chunk_out_kernel<NP>, grid, dim3(kOutThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -752,7 +769,7 @@ hipError_t run_gemm(const m2_layer_s &L, bool in_proj, const float *A, int lda, 
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_bf16_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((N + GBN - 1) / GBN, (M + GBM - 1) / GBM), dim3(256), kGemmLds, stream, g);
+    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(((N + GBN - 1) / GBN) * ((M + GBM - 1) / GBM)), dim3(256), kGemmLds, stream, g);
     return hipGetLastError();
   }
   GemmValuArgs g{};
