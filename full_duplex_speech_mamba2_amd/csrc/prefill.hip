@@ -18,7 +18,7 @@
 //   gemm (in_proj)   ZX[BT][d_in_proj] = X W_in^T: bf16 MFMA 32x32x16, fp32 activations
 //                    split into bf16 hi + lo so that bf16 weights multiply exactly
 //   conv_dt          causal conv + SiLU over T (halo from the conv cache), softplus dt
-//   cb               per (session, chunk, group): C B^T tiles (f32 MFMA 16x16x4), s-tile <= t-tile
+//   cb               per (t-tile, chunk, group, session): C B^T tiles (f32 MFMA 16x16x4), s-tile <= t-tile
 //   chunk_state      per (session, chunk, head): cumsum of dt A, S_c
 //   state_pass       per (session, head): H_c recurrence; entering states; final state -> slot
 //   chunk_out        per (session, chunk, head): y, gate, v * norm_w, per-head sum of squares
@@ -362,34 +362,38 @@ __device__ __forceinline__ int npairs(int nt) { return nt * (nt + 1) / 2; }
 // tile pair (si <= ti) -> index, row-major over ti
 __device__ __forceinline__ int pair_index(int si, int ti) { return ti * (ti + 1) / 2 + si; }
 
-// C B^T tiles for one (session, chunk, group): CBT[s][t] = sum_n B_s[n] C_t[n] for
-// 16 x 16 tiles with s-tile <= t-tile, stored in MFMA accumulator order
-// (lane l, reg r -> s = 16 si + 4 (l/16) + r, t = 16 ti + l % 16).
+// C B^T tiles: CBT[s][t] = sum_n B_s[n] C_t[n] for 16 x 16 tiles with s-tile <= t-tile,
+// stored in MFMA accumulator order (lane l, reg r -> s = 16 si + 4 (l/16) + r,
+// t = 16 ti + l % 16). One workgroup per (t-tile, chunk, group, session), its 4 waves
+// striding over the s-tiles. The k index of the 16x16x4 MFMA runs over n in the order
+// that makes each lane read 4 consecutive n of its row with one 16-byte load (lane group
+// j = l/16 takes n = 16 kb + 4 j + e at k-step (kb, e)), so a load instruction covers 16
+// rows x 64 contiguous bytes.
 __global__ __launch_bounds__(256) void cb_kernel(ScanArgs a) {
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int ti = blockIdx.x, c = blockIdx.y, g = blockIdx.z % a.G, b = blockIdx.z / a.G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = c * a.Q;
   const int Qc = min(a.Q, a.T - t0);
-  const int nt = (Qc + 15) / 16, np = npairs(a.Q / 16);
+  if (16 * ti >= Qc) return;
+  const int np = npairs(a.Q / 16);
   const size_t rowbase = (size_t)b * a.T + t0;
-  const int boff = a.d_inner + g * a.N, coff = a.d_inner + a.G * a.N + g * a.N;
+  const int j4 = 4 * (lane >> 4);
+  const int t = 16 * ti + (lane & 15);
+  const bool t_ok = t < Qc;
+  const float *ct = a.xc + (rowbase + (t_ok ? t : 0)) * a.conv_dim + a.d_inner + a.G * a.N + g * a.N + j4;
   float *out = a.cbt + (((size_t)b * a.nch + c) * a.G + g) * (size_t)np * 256;
-  for (int pi = wave; pi < npairs(nt); pi += 4) {
-    int ti = 0;
-    while (pair_index(0, ti + 1) <= pi) ++ti;
-    const int si = pi - pair_index(0, ti);
-    const int s = 16 * si + (lane & 15), t = 16 * ti + (lane & 15);
-    const bool s_ok = s < Qc, t_ok = t < Qc;
-    const float *bs = a.xc + (rowbase + (s_ok ? s : 0)) * a.conv_dim + boff;
-    const float *ct = a.xc + (rowbase + (t_ok ? t : 0)) * a.conv_dim + coff;
+  for (int si = wave; si <= ti; si += 4) {
+    const int s = 16 * si + (lane & 15);
+    const bool s_ok = s < Qc;
+    const float *bs = a.xc + (rowbase + (s_ok ? s : 0)) * a.conv_dim + a.d_inner + g * a.N + j4;
     f32x4 acc = {};
-    for (int k0 = 0; k0 < a.N; k0 += 4) {
-      const int n = k0 + (lane >> 4);
-      const float av = s_ok ? bs[n] : 0.0f;   // A (s x n): lane -> s = l%16, n = k0 + l/16
-      const float bv = t_ok ? ct[n] : 0.0f;   // B (n x t): lane -> n = k0 + l/16, t = l%16
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+    for (int kb = 0; kb < a.N; kb += 16) {
+      const f32x4 bv = s_ok ? *reinterpret_cast<const f32x4 *>(bs + kb) : f32x4{};
+      const f32x4 cv = t_ok ? *reinterpret_cast<const f32x4 *>(ct + kb) : f32x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[e], cv[e], acc, 0, 0, 0);
     }
-    reinterpret_cast<f32x4 *>(out)[(size_t)pi * 64 + lane] = acc;
+    reinterpret_cast<f32x4 *>(out)[(size_t)pair_index(si, ti) * 64 + lane] = acc;
   }
 }
 
@@ -856,7 +860,7 @@ hipError_t launch_prefill(const m2_layer_s &L, const m2_state_s &S, const float 
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // 3. C B^T tiles
-  hipLaunchKernelGGL(cb_kernel, dim3(a.nch, c.n_groups, B), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(cb_kernel, dim3(Q / 16, a.nch, c.n_groups * B), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 4. chunk states
   {
