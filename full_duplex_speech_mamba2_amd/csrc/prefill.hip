@@ -485,6 +485,117 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ScanArgs a) {
         out[(size_t)(16 * wave + 4 * (lane >> 4) + r) * a.N + 16 * j + (lane & 15)] = acc[j][r];
 }
 
+// The same for all heads of a group at once (one workgroup per (session, chunk,
+// group), 8 waves): the group's B chunk is staged in LDS once instead of once per
+// head. Each wave scans dt A of its heads (4 tokens per lane, prefix over the wave by
+// shuffles) into the weights w[head][s] = exp(cs_end - cs_s) dt_s, then the waves take
+// (head, p-tile) tasks in turn. LDS: bs [Q][N + 4], w [hpg][Q].
+template <int NT>
+__global__ __launch_bounds__(512) void chunk_state_group_kernel(ScanArgs a) {
+  extern __shared__ float lds[];
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = c * a.Q;
+  const int Qc = min(a.Q, a.T - t0);
+  const int NN = a.N + 4;
+  float *bs = lds;
+  float *ws = bs + (size_t)a.Q * NN;
+  const size_t rowbase = (size_t)b * a.T + t0;
+  // 1. per head: inclusive cumsum of dt A (Q <= 256: 4 tokens per lane)
+  for (int hh = wave; hh < a.hpg; hh += 8) {
+    const int h = g * a.hpg + hh;
+    const float A = -expf(a.A_log[h]);
+    float v[4], dtv[4];
+    float run = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = 4 * lane + i;
+      dtv[i] = s < Qc ? a.dt[(rowbase + s) * a.H + h] : 0.0f;
+      run += dtv[i] * A;
+      v[i] = run;
+    }
+    float pre = run;   // inclusive prefix of the lane totals
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(pre, off, 64);
+      if (lane >= off) pre += o;
+    }
+    const float base = pre - run;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += base;
+    const int le = (Qc - 1) >> 2, ie = (Qc - 1) & 3;
+    float ve = v[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) if (ie == i) ve = v[i];
+    const float cend = __shfl(ve, le, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = 4 * lane + i;
+      if (s < a.Q) ws[hh * a.Q + s] = s < Qc ? expf(cend - v[i]) * dtv[i] : 0.0f;
+      if (s < Qc) a.cs[(rowbase + s) * a.H + h] = v[i];
+    }
+    if (lane == 0) a.cse[((size_t)b * a.nch + c) * a.H + h] = cend;
+  }
+  // 2. the group's B chunk
+  const int boff = a.d_inner + g * a.N;
+  const int n4 = a.N / 4;
+  for (int i = tid; i < a.Q * n4; i += 512) {
+    const int s = i / n4, q = i - s * n4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s < Qc) v = *reinterpret_cast<const float4 *>(a.xc + (rowbase + s) * a.conv_dim + boff + 4 * q);
+    *reinterpret_cast<float4 *>(bs + s * NN + 4 * q) = v;
+  }
+  __syncthreads();
+  // 3. tasks (head, p-tile); k index of lane group l/16 at step kk of block s0 is s = s0 + 4 (l/16) + kk
+  const int npt = a.P / 16;
+#pragma unroll 1
+  for (int task = wave; task < a.hpg * npt; task += 8) {
+    const int hh = task / npt, pt = task - hh * npt;
+    const int h = g * a.hpg + hh;
+    const float *wh = ws + hh * a.Q;
+    const int p = 16 * pt + (lane & 15);
+    const float *xcol = a.xc + rowbase * a.conv_dim + h * a.P + p;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = f32x4{};
+    // x two blocks ahead of its use
+    float xa[4], xb[4], xn[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int s = 4 * (lane >> 4) + kk;
+      xa[kk] = s < Qc ? xcol[(size_t)s * a.conv_dim] : 0.0f;
+      xb[kk] = s + 16 < Qc ? xcol[(size_t)(s + 16) * a.conv_dim] : 0.0f;
+    }
+    for (int s0 = 0; s0 < Qc; s0 += 16) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int s = s0 + 32 + 4 * (lane >> 4) + kk;
+        xn[kk] = s < Qc ? xcol[(size_t)s * a.conv_dim] : 0.0f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int s = s0 + 4 * (lane >> 4) + kk;
+        const float av = xa[kk] * wh[s];
+        const float *brow = bs + s * NN + (lane & 15);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, brow[16 * j], acc[j], 0, 0, 0);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        xa[kk] = xb[kk];
+        xb[kk] = xn[kk];
+      }
+    }
+    // lane l, reg r -> p = 16 pt + 4 (l/16) + r, n = 16 j + l % 16
+    float *out = a.sc + (((size_t)b * a.nch + c) * a.H + h) * (size_t)a.P * a.N;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        out[(size_t)(16 * pt + 4 * (lane >> 4) + r) * a.N + 16 * j + (lane & 15)] = acc[j][r];
+  }
+}
+
 // Per (session, head, state element): H_c = exp(cs_end_c) H_{c-1} + S_c over the
 // chunks; sc[c] is overwritten with the state entering chunk c; the final state
 // goes to the session's slot.
@@ -659,6 +770,8 @@ __global__ void cache_update_kernel(ScanArgs a) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr size_t kLdsBytes = 160 * 1024;   // LDS per workgroup on gfx950
+
 struct PrefillWs {
   float *zx, *xc, *dt, *cs, *cse, *sc, *cbt, *vw, *ssh, *rn;
   size_t bytes;
@@ -711,6 +824,25 @@ hipError_t launch_chunk_state_t(const ScanArgs &a, size_t lds, dim3 grid, dim3 b
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chunk_state_kernel<NT>, grid, block, lds, stream, a);
   return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_chunk_state_group_t(const ScanArgs &a, size_t lds, dim3 grid, hipStream_t stream) {
+  hipError_t e = allow_lds(chunk_state_group_kernel<NT>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_state_group_kernel<NT>, grid, dim3(512), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_state_group(int nt, const ScanArgs &a, size_t lds, dim3 grid, hipStream_t stream) {
+  switch (nt) {
+    case 1: return launch_chunk_state_group_t<1>(a, lds, grid, stream);
+    case 2: return launch_chunk_state_group_t<2>(a, lds, grid, stream);
+    case 4: return launch_chunk_state_group_t<4>(a, lds, grid, stream);
+    case 8: return launch_chunk_state_group_t<8>(a, lds, grid, stream);
+    case 16: return launch_chunk_state_group_t<16>(a, lds, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // n-tiles of the state: d_state / 16 in {1, 2, 4, 8, 16}
@@ -802,6 +934,9 @@ hipError_t run_gemm(const m2_layer_s &L, bool in_proj, const float *A, int lda, 
 
 size_t prefill_ws_bytes(const m2_layer_s &L, int batch, int seqlen, int chunk) {
   if (!prefill_supported(L)) return 0;
+  // the scan kernels hold a chunk's operands in LDS: refuse chunk lengths whose tiles do
+  // not fit, before anything is launched
+  if (scan_lds_out(L, chunk) > kLdsBytes || scan_lds_state(L, chunk) > kLdsBytes) return 0;
   return prefill_layout(L, batch, seqlen, chunk, nullptr).bytes;
 }
 
@@ -864,10 +999,17 @@ hipError_t launch_prefill(const m2_layer_s &L, const m2_state_s &S, const float 
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 4. chunk states
   {
-    const size_t lds = scan_lds_state(L, Q);
-    if ((e = launch_chunk_state(c.d_state / 16, a, lds, dim3(a.nch, c.n_heads, B), dim3(64 * (c.head_dim / 16)),
-                                stream)) != hipSuccess)
-      return e;
+    // per group when its B chunk and the weights of its heads fit in LDS, else per head
+    const size_t lds_g = sizeof(float) * ((size_t)Q * (c.d_state + 4) + (size_t)L.hpg * Q);
+    if (lds_g <= kLdsBytes) {
+      if ((e = launch_chunk_state_group(c.d_state / 16, a, lds_g, dim3(a.nch, c.n_groups, B), stream)) != hipSuccess)
+        return e;
+    } else {
+      const size_t lds = scan_lds_state(L, Q);
+      if ((e = launch_chunk_state(c.d_state / 16, a, lds, dim3(a.nch, c.n_heads, B), dim3(64 * (c.head_dim / 16)),
+                                  stream)) != hipSuccess)
+        return e;
+    }
   }
   // 5. inter-chunk pass (reads the slots' states, writes the final ones)
   {

@@ -131,3 +131,28 @@ def test_step_rejects_bad_calls_without_launching():
     assert L.m2_state_zero(st, FAKE, 3, None) == m2.M2_ERR_SLOT
     L.m2_state_destroy(st)
     L.m2_layer_destroy(h)
+
+
+def test_prefill_refuses_chunks_whose_scan_tiles_exceed_lds():
+    """The scan kernels keep a chunk's x, state and B tiles in LDS (160 KB per workgroup):
+    a chunk length whose tiles do not fit is refused before anything is launched."""
+    L = m2.lib()
+    wide = synth.MixerDims(d_model=1024, n_heads=16, head_dim=64, d_state=256, n_groups=1, wtype="bf16")
+    rc, h = create(wide)
+    assert rc == 0
+    assert L.m2_prefill_workspace(h, 1, 512, 256) == 0        # B chunk alone: 256 x 260 floats
+    assert L.m2_prefill_workspace(h, 1, 512, 128) > 0
+    st = C.c_void_p()
+    assert L.m2_state_create(h, 1, FAKE, FAKE, C.byref(st)) == 0
+    assert L.m2_prefill(h, st, FAKE, FAKE * 2, 1, 512, 256, None, 0, FAKE, 1 << 40, None) == m2.M2_ERR_UNSUPPORTED
+    L.m2_state_destroy(st)
+    L.m2_layer_destroy(h)
+    # a 128 x 256 entering-state tile (133 KB) leaves room for a 16-token x tile only
+    rc, h = create(wide.replace(n_heads=8, head_dim=128))
+    assert rc == 0
+    assert L.m2_prefill_workspace(h, 1, 512, 16) > 0
+    assert L.m2_prefill_workspace(h, 1, 512, 64) == 0 and L.m2_prefill_workspace(h, 1, 512, 256) == 0
+    L.m2_layer_destroy(h)
+    rc, h = create(synth.NINE_B)
+    assert L.m2_prefill_workspace(h, 4, 2048, 256) > 0        # the 9B shape at chunk 256 fits
+    L.m2_layer_destroy(h)

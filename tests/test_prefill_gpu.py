@@ -98,3 +98,13 @@ def test_9b_shape_short_prompt():
     x = synth.make_prompt(dims, 131, 2, 300)
     ssm0, conv0 = synth.make_state(dims, 132, 2, 0.1)
     _check("9b-T300", dims, w, x, ssm0, conv0, 256)
+
+
+def test_many_heads_per_group_uses_per_head_chunk_states():
+    """64 heads in one group at chunk 256: the group's B chunk (135 KB) and the 64 heads'
+    weights (64 KB) exceed LDS, so the chunk states are formed per head instead of per group."""
+    dims = synth.MixerDims(d_model=256, n_heads=64, head_dim=16, d_state=128, n_groups=1, wtype="bf16")
+    w = synth.make_layer_weights(dims, 141)
+    x = synth.make_prompt(dims, 142, 2, 300)
+    ssm0, conv0 = synth.make_state(dims, 143, 2, 0.1)
+    _check("hpg64-c256", dims, w, x, ssm0, conv0, 256)
