@@ -20,6 +20,12 @@ reproducible on its own.
 Distributions (variance reading of "N(0, v)"):
   W_in ~ N(0, 1/d_model), W_out ~ N(0, 1/d_inner)   (bf16: rounded to nearest even)
   int8 weights: q ~ U{-127..127}, fp16 scales ~ U[0.5, 2]/127 per (row, K-group)
+  4- and 3-bit weights: the fp32 N(0, 1/K) matrix quantized per (row, group of
+    q_group columns) to nearest with the group's min and max: scale =
+    fp16((max - min) / (2^bits - 1)), bias = fp16(min), code = clip(rint((w - bias) /
+    scale)), so w ~ scale code + bias; packed as the library and the oracle read them
+    (4-bit: two codes per byte, the even one in the low nibble; 3-bit: 32 codes in 12
+    bytes, code i at bits 3i..3i+2 of the little-endian 96-bit run)
   conv_w, conv_b ~ N(0, 1/4); norm_w ~ U[0.5, 1.5]; D ~ N(0, 1)
   A_log ~ U[0, ln 16]  (so A = -exp(A_log) lies in [-16, -1])
   dt_bias = softplus^-1(dt0), dt0 = exp(U[ln 1e-3, ln 0.1])
@@ -33,7 +39,8 @@ from typing import Dict, Optional
 
 import numpy as np
 
-WTYPES = ("f32", "bf16", "int8g")
+WTYPES = ("f32", "bf16", "int8g", "int4g", "int3g")
+LOWBIT = {"int4g": 4, "int3g": 3}
 
 # one integer tag per tensor: the third word of the SeedSequence
 _TAGS = {
@@ -55,7 +62,7 @@ class MixerDims:
     norm_eps: float = 1e-5
     wtype: str = "bf16"
     q_group: int = 128
-    q_gamma_in: float = 1.0      # per-tensor dequant multiplier (int8 only)
+    q_gamma_in: float = 1.0      # per-tensor dequant multiplier (quantized weights)
     q_gamma_out: float = 1.0
 
     @property
@@ -85,6 +92,8 @@ NINE_B = MixerDims(d_model=4480, n_heads=128, head_dim=80, d_state=128, n_groups
 NINE_B_INT8 = NINE_B.replace(wtype="int8g", q_group=128,
                              q_gamma_in=float(np.float32(1.0 / math.sqrt(4480))),
                              q_gamma_out=float(np.float32(1.0 / math.sqrt(10240))))
+NINE_B_INT4 = NINE_B.replace(wtype="int4g", q_group=64)
+NINE_B_INT3 = NINE_B.replace(wtype="int3g", q_group=64)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -111,6 +120,10 @@ WORKLOADS: Dict[int, Workload] = {
                 steps=100, layers=27, weight_seed=3, seed=3),
     4: Workload("mamba2_9b_bf16_b4_prefill2048_decode750", NINE_B, batch=4, steps=750,
                 prefill=2048, chunk=256, weight_seed=1, seed=4),
+    5: Workload("mamba2_9b_int4g64_b1_decode750", NINE_B_INT4, batch=1, steps=750,
+                weight_seed=5, seed=5),
+    6: Workload("mamba2_9b_int3g64_b1_decode750", NINE_B_INT3, batch=1, steps=750,
+                weight_seed=6, seed=6),
 }
 
 
@@ -165,12 +178,58 @@ def _int8(seed, layer, tq, ts, rows, k, group):
     return q, s
 
 
+def pack_codes(q: np.ndarray, bits: int) -> np.ndarray:
+    """Unsigned codes q [rows][K] (values < 2^bits) -> packed uint8 rows [rows][K bits / 8]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    rows, K = q.shape
+    if bits == 4:
+        return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    runs = q.reshape(rows, K // 32, 32).astype(np.uint64)
+    lo = np.zeros((rows, K // 32), np.uint64)      # bits 0..63 of each 96-bit run
+    hi = np.zeros((rows, K // 32), np.uint64)      # bits 64..95
+    for i in range(32):
+        b = 3 * i
+        if b + 3 <= 64:
+            lo |= runs[..., i] << np.uint64(b)
+        elif b >= 64:
+            hi |= runs[..., i] << np.uint64(b - 64)
+        else:                                      # straddles bit 64
+            lo |= (runs[..., i] << np.uint64(b)) & np.uint64(0xFFFFFFFFFFFFFFFF)
+            hi |= runs[..., i] >> np.uint64(64 - b)
+    out = np.empty((rows, K // 32, 12), np.uint8)
+    out[..., :8] = lo[..., None].view(np.uint8).reshape(rows, K // 32, 8)
+    out[..., 8:] = hi[..., None].view(np.uint8).reshape(rows, K // 32, 8)[..., :4]
+    return out.reshape(rows, K // 32 * 12)
+
+
+def _lowbit(seed, layer, tq, rows, k, group, bits, std):
+    packed = np.empty((rows, k * bits // 8), np.uint8)
+    sb = np.empty((rows, k // group, 2), np.float16)
+    top = float(2 ** bits - 1)
+
+    def fill(i, r0, r1):
+        w = _rng(seed, layer, tq, i).standard_normal((r1 - r0, k), dtype=np.float32) * np.float32(std)
+        g = w.reshape(r1 - r0, k // group, group)
+        mn, mx = g.min(axis=2), g.max(axis=2)
+        sc = ((mx - mn) / np.float32(top)).astype(np.float16)
+        bi = mn.astype(np.float16)
+        scf = np.maximum(sc.astype(np.float32), np.float32(1e-7))
+        q = np.clip(np.rint((g - bi.astype(np.float32)[..., None]) / scf[..., None]), 0, top).astype(np.uint8)
+        packed[r0:r1] = pack_codes(q.reshape(r1 - r0, k), bits)
+        sb[r0:r1, :, 0] = sc
+        sb[r0:r1, :, 1] = bi
+    _blocked(rows, fill)
+    return packed, sb
+
+
 def make_layer_weights(dims: MixerDims, seed: int, layer: int = 0) -> Dict[str, Optional[np.ndarray]]:
     """All parameters of one mixer layer.
 
     w_in [d_in_proj][d_model] and w_out [d_model][d_inner] are row-major with K
     contiguous: float32 (wtype f32), uint16 bf16 bits (bf16) or int8 (int8g, with
-    float16 scales s_in [d_in_proj][d_model/q_group], s_out [d_model][d_inner/q_group]).
+    float16 scales s_in [d_in_proj][d_model/q_group], s_out [d_model][d_inner/q_group]),
+    or packed 4/3-bit codes as uint8 [rows][K bits/8] (int4g, int3g) with float16
+    (scale, bias) pairs s_in [d_in_proj][d_model/q_group][2], s_out [d_model][d_inner/q_group][2].
     conv_w is [conv_dim][d_conv] with tap d_conv-1 multiplying the newest input.
     """
     d = dims
@@ -178,6 +237,12 @@ def make_layer_weights(dims: MixerDims, seed: int, layer: int = 0) -> Dict[str, 
     if d.wtype == "int8g":
         w["w_in"], w["s_in"] = _int8(seed, layer, "w_in", "s_in", d.d_in_proj, d.d_model, d.q_group)
         w["w_out"], w["s_out"] = _int8(seed, layer, "w_out", "s_out", d.d_model, d.d_inner, d.q_group)
+    elif d.wtype in LOWBIT:
+        b = LOWBIT[d.wtype]
+        w["w_in"], w["s_in"] = _lowbit(seed, layer, "w_in", d.d_in_proj, d.d_model, d.q_group, b,
+                                       1.0 / math.sqrt(d.d_model))
+        w["w_out"], w["s_out"] = _lowbit(seed, layer, "w_out", d.d_model, d.d_inner, d.q_group, b,
+                                         1.0 / math.sqrt(d.d_inner))
     else:
         w["w_in"] = _normal(seed, layer, "w_in", (d.d_in_proj, d.d_model),
                             1.0 / math.sqrt(d.d_model), d.wtype)

@@ -6,7 +6,8 @@ from ``m2_oracle.c``; see that file's header for the definition it follows and
 the passages of the pages it rests on). It shares no code with the HIP library.
 
 Arrays are numpy. Weights are passed in their stored form (float32, bf16 bit
-patterns as uint16, or int8 with float16 scales); the oracle decodes them itself.
+patterns as uint16, int8 with float16 scales, or packed 4- or 3-bit codes as uint8
+rows with float16 (scale, bias) pairs); the oracle decodes them itself.
 States are float64 and are updated in place.
 """
 from __future__ import annotations
@@ -22,7 +23,8 @@ _SRC = os.path.join(_HERE, "m2_oracle.c")
 _HDR = os.path.join(_HERE, "m2_oracle.h")
 LIB_PATH = os.path.join(_HERE, "liboracle_m2.so")
 
-_WT = {"f32": 0, "bf16": 1, "int8g": 2}
+_WT = {"f32": 0, "bf16": 1, "int8g": 2, "int4g": 3, "int3g": 4}
+_BITS = {"int4g": 4, "int3g": 3}
 
 
 def build(force: bool = False) -> str:
@@ -75,6 +77,8 @@ def lib():
         for f in ("orc_bf16_to_double", "orc_fp16_to_double"):
             getattr(_lib, f).argtypes = [C.c_uint16]
             getattr(_lib, f).restype = C.c_double
+        _lib.orc_lowbit_code.argtypes = [i32, P, C.c_int64, C.c_int64, C.c_int64]
+        _lib.orc_lowbit_code.restype = C.c_int32
         for f in ("orc_softplus", "orc_silu"):
             getattr(_lib, f).argtypes = [C.c_double]
             getattr(_lib, f).restype = C.c_double
@@ -115,18 +119,21 @@ class Layer:
                         float(d.q_gamma_in), float(d.q_gamma_out))
         keep = {}
         for k in ("w_in", "w_out"):
-            want = {"f32": np.float32, "bf16": np.uint16, "int8g": np.int8}[d.wtype]
+            want = {"f32": np.float32, "bf16": np.uint16, "int8g": np.int8, "int4g": np.uint8,
+                    "int3g": np.uint8}[d.wtype]
             keep[k] = np.ascontiguousarray(w[k], dtype=want)
         for k in ("s_in", "s_out"):
             keep[k] = None if w.get(k) is None else np.ascontiguousarray(w[k], dtype=np.float16).view(np.uint16)
         for k in ("conv_w", "conv_b", "dt_bias", "A_log", "D", "norm_w"):
             keep[k] = np.ascontiguousarray(w[k], dtype=np.float32)
-        if keep["w_in"].shape != (d.d_in_proj, d.d_model) or keep["w_out"].shape != (d.d_model, d.d_inner):
+        bits = _BITS.get(d.wtype)
+        cols = (lambda K: K) if bits is None else (lambda K: K * bits // 8)   # packed bytes per row
+        if keep["w_in"].shape != (d.d_in_proj, cols(d.d_model)) or keep["w_out"].shape != (d.d_model, cols(d.d_inner)):
             raise ValueError("weight shapes do not match the dimensions")
         if keep["conv_w"].shape != (d.conv_dim, d.d_conv):
             raise ValueError("conv_w shape")
-        if d.wtype == "int8g" and (keep["s_in"] is None or keep["s_out"] is None):
-            raise ValueError("int8 weights need scales")
+        if d.wtype in ("int8g", "int4g", "int3g") and (keep["s_in"] is None or keep["s_out"] is None):
+            raise ValueError("quantized weights need scales")
         self._keep = keep
         self.w = _Weights(*[_ptr(keep[k]) for k in ("w_in", "s_in", "w_out", "s_out", "conv_w",
                                                      "conv_b", "dt_bias", "A_log", "D", "norm_w")])
@@ -228,3 +235,10 @@ def softplus(x: float) -> float:
 
 def silu(x: float) -> float:
     return lib().orc_silu(x)
+
+
+def lowbit_code(wtype: str, w: np.ndarray, row: int, k: int) -> int:
+    """Code k of row `row` of packed low-bit weights w [rows][packed bytes] (the oracle's decoder)."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    K = w.shape[1] * 8 // _BITS[wtype]
+    return int(lib().orc_lowbit_code(_WT[wtype], _ptr(w), row, K, k))

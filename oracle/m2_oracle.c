@@ -38,6 +38,23 @@ double orc_fp16_to_double(uint16_t h) {
   return sign ? -v : v;
 }
 
+/* Code k of row `row` of a low-bit [rows][K] weight matrix.
+ * 4-bit: a row is K/2 bytes; byte j holds code 2j in bits 0-3 and code 2j+1 in bits 4-7.
+ * 3-bit: a row is 3K/8 bytes; each run of 32 codes fills 12 bytes read as one 96-bit
+ * little-endian integer, code i of the run in bits 3i .. 3i+2. */
+int32_t orc_lowbit_code(int32_t wtype, const void *w, int64_t row, int64_t K, int64_t k) {
+  const uint8_t *p = (const uint8_t *)w;
+  if (wtype == ORC_W_INT4G) {
+    const uint8_t byte = p[row * (K / 2) + k / 2];
+    return (k & 1) ? byte >> 4 : byte & 15;
+  }
+  const uint8_t *blk = p + row * (K / 32) * 12 + (k / 32) * 12;
+  const int64_t bit = 3 * (k % 32);
+  uint32_t v = blk[bit / 8];
+  if (bit % 8 > 5) v |= (uint32_t)blk[bit / 8 + 1] << 8;   /* the code straddles two bytes */
+  return (int32_t)((v >> (bit % 8)) & 7);
+}
+
 /* ---- scalar functions ---- */
 
 double orc_softplus(double x) {
@@ -66,12 +83,23 @@ static void dequant_row(const orc_cfg *c, const void *w, const uint16_t *s, int6
   } else if (c->wtype == ORC_W_BF16) {
     const uint16_t *p = (const uint16_t *)w + row * K;
     for (int64_t k = 0; k < K; ++k) dst[k] = orc_bf16_to_double(p[k]);
-  } else {
+  } else if (c->wtype == ORC_W_INT8G) {
     const int8_t *p = (const int8_t *)w + row * K;
     const int64_t ng = K / c->q_group;
     for (int64_t j = 0; j < ng; ++j) {            /* one scale per q_group columns */
       const double sj = orc_fp16_to_double(s[row * ng + j]);
       for (int64_t k = j * c->q_group; k < (j + 1) * c->q_group; ++k) dst[k] = (double)p[k] * sj * gamma;
+    }
+  } else {
+    /* low-bit affine groups: code q (unsigned, 4 or 3 bits), per q_group columns a
+       (scale, bias) pair of fp16, w = gamma (scale q + bias) */
+    const int64_t ng = K / c->q_group;
+    for (int64_t k = 0; k < K; ++k) {
+      const int32_t q = orc_lowbit_code(c->wtype, w, row, K, k);
+      const int64_t j = k / c->q_group;
+      const double sj = orc_fp16_to_double(s[(row * ng + j) * 2]);
+      const double mj = orc_fp16_to_double(s[(row * ng + j) * 2 + 1]);
+      dst[k] = (sj * (double)q + mj) * gamma;
     }
   }
 }
@@ -181,9 +209,10 @@ static int check_cfg(const orc_cfg *c) {
     return -1;
   if (c->n_heads % c->n_groups) return -1;
   if ((c->n_heads * c->head_dim) % c->norm_group) return -1;
-  if (c->wtype == ORC_W_INT8G) {
+  if (c->wtype == ORC_W_INT8G || c->wtype == ORC_W_INT4G || c->wtype == ORC_W_INT3G) {
     if (c->q_group <= 0 || c->d_model % c->q_group || (c->n_heads * c->head_dim) % c->q_group)
       return -1;
+    if (c->wtype != ORC_W_INT8G && c->q_group % 32) return -1;   /* whole 32-code runs per group */
   } else if (c->wtype != ORC_W_F32 && c->wtype != ORC_W_BF16) {
     return -1;
   }

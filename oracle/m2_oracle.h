@@ -37,22 +37,27 @@
 extern "C" {
 #endif
 
-enum { ORC_W_F32 = 0, ORC_W_BF16 = 1, ORC_W_INT8G = 2 };
+enum { ORC_W_F32 = 0, ORC_W_BF16 = 1, ORC_W_INT8G = 2, ORC_W_INT4G = 3, ORC_W_INT3G = 4 };
 
 typedef struct {
   int32_t d_model, n_heads, head_dim, d_state, n_groups, d_conv;
   int32_t norm_group;          /* channels per RMS group (> 0) */
   double norm_eps;
   int32_t wtype;               /* ORC_W_* */
-  int32_t q_group;             /* K-group of the int8 scales */
+  int32_t q_group;             /* K-group of the int8 scales / low-bit (scale, bias) pairs */
   double q_gamma_in, q_gamma_out;
 } orc_cfg;
 
+/* Low-bit weights (the GPTQ page, introduction and "Details": the LLM quantized to
+ * 3 bits with groups of 64, and a 4-bit build): unsigned codes q with, per row and per
+ * q_group columns, an fp16 (scale, bias) pair; w = gamma (scale q + bias). Packing:
+ * see orc_lowbit_code. */
 typedef struct {
-  const void *w_in;            /* [d_in_proj][d_model]: float, bf16 bits (uint16) or int8 */
-  const uint16_t *s_in;        /* fp16 bits [d_in_proj][d_model/q_group] (int8 only) */
+  const void *w_in;            /* [d_in_proj][d_model]: float, bf16 bits (uint16), int8, or packed codes */
+  const uint16_t *s_in;        /* fp16 bits: int8 scales [d_in_proj][d_model/q_group], low-bit
+                                  (scale, bias) pairs [d_in_proj][d_model/q_group][2] */
   const void *w_out;           /* [d_model][d_inner] */
-  const uint16_t *s_out;       /* fp16 bits [d_model][d_inner/q_group] (int8 only) */
+  const uint16_t *s_out;       /* as s_in, [d_model][d_inner/q_group]([2]) */
   const float *conv_w;         /* [conv_dim][d_conv], tap d_conv-1 = newest */
   const float *conv_b;         /* [conv_dim] */
   const float *dt_bias, *A_log, *D;   /* [n_heads] */
@@ -76,6 +81,10 @@ typedef struct {
 int orc_step(const orc_cfg *cfg, const orc_weights *w, double *ssm, double *conv, int32_t n_slots,
              const double *x, double *y, int32_t batch, const int32_t *slot_ids, int32_t residual,
              orc_trace *trace);
+
+/* Code k (unsigned) of row `row` of a packed low-bit [rows][K] matrix (wtype ORC_W_INT4G or
+ * ORC_W_INT3G). */
+int32_t orc_lowbit_code(int32_t wtype, const void *w, int64_t row, int64_t K, int64_t k);
 
 /* Prompt prefill as `seqlen` recurrent steps: x, y [batch][seqlen][d_model]. */
 int orc_prefill(const orc_cfg *cfg, const orc_weights *w, double *ssm, double *conv, int32_t n_slots,

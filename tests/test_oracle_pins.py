@@ -30,8 +30,23 @@ SMALL_G2 = synth.MixerDims(d_model=64, n_heads=4, head_dim=8, d_state=16, n_grou
                            d_conv=4, wtype="f32")
 
 
+def codes_from_bytes(row_bytes, bits):
+    """Codes of one packed row, decoded here from the stated format with Python integers:
+    4-bit, the even code in the low nibble; 3-bit, each 12-byte run is a little-endian
+    96-bit integer holding code i at bits 3i .. 3i+2."""
+    b = bytes(np.asarray(row_bytes, np.uint8))
+    if bits == 4:
+        return [c for byte in b for c in (byte & 15, byte >> 4)]
+    out = []
+    for r in range(0, len(b), 12):
+        v = int.from_bytes(b[r:r + 12], "little")
+        out += [(v >> (3 * i)) & 7 for i in range(32)]
+    return out
+
+
 def decoded(dims, w, which):
-    """Dequantised weight matrix via numpy (float32 view of bf16 bits, int8 * fp16 * gamma)."""
+    """Dequantised weight matrix via numpy (float32 view of bf16 bits, int8 * fp16 * gamma,
+    low-bit (scale code + bias) * gamma with codes from codes_from_bytes)."""
     m = w[which]
     if dims.wtype == "f32":
         return m.astype(np.float64)
@@ -39,6 +54,9 @@ def decoded(dims, w, which):
         return (m.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     s = w["s_in" if which == "w_in" else "s_out"].astype(np.float64)
     gamma = dims.q_gamma_in if which == "w_in" else dims.q_gamma_out
+    if dims.wtype in synth.LOWBIT:
+        q = np.array([codes_from_bytes(r, synth.LOWBIT[dims.wtype]) for r in m], np.float64)
+        return (q * np.repeat(s[..., 0], dims.q_group, axis=1) + np.repeat(s[..., 1], dims.q_group, axis=1)) * gamma
     return m.astype(np.float64) * np.repeat(s, dims.q_group, axis=1) * gamma
 
 
@@ -71,6 +89,29 @@ def test_bf16_decoder_is_top_half_of_binary32():
     for b in rng.integers(0, 0x7F80, 200):
         ref = np.array([int(b) << 16], np.uint32).view(np.float32)[0]
         assert oracle.bf16_to_double(int(b)) == float(ref)
+
+
+def test_lowbit_decoder_against_hand_packed_bytes():
+    # 4-bit: byte 0x21 holds codes 1 (low nibble, even k) then 2
+    row = np.array([[0x21, 0x43, 0xF0, 0x0E] + [0] * 28], np.uint8)
+    got = [oracle.lowbit_code("int4g", row, 0, k) for k in range(8)]
+    assert got == [1, 2, 3, 4, 0, 15, 14, 0]
+    # 3-bit: two rows of two 32-code runs built as 96-bit integers here
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 8, size=(2, 64))
+    packed = np.zeros((2, 24), np.uint8)
+    for r in range(2):
+        for run in range(2):
+            v = sum(int(c) << (3 * i) for i, c in enumerate(codes[r, 32 * run:32 * run + 32]))
+            packed[r, 12 * run:12 * run + 12] = np.frombuffer(v.to_bytes(12, "little"), np.uint8)
+    for r in range(2):
+        assert [oracle.lowbit_code("int3g", packed, r, k) for k in range(64)] == list(codes[r])
+    # the generator's packer agrees with both
+    for bits, wt in ((4, "int4g"), (3, "int3g")):
+        q = rng.integers(0, 2 ** bits, size=(3, 128)).astype(np.uint8)
+        pk = synth.pack_codes(q, bits)
+        assert [codes_from_bytes(r, bits) for r in pk] == q.tolist()
+        assert [oracle.lowbit_code(wt, pk, 2, k) for k in range(128)] == q[2].tolist()
 
 
 def test_bf16_rounding_of_generator_is_nearest_even():
@@ -153,7 +194,10 @@ def _layer(dims, seed=0, **override):
 
 def test_in_and_out_projection_match_numpy_matmul():
     for dims in (SMALL_G2, synth.TINY.replace(wtype="bf16"),
-                 synth.TINY.replace(wtype="int8g", q_group=128, q_gamma_in=0.0625, q_gamma_out=0.0625)):
+                 synth.TINY.replace(wtype="int8g", q_group=128, q_gamma_in=0.0625, q_gamma_out=0.0625),
+                 synth.TINY.replace(wtype="int4g", q_group=64),
+                 synth.TINY.replace(wtype="int3g", q_group=32, q_gamma_in=0.5, q_gamma_out=2.0),
+                 synth.TINY.replace(wtype="int3g", q_group=128)):
         lay, w = _layer(dims, seed=11)
         ssm, conv = lay.new_state(2)
         x = np.random.default_rng(1).standard_normal((2, dims.d_model))
