@@ -10,9 +10,10 @@ single-session decode of a 9B-shaped layer (d_model 4480, 128 heads x 80,
 d_state 128, 8 groups, bf16 weights, fp32 state), 750 frames of 80 ms.
 
 The layer's weights are held in `--copies` identical device copies used in
-turn (default 2, 590 MB), so the 256 MB last-level cache cannot serve a step
-from the previous step's weights, as in a real stack where every other layer's
-weights stream through in between.
+turn (default: enough copies for at least 590 MB, i.e. 2 for bf16 weights and 8
+for 4-bit codes), so the 256 MB last-level cache cannot serve a step from the
+weights of a recent step, as in a real stack where every other layer's weights
+stream through in between.
 
 Prints one JSON line. Besides steps/s it reports the step's algorithmic HBM
 bytes and bandwidth, per-kernel durations measured with HIP events on the
@@ -42,8 +43,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=1,
-                    help="workload: 1 (default), 2 (32 sessions), 3 (27-layer int8 stack), 4 (prefill + 4 sessions)")
-    ap.add_argument("--copies", type=int, default=2, help="identical weight copies used in turn")
+                    help="workload: 1 (default), 2 (32 sessions), 3 (27-layer int8 stack), 4 (prefill + 4 sessions), "
+                         "5 (int4 g64 weights, 1 session), 6 (int3 g64 weights, 1 session)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="identical weight copies used in turn (0: enough for >= 590 MB)")
     ap.add_argument("--no-graph", action="store_true", help="time plain launches only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity")
@@ -55,7 +58,8 @@ def parse():
 
 
 def wbytes(dims):
-    return {"f32": 4, "bf16": 2, "int8g": 1}[dims.wtype]
+    """Bytes per weight element as stored (4- and 3-bit codes packed)."""
+    return {"f32": 4, "bf16": 2, "int8g": 1, "int4g": 0.5, "int3g": 0.375}[dims.wtype]
 
 
 # phases of m2_step_timed (the same for both step plans of m2_step_plan)
@@ -71,7 +75,9 @@ def kernel_bytes(dims, B):
     wb = wbytes(d)
 
     def w_rows(rows, K):
-        return rows * K * wb + (rows * (K // d.q_group) * 2 if d.wtype == "int8g" else 0)
+        # int8: one fp16 scale per group; low-bit: an fp16 (scale, bias) pair per group
+        scales = {"int8g": 2, "int4g": 4, "int3g": 4}.get(d.wtype, 0)
+        return int(rows * K * wb) + rows * (K // d.q_group) * scales
 
     state = 2 * B * d.n_heads * d.head_dim * d.d_state * f
     cache_rd = B * (d.d_conv - 1) * d.conv_dim * f
@@ -164,7 +170,11 @@ def main():
     if wl.layers == 1:
         # one layer's weights in identical copies used in turn
         w = synth.make_layer_weights(dims, wl.weight_seed)
-        layers = [m2.Layer(dims, w, dev) for _ in range(max(1, args.copies))]
+        ncopy = args.copies
+        if ncopy <= 0:
+            per = kernel_bytes(dims, 1)["gemv_in"] + kernel_bytes(dims, 1)["gemv_out"]
+            ncopy = max(2, -(-590_000_000 // per))
+        layers = [m2.Layer(dims, w, dev) for _ in range(ncopy)]
         states = [m2.State(layers[0], B, torch.from_numpy(ssm0).to(dev), torch.from_numpy(conv0).to(dev))]
     else:
         # a residual stack: every layer its own seeded weights and zero state

@@ -33,6 +33,7 @@ namespace m2d {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kNormF4PerThread = 5;          // gemv_wave out_proj: float4 activations held per thread (K <= 10240 at 512 threads)
@@ -49,14 +50,35 @@ __device__ __forceinline__ float i8(uint32_t u, int j) {
   return (float)((int32_t)(u << (24 - 8 * j)) >> 24);
 }
 
+// A weight row is read in chunks of EPC elements, CB bytes each: 16 bytes for every type
+// but 3-bit codes, whose 32-code runs are 12 bytes.
 template <int WT> struct WTraits;
-template <> struct WTraits<M2_W_F32> { static constexpr int EPC = 4; static constexpr int ESZ = 4; };
-template <> struct WTraits<M2_W_BF16> { static constexpr int EPC = 8; static constexpr int ESZ = 2; };
-template <> struct WTraits<M2_W_INT8G> { static constexpr int EPC = 16; static constexpr int ESZ = 1; };
+template <> struct WTraits<M2_W_F32> { static constexpr int EPC = 4; static constexpr int CB = 16; using chunk_t = u32x4; };
+template <> struct WTraits<M2_W_BF16> { static constexpr int EPC = 8; static constexpr int CB = 16; using chunk_t = u32x4; };
+template <> struct WTraits<M2_W_INT8G> { static constexpr int EPC = 16; static constexpr int CB = 16; using chunk_t = u32x4; };
+template <> struct WTraits<M2_W_INT4G> { static constexpr int EPC = 32; static constexpr int CB = 16; using chunk_t = u32x4; };
+struct W3 { uint32_t x, y, z; };
+template <> struct WTraits<M2_W_INT3G> { static constexpr int EPC = 32; static constexpr int CB = 12; using chunk_t = W3; };
 
 template <int NT> __device__ __forceinline__ u32x4 wload(const u32x4 *p) {
   if (NT) return __builtin_nontemporal_load(p);
   return *p;
+}
+
+template <int NT> __device__ __forceinline__ uint32_t wload1(const uint32_t *p) {
+  if (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+// Chunk c of a row that starts at byte pointer rowp.
+template <int WT, int NT>
+__device__ __forceinline__ typename WTraits<WT>::chunk_t load_chunk(const char *rowp, int c) {
+  if constexpr (WT == M2_W_INT3G) {
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(rowp + 12 * (size_t)c);
+    return W3{wload1<NT>(p), wload1<NT>(p + 1), wload1<NT>(p + 2)};
+  } else {
+    return wload<NT>(reinterpret_cast<const u32x4 *>(rowp) + c);
+  }
 }
 
 // Dot product of one 16-byte weight chunk with EPC consecutive fp32 activations.
@@ -99,14 +121,87 @@ template <> __device__ __forceinline__ float chunk_dot<M2_W_INT8G>(const u32x4 &
   return s;
 }
 
+// Low-bit chunks: 32 unsigned codes. 4-bit: word j holds codes 8j .. 8j+7, code 2i of the
+// word in bits 8i .. 8i+3 and code 2i+1 in bits 8i+4 .. 8i+7. 3-bit: the three words are
+// one little-endian 96-bit run, code i in bits 3i .. 3i+2.
+__device__ __forceinline__ float lb4_code(const u32x4 &w, int i) {
+  const uint32_t word = i < 8 ? w.x : i < 16 ? w.y : i < 24 ? w.z : w.w;
+  return (float)((word >> (4 * (i & 7))) & 15u);
+}
+
+__device__ __forceinline__ float lb3_code(const W3 &w, int i) {
+  const int bit = 3 * i, off = bit & 31;
+  const uint32_t lo = bit < 32 ? w.x : bit < 64 ? w.y : w.z;
+  if (off <= 29) return (float)__builtin_amdgcn_ubfe(lo, off, 3);
+  const uint32_t hi = bit < 32 ? w.y : w.z;                    // the code straddles two words
+  return (float)(__builtin_amdgcn_alignbit(hi, lo, off) & 7u);
+}
+
+// sum_i code_i a_i and sum_i a_i over the chunk's 32 codes
+template <int WT>
+__device__ __forceinline__ float2 lowbit_dots(const typename WTraits<WT>::chunk_t &w, const float *a) {
+  float dq = 0.0f, dx = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float4 x = *reinterpret_cast<const float4 *>(a + 4 * q);
+    const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float code;
+      if constexpr (WT == M2_W_INT4G) code = lb4_code(w, 4 * q + j);
+      else code = lb3_code(w, 4 * q + j);
+      dq = fmaf(code, xv[j], dq);
+      dx += xv[j];
+    }
+  }
+  return make_float2(dq, dx);
+}
+
+// Per-chunk quantization parameters: int8 scale, or low-bit (scale, bias) of the chunk's group.
+struct QScale { float s, m; };
+
+template <int WT>
+__device__ __forceinline__ QScale load_qscale(const void *srow, int c, int q_shift) {
+  QScale r{1.0f, 0.0f};
+  if constexpr (WT == M2_W_INT8G) {
+    r.s = __half2float(static_cast<const __half *>(srow)[c >> q_shift]);
+  } else if constexpr (WT == M2_W_INT4G || WT == M2_W_INT3G) {
+    const __half2 sm = static_cast<const __half2 *>(srow)[c >> q_shift];
+    r.s = __low2float(sm);
+    r.m = __high2float(sm);
+  }
+  return r;
+}
+
+// acc += the chunk's contribution (one session)
+template <int WT>
+__device__ __forceinline__ float chunk_acc(const typename WTraits<WT>::chunk_t &w, const float *a, const QScale &q,
+                                           float acc) {
+  if constexpr (WT == M2_W_INT4G || WT == M2_W_INT3G) {
+    const float2 d = lowbit_dots<WT>(w, a);
+    return fmaf(q.s, d.x, fmaf(q.m, d.y, acc));
+  } else if constexpr (WT == M2_W_INT8G) {
+    return fmaf(q.s, chunk_dot<WT>(w, a), acc);
+  } else {
+    return acc + chunk_dot<WT>(w, a);
+  }
+}
+
+// Scale columns of a row (int8: one fp16 per group; low-bit: one (scale, bias) pair).
+template <int WT>
+__device__ __forceinline__ const void *scale_row(const void *S, size_t row, int ngroups) {
+  if constexpr (WT == M2_W_INT4G || WT == M2_W_INT3G) return static_cast<const __half2 *>(S) + row * ngroups;
+  return static_cast<const __half *>(S) + row * ngroups;
+}
+
 enum { PRO_PLAIN = 0, PRO_NORM = 1 };
 enum { EPI_INPROJ = 0, EPI_OUT = 1 };
 
 struct GemvArgs {
   const void *W;          // [rows][K]
-  const __half *S;        // int8 scales [rows][K / q_group]
+  const void *S;          // int8 scales [rows][K / q_group] (fp16), or low-bit (scale, bias) fp16 pairs
   int rows, K;
-  int q_shift;            // log2(q_group / EPC): chunk index -> scale column (int8 only)
+  int q_shift;            // log2(q_group / EPC): chunk index -> scale column (quantized types)
   float gamma;
   const float *act;       // [B][K]: x (in_proj) or v * norm_w (out_proj)
   int B, KT;              // sessions, activation K tile (tiled kernel)
@@ -162,6 +257,30 @@ __device__ __forceinline__ EpiIn epilogue_prefetch(const GemvArgs &a, int row, i
     if (row >= a.d_inner + a.conv_dim) e.bias = a.dt_bias[row - a.d_inner - a.conv_dim];
   } else if (a.resid) {
     e.resid = a.resid[(size_t)b * a.rows + row];
+  }
+  return e;
+}
+
+// The same inputs with every load unconditional (indices clamped, values selected after),
+// for kernels that keep later loads in flight across the epilogue: a conditional load
+// would make the compiler wait for all of them.
+template <int EPI>
+__device__ __forceinline__ EpiIn epilogue_load_all(const GemvArgs &a, int row, int b) {
+  EpiIn e;
+  const int32_t *sp = a.slots ? a.slots + b : reinterpret_cast<const int32_t *>(a.act);
+  const int32_t sv = *sp;
+  e.slot = a.slots ? sv : b;
+  e.sok = e.slot >= 0 && e.slot < a.n_slots;
+  e.bias = 0.0f;
+  e.resid = 0.0f;
+  if (EPI == EPI_INPROJ) {
+    const int j = row - a.d_inner - a.conv_dim;
+    const float bv = a.dt_bias[min(max(j, 0), a.rows - a.d_inner - a.conv_dim - 1)];
+    e.bias = j >= 0 ? bv : 0.0f;
+  } else {
+    const float *rp = a.resid ? a.resid + (size_t)b * a.rows + row : a.act;
+    const float rv = *rp;
+    e.resid = a.resid ? rv : 0.0f;
   }
   return e;
 }
@@ -276,23 +395,23 @@ __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
   extern __shared__ float lds[];
   constexpr int WPB = TPB / 64;
   constexpr int EPC = WTraits<WT>::EPC;
-  constexpr int ESZ = WTraits<WT>::ESZ;
+  constexpr int CB = WTraits<WT>::CB;
+  using chunk_t = typename WTraits<WT>::chunk_t;
   const int tid = threadIdx.x, lane = tid & 63;
   const int row = blockIdx.x * WPB + (tid >> 6);
   const bool row_ok = row < a.rows;
   const int nb = min(BT, a.B);
   const int K = a.K;
   const int NC = K / EPC;
-  const u32x4 *wr = reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.W) +
-                                                    (size_t)(row_ok ? row : 0) * K * ESZ);
-  const __half *srow = a.S + (size_t)(row_ok ? row : 0) * (NC >> a.q_shift);
+  const char *wr = static_cast<const char *>(a.W) + (size_t)(row_ok ? row : 0) * NC * CB;
+  const void *srow = scale_row<WT>(a.S, (size_t)(row_ok ? row : 0), NC >> a.q_shift);
 
   // weights do not depend on the activations: put the first U loads in flight first
-  u32x4 w[U];
+  chunk_t w[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int c = lane + 64 * u;
-    w[u] = (row_ok && c < NC) ? wload<NT>(wr + c) : u32x4{0u, 0u, 0u, 0u};
+    w[u] = (row_ok && c < NC) ? load_chunk<WT, NT>(wr, c) : chunk_t{};
   }
   EpiIn epi{};
   if (row_ok && lane < nb) epi = epilogue_prefetch<EPI>(a, row, lane);
@@ -320,13 +439,9 @@ __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
       for (int u = 0; u < U; ++u) {
         const int c = cb + 64 * u;
         if (c < NC) {
-          float sc = 1.0f;
-          if (WT == M2_W_INT8G) sc = __half2float(srow[c >> a.q_shift]);
+          const QScale qs = load_qscale<WT>(srow, c, a.q_shift);
 #pragma unroll
-          for (int bb = 0; bb < BT; ++bb) {
-            const float d = chunk_dot<WT>(w[u], act_s + bb * K + c * EPC);
-            acc[bb] = WT == M2_W_INT8G ? fmaf(sc, d, acc[bb]) : acc[bb] + d;
-          }
+          for (int bb = 0; bb < BT; ++bb) acc[bb] = chunk_acc<WT>(w[u], act_s + bb * K + c * EPC, qs, acc[bb]);
         }
       }
       cb += 64 * U;
@@ -334,7 +449,7 @@ __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = cb + 64 * u;
-        w[u] = c < NC ? wload<NT>(wr + c) : u32x4{0u, 0u, 0u, 0u};
+        w[u] = c < NC ? load_chunk<WT, NT>(wr, c) : chunk_t{};
       }
     }
   }
@@ -354,6 +469,209 @@ __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// gemv_lowbit: 4- and 3-bit codes, BT (1 or 2) sessions. A wave takes R rows and walks
+// their 32-code chunks together, lane l taking chunk columns l, l + 64, ...: one read of
+// an activation chunk from LDS serves the R rows, and each chunk's (scale, bias) pair is
+// loaded with the chunk. The activations are staged with all their loads issued before
+// any LDS write (the weight loads go out first), then the sum of every 32-element chunk
+// of each session is formed once, for the group bias: w = s q + m gives
+// sum_k w_k x_k = s sum_k q_k x_k + m sum_k x_k.
+// LDS: act [BT][K] | xsum [BT][K/32] (| part [BT][n_partials] | rn [BT][n_norm], out_proj)
+constexpr int kLbThreads = 512;
+
+template <int WT, int BT, int PRO>
+__device__ __forceinline__ void lb_stage(const GemvArgs &a, float *lds, int tid) {
+  constexpr int TPB = kLbThreads;
+  constexpr int MAXF = kNormF4PerThread;
+  const int K = a.K, nf = K / 4, nb = min(BT, a.B);
+  f32x4 v[BT][MAXF];
+  float pv[BT];
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb) {
+    const int sb = min(bb, nb - 1);
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(a.act + (size_t)sb * K);
+#pragma unroll
+    for (int i = 0; i < MAXF; ++i) v[bb][i] = src[min(tid + TPB * i, nf - 1)];   // clamped index
+    pv[bb] = PRO != PRO_NORM ? 0.0f : a.ss[(size_t)sb * a.n_partials + min(tid, a.n_partials - 1)];
+  }
+  f32x4 *act4 = reinterpret_cast<f32x4 *>(lds);
+  if (PRO == PRO_NORM) {
+    float *part = lds + BT * (K + K / 32);
+    float *rn = part + BT * a.n_partials;
+    if (tid < a.n_partials) {
+#pragma unroll
+      for (int bb = 0; bb < BT; ++bb) part[bb * a.n_partials + tid] = pv[bb];
+    }
+    __syncthreads();
+    const int per = a.n_partials / a.n_norm;
+    for (int j = tid; j < BT * a.n_norm; j += TPB) {
+      const int bb = j / a.n_norm, q = j - bb * a.n_norm;
+      float sum = 0.0f;
+      for (int k = 0; k < per; ++k) sum += part[bb * a.n_partials + q * per + k];
+      rn[j] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
+    }
+    __syncthreads();
+    const int ng4 = a.ng / 4;
+#pragma unroll
+    for (int bb = 0; bb < BT; ++bb)
+#pragma unroll
+      for (int i = 0; i < MAXF; ++i) {
+        const int f = min(tid + TPB * i, nf - 1);    // past the row: rewrites the last float4
+        act4[bb * nf + f] = v[bb][i] * rn[bb * a.n_norm + f / ng4];
+      }
+  } else {
+#pragma unroll
+    for (int bb = 0; bb < BT; ++bb)
+#pragma unroll
+      for (int i = 0; i < MAXF; ++i) act4[bb * nf + min(tid + TPB * i, nf - 1)] = v[bb][i];
+  }
+  __syncthreads();
+  // chunk sums, each in a fixed order
+  float *xsum = lds + BT * K;
+  const int nc = K / 32;
+  for (int j = tid; j < BT * nc; j += TPB) {
+    const int bb = j / nc, c = j - bb * nc;
+    const f32x4 *p = act4 + bb * nf + 8 * c;
+    f32x4 s4 = p[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) s4 += p[q];
+    xsum[j] = (s4.x + s4.y) + (s4.z + s4.w);
+  }
+  __syncthreads();
+}
+
+// sum_i code_i x_i over one chunk of 32 codes, x from LDS; R rows share each x read
+template <int WT, int R>
+__device__ __forceinline__ void lb_dots(const typename WTraits<WT>::chunk_t (&w)[R], const float *x, float (&dq)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) dq[r] = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float4 xv = *reinterpret_cast<const float4 *>(x + 4 * q);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float c0, c1, c2, c3;
+      if constexpr (WT == M2_W_INT4G) {
+        // word q/2 holds codes 8(q/2) .. +7; even codes in the low nibbles
+        const uint32_t word = (q >> 1) == 0 ? w[r].x : (q >> 1) == 1 ? w[r].y : (q >> 1) == 2 ? w[r].z : w[r].w;
+        const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+        const int sh = (q & 1) * 16;
+        c0 = (float)((lo >> sh) & 0xffu);
+        c1 = (float)((hi >> sh) & 0xffu);
+        c2 = (float)((lo >> (sh + 8)) & 0xffu);
+        c3 = (float)((hi >> (sh + 8)) & 0xffu);
+      } else {
+        c0 = lb3_code(w[r], 4 * q);
+        c1 = lb3_code(w[r], 4 * q + 1);
+        c2 = lb3_code(w[r], 4 * q + 2);
+        c3 = lb3_code(w[r], 4 * q + 3);
+      }
+      dq[r] = fmaf(c0, xv.x, dq[r]);
+      dq[r] = fmaf(c1, xv.y, dq[r]);
+      dq[r] = fmaf(c2, xv.z, dq[r]);
+      dq[r] = fmaf(c3, xv.w, dq[r]);
+    }
+  }
+}
+
+// A persistent grid: wave w takes row groups (R rows) w, w + W, w + 2W, ... (W waves in
+// all); every chunk column of a group is requested at once (U columns per lane cover the
+// row, U * 64 >= K / 32), and the next group's loads are issued before the current group
+// is multiplied, so two groups per wave are in flight. Loads are unconditional (group
+// and column indices clamped), so that waiting for one group never waits for the next.
+template <int WT, int BT, int R, int U, int NT, int PRO, int EPI>
+__global__ __launch_bounds__(kLbThreads) void gemv_lowbit_kernel(GemvArgs a) {
+  extern __shared__ float lds[];
+  constexpr int WPB = kLbThreads / 64;
+  constexpr int CB = WTraits<WT>::CB;
+  using chunk_t = typename WTraits<WT>::chunk_t;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, NC = K / 32, nb = min(BT, a.B);
+  const int ngroups = (a.rows + R - 1) / R;
+  const int gstride = gridDim.x * WPB;
+  const int g0 = blockIdx.x * WPB + wave;
+
+  struct Set {
+    chunk_t w[U][R];
+    __half2 sm[U][R];
+    EpiIn epi[R];
+  };
+  auto load_group = [&](int g, Set &st) {
+    g = min(g, ngroups - 1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(g * R + r, a.rows - 1);
+      st.epi[r] = epilogue_load_all<EPI>(a, row, min(lane, nb - 1));
+      const char *wr = static_cast<const char *>(a.W) + (size_t)row * NC * CB;
+      const __half2 *sr = static_cast<const __half2 *>(a.S) + (size_t)row * (NC >> a.q_shift);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = min(lane + 64 * u, NC - 1);   // columns past the row are not used
+        st.w[u][r] = load_chunk<WT, NT>(wr, c);
+        st.sm[u][r] = sr[c >> a.q_shift];
+      }
+    }
+  };
+  Set sa, sb;
+  load_group(g0, sa);
+  lb_stage<WT, BT, PRO>(a, lds, tid);
+  const float *act_s = lds;
+  const float *xsum = lds + BT * K;
+
+  auto run_group = [&](int g, const Set &st) {
+    float acc[R][BT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int bb = 0; bb < BT; ++bb) acc[r][bb] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = lane + 64 * u;
+      if (c < NC) {
+#pragma unroll
+        for (int bb = 0; bb < BT; ++bb) {
+          float dq[R];
+          lb_dots<WT, R>(st.w[u], act_s + bb * K + 32 * c, dq);
+          const float xs = xsum[bb * NC + c];
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            acc[r][bb] = fmaf(__low2float(st.sm[u][r]), dq[r], fmaf(__high2float(st.sm[u][r]), xs, acc[r][bb]));
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int bb = 0; bb < BT; ++bb)
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc[r][bb] += __shfl_xor(acc[r][bb], off, 64);
+    if (lane < nb) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = g * R + r;
+        if (row < a.rows) {
+          float val = 0.0f;
+#pragma unroll
+          for (int bb = 0; bb < BT; ++bb)
+            if (lane == bb) val = acc[r][bb];
+          gemv_epilogue<EPI>(a, row, lane, val, st.epi[r]);
+        }
+      }
+    }
+  };
+  // two groups per iteration so that the register sets keep static names
+  for (int g = g0; g < ngroups; g += 2 * gstride) {
+    load_group(g + gstride, sb);
+    run_group(g, sa);
+    if (g + gstride >= ngroups) break;
+    load_group(g + 2 * gstride, sa);
+    run_group(g + gstride, sb);
+  }
+  if (EPI == EPI_OUT && a.conv_cache)
+    conv_cache_shift(a, (size_t)blockIdx.x * kLbThreads + tid, (size_t)gridDim.x * kLbThreads);
+}
+
+// ---------------------------------------------------------------------------
 // gemv_tiled: one workgroup computes RPW = 16/KS rows for a tile of BT sessions.
 // Threads form 16 groups of 16 lanes; group (ks, r) covers row r over the ks-th
 // share of each K tile, lanes striding over 16-byte chunks, U chunks in flight.
@@ -363,7 +681,8 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
   extern __shared__ float lds[];
   constexpr int RPW = 16 / KS;
   constexpr int EPC = WTraits<WT>::EPC;
-  constexpr int ESZ = WTraits<WT>::ESZ;
+  constexpr int CB = WTraits<WT>::CB;
+  using chunk_t = typename WTraits<WT>::chunk_t;
   const int tid = threadIdx.x, lane = tid & 15, gid = tid >> 4;
   const int ks = gid / RPW, rl = gid % RPW;
   const int row = blockIdx.x * RPW + rl;
@@ -381,7 +700,7 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) acc[bb] = 0.0f;
 
-  const __half *srow = a.S + (size_t)(row_ok ? row : 0) * ((a.K / EPC) >> a.q_shift);
+  const void *srow = scale_row<WT>(a.S, (size_t)(row_ok ? row : 0), (a.K / EPC) >> a.q_shift);
   for (int kt = 0; kt < a.K; kt += a.KT) {
     const int klen = min(a.KT, a.K - kt);
     // stage act[b0 .. b0+BT)[kt .. kt+klen) (times the RMS factor for out_proj); klen % 4 == 0
@@ -412,26 +731,21 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
       const int per = (nch + KS - 1) / KS;
       const int c0 = ks * per, c1 = min(nch, c0 + per);
       const int cbase = kt / EPC;
-      const u32x4 *wrow =
-          reinterpret_cast<const u32x4 *>(static_cast<const char *>(a.W) + ((size_t)row * a.K + kt) * ESZ);
+      const char *wrow = static_cast<const char *>(a.W) + ((size_t)row * (a.K / EPC) + cbase) * CB;
       for (int cb = c0 + lane; cb < c1; cb += 16 * U) {
-        u32x4 wv[U];
+        chunk_t wv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = cb + 16 * u;
-          wv[u] = c < c1 ? wrow[c] : u32x4{0u, 0u, 0u, 0u};
+          wv[u] = c < c1 ? load_chunk<WT, 0>(wrow, c) : chunk_t{};
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = cb + 16 * u;
           if (c < c1) {
-            float sc = 1.0f;
-            if (WT == M2_W_INT8G) sc = __half2float(srow[(cbase + c) >> a.q_shift]);
+            const QScale qs = load_qscale<WT>(srow, cbase + c, a.q_shift);
 #pragma unroll
-            for (int bb = 0; bb < BT; ++bb) {
-              const float d = chunk_dot<WT>(wv[u], act_s + bb * a.KT + c * EPC);
-              acc[bb] = WT == M2_W_INT8G ? fmaf(sc, d, acc[bb]) : acc[bb] + d;
-            }
+            for (int bb = 0; bb < BT; ++bb) acc[bb] = chunk_acc<WT>(wv[u], act_s + bb * a.KT + c * EPC, qs, acc[bb]);
           }
         }
       }
@@ -642,7 +956,6 @@ __global__ __launch_bounds__(NW * 64) void ssd_step_kernel(SsdArgs a) {
 // applies the row epilogue, so results do not depend on scheduling.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
@@ -962,9 +1275,43 @@ int pick_kt(int K, int BT) {
   return K <= kt ? K : kt;
 }
 
-// in_proj: U=5 nontemporal loads; out_proj: U=8 cached loads (measured best on gfx950)
+size_t lowbit_lds_bytes(const GemvArgs &a, int BT, int PRO) {
+  return sizeof(float) * ((size_t)BT * (a.K + a.K / 32) +
+                          (PRO == PRO_NORM ? (size_t)BT * (a.n_partials + a.n_norm) : 0));
+}
+
+template <int WT, int BT, int R, int U, int NT, int PRO, int EPI>
+hipError_t launch_lowbit(const GemvArgs &a, hipStream_t stream) {
+  const size_t lds = lowbit_lds_bytes(a, BT, PRO);
+  auto *k = gemv_lowbit_kernel<WT, BT, R, U, NT, PRO, EPI>;
+  hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+  // persistent: at most the workgroups resident at once (two per CU), at least one group each
+  const int rows_per_block = (kLbThreads / 64) * R;
+  const int blocks = std::min((a.rows + rows_per_block - 1) / rows_per_block, 2 * 256);
+  hipLaunchKernelGGL(k, dim3(blocks), dim3(kLbThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+// in_proj: U=5 nontemporal loads; out_proj: U=8 cached loads (measured best on gfx950).
+// Low-bit codes at 1-2 sessions: the persistent low-bit GEMV, 2 rows per wave group for
+// in_proj and 1 for out_proj, 3 or 5 chunk columns per lane (rows of up to 6144 or 10240 codes).
 template <int WT, int PRO, int EPI>
 hipError_t dispatch_bt(GemvArgs a, hipStream_t stream) {
+  constexpr bool LOWBIT = WT == M2_W_INT4G || WT == M2_W_INT3G;
+  if constexpr (LOWBIT) {
+    const bool fits = a.K / 4 <= kLbThreads * kNormF4PerThread && (PRO != PRO_NORM || a.n_partials <= kLbThreads) &&
+                      lowbit_lds_bytes(a, a.B, PRO) <= kWaveLdsMax && a.K / 32 <= 64 * 5;
+    if (a.B <= 2 && fits) {
+      const bool u3 = a.K / 32 <= 64 * 3;
+      if (EPI == EPI_INPROJ) {
+        if (a.B == 1) return u3 ? launch_lowbit<WT, 1, 2, 3, 1, PRO, EPI>(a, stream) : launch_lowbit<WT, 1, 2, 5, 1, PRO, EPI>(a, stream);
+        return u3 ? launch_lowbit<WT, 2, 2, 3, 1, PRO, EPI>(a, stream) : launch_lowbit<WT, 2, 2, 5, 1, PRO, EPI>(a, stream);
+      }
+      if (a.B == 1) return u3 ? launch_lowbit<WT, 1, 1, 3, 0, PRO, EPI>(a, stream) : launch_lowbit<WT, 1, 1, 5, 0, PRO, EPI>(a, stream);
+      return u3 ? launch_lowbit<WT, 2, 1, 3, 0, PRO, EPI>(a, stream) : launch_lowbit<WT, 2, 1, 5, 0, PRO, EPI>(a, stream);
+    }
+  }
   constexpr int KS = EPI == EPI_INPROJ ? 1 : 4;
   const bool regs_ok = PRO != PRO_NORM || (a.K / 4 <= 512 * kNormF4PerThread && a.n_partials <= 512 && a.n_norm <= 512);
   if (a.B <= 2 && regs_ok && wave_lds_bytes(a, a.B, PRO) <= kWaveLdsMax) {
@@ -992,6 +1339,8 @@ hipError_t dispatch_wt(int wtype, const GemvArgs &a, hipStream_t stream) {
   switch (wtype) {
     case M2_W_F32: return dispatch_bt<M2_W_F32, PRO, EPI>(a, stream);
     case M2_W_BF16: return dispatch_bt<M2_W_BF16, PRO, EPI>(a, stream);
+    case M2_W_INT4G: return dispatch_bt<M2_W_INT4G, PRO, EPI>(a, stream);
+    case M2_W_INT3G: return dispatch_bt<M2_W_INT3G, PRO, EPI>(a, stream);
     default: return dispatch_bt<M2_W_INT8G, PRO, EPI>(a, stream);
   }
 }
@@ -1044,7 +1393,7 @@ hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, float *part, hip
   const MfmaPlan p = mfma_plan(g.rows, g.K, g.B, RMS ? g.ng : 0);
   MfmaArgs m{};
   m.W = g.W;
-  m.S = g.S;
+  m.S = static_cast<const __half *>(g.S);
   m.rows = g.rows;
   m.K = g.K;
   m.q_group = c.wtype == M2_W_INT8G ? c.q_group : g.K;
@@ -1125,18 +1474,19 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   auto mark = [&](int i) -> hipError_t {
     return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess;
   };
-  const int epc = c.wtype == M2_W_F32 ? 4 : c.wtype == M2_W_BF16 ? 8 : 16;
-  const int q_shift = c.wtype == M2_W_INT8G ? log2i(c.q_group / epc) : 30;
+  const bool quantized = c.wtype == M2_W_INT8G || c.wtype == M2_W_INT4G || c.wtype == M2_W_INT3G;
+  const int epc = c.wtype == M2_W_F32 ? 4 : c.wtype == M2_W_BF16 ? 8 : c.wtype == M2_W_INT8G ? 16 : 32;
+  const int q_shift = quantized ? log2i(c.q_group / epc) : 30;
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
   // 1. in_proj + conv + dt
   GemvArgs gi{};
   gi.W = L.w.w_in;
-  gi.S = static_cast<const __half *>(L.w.s_in);
+  gi.S = L.w.s_in;
   gi.rows = L.d_in_proj;
   gi.K = c.d_model;
   gi.q_shift = q_shift;
-  gi.gamma = c.wtype == M2_W_INT8G ? c.q_gamma_in : 1.0f;
+  gi.gamma = quantized ? c.q_gamma_in : 1.0f;
   gi.act = x;
   gi.B = batch;
   gi.zx = ws.zx;
@@ -1183,11 +1533,11 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   // 3. RMSNorm + out_proj (+ residual)
   GemvArgs go{};
   go.W = L.w.w_out;
-  go.S = static_cast<const __half *>(L.w.s_out);
+  go.S = L.w.s_out;
   go.rows = c.d_model;
   go.K = L.d_inner;
   go.q_shift = q_shift;
-  go.gamma = c.wtype == M2_W_INT8G ? c.q_gamma_out : 1.0f;
+  go.gamma = quantized ? c.q_gamma_out : 1.0f;
   go.act = ws.v;
   go.B = batch;
   go.ss = ws.ss;

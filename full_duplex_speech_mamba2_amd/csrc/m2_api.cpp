@@ -57,8 +57,16 @@ int check_config(const m2_config *c) {
   if (ng % 4) return fail(M2_ERR_SHAPE, "channels per RMS group (%ld) must be a multiple of 4", ng);
   if (!(c->norm_eps >= 0.0f)) return fail(M2_ERR_SHAPE, "norm_eps must be >= 0");
   if (d_inner / ng > 4096) return fail(M2_ERR_UNSUPPORTED, "more than 4096 RMS groups");
-  if (c->wtype != M2_W_F32 && c->wtype != M2_W_BF16 && c->wtype != M2_W_INT8G)
+  if (c->wtype != M2_W_F32 && c->wtype != M2_W_BF16 && c->wtype != M2_W_INT8G && c->wtype != M2_W_INT4G &&
+      c->wtype != M2_W_INT3G)
     return fail(M2_ERR_DTYPE, "unknown wtype %d", c->wtype);
+  if (c->wtype == M2_W_INT4G || c->wtype == M2_W_INT3G) {
+    if (c->q_group < 32 || (c->q_group & (c->q_group - 1)))
+      return fail(M2_ERR_SHAPE, "q_group %d must be a power of two >= 32", c->q_group);
+    if (c->d_model % c->q_group || d_inner % c->q_group)
+      return fail(M2_ERR_SHAPE, "q_group %d does not divide d_model %d and d_inner %ld", c->q_group,
+                  c->d_model, d_inner);
+  }
   if (c->wtype == M2_W_INT8G) {
     if (c->q_group < 16 || (c->q_group & (c->q_group - 1)))
       return fail(M2_ERR_SHAPE, "q_group %d must be a power of two >= 16", c->q_group);
@@ -91,11 +99,12 @@ int m2_layer_create(const m2_config *cfg, const m2_weights *w, m2_layer *out) {
   const char *names[] = {"w_in", "w_out", "conv_w", "conv_b", "dt_bias", "A_log", "D", "norm_w"};
   for (int i = 0; i < 8; ++i)
     if (!req[i]) return fail(M2_ERR_NULL, "weight pointer %s is NULL", names[i]);
-  if (cfg->wtype == M2_W_INT8G && (!w->s_in || !w->s_out))
-    return fail(M2_ERR_NULL, "int8 weights need s_in and s_out");
+  const bool quantized = cfg->wtype == M2_W_INT8G || cfg->wtype == M2_W_INT4G || cfg->wtype == M2_W_INT3G;
+  if (quantized && (!w->s_in || !w->s_out))
+    return fail(M2_ERR_NULL, "quantized weights need s_in and s_out");
   if (!aligned16(w->w_in) || !aligned16(w->w_out))
     return fail(M2_ERR_ALIGN, "w_in and w_out must be 16-byte aligned");
-  if (cfg->wtype == M2_W_INT8G && (!aligned16(w->s_in) || !aligned16(w->s_out)))
+  if (quantized && (!aligned16(w->s_in) || !aligned16(w->s_out)))
     return fail(M2_ERR_ALIGN, "s_in and s_out must be 16-byte aligned");
   for (int i = 2; i < 8; ++i)
     if (!aligned16(req[i])) return fail(M2_ERR_ALIGN, "%s must be 16-byte aligned", names[i]);

@@ -25,7 +25,7 @@
 //   rms              RMS factor per (token, norm group)
 //   gemm (out_proj)  Y = (v norm_w r) W_out^T (+ residual), same GEMM with a row-group scale on A
 //   cache_update     conv cache <- last d_conv-1 raw inputs (mixing with the old cache if T is short)
-// Weights stored as fp32 or int8 use a fp32 VALU GEMM instead of the MFMA GEMM.
+// Weights stored as fp32, int8 or 4/3-bit codes use a fp32 VALU GEMM instead of the MFMA GEMM.
 #include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
 
@@ -216,8 +216,24 @@ struct GemmValuArgs {
 __device__ __forceinline__ float weight_at(const GemmValuArgs &g, int n, int k) {
   if (g.wtype == M2_W_F32) return static_cast<const float *>(g.W)[(size_t)n * g.K + k];
   if (g.wtype == M2_W_BF16) return bf16_to_f(static_cast<const unsigned short *>(g.W)[(size_t)n * g.K + k]);
-  const float q = (float)static_cast<const int8_t *>(g.W)[(size_t)n * g.K + k];
-  return q * __half2float(g.S[(size_t)n * (g.K / g.q_group) + k / g.q_group]);
+  if (g.wtype == M2_W_INT8G) {
+    const float q = (float)static_cast<const int8_t *>(g.W)[(size_t)n * g.K + k];
+    return q * __half2float(g.S[(size_t)n * (g.K / g.q_group) + k / g.q_group]);
+  }
+  // low-bit codes: 4-bit two per byte (even code low), 3-bit 32 per 12-byte little-endian run
+  const unsigned char *row = static_cast<const unsigned char *>(g.W);
+  unsigned code;
+  if (g.wtype == M2_W_INT4G) {
+    const unsigned byte = row[(size_t)n * (g.K / 2) + k / 2];
+    code = (k & 1) ? byte >> 4 : byte & 15u;
+  } else {
+    const unsigned char *run = row + (size_t)n * (g.K / 32) * 12 + (k / 32) * 12;
+    const int bit = 3 * (k & 31), b = bit >> 3;
+    const unsigned v = run[b] | (b < 11 ? (unsigned)run[b + 1] << 8 : 0u);
+    code = (v >> (bit & 7)) & 7u;
+  }
+  const __half2 sm = reinterpret_cast<const __half2 *>(g.S)[(size_t)n * (g.K / g.q_group) + k / g.q_group];
+  return fmaf(__low2float(sm), (float)code, __high2float(sm));
 }
 
 __global__ __launch_bounds__(256) void gemm_valu_kernel(GemmValuArgs g) {
@@ -914,8 +930,9 @@ hipError_t run_gemm(const m2_layer_s &L, bool in_proj, const float *A, int lda, 
   g.W = in_proj ? L.w.w_in : L.w.w_out;
   g.S = static_cast<const __half *>(in_proj ? L.w.s_in : L.w.s_out);
   g.wtype = c.wtype;
-  g.q_group = c.wtype == M2_W_INT8G ? c.q_group : K;
-  g.gamma = c.wtype == M2_W_INT8G ? (in_proj ? c.q_gamma_in : c.q_gamma_out) : 1.0f;
+  const bool quantized = c.wtype == M2_W_INT8G || c.wtype == M2_W_INT4G || c.wtype == M2_W_INT3G;
+  g.q_group = quantized ? c.q_group : K;
+  g.gamma = quantized ? (in_proj ? c.q_gamma_in : c.q_gamma_out) : 1.0f;
   g.C = C;
   g.ldc = ldc;
   g.R = R;

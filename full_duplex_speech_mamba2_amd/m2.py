@@ -27,7 +27,7 @@ _lib = C.CDLL(LIB_PATH)
 M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIGN = 0, -1, -2, -3, -4
 M2_ERR_WORKSPACE, M2_ERR_SLOT, M2_ERR_UNSUPPORTED, M2_ERR_HIP = -5, -6, -7, -8
 M2_RESIDUAL = 1
-WTYPE = {"f32": 0, "bf16": 1, "int8g": 2}
+WTYPE = {"f32": 0, "bf16": 1, "int8g": 2, "int4g": 3, "int3g": 4}
 
 
 class Config(C.Structure):

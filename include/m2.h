@@ -67,7 +67,14 @@ typedef enum {
 typedef enum {
   M2_W_F32 = 0,             /* float32 */
   M2_W_BF16 = 1,            /* bfloat16 */
-  M2_W_INT8G = 2            /* int8, symmetric, one fp16 scale per (row, q_group columns) */
+  M2_W_INT8G = 2,           /* int8, symmetric, one fp16 scale per (row, q_group columns) */
+  /* Low-bit weights (page "NemotronLabs VoiceChat 11B: GPTQ 3-bit LLM, MLX", introduction
+     and "Details": the LLM quantized to 3 bits with groups of 64, and a 4-bit build):
+     unsigned codes q, and per (row, q_group columns) an fp16 (scale, bias) pair;
+     w = scale * q + bias (times q_gamma). A row of K codes is packed as */
+  M2_W_INT4G = 3,           /* K/2 bytes: byte j holds code 2j in bits 0-3, code 2j+1 in bits 4-7 */
+  M2_W_INT3G = 4            /* 3K/8 bytes: every 32 codes fill 12 bytes read as one little-endian
+                               96-bit integer, code i of the run in bits 3i .. 3i+2 */
 } m2_wtype;
 
 /* flags */
@@ -83,18 +90,20 @@ typedef struct {
   int32_t norm_group;       /* channels per RMS group (multiple of 4); 0 means d_inner / n_groups */
   float norm_eps;           /* RMSNorm epsilon */
   int32_t wtype;            /* m2_wtype */
-  int32_t q_group;          /* columns per int8 scale (M2_W_INT8G); power of two >= 16 */
-  float q_gamma_in;         /* per-tensor multiplier applied to int8 in_proj results (1 = none) */
-  float q_gamma_out;        /* per-tensor multiplier applied to int8 out_proj results */
+  int32_t q_group;          /* columns per scale: M2_W_INT8G power of two >= 16; low-bit types
+                               power of two >= 32 */
+  float q_gamma_in;         /* per-tensor multiplier applied to quantized in_proj results (1 = none) */
+  float q_gamma_out;        /* per-tensor multiplier applied to quantized out_proj results */
 } m2_config;
 
 /* Layer parameters, all device pointers, each 16-byte aligned, row-major. */
 typedef struct {
   const void *w_in;         /* [d_in_proj][d_model], d_in_proj = 2 d_inner + 2 G N + H;
                                rows [z: d_inner | x: d_inner | B: G N | C: G N | dt: H] */
-  const void *s_in;         /* fp16 [d_in_proj][d_model / q_group] (int8 only, else NULL) */
+  const void *s_in;         /* int8: fp16 scales [d_in_proj][d_model / q_group]; low-bit: fp16
+                               (scale, bias) pairs [d_in_proj][d_model / q_group][2]; else NULL */
   const void *w_out;        /* [d_model][d_inner] */
-  const void *s_out;        /* fp16 [d_model][d_inner / q_group] (int8 only, else NULL) */
+  const void *s_out;        /* as s_in, [d_model][d_inner / q_group]([2]) */
   const float *conv_w;      /* [conv_dim][d_conv], conv_dim = d_inner + 2 G N; tap d_conv-1 = newest */
   const float *conv_b;      /* [conv_dim] */
   const float *dt_bias;     /* [H] */

@@ -51,7 +51,8 @@ def fake_weights(int8=False):
 def create(dims, w=None):
     cfg = m2.config_from_dims(dims)
     h = C.c_void_p()
-    rc = m2.lib().m2_layer_create(C.byref(cfg), C.byref(w or fake_weights(dims.wtype == "int8g")), C.byref(h))
+    rc = m2.lib().m2_layer_create(C.byref(cfg), C.byref(w or fake_weights(dims.wtype in ("int8g", "int4g", "int3g"))),
+                                  C.byref(h))
     return rc, h
 
 
@@ -69,6 +70,9 @@ GOOD = synth.MixerDims(d_model=256, n_heads=8, head_dim=32, d_state=16, n_groups
     (dict(norm_group=2), m2.M2_ERR_SHAPE),                   # not a multiple of 4
     (dict(head_dim=6, n_heads=8), m2.M2_ERR_SHAPE),           # head_dim not a multiple of 4
     (dict(wtype="int8g", q_group=512), m2.M2_ERR_SHAPE),     # does not divide d_inner
+    (dict(wtype="int4g", q_group=16), m2.M2_ERR_SHAPE),      # low-bit groups are >= 32 codes
+    (dict(wtype="int3g", q_group=48), m2.M2_ERR_SHAPE),      # not a power of two
+    (dict(wtype="int3g", q_group=512), m2.M2_ERR_SHAPE),     # does not divide d_model
 ])
 def test_layer_create_rejects_bad_configs(bad, status):
     rc, h = create(GOOD.replace(**bad))
@@ -84,6 +88,8 @@ def test_layer_create_rejects_nulls_alignment_and_dtype():
     w.w_in = FAKE + 8
     assert create(GOOD, w)[0] == m2.M2_ERR_ALIGN
     assert create(GOOD.replace(wtype="int8g"), fake_weights(False))[0] == m2.M2_ERR_NULL
+    assert create(GOOD.replace(wtype="int4g", q_group=64), fake_weights(False))[0] == m2.M2_ERR_NULL
+    assert create(GOOD.replace(wtype="int3g", q_group=64))[0] == m2.M2_OK
     cfg = m2.config_from_dims(GOOD)
     cfg.wtype = 9
     h = C.c_void_p()

@@ -179,3 +179,23 @@ def test_state_size_extremes(d_state, batch):
     xs = synth.make_inputs(dims, 142, 6, batch)
     ssm0, conv0 = synth.make_state(dims, 143, batch, 0.1)
     _check("dstate%d-b%d" % (d_state, batch), dims, w, xs, ssm0, conv0)
+
+
+LOWBIT = synth.MixerDims(d_model=512, n_heads=8, head_dim=32, d_state=32, n_groups=2, d_conv=4)
+
+
+@pytest.mark.parametrize("batch", [1, 2, 5])
+@pytest.mark.parametrize("wtype,q_group", [("int4g", 64), ("int3g", 64), ("int4g", 32), ("int3g", 256)])
+def test_lowbit_weights(wtype, q_group, batch):
+    """4- and 3-bit codes with (scale, bias) groups: 1-2 sessions take the wave GEMVs,
+    5 the tiled GEMVs; one case with slots, residual and per-tensor gammas."""
+    dims = LOWBIT.replace(wtype=wtype, q_group=q_group)
+    slots, n_slots, residual = None, batch, False
+    if q_group == 32:
+        dims = dims.replace(q_gamma_in=0.5, q_gamma_out=2.0)
+        n_slots, slots, residual = 6, np.array([5, 0, 3, 1, 2][:batch], np.int32), True
+    w = synth.make_layer_weights(dims, 51)
+    xs = synth.make_inputs(dims, 52, 7, batch)
+    ssm0, conv0 = synth.make_state(dims, 53, n_slots, 0.1)
+    _check("lowbit-%s-g%d-b%d" % (wtype, q_group, batch), dims, w, xs, ssm0, conv0, slot_ids=slots,
+           residual=residual)

@@ -108,3 +108,12 @@ def test_many_heads_per_group_uses_per_head_chunk_states():
     x = synth.make_prompt(dims, 142, 2, 300)
     ssm0, conv0 = synth.make_state(dims, 143, 2, 0.1)
     _check("hpg64-c256", dims, w, x, ssm0, conv0, 256)
+
+
+@pytest.mark.parametrize("wtype", ["int4g", "int3g"])
+def test_lowbit_prefill(wtype):
+    dims = synth.MixerDims(d_model=256, n_heads=4, head_dim=32, d_state=32, n_groups=2, wtype=wtype, q_group=64)
+    w = synth.make_layer_weights(dims, 151)
+    x = synth.make_prompt(dims, 152, 2, 70)
+    ssm0, conv0 = synth.make_state(dims, 153, 2, 0.1)
+    _check("lowbit-%s" % wtype, dims, w, x, ssm0, conv0, 32)

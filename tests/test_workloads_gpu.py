@@ -7,6 +7,8 @@ launch configurations the bench times (m2_step / m2_prefill through the C ABI):
       x 100 steps                                   tests/golden/make_golden.py
   bf16, 4 sessions, 2048-token chunked prefill      (2 sessions, sampled steps and
       then 750 decode steps                         state positions)
+  int4 g64 and int3 g64 weights, 1 session,         oracle run live
+      750 steps
 
 The tiny fp32 workload runs in test_decode_gpu.py. Sessions are independent, so
 checking a subset of them checks the batched kernels on those sessions; the
@@ -51,6 +53,20 @@ def e_conv_sampled(C, cpos, csamples, cmax):
 
 def test_9b_bf16_single_session_750_steps():
     wl = synth.workload(1)
+    w = synth.make_layer_weights(wl.dims, wl.weight_seed)
+    xs = synth.make_inputs(wl.dims, wl.seed, wl.steps, wl.batch)
+    ssm0, conv0 = synth.make_state(wl.dims, wl.seed, wl.batch, wl.state_var)
+    yg, sg, cg = gpu_decode(wl.dims, w, xs, ssm0, conv0)
+    yo, so, co = oracle_decode(wl.dims, w, xs, ssm0, conv0)
+    eo, es, ec = e_out(yg, yo), e_state(sg, so), e_conv(cg, co)
+    _report(wl.name, e_out=eo, e_state=es, e_conv=ec)
+    assert eo <= TOL_OUT and es <= TOL_STATE and ec <= TOL_STATE
+
+
+@pytest.mark.parametrize("config", [5, 6])
+def test_9b_lowbit_single_session_750_steps(config):
+    """The 9B-shaped layer with 4-bit and 3-bit group-64 weights, oracle run live."""
+    wl = synth.workload(config)
     w = synth.make_layer_weights(wl.dims, wl.weight_seed)
     xs = synth.make_inputs(wl.dims, wl.seed, wl.steps, wl.batch)
     ssm0, conv0 = synth.make_state(wl.dims, wl.seed, wl.batch, wl.state_var)
