@@ -39,6 +39,15 @@ constexpr int kThreads = 256;
 constexpr int kNormF4PerThread = 5;          // gemv_wave out_proj: float4 activations held per thread (K <= 10240 at 512 threads)
 constexpr int kLdsFloatsPerBatch = 12288;   // tiled kernel: activation tile budget (48 KB at 1 session)
 
+// Activations of the low-bit GEMV sit in LDS with 4 floats of padding after every 64: lane l
+// reads the 32 floats of chunk l, and without the padding every lane of an LDS cycle falls
+// on the same 4 banks. With it, the 16 lanes of one cycle read 16 distinct 4-bank groups
+// (for any chunk of 4 to 32 floats). The bf16 wave GEMV reads 8-float chunks, a 2-way
+// conflict that costs it nothing measurable; padding its rows made it slower, so it keeps
+// them dense.
+__host__ __device__ constexpr int lds_pad(int k) { return k + 4 * (k >> 6); }
+__host__ __device__ constexpr int lds_padded(int K) { return lds_pad(K - 1) + 1; }   // a multiple of 4 for K % 4 == 0
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
@@ -494,9 +503,10 @@ __device__ __forceinline__ void lb_stage(const GemvArgs &a, float *lds, int tid)
     for (int i = 0; i < MAXF; ++i) v[bb][i] = src[min(tid + TPB * i, nf - 1)];   // clamped index
     pv[bb] = PRO != PRO_NORM ? 0.0f : a.ss[(size_t)sb * a.n_partials + min(tid, a.n_partials - 1)];
   }
-  f32x4 *act4 = reinterpret_cast<f32x4 *>(lds);
+  const int KP = lds_padded(K);
+  float *acts = lds;
   if (PRO == PRO_NORM) {
-    float *part = lds + BT * (K + K / 32);
+    float *part = lds + BT * (KP + K / 32);
     float *rn = part + BT * a.n_partials;
     if (tid < a.n_partials) {
 #pragma unroll
@@ -517,21 +527,21 @@ __device__ __forceinline__ void lb_stage(const GemvArgs &a, float *lds, int tid)
 #pragma unroll
       for (int i = 0; i < MAXF; ++i) {
         const int f = min(tid + TPB * i, nf - 1);    // past the row: rewrites the last float4
-        act4[bb * nf + f] = v[bb][i] * rn[bb * a.n_norm + f / ng4];
+        *reinterpret_cast<f32x4 *>(acts + bb * KP + lds_pad(4 * f)) = v[bb][i] * rn[bb * a.n_norm + f / ng4];
       }
   } else {
 #pragma unroll
     for (int bb = 0; bb < BT; ++bb)
 #pragma unroll
-      for (int i = 0; i < MAXF; ++i) act4[bb * nf + min(tid + TPB * i, nf - 1)] = v[bb][i];
+      for (int i = 0; i < MAXF; ++i) *reinterpret_cast<f32x4 *>(acts + bb * KP + lds_pad(4 * min(tid + TPB * i, nf - 1))) = v[bb][i];
   }
   __syncthreads();
   // chunk sums, each in a fixed order
-  float *xsum = lds + BT * K;
+  float *xsum = lds + BT * KP;
   const int nc = K / 32;
   for (int j = tid; j < BT * nc; j += TPB) {
     const int bb = j / nc, c = j - bb * nc;
-    const f32x4 *p = act4 + bb * nf + 8 * c;
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(acts + bb * KP + lds_pad(32 * c));
     f32x4 s4 = p[0];
 #pragma unroll
     for (int q = 1; q < 8; ++q) s4 += p[q];
@@ -615,8 +625,9 @@ __global__ __launch_bounds__(kLbThreads) void gemv_lowbit_kernel(GemvArgs a) {
   Set sa, sb;
   load_group(g0, sa);
   lb_stage<WT, BT, PRO>(a, lds, tid);
+  const int KP = lds_padded(K);
   const float *act_s = lds;
-  const float *xsum = lds + BT * K;
+  const float *xsum = lds + BT * KP;
 
   auto run_group = [&](int g, const Set &st) {
     float acc[R][BT];
@@ -631,7 +642,7 @@ __global__ __launch_bounds__(kLbThreads) void gemv_lowbit_kernel(GemvArgs a) {
 #pragma unroll
         for (int bb = 0; bb < BT; ++bb) {
           float dq[R];
-          lb_dots<WT, R>(st.w[u], act_s + bb * K + 32 * c, dq);
+          lb_dots<WT, R>(st.w[u], act_s + bb * KP + lds_pad(32 * c), dq);
           const float xs = xsum[bb * NC + c];
 #pragma unroll
           for (int r = 0; r < R; ++r)
@@ -1276,7 +1287,7 @@ int pick_kt(int K, int BT) {
 }
 
 size_t lowbit_lds_bytes(const GemvArgs &a, int BT, int PRO) {
-  return sizeof(float) * ((size_t)BT * (a.K + a.K / 32) +
+  return sizeof(float) * ((size_t)BT * (lds_padded(a.K) + a.K / 32) +
                           (PRO == PRO_NORM ? (size_t)BT * (a.n_partials + a.n_norm) : 0));
 }
 
@@ -1294,8 +1305,9 @@ hipError_t launch_lowbit(const GemvArgs &a, hipStream_t stream) {
 }
 
 // in_proj: U=5 nontemporal loads; out_proj: U=8 cached loads (measured best on gfx950).
-// Low-bit codes at 1-2 sessions: the persistent low-bit GEMV, 2 rows per wave group for
-// in_proj and 1 for out_proj, 3 or 5 chunk columns per lane (rows of up to 6144 or 10240 codes).
+// Low-bit codes at 1-2 sessions: the persistent low-bit GEMV, one row per wave group
+// (two for in_proj at 2 sessions), 3 or 5 chunk columns per lane (rows of up to 6144 or
+// 10240 codes).
 template <int WT, int PRO, int EPI>
 hipError_t dispatch_bt(GemvArgs a, hipStream_t stream) {
   constexpr bool LOWBIT = WT == M2_W_INT4G || WT == M2_W_INT3G;
@@ -1305,7 +1317,7 @@ hipError_t dispatch_bt(GemvArgs a, hipStream_t stream) {
     if (a.B <= 2 && fits) {
       const bool u3 = a.K / 32 <= 64 * 3;
       if (EPI == EPI_INPROJ) {
-        if (a.B == 1) return u3 ? launch_lowbit<WT, 1, 2, 3, 1, PRO, EPI>(a, stream) : launch_lowbit<WT, 1, 2, 5, 1, PRO, EPI>(a, stream);
+        if (a.B == 1) return u3 ? launch_lowbit<WT, 1, 1, 3, 1, PRO, EPI>(a, stream) : launch_lowbit<WT, 1, 1, 5, 1, PRO, EPI>(a, stream);
         return u3 ? launch_lowbit<WT, 2, 2, 3, 1, PRO, EPI>(a, stream) : launch_lowbit<WT, 2, 2, 5, 1, PRO, EPI>(a, stream);
       }
       if (a.B == 1) return u3 ? launch_lowbit<WT, 1, 1, 3, 0, PRO, EPI>(a, stream) : launch_lowbit<WT, 1, 1, 5, 0, PRO, EPI>(a, stream);
