@@ -199,3 +199,16 @@ def test_lowbit_weights(wtype, q_group, batch):
     ssm0, conv0 = synth.make_state(dims, 53, n_slots, 0.1)
     _check("lowbit-%s-g%d-b%d" % (wtype, q_group, batch), dims, w, xs, ssm0, conv0, slot_ids=slots,
            residual=residual)
+
+
+@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("wtype,q_group,d_model", [("int4g", 32, 544), ("int3g", 32, 544), ("int4g", 64, 576)])
+def test_lowbit_ragged_k(wtype, q_group, d_model, batch):
+    """in_proj K of 17 or 18 chunks of 32 codes (a partial 128-code block), rows not a
+    multiple of 16; out_proj K = 384."""
+    dims = synth.MixerDims(d_model=d_model, n_heads=6, head_dim=64, d_state=32, n_groups=2, d_conv=4,
+                           wtype=wtype, q_group=q_group)
+    w = synth.make_layer_weights(dims, 61)
+    xs = synth.make_inputs(dims, 62, 6, batch)
+    ssm0, conv0 = synth.make_state(dims, 63, batch, 0.1)
+    _check("lowbit-ragged-%s-g%d-k%d-b%d" % (wtype, q_group, d_model, batch), dims, w, xs, ssm0, conv0)
