@@ -30,6 +30,7 @@ Distributions (variance reading of "N(0, v)"):
   A_log ~ U[0, ln 16]  (so A = -exp(A_log) lies in [-16, -1])
   dt_bias = softplus^-1(dt0), dt0 = exp(U[ln 1e-3, ln 0.1])
   per-frame inputs x ~ N(0, 1) fp32
+  output heads [vocab][d_model] as W_in (tags text_head, func_head); head inputs h ~ N(0, 1)
 """
 from __future__ import annotations
 
@@ -47,6 +48,7 @@ _TAGS = {
     "w_in": 1, "s_in": 2, "w_out": 3, "s_out": 4, "conv_w": 5, "conv_b": 6,
     "dt_bias": 7, "A_log": 8, "D": 9, "norm_w": 10,
     "x": 20, "prompt": 21, "ssm0": 22, "conv0": 23,
+    "text_head": 30, "text_head_s": 31, "func_head": 32, "func_head_s": 33, "head_h": 34,
 }
 
 
@@ -283,3 +285,19 @@ def make_state(dims: MixerDims, seed: int, n_slots: int, var: float, layer: int 
 
 def workload(i: int) -> Workload:
     return WORKLOADS[i]
+
+
+def make_head_weights(vocab: int, d_model: int, wtype: str, q_group: int, seed: int,
+                      tag: str = "text_head"):
+    """An output head [vocab][d_model] in the layer matrices' storage formats, W ~ N(0, 1/d_model)
+    (int8g: uniform codes with scales as for w_in); returns (w, scales or None)."""
+    if wtype == "int8g":
+        return _int8(seed, 0, tag, tag + "_s", vocab, d_model, q_group)
+    if wtype in LOWBIT:
+        return _lowbit(seed, 0, tag, vocab, d_model, q_group, LOWBIT[wtype], 1.0 / math.sqrt(d_model))
+    return _normal(seed, 0, tag, (vocab, d_model), 1.0 / math.sqrt(d_model), wtype), None
+
+
+def make_head_states(d_model: int, batch: int, seed: int, tag: str = "head_h") -> np.ndarray:
+    """Final hidden states h[batch][d_model] ~ N(0, 1), float32, fed to the output heads."""
+    return _rng(seed, 0, tag).standard_normal((batch, d_model), dtype=np.float32)

@@ -83,6 +83,8 @@ def lib():
             getattr(_lib, f).argtypes = [C.c_double]
             getattr(_lib, f).restype = C.c_double
         _lib.orc_num_threads.restype = C.c_int
+        _lib.orc_head_argmax.argtypes = [i32, i32, C.c_double, C.c_int64, C.c_int64, P, P, P, i32, P, P]
+        _lib.orc_head_argmax.restype = C.c_int
     return _lib
 
 
@@ -242,3 +244,22 @@ def lowbit_code(wtype: str, w: np.ndarray, row: int, k: int) -> int:
     w = np.ascontiguousarray(w, dtype=np.uint8)
     K = w.shape[1] * 8 // _BITS[wtype]
     return int(lib().orc_lowbit_code(_WT[wtype], _ptr(w), row, K, k))
+
+
+def head_argmax(wtype: str, w: np.ndarray, h, scales=None, q_group: int = 0, gamma: float = 1.0):
+    """Output head: (logits [B][vocab] fp64, greedy tokens [B] int32) of W h for w in the
+    layer's storage formats (bf16 as uint16 bits, low-bit as packed codes [vocab][bytes])."""
+    h = _f64(h)
+    if h.ndim == 1:
+        h = h[None]
+    B, K = h.shape
+    w = np.ascontiguousarray(w)
+    vocab = w.shape[0]
+    s = None if scales is None else np.ascontiguousarray(scales).view(np.uint16)
+    logits = np.zeros((B, vocab), np.float64)
+    token = np.zeros(B, np.int32)
+    rc = lib().orc_head_argmax(_WT[wtype], q_group, float(gamma), vocab, K, _ptr(w), _ptr(s), _ptr(h), B,
+                               _ptr(logits), _ptr(token))
+    if rc != 0:
+        raise ValueError("orc_head_argmax: bad arguments")
+    return logits, token

@@ -124,6 +124,28 @@ static void gemv(const orc_cfg *c, const void *w, const uint16_t *s, int64_t row
   }
 }
 
+int orc_head_argmax(int32_t wtype, int32_t q_group, double gamma, int64_t vocab, int64_t K, const void *w,
+                    const uint16_t *s, const double *h, int32_t B, double *logits, int32_t *token) {
+  if (wtype < ORC_W_F32 || wtype > ORC_W_INT3G || vocab < 1 || K < 1 || B < 1 || !w || !h || !logits || !token)
+    return -1;
+  if (wtype >= ORC_W_INT8G && (!s || q_group < 1 || K % q_group)) return -1;
+  orc_cfg c;
+  memset(&c, 0, sizeof c);
+  c.wtype = wtype;
+  c.q_group = q_group;
+  gemv(&c, w, s, vocab, K, gamma, h, logits, B);
+  for (int32_t b = 0; b < B; ++b) {
+    int64_t best = -1;
+    for (int64_t v = 0; v < vocab; ++v) {
+      const double l = logits[b * vocab + v];
+      if (isnan(l)) continue;
+      if (best < 0 || l > logits[b * vocab + best]) best = v;   /* equal: the earlier index stays */
+    }
+    token[b] = (int32_t)best;
+  }
+  return 0;
+}
+
 /* ---- SSD token update (steps 6 and 7 for one head) ---- */
 
 static void ssd_token(int32_t P, int32_t N, double dt, double A, double D, const double *x,

@@ -442,3 +442,73 @@ def test_tiny_workload_runs_and_stays_bounded():
     for t in range(wl.steps):
         y = lay.step(ssm, conv, xs[t])
         assert np.all(np.isfinite(y)) and np.max(np.abs(y)) < 50
+
+
+# ---- output heads: logits W h and the greedy token ----
+
+def _head_decoded(wtype, w, s, q_group, gamma):
+    """The head matrix as fp64 via the same numpy decoding as `decoded`."""
+    dims = synth.TINY.replace(wtype=wtype, q_group=q_group or 1, q_gamma_in=gamma)
+    return decoded(dims, {"w_in": w, "s_in": s}, "w_in")
+
+
+@pytest.mark.parametrize("wtype,q_group,gamma", [("f32", 0, 1.0), ("bf16", 0, 1.0), ("int8g", 64, 0.5),
+                                                 ("int4g", 32, 1.0), ("int3g", 64, 2.0)])
+def test_head_logits_match_numpy_matmul_and_argmax(wtype, q_group, gamma):
+    V, K, B = 333, 256, 3
+    w, s = synth.make_head_weights(V, K, wtype, q_group, seed=7)
+    h = synth.make_head_states(K, B, seed=8)
+    logits, token = oracle.head_argmax(wtype, w, h, s, q_group, gamma)
+    ref = h.astype(np.float64) @ _head_decoded(wtype, w, s, q_group, gamma).T
+    assert rel(logits, ref) < RTOL
+    assert np.array_equal(token, np.argmax(ref, axis=1))
+    assert logits.shape == (B, V) and token.dtype == np.int32
+
+
+def test_head_ties_take_the_lowest_index():
+    rng = np.random.default_rng(3)
+    V, K = 40, 32
+    w = rng.standard_normal((V, K)).astype(np.float32)
+    h = rng.standard_normal((2, K))
+    w[[29, 11, 36]] = 10.0 * np.sign(h[0]).astype(np.float32)   # three equal rows, far above the rest
+    _, token = oracle.head_argmax("f32", w, h)
+    assert token[0] == 11
+    w2 = np.zeros((V, K), np.float32)                            # every logit exactly 0
+    _, token = oracle.head_argmax("f32", w2, h)
+    assert np.array_equal(token, [0, 0])
+
+
+def test_head_nan_is_never_chosen_and_infinities_order():
+    rng = np.random.default_rng(4)
+    V, K = 12, 16
+    h = np.abs(rng.standard_normal((1, K))) + 0.5                # every entry positive
+    w = rng.standard_normal((V, K)).astype(np.float32)
+    w[2, 5] = np.nan                                             # NaN logit
+    w[6, 0] = -np.inf                                            # -inf logit
+    w[9, 3] = np.inf                                             # +inf logit: the maximum
+    logits, token = oracle.head_argmax("f32", w, h)
+    assert np.isnan(logits[0, 2]) and logits[0, 6] == -np.inf and logits[0, 9] == np.inf
+    assert token[0] == 9
+    w[9, 3] = 0.0
+    _, token = oracle.head_argmax("f32", w, h)
+    with np.errstate(invalid="ignore"):
+        ref = h @ w.astype(np.float64).T                         # NaN and -inf carry through
+    assert token[0] == int(np.nanargmax(ref[0])) and token[0] not in (2, 6)
+    w[:] = -np.inf                                               # every logit -inf: the lowest index
+    _, token = oracle.head_argmax("f32", w, h)
+    assert token[0] == 0
+    w[:] = np.nan                                                # every logit NaN: no token
+    _, token = oracle.head_argmax("f32", w, h)
+    assert token[0] == -1
+
+
+def test_head_single_row_and_sessions_are_independent():
+    w, _ = synth.make_head_weights(1, 64, "bf16", 0, seed=2)
+    h = synth.make_head_states(64, 4, seed=3)
+    logits, token = oracle.head_argmax("bf16", w, h)
+    assert np.array_equal(token, [0, 0, 0, 0])
+    w, _ = synth.make_head_weights(50, 64, "bf16", 0, seed=2)
+    full, tok = oracle.head_argmax("bf16", w, h)
+    for b in range(4):
+        one, t1 = oracle.head_argmax("bf16", w, h[b])
+        assert np.array_equal(one[0], full[b]) and t1[0] == tok[b]
