@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=1,
                     help="workload: 1 (default), 2 (32 sessions), 3 (27-layer int8 stack), 4 (prefill + 4 sessions), "
-                         "5 (int4 g64 weights, 1 session), 6 (int3 g64 weights, 1 session)")
+                         "5 (int4 g64 weights, 1 session), 6 (int3 g64 weights, 1 session), "
+                         "7 (text and function output heads with greedy argmax, 1 session)")
     ap.add_argument("--copies", type=int, default=0,
                     help="identical weight copies used in turn (0: enough for >= 590 MB)")
     ap.add_argument("--no-graph", action="store_true", help="time plain launches only")
@@ -153,6 +154,8 @@ def main():
     import torch
     from full_duplex_speech_mamba2_amd import m2, synth
 
+    if args.config in synth.HEAD_WORKLOADS:
+        return bench_heads(args, synth.HEAD_WORKLOADS[args.config])
     wl = synth.workload(args.config)
     dims, B = wl.dims, wl.batch
     dev = torch.device("cuda:0")
@@ -292,6 +295,137 @@ def main():
     if not args.no_cpu and wl.layers == 1:
         out["cpu_baseline"], out["parity"] = cpu_baseline_and_parity(args, wl, w, xs_np, ssm0, conv0)
     print(json.dumps(out), flush=True)
+
+
+HEAD_METRIC = "Output-head greedy decode frames/s + achieved HBM GB/s (% peak), text + function head"
+
+
+def head_bytes(wl):
+    """Algorithmic HBM bytes of one head GEMV launch (the weights and the hidden states read
+    once, the tokens written) and of one frame (every head)."""
+    wb = {"f32": 4, "bf16": 2, "int8g": 1, "int4g": 0.5, "int3g": 0.375}[wl.wtype]
+    scales = {"int8g": 2, "int4g": 4, "int3g": 4}.get(wl.wtype, 0)
+    w = int(wl.vocab * wl.d_model * wb) + (wl.vocab * (wl.d_model // wl.q_group) * scales if scales else 0)
+    launch = w + wl.batch * wl.d_model * 4
+    return {"head_wave": launch, "frame": wl.heads * (launch + wl.batch * 4)}
+
+
+def bench_heads(args, wl):
+    """Frames/s of the output heads: per frame every head (text, then function) maps each
+    session's hidden state to its greedy token; nothing else runs in the timed region."""
+    import numpy as np
+    import torch
+    import ctypes as C
+    from full_duplex_speech_mamba2_amd import m2, synth
+
+    dev = torch.device("cuda:0")
+    B, K, V = wl.batch, wl.d_model, wl.vocab
+    print("[bench] workload %s: generating inputs" % wl.name, file=sys.stderr, flush=True)
+    tags = ["text_head", "func_head"][:wl.heads]
+    host_w = [synth.make_head_weights(V, K, wl.wtype, wl.q_group, wl.seed, tag) for tag in tags]
+    heads = [m2.Head(K, V, w, s, wtype=wl.wtype, q_group=wl.q_group, device=dev) for w, s in host_w]
+    nx = min(wl.steps, 750)
+    hs_np = synth.make_head_states(K, nx * B, wl.seed).reshape(nx, B, K)
+    hs = torch.from_numpy(hs_np).to(dev)
+    toks = torch.empty((nx, wl.heads, B), dtype=torch.int32, device=dev)
+
+    def run(t0, n):
+        for t in range(t0, t0 + n):
+            for i, hd in enumerate(heads):
+                hd.argmax(hs[t % nx], token=toks[t % nx, i])
+
+    run(0, args.warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run(args.warmup, args.steps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / args.steps
+    ms_graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                run(0, args.steps)
+        torch.cuda.current_stream().wait_stream(st)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / args.steps
+        del g
+    ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
+    fps = 1000.0 / ms
+
+    # per-kernel durations from HIP events between the two kernels of each head call
+    kp = max(10, args.prof_steps)
+    hip = hip_runtime()
+    evs = [[hip_event(hip) for _ in range(3)] for _ in range(kp)]
+    tok1 = torch.empty(B, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    for t in range(kp):
+        heads[t % len(heads)].argmax_timed(hs[t % nx], tok1, evs[t])
+    torch.cuda.synchronize()
+    wave_us = 1000.0 * float(np.mean([hip_elapsed_ms(hip, e[0], e[1]) for e in evs]))
+    red_us = 1000.0 * float(np.mean([hip_elapsed_ms(hip, e[1], e[2]) for e in evs]))
+    for row in evs:
+        for e in row:
+            hip.hipEventDestroy(e)
+    hb = head_bytes(wl)
+    achieved = hb["head_wave"] / (wave_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": "head_wave", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_for("head_wave", wl.name),
+                "algorithmic_bytes": hb["head_wave"], "avg_duration_us": round(wave_us, 2)}
+    out = {
+        "metric": HEAD_METRIC, "value": round(fps, 1), "unit": "frames/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "d_model": K, "vocab": V, "heads": wl.heads, "batch": B,
+                   "weight_dtype": wl.wtype,
+                   "timing": "graph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"},
+        "achieved_GBps": round(hb["frame"] * fps / 1e9, 1),
+        "hbm_peak_frac": round(hb["frame"] * fps / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_algorithmic_bytes": hb["frame"],
+        "ms_per_step_eager": round(ms_eager, 5),
+        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
+        "kernel_us": {"head_wave": round(wave_us, 2), "head_reduce": round(red_us, 2)},
+        "roofline": roofline, "cpu_baseline": None, "parity": None,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"], out["parity"] = head_cpu_baseline_and_parity(args, wl, host_w, hs_np, toks)
+    print(json.dumps(out), flush=True)
+
+
+def head_cpu_baseline_and_parity(args, wl, host_w, hs_np, toks):
+    """Time the oracle on the first frames (bounded by --cpu-seconds) and compare the GPU
+    tokens of those frames with its greedy tokens: equal, or within fp32 rounding of a tie."""
+    import numpy as np
+    import oracle
+    gpu = toks.cpu().numpy()
+    t0 = time.perf_counter()
+    n, same, worst = 0, 0, 0.0
+    while n < hs_np.shape[0] and (n < 1 or time.perf_counter() - t0 < args.cpu_seconds):
+        for i, (w, s) in enumerate(host_w):
+            lo, to = oracle.head_argmax(wl.wtype, w, hs_np[n], s, wl.q_group)
+            g = gpu[n, i]
+            same += int(np.sum(g == to))
+            gap = (lo[np.arange(wl.batch), to] - lo[np.arange(wl.batch), np.maximum(g, 0)]) / np.max(np.abs(lo))
+            worst = max(worst, float(np.max(np.where(g < 0, np.inf, gap))))
+        n += 1
+    wall = time.perf_counter() - t0
+    base = {"value": round(n / wall, 4), "unit": "frames/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "first %d frames of %s (%d heads, batch %d), fp64 C oracle, %.1f s wall"
+                      % (n, wl.name, wl.heads, wl.batch, wall)}
+    total = n * wl.heads * wl.batch
+    return base, {"frames": n, "tokens_equal": same, "tokens": total, "worst_rel_logit_gap": worst,
+                  "tol_rel_logit_gap": 1e-5, "ok": bool(worst <= 1e-5)}
 
 
 def prefill_flops(dims, B, T, Q):

@@ -27,6 +27,8 @@
 //               activations staged in K tiles for tiles of 4 sessions.
 #include <hip/hip_fp16.h>
 
+#include <climits>
+
 #include "m2_internal.h"
 
 namespace m2d {
@@ -1434,6 +1436,195 @@ int log2i(int v) {
   return s;
 }
 
+// ---------------------------------------------------------------------------
+// Output heads (text head, function head): logits = gamma * W h for a [V][K] matrix and
+// the greedy token argmax_v logits (the lowest index among equal maxima; a NaN logit never
+// wins), per session. head_wave_kernel: one row per wave as in gemv_wave_kernel (U chunks
+// in flight, activations staged once per workgroup), then the workgroup's best (logit,
+// index) per session into part[session][workgroup]; head_reduce_kernel: one workgroup per
+// session takes the best over the partials. Both reductions keep the winner by value,
+// then by index, so the result does not depend on the order in which they combine.
+struct HeadArgs {
+  const void *W;
+  const void *S;
+  int rows, K, q_shift;
+  float gamma;
+  const float *h;         // [B][K]
+  int B;
+  float *logits;          // [B][rows] or null
+  int32_t *token;         // [B]
+  float2 *part;           // [4][gridDim]: per session the workgroups' (logit, index bits)
+  int nparts;
+};
+
+__device__ __forceinline__ bool head_better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+template <int WT, int BT, int U>
+__global__ __launch_bounds__(512) void head_wave_kernel(HeadArgs a) {
+  extern __shared__ float lds[];
+  constexpr int TPB = 512, WPB = TPB / 64;
+  constexpr int EPC = WTraits<WT>::EPC;
+  constexpr int CB = WTraits<WT>::CB;
+  using chunk_t = typename WTraits<WT>::chunk_t;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x * WPB + wave;
+  const bool row_ok = row < a.rows;
+  const int nb = min(BT, a.B);
+  const int K = a.K, NC = K / EPC;
+  const char *wr = static_cast<const char *>(a.W) + (size_t)(row_ok ? row : 0) * NC * CB;
+  const void *srow = scale_row<WT>(a.S, (size_t)(row_ok ? row : 0), NC >> a.q_shift);
+  chunk_t w[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = lane + 64 * u;
+    w[u] = (row_ok && c < NC) ? load_chunk<WT, 1>(wr, c) : chunk_t{};
+  }
+  float *act_s = lds;
+  float2 *best = reinterpret_cast<float2 *>(lds + BT * K);   // [WPB][BT]
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb)
+    for (int i = tid * 4; i < K; i += TPB * 4) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (bb < nb) v = *reinterpret_cast<const float4 *>(a.h + (size_t)bb * K + i);
+      *reinterpret_cast<float4 *>(act_s + bb * K + i) = v;
+    }
+  __syncthreads();
+  float acc[BT];
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb) acc[bb] = 0.0f;
+  if (row_ok) {
+    for (int cb = lane;;) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = cb + 64 * u;
+        if (c < NC) {
+          const QScale qs = load_qscale<WT>(srow, c, a.q_shift);
+#pragma unroll
+          for (int bb = 0; bb < BT; ++bb) acc[bb] = chunk_acc<WT>(w[u], act_s + bb * K + c * EPC, qs, acc[bb]);
+        }
+      }
+      cb += 64 * U;
+      if (cb >= NC) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = cb + 64 * u;
+        w[u] = c < NC ? load_chunk<WT, 1>(wr, c) : chunk_t{};
+      }
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < BT; ++bb) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc[bb] += __shfl_xor(acc[bb], off, 64);
+  }
+  if (lane < BT) {
+    float val = 0.0f;
+#pragma unroll
+    for (int bb = 0; bb < BT; ++bb)
+      if (lane == bb) val = acc[bb];
+    val *= a.gamma;
+    const bool ok = row_ok && lane < nb;
+    if (ok && a.logits) a.logits[(size_t)lane * a.rows + row] = val;
+    best[wave * BT + lane] = ok ? make_float2(val, __int_as_float(row)) : make_float2(-INFINITY, __int_as_float(INT_MAX));
+  }
+  __syncthreads();
+  if (tid < BT) {                       // rows rise with the wave index
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int w8 = 0; w8 < WPB; ++w8) {
+      const float2 e = best[w8 * BT + tid];
+      if (head_better(e.x, __float_as_int(e.y), bv, bi)) {
+        bv = e.x;
+        bi = __float_as_int(e.y);
+      }
+    }
+    a.part[(size_t)tid * a.nparts + blockIdx.x] = make_float2(bv, __int_as_float(bi));
+  }
+}
+
+// One workgroup of 1024 threads per session; every thread first issues all of its (up to 16
+// per pass) loads of the session's contiguous partials, then combines them, so that a pass
+// costs one memory latency rather than one per partial.
+__global__ __launch_bounds__(1024) void head_reduce_kernel(HeadArgs a) {
+  constexpr int TPB = 1024, L = 16;
+  __shared__ float sv[TPB / 64];
+  __shared__ int si[TPB / 64];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float2 *part = a.part + (size_t)b * a.nparts;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  for (int p0 = tid; p0 < a.nparts; p0 += TPB * L) {
+    float2 e[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const int p = p0 + j * TPB;
+      e[j] = p < a.nparts ? part[p] : make_float2(-INFINITY, __int_as_float(INT_MAX));
+    }
+#pragma unroll
+    for (int j = 0; j < L; ++j)
+      if (head_better(e[j].x, __float_as_int(e[j].y), bv, bi)) {
+        bv = e[j].x;
+        bi = __float_as_int(e[j].y);
+      }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off, 64);
+    const int oi = __shfl_xor(bi, off, 64);
+    if (head_better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < TPB / 64; ++w)
+      if (head_better(sv[w], si[w], bv, bi)) {
+        bv = sv[w];
+        bi = si[w];
+      }
+    a.token[b] = bi == INT_MAX ? -1 : bi;
+  }
+}
+
+hipError_t record(hipEvent_t const *ev, int i, hipStream_t stream) {
+  return (ev && ev[i]) ? hipEventRecord(ev[i], stream) : hipSuccess;
+}
+
+template <int WT, int BT>
+hipError_t launch_head_bt(const HeadArgs &a, hipStream_t stream, hipEvent_t const *ev) {
+  const size_t lds = sizeof(float) * ((size_t)BT * a.K + 2 * 8 * BT);
+  auto *k = head_wave_kernel<WT, BT, 5>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = record(ev, 0, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3(a.nparts), dim3(512), lds, stream, a);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = record(ev, 1, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(head_reduce_kernel, dim3(a.B), dim3(1024), 0, stream, a);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = record(ev, 2, stream);
+  return e;
+}
+
+template <int WT>
+hipError_t launch_head_wt(const HeadArgs &a, hipStream_t stream, hipEvent_t const *ev) {
+  if (a.B == 1) return launch_head_bt<WT, 1>(a, stream, ev);
+  if (a.B == 2) return launch_head_bt<WT, 2>(a, stream, ev);
+  return launch_head_bt<WT, 4>(a, stream, ev);
+}
+
 }  // namespace
 
 StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base) {
@@ -1600,6 +1791,39 @@ hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, h
   hipLaunchKernelGGL(state_zero_kernel, dim3(gx, n), dim3(256), 0, stream, S.ssm, S.conv, ssm_per,
                      conv_per, slots, n, S.n_slots);
   return hipGetLastError();
+}
+
+size_t head_ws_bytes(int vocab) { return sizeof(float2) * 4 * (size_t)((vocab + 7) / 8); }
+
+hipError_t launch_head(const m2_head_config &c, const void *w, const void *scales, const float *h, int batch,
+                       int32_t *token, float *logits, void *ws, hipStream_t stream, hipEvent_t const *events) {
+  const int epc = c.wtype == M2_W_F32 ? 4 : c.wtype == M2_W_BF16 ? 8 : c.wtype == M2_W_INT8G ? 16 : 32;
+  const bool quantized = c.wtype == M2_W_INT8G || c.wtype == M2_W_INT4G || c.wtype == M2_W_INT3G;
+  HeadArgs a{};
+  a.W = w;
+  a.S = scales;
+  a.rows = c.vocab;
+  a.K = c.d_model;
+  a.q_shift = quantized ? log2i(c.q_group / epc) : 30;
+  a.gamma = quantized ? c.q_gamma : 1.0f;
+  a.part = static_cast<float2 *>(ws);
+  a.nparts = (c.vocab + 7) / 8;
+  for (int b0 = 0; b0 < batch; b0 += 4) {      // up to 4 sessions per launch, in stream order
+    a.h = h + (size_t)b0 * c.d_model;
+    a.B = batch - b0 < 4 ? batch - b0 : 4;
+    a.logits = logits ? logits + (size_t)b0 * c.vocab : nullptr;
+    a.token = token + b0;
+    hipError_t e;
+    switch (c.wtype) {
+      case M2_W_F32: e = launch_head_wt<M2_W_F32>(a, stream, events); break;
+      case M2_W_BF16: e = launch_head_wt<M2_W_BF16>(a, stream, events); break;
+      case M2_W_INT4G: e = launch_head_wt<M2_W_INT4G>(a, stream, events); break;
+      case M2_W_INT3G: e = launch_head_wt<M2_W_INT3G>(a, stream, events); break;
+      default: e = launch_head_wt<M2_W_INT8G>(a, stream, events); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace m2d

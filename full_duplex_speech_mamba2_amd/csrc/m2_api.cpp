@@ -228,6 +228,62 @@ int m2_step_plan(m2_layer layer, int32_t batch) {
   return m2d::step_plan(*layer, batch);
 }
 
+static int check_head(const m2_head_config *c) {
+  if (!c) return fail(M2_ERR_NULL, "head config is NULL");
+  if (c->wtype != M2_W_F32 && c->wtype != M2_W_BF16 && c->wtype != M2_W_INT8G && c->wtype != M2_W_INT4G &&
+      c->wtype != M2_W_INT3G)
+    return fail(M2_ERR_DTYPE, "unknown wtype %d", c->wtype);
+  if (c->vocab < 1 || c->vocab > (1 << 24)) return fail(M2_ERR_SHAPE, "vocab %d outside [1, 2^24]", c->vocab);
+  const int epc = c->wtype == M2_W_F32 ? 4 : c->wtype == M2_W_BF16 ? 8 : c->wtype == M2_W_INT8G ? 16 : 32;
+  if (c->d_model <= 0 || c->d_model % epc)
+    return fail(M2_ERR_SHAPE, "d_model %d is not a positive multiple of %d", c->d_model, epc);
+  if (c->d_model > 8192) return fail(M2_ERR_UNSUPPORTED, "d_model %d above 8192", c->d_model);
+  if (c->wtype == M2_W_INT8G || c->wtype == M2_W_INT4G || c->wtype == M2_W_INT3G) {
+    const int qmin = c->wtype == M2_W_INT8G ? 16 : 32;
+    if (c->q_group < qmin || (c->q_group & (c->q_group - 1)) || c->d_model % c->q_group)
+      return fail(M2_ERR_SHAPE, "q_group %d must be a power of two >= %d dividing d_model %d", c->q_group, qmin,
+                  c->d_model);
+  }
+  return M2_OK;
+}
+
+size_t m2_head_workspace(const m2_head_config *cfg, int32_t batch) {
+  if (check_head(cfg) || batch <= 0) return 0;
+  return m2d::head_ws_bytes(cfg->vocab);
+}
+
+static int head_impl(const m2_head_config *cfg, const void *w, const void *scales, const float *h, int32_t batch,
+                     int32_t *token, float *logits, void *ws, size_t ws_bytes, void *stream, void *const *events) {
+  int rc = check_head(cfg);
+  if (rc) return rc;
+  if (!w || !h || !token) return fail(M2_ERR_NULL, "w, h and token are required");
+  const bool quantized = cfg->wtype == M2_W_INT8G || cfg->wtype == M2_W_INT4G || cfg->wtype == M2_W_INT3G;
+  if (quantized && !scales) return fail(M2_ERR_NULL, "quantized heads need scales");
+  if (!aligned16(w) || !aligned16(h) || (quantized && !aligned16(scales)))
+    return fail(M2_ERR_ALIGN, "w, h and scales must be 16-byte aligned");
+  if (batch <= 0) return fail(M2_ERR_SHAPE, "batch must be positive");
+  const size_t need = m2d::head_ws_bytes(cfg->vocab);
+  if (!ws || ws_bytes < need)
+    return fail(M2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(M2_ERR_ALIGN, "workspace must be 16-byte aligned");
+  hipError_t e = m2d::launch_head(*cfg, w, scales, h, batch, token, logits, ws, static_cast<hipStream_t>(stream),
+                                  reinterpret_cast<hipEvent_t const *>(events));
+  if (e != hipSuccess) return fail(M2_ERR_HIP, "head launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int m2_head_argmax(const m2_head_config *cfg, const void *w, const void *scales, const float *h, int32_t batch,
+                   int32_t *token, float *logits, void *ws, size_t ws_bytes, void *stream) {
+  return head_impl(cfg, w, scales, h, batch, token, logits, ws, ws_bytes, stream, nullptr);
+}
+
+int m2_head_argmax_timed(const m2_head_config *cfg, const void *w, const void *scales, const float *h,
+                         int32_t batch, int32_t *token, float *logits, void *ws, size_t ws_bytes, void *stream,
+                         void *const *events) {
+  if (batch > 4) return fail(M2_ERR_UNSUPPORTED, "timed head calls take at most 4 sessions (one launch pair)");
+  return head_impl(cfg, w, scales, h, batch, token, logits, ws, ws_bytes, stream, events);
+}
+
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk) {
   if (!layer || batch <= 0 || seqlen <= 0 || chunk < 16 || chunk > 256 || chunk % 16) return 0;
   return m2d::prefill_ws_bytes(*layer, batch, seqlen, chunk);

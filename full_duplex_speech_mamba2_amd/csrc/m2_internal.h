@@ -56,6 +56,12 @@ bool step_uses_mfma(const m2_layer_s &L, int batch);
 
 hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, hipStream_t stream);
 
+// Output heads: greedy argmax of W h (m2_head_argmax).
+size_t head_ws_bytes(int vocab);
+hipError_t launch_head(const m2_head_config &c, const void *w, const void *scales, const float *h, int batch,
+                       int32_t *token, float *logits, void *ws, hipStream_t stream,
+                       hipEvent_t const *events = nullptr);
+
 // Prefill
 size_t prefill_ws_bytes(const m2_layer_s &L, int batch, int seqlen, int chunk);
 hipError_t launch_prefill(const m2_layer_s &L, const m2_state_s &S, const float *x, float *y, int batch,

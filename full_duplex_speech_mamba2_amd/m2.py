@@ -37,6 +37,11 @@ class Config(C.Structure):
                 ("q_group", C.c_int32), ("q_gamma_in", C.c_float), ("q_gamma_out", C.c_float)]
 
 
+class HeadConfig(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("vocab", C.c_int32), ("wtype", C.c_int32),
+                ("q_group", C.c_int32), ("q_gamma", C.c_float)]
+
+
 class Weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("w_in", "s_in", "w_out", "s_out", "conv_w", "conv_b",
                                           "dt_bias", "A_log", "D", "norm_w")]
@@ -63,8 +68,12 @@ _lib.m2_step_plan.restype = C.c_int
 _lib.m2_prefill_workspace.argtypes = [_P, _i32, _i32, _i32]
 _lib.m2_prefill_workspace.restype = C.c_size_t
 _lib.m2_prefill.argtypes = [_P, _P, _P, _P, _i32, _i32, _i32, _P, _i32, _P, C.c_size_t, _P]
+_lib.m2_head_workspace.argtypes = [_P, _i32]
+_lib.m2_head_workspace.restype = C.c_size_t
+_lib.m2_head_argmax.argtypes = [_P, _P, _P, _P, _i32, _P, _P, _P, C.c_size_t, _P]
+_lib.m2_head_argmax_timed.argtypes = [_P, _P, _P, _P, _i32, _P, _P, _P, C.c_size_t, _P, _P]
 for _f in ("m2_layer_create", "m2_state_sizes", "m2_state_create", "m2_state_zero", "m2_step",
-           "m2_step_timed", "m2_prefill"):
+           "m2_step_timed", "m2_prefill", "m2_head_argmax", "m2_head_argmax_timed"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -197,6 +206,12 @@ def _act(t: torch.Tensor, shape) -> torch.Tensor:
     return t
 
 
+def _tokens(t: torch.Tensor, n: int) -> torch.Tensor:
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != n:
+        raise ValueError("expected a contiguous int32 tensor of %d tokens, got %s %s" % (n, t.dtype, tuple(t.shape)))
+    return t
+
+
 def step(layer: Layer, state: State, x: torch.Tensor, y: Optional[torch.Tensor] = None,
          slot_ids: Optional[torch.Tensor] = None, residual: bool = False,
          ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -244,3 +259,50 @@ def prefill(layer: Layer, state: State, x: torch.Tensor, y: Optional[torch.Tenso
     _check(_lib.m2_prefill(layer.handle, state.handle, _ptr(x), _ptr(y), B, T, chunk, _ptr(slot_ids),
                            M2_RESIDUAL if residual else 0, _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+class Head:
+    """An output head (m2_head_argmax) over device copies of its matrix and scales."""
+
+    def __init__(self, d_model: int, vocab: int, w, scales=None, wtype: str = "bf16", q_group: int = 0,
+                 q_gamma: float = 1.0, device="cuda"):
+        self.cfg = HeadConfig(d_model, vocab, WTYPE[wtype], q_group, float(q_gamma))
+        self.w = to_device(w, device)
+        self.s = to_device(scales, device)
+        self._ws: Dict[int, torch.Tensor] = {}
+
+    def workspace(self, batch: int) -> torch.Tensor:
+        n = _lib.m2_head_workspace(C.byref(self.cfg), batch)
+        if n == 0:
+            raise M2Error(M2_ERR_SHAPE, "invalid head configuration")
+        if n not in self._ws:
+            self._ws[n] = torch.empty(n, dtype=torch.uint8, device=self.w.device)
+        return self._ws[n]
+
+    def argmax(self, h: torch.Tensor, token: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+        """Greedy token of each session of h [B][d_model] (device fp32); logits, if given,
+        [B][vocab] fp32, receive W h."""
+        B = h.shape[0]
+        _act(h, (B, self.cfg.d_model))
+        if logits is not None:
+            _act(logits, (B, self.cfg.vocab))
+        if token is None:
+            token = torch.empty(B, dtype=torch.int32, device=h.device)
+        _tokens(token, B)
+        ws = self.workspace(B)
+        _check(_lib.m2_head_argmax(C.byref(self.cfg), _ptr(self.w), _ptr(self.s), _ptr(h), B, _ptr(token),
+                                   _ptr(logits), _ptr(ws), ws.numel(), _stream(stream)))
+        return token
+
+    def argmax_timed(self, h: torch.Tensor, token: torch.Tensor, events, stream=None) -> torch.Tensor:
+        """argmax (no logits) recording three hipEvent_t handles: before the GEMV kernel,
+        between it and the reduction, after the reduction. At most 4 sessions."""
+        B = h.shape[0]
+        _act(h, (B, self.cfg.d_model))
+        _tokens(token, B)
+        ws = self.workspace(B)
+        ev = (C.c_void_p * 3)(*[getattr(e, "cuda_event", e) for e in events])
+        _check(_lib.m2_head_argmax_timed(C.byref(self.cfg), _ptr(self.w), _ptr(self.s), _ptr(h), B, _ptr(token),
+                                         None, _ptr(ws), ws.numel(), _stream(stream), ev))
+        return token

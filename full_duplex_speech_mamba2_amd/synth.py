@@ -129,6 +129,29 @@ WORKLOADS: Dict[int, Workload] = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class HeadWorkload:
+    """Per-frame greedy decode of the output heads: `heads` matrices of [vocab][d_model]
+    (the text head, then the function head) over `batch` sessions' final hidden states."""
+    name: str
+    d_model: int
+    vocab: int
+    heads: int
+    wtype: str
+    batch: int
+    steps: int
+    q_group: int = 0
+    seed: int = 0
+
+
+# The pages give no vocabulary size: 131072 rows per head is a configured reading, with the
+# function head taken to be a second head of the text head's shape.
+HEAD_WORKLOADS: Dict[int, HeadWorkload] = {
+    7: HeadWorkload("heads_2x131072x4480_bf16_b1_decode750", d_model=4480, vocab=131072, heads=2,
+                    wtype="bf16", batch=1, steps=750, seed=7),
+}
+
+
 def _rng(seed: int, layer: int, tag: str, block: int = -1) -> np.random.Generator:
     words = [seed, layer, _TAGS[tag]] + ([block] if block >= 0 else [])
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(words)))

@@ -177,6 +177,39 @@ int m2_prefill(m2_layer layer, m2_state st, const float *x, float *y, int32_t ba
                int32_t seqlen, int32_t chunk, const int32_t *slot_ids, int32_t flags, void *ws,
                size_t ws_bytes, void *stream);
 
+/* Output heads (page "NemotronLabs VoiceChat" of the SGLang-Omni cookbook, introduction and
+ * "Request parameters": every 80 ms frame yields a token from each of two heads, text and
+ * function, chosen greedily). A head is a [vocab][d_model] matrix W; for each
+ * session b, logits[b][v] = W[v] . h[b] (times q_gamma for quantized types) and the
+ * token is argmax_v logits[b][v]: the lowest index among equal maxima, a NaN logit never
+ * chosen, -1 if every logit is NaN. Call once per head. */
+typedef struct {
+  int32_t d_model;          /* K, at most 8192: a multiple of 4 (f32), 8 (bf16), 16 (int8) or 32 (low-bit) */
+  int32_t vocab;            /* rows V, 1 .. 2^24 */
+  int32_t wtype;            /* m2_wtype; packing and scales as for the layer's matrices */
+  int32_t q_group;          /* quantized types: as m2_config.q_group; must divide d_model */
+  float q_gamma;            /* quantized types: per-tensor multiplier (1 = none) */
+} m2_head_config;
+
+/* Workspace bytes m2_head_argmax needs (any batch; partial maxima of one launch). */
+size_t m2_head_workspace(const m2_head_config *cfg, int32_t batch);
+
+/* Greedy decode of one head for `batch` sessions. w: device [vocab][d_model] (16-byte
+ * aligned); scales: quantized types as s_in of m2_weights (else NULL); h: device fp32
+ * [batch][d_model], 16-byte aligned; token: device int32 [batch]; logits: device fp32
+ * [batch][vocab] or NULL (not written). Asynchronous on `stream`; errors as m2_status. */
+int m2_head_argmax(const m2_head_config *cfg, const void *w, const void *scales, const float *h,
+                   int32_t batch, int32_t *token, float *logits, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/* m2_head_argmax for at most 4 sessions (M2_ERR_UNSUPPORTED above) that also records
+ * hipEvent_t events[0..2] on `stream`: before the GEMV kernel, between it and the argmax
+ * reduction, and after the reduction. For per-kernel timing; the events must have been
+ * created by the caller; NULL events are skipped. */
+int m2_head_argmax_timed(const m2_head_config *cfg, const void *w, const void *scales, const float *h,
+                         int32_t batch, int32_t *token, float *logits, void *ws, size_t ws_bytes,
+                         void *stream, void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -107,16 +107,16 @@ void orc_ssd_quadratic(int32_t T, int32_t H, int32_t P, int32_t N, int32_t G, co
                        const double *Bm, const double *Cm, const double *dt, const double *A,
                        const double *D, const double *S0, double *y, double *S_final);
 
-/* Helpers exposed so tests can pin them: element decoders and scalar functions. */
 /* Output head (page "NemotronLabs VoiceChat" of the SGLang-Omni cookbook, introduction and
- * "Request parameters": one text token and one function token per frame, always decoded
- * greedily). For each session b < B: logits[b][v] = W[v] . h[b] for a [vocab][K] matrix in
- * the layer's weight formats (quantized types times gamma), and token[b] = the lowest v
- * whose logit is the largest; a NaN logit is never chosen, -1 if all are NaN.
+ * "Request parameters": every frame yields a token from each of two heads, text and
+ * function, chosen greedily). For each session b < B: logits[b][v] = W[v] . h[b] for a
+ * [vocab][K] matrix in the layer's weight formats (quantized types times gamma), and
+ * token[b] = the lowest v whose logit is the largest; a NaN logit is never chosen, -1 if all are NaN.
  * Returns 0, or -1 on bad arguments. */
 int orc_head_argmax(int32_t wtype, int32_t q_group, double gamma, int64_t vocab, int64_t K, const void *w,
                     const uint16_t *s, const double *h, int32_t B, double *logits, int32_t *token);
 
+/* Helpers exposed so tests can pin them: element decoders and scalar functions. */
 double orc_bf16_to_double(uint16_t h);
 double orc_fp16_to_double(uint16_t h);
 double orc_softplus(double x);

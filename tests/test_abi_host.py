@@ -162,3 +162,52 @@ def test_prefill_refuses_chunks_whose_scan_tiles_exceed_lds():
     rc, h = create(synth.NINE_B)
     assert L.m2_prefill_workspace(h, 4, 2048, 256) > 0        # the 9B shape at chunk 256 fits
     L.m2_layer_destroy(h)
+
+
+def test_head_rejects_bad_configs_and_calls_without_launching():
+    L = m2.lib()
+
+    def ws(**kw):
+        c = dict(d_model=4480, vocab=131072, wtype=m2.WTYPE["bf16"], q_group=0, q_gamma=1.0)
+        c.update(kw)
+        return L.m2_head_workspace(C.byref(m2.HeadConfig(**c)), 1)
+
+    assert ws() == 8 * 4 * (131072 // 8)                      # one (logit, index) per workgroup and session
+    assert ws(vocab=1) == 32 and ws(vocab=9) == 64
+    assert ws(vocab=0) == 0 and ws(vocab=(1 << 24) + 1) == 0
+    assert ws(wtype=7) == 0 and ws(d_model=4484) == 0 and ws(d_model=8200) == 0 and ws(d_model=0) == 0
+    assert ws(wtype=m2.WTYPE["f32"], d_model=4484) > 0
+    assert ws(wtype=m2.WTYPE["int8g"], q_group=128) > 0 and ws(wtype=m2.WTYPE["int8g"], q_group=0) == 0
+    assert ws(wtype=m2.WTYPE["int8g"], q_group=96) == 0       # not a power of two
+    assert ws(wtype=m2.WTYPE["int4g"], q_group=64) > 0 and ws(wtype=m2.WTYPE["int4g"], q_group=16) == 0
+    assert ws(wtype=m2.WTYPE["int3g"], q_group=256) == 0      # 4480 is not a multiple of 256
+    assert L.m2_head_workspace(None, 1) == 0
+    assert L.m2_head_workspace(C.byref(m2.HeadConfig(4480, 1000, m2.WTYPE["bf16"], 0, 1.0)), 0) == 0
+
+    cfg = m2.HeadConfig(256, 1000, m2.WTYPE["bf16"], 0, 1.0)
+    need = L.m2_head_workspace(C.byref(cfg), 3)
+    call = lambda c=cfg, w=FAKE, s=None, h=FAKE, b=3, t=FAKE, lg=None, wsp=FAKE, n=need: \
+        L.m2_head_argmax(C.byref(c) if c is not None else None, w, s, h, b, t, lg, wsp, n, None)
+    assert call(c=None) == m2.M2_ERR_NULL
+    assert call(w=None) == m2.M2_ERR_NULL and call(h=None) == m2.M2_ERR_NULL and call(t=None) == m2.M2_ERR_NULL
+    assert call(w=FAKE + 8) == m2.M2_ERR_ALIGN and call(h=FAKE + 4) == m2.M2_ERR_ALIGN
+    assert call(b=0) == m2.M2_ERR_SHAPE
+    assert call(n=need - 1) == m2.M2_ERR_WORKSPACE and call(wsp=None) == m2.M2_ERR_WORKSPACE
+    assert call(wsp=FAKE + 8) == m2.M2_ERR_ALIGN
+    q = m2.HeadConfig(256, 1000, m2.WTYPE["int4g"], 64, 1.0)
+    assert call(c=q) == m2.M2_ERR_NULL                        # quantized without scales
+    assert call(c=q, s=FAKE + 2) == m2.M2_ERR_ALIGN
+    assert call(c=m2.HeadConfig(256, 1000, 9, 0, 1.0)) == m2.M2_ERR_DTYPE
+    assert call(c=m2.HeadConfig(16384, 1000, m2.WTYPE["bf16"], 0, 1.0)) == m2.M2_ERR_UNSUPPORTED
+    assert b"8192" in L.m2_last_error()
+
+
+def test_head_timed_call_takes_at_most_four_sessions():
+    L = m2.lib()
+    cfg = m2.HeadConfig(256, 1000, m2.WTYPE["bf16"], 0, 1.0)
+    need = L.m2_head_workspace(C.byref(cfg), 5)
+    ev = (C.c_void_p * 3)()
+    assert L.m2_head_argmax_timed(C.byref(cfg), FAKE, None, FAKE, 5, FAKE, None, FAKE, need, None, ev) == \
+        m2.M2_ERR_UNSUPPORTED
+    assert L.m2_head_argmax_timed(C.byref(cfg), None, None, FAKE, 4, FAKE, None, FAKE, need, None, ev) == \
+        m2.M2_ERR_NULL
