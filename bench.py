@@ -154,10 +154,6 @@ def main():
     import torch
     from full_duplex_speech_mamba2_amd import m2, synth
 
-    if args.config in synth.HEAD_WORKLOADS:
-        return bench_heads(args, synth.HEAD_WORKLOADS[args.config])
-    wl = synth.workload(args.config)
-    dims, B = wl.dims, wl.batch
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
@@ -167,6 +163,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.config in synth.HEAD_WORKLOADS:
+        return bench_heads(args, synth.HEAD_WORKLOADS[args.config])
+    wl = synth.workload(args.config)
+    dims, B = wl.dims, wl.batch
     print("[bench] workload %s: generating inputs" % wl.name, file=sys.stderr, flush=True)
     xs_np = synth.make_inputs(dims, wl.seed, wl.steps, B)
     ssm0, conv0 = synth.make_state(dims, wl.seed, B, wl.state_var)
