@@ -31,6 +31,9 @@ Distributions (variance reading of "N(0, v)"):
   dt_bias = softplus^-1(dt0), dt0 = exp(U[ln 1e-3, ln 0.1])
   per-frame inputs x ~ N(0, 1) fp32
   output heads [vocab][d_model] as W_in (tags text_head, func_head); head inputs h ~ N(0, 1)
+  attention layers: W_qkv ~ N(0, 1/d_model), W_o ~ N(0, 1/(n_q head_dim)) in the same
+    formats; cached keys and values ~ N(0, 1) rounded to bf16 below each session's
+    position and NaN at and above it (so that any read past the position shows)
 """
 from __future__ import annotations
 
@@ -49,6 +52,7 @@ _TAGS = {
     "dt_bias": 7, "A_log": 8, "D": 9, "norm_w": 10,
     "x": 20, "prompt": 21, "ssm0": 22, "conv0": 23,
     "text_head": 30, "text_head_s": 31, "func_head": 32, "func_head_s": 33, "head_h": 34,
+    "w_qkv": 40, "s_qkv": 41, "w_o": 42, "s_o": 43, "kv_k": 44, "kv_v": 45, "attn_x": 46,
 }
 
 
@@ -127,6 +131,38 @@ WORKLOADS: Dict[int, Workload] = {
     6: Workload("mamba2_9b_int3g64_b1_decode750", NINE_B_INT3, batch=1, steps=750,
                 weight_seed=6, seed=6),
 }
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnDims:
+    """An attention layer of the hybrid backbone: n_q query heads sharing n_kv key/value
+    heads of head_dim, a bf16 KV cache of max_len positions per session."""
+    d_model: int
+    n_q: int
+    n_kv: int
+    head_dim: int
+    max_len: int
+    wtype: str = "bf16"
+    q_group: int = 128
+    q_gamma_qkv: float = 1.0
+    q_gamma_o: float = 1.0
+
+    @property
+    def qkv_rows(self) -> int:
+        return (self.n_q + 2 * self.n_kv) * self.head_dim
+
+    @property
+    def o_dim(self) -> int:
+        return self.n_q * self.head_dim
+
+    def replace(self, **kw) -> "AttnDims":
+        return dataclasses.replace(self, **kw)
+
+
+# The pages give no attention shapes: a 9B-class grouped-query layout (40 query heads, 8
+# key/value heads of 128) is a configured reading; 1500 positions = the 2-minute context
+# at one token per 80 ms frame.
+ATTN_9B = AttnDims(d_model=4480, n_q=40, n_kv=8, head_dim=128, max_len=1500)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -324,3 +360,37 @@ def make_head_weights(vocab: int, d_model: int, wtype: str, q_group: int, seed: 
 def make_head_states(d_model: int, batch: int, seed: int, tag: str = "head_h") -> np.ndarray:
     """Final hidden states h[batch][d_model] ~ N(0, 1), float32, fed to the output heads."""
     return _rng(seed, 0, tag).standard_normal((batch, d_model), dtype=np.float32)
+
+
+def make_attn_weights(dims: AttnDims, seed: int, layer: int = 0) -> Dict[str, Optional[np.ndarray]]:
+    """W_qkv [(n_q + 2 n_kv) head_dim][d_model] and W_o [d_model][n_q head_dim] in the layer
+    matrices' storage formats, with scales s_qkv, s_o for the quantized ones."""
+    d = dims
+    w: Dict[str, Optional[np.ndarray]] = {"s_qkv": None, "s_o": None}
+    for wn, sn, rows, k in (("w_qkv", "s_qkv", d.qkv_rows, d.d_model), ("w_o", "s_o", d.d_model, d.o_dim)):
+        if d.wtype == "int8g":
+            w[wn], w[sn] = _int8(seed, layer, wn, sn, rows, k, d.q_group)
+        elif d.wtype in LOWBIT:
+            w[wn], w[sn] = _lowbit(seed, layer, wn, rows, k, d.q_group, LOWBIT[d.wtype], 1.0 / math.sqrt(k))
+        else:
+            w[wn] = _normal(seed, layer, wn, (rows, k), 1.0 / math.sqrt(k), d.wtype)
+    return w
+
+
+def make_kv_cache(dims: AttnDims, seed: int, pos, layer: int = 0):
+    """bf16 bits k, v [n_slots][n_kv][max_len][head_dim] for sessions at positions pos
+    [n_slots]: N(0, 1) entries below pos[s], NaN (0x7FC0) from pos[s] on."""
+    pos = np.asarray(pos, np.int32)
+    shape = (len(pos), dims.n_kv, dims.max_len, dims.head_dim)
+    out = []
+    for tag in ("kv_k", "kv_v"):
+        c = f32_to_bf16_bits(_rng(seed, layer, tag).standard_normal(shape, dtype=np.float32))
+        for s_, p in enumerate(pos):
+            c[s_, :, p:, :] = 0x7FC0
+        out.append(c)
+    return out[0], out[1]
+
+
+def make_attn_inputs(dims: AttnDims, seed: int, steps: int, batch: int) -> np.ndarray:
+    """Per-frame attention-layer inputs u[steps][batch][d_model] ~ N(0, 1), float32."""
+    return _rng(seed, 0, "attn_x").standard_normal((steps, batch, dims.d_model), dtype=np.float32)

@@ -85,6 +85,10 @@ def lib():
         _lib.orc_num_threads.restype = C.c_int
         _lib.orc_head_argmax.argtypes = [i32, i32, C.c_double, C.c_int64, C.c_int64, P, P, P, i32, P, P]
         _lib.orc_head_argmax.restype = C.c_int
+        _lib.orc_attn_step.argtypes = [P, P, P, P, P, P, P, P, i32, P, P, i32, P, i32, P, P]
+        _lib.orc_attn_step.restype = C.c_int
+        _lib.orc_double_to_bf16.argtypes = [C.c_double]
+        _lib.orc_double_to_bf16.restype = C.c_uint16
     return _lib
 
 
@@ -263,3 +267,51 @@ def head_argmax(wtype: str, w: np.ndarray, h, scales=None, q_group: int = 0, gam
     if rc != 0:
         raise ValueError("orc_head_argmax: bad arguments")
     return logits, token
+
+
+class _AttnCfg(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("n_q", C.c_int32), ("n_kv", C.c_int32), ("head_dim", C.c_int32),
+                ("max_len", C.c_int32), ("wtype", C.c_int32), ("q_group", C.c_int32),
+                ("q_gamma_qkv", C.c_double), ("q_gamma_o", C.c_double)]
+
+
+class AttnLayer:
+    """The attention decode step (orc_attn_step) over host copies of the weights."""
+
+    def __init__(self, dims, weights):
+        self.dims = d = dims
+        self.cfg = _AttnCfg(d.d_model, d.n_q, d.n_kv, d.head_dim, d.max_len, _WT[d.wtype], d.q_group,
+                            float(np.float32(d.q_gamma_qkv)), float(np.float32(d.q_gamma_o)))
+        self.w = {k: (None if v is None else np.ascontiguousarray(v)) for k, v in weights.items()}
+        for k in ("s_qkv", "s_o"):
+            if self.w.get(k) is not None:
+                self.w[k] = self.w[k].view(np.uint16)
+
+    def step(self, kc, vc, pos, x, slot_ids=None, residual=False, trace=False):
+        """One token for x [B][d_model]; kc, vc (uint16 bf16 bits) and pos (int32) are
+        updated in place. Returns y [B][d_model] (and the qkv and o intermediates)."""
+        d = self.dims
+        x = _f64(x)
+        if x.ndim == 1:
+            x = x[None]
+        B = x.shape[0]
+        for a, dt in ((kc, np.uint16), (vc, np.uint16), (pos, np.int32)):
+            if a.dtype != dt or not a.flags.c_contiguous:
+                raise ValueError("kv cache must be contiguous uint16, pos contiguous int32")
+        n_slots = pos.shape[0]
+        if kc.shape != (n_slots, d.n_kv, d.max_len, d.head_dim) or vc.shape != kc.shape:
+            raise ValueError("kv cache shape")
+        sl = None if slot_ids is None else np.ascontiguousarray(slot_ids, np.int32)
+        y = np.zeros((B, d.d_model))
+        qkv = np.zeros((B, d.qkv_rows)) if trace else None
+        o = np.zeros((B, d.o_dim)) if trace else None
+        rc = lib().orc_attn_step(C.byref(self.cfg), _ptr(self.w["w_qkv"]), _ptr(self.w.get("s_qkv")),
+                                 _ptr(self.w["w_o"]), _ptr(self.w.get("s_o")), _ptr(kc), _ptr(vc), _ptr(pos),
+                                 n_slots, _ptr(x), _ptr(y), B, _ptr(sl), int(bool(residual)), _ptr(qkv), _ptr(o))
+        if rc != 0:
+            raise ValueError("orc_attn_step: bad arguments")
+        return (y, {"qkv": qkv, "o": o}) if trace else y
+
+
+def double_to_bf16(v: float) -> int:
+    return int(lib().orc_double_to_bf16(float(v)))

@@ -146,6 +146,104 @@ int orc_head_argmax(int32_t wtype, int32_t q_group, double gamma, int64_t vocab,
   return 0;
 }
 
+/* ---- attention decode (orc_attn_step) ---- */
+
+uint16_t orc_double_to_bf16(double v) {
+  if (isnan(v)) return 0x7FC0;
+  const uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);                       /* a = f 2^e, f in [0.5, 1): leading bit at 2^(e-1) */
+  int lsb = e - 8;                    /* 8 significant bits */
+  if (lsb < -133) lsb = -133;         /* subnormal spacing 2^-133 */
+  double r = nearbyint(ldexp(a, -lsb));   /* default rounding: to nearest, ties to even */
+  r = ldexp(r, lsb);
+  if (r >= ldexp(1.0, 128)) return sign | 0x7F80;     /* overflow -> infinity */
+  float f = (float)r;                 /* exact: r has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return sign | (uint16_t)((u >> 16) & 0x7FFF);
+}
+
+int orc_attn_step(const orc_attn_cfg *c, const void *w_qkv, const uint16_t *s_qkv, const void *w_o,
+                  const uint16_t *s_o, uint16_t *kc, uint16_t *vc, int32_t *pos, int32_t n_slots,
+                  const double *x, double *y, int32_t B, const int32_t *slot_ids, int32_t residual,
+                  double *qkv_out, double *o_out) {
+  if (!c || !w_qkv || !w_o || !kc || !vc || !pos || !x || !y || B < 1 || n_slots < 1) return -1;
+  if (c->n_q < 1 || c->n_kv < 1 || c->n_q % c->n_kv || c->head_dim < 1 || c->max_len < 1 || c->d_model < 1)
+    return -1;
+  if (c->wtype < ORC_W_F32 || c->wtype > ORC_W_INT3G) return -1;
+  const int64_t D = c->head_dim, Hq = c->n_q, Hk = c->n_kv, L = c->max_len;
+  const int64_t rows = (Hq + 2 * Hk) * D, K = c->d_model, Ko = Hq * D;
+  if (c->wtype >= ORC_W_INT8G && (!s_qkv || !s_o || c->q_group < 1 || K % c->q_group || Ko % c->q_group))
+    return -1;
+  orc_cfg wc;
+  memset(&wc, 0, sizeof wc);
+  wc.wtype = c->wtype;
+  wc.q_group = c->q_group;
+  double *qkv = (double *)malloc(sizeof(double) * (size_t)(B * rows));
+  double *o = (double *)malloc(sizeof(double) * (size_t)(B * Ko));
+  double *out = (double *)malloc(sizeof(double) * (size_t)(B * K));
+  double *sc = (double *)malloc(sizeof(double) * (size_t)L);
+  /* step 1 */
+  gemv(&wc, w_qkv, s_qkv, rows, K, c->q_gamma_qkv, x, qkv, B);
+  if (qkv_out) memcpy(qkv_out, qkv, sizeof(double) * (size_t)(B * rows));
+  int *live = (int *)malloc(sizeof(int) * (size_t)B);
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t slot = slot_ids ? slot_ids[b] : b;
+    live[b] = slot >= 0 && slot < n_slots && pos[slot] >= 0 && pos[slot] < L;
+    double *ob = o + b * Ko;
+    if (!live[b]) {
+      for (int64_t i = 0; i < Ko; ++i) ob[i] = NAN;
+      continue;
+    }
+    const int64_t t = pos[slot];
+    const double *q = qkv + b * rows, *kn = q + Hq * D, *vn = kn + Hk * D;
+    uint16_t *ks = kc + (size_t)slot * Hk * L * D, *vs = vc + (size_t)slot * Hk * L * D;
+    /* step 2 */
+    for (int64_t g = 0; g < Hk; ++g)
+      for (int64_t d = 0; d < D; ++d) {
+        ks[(g * L + t) * D + d] = orc_double_to_bf16(kn[g * D + d]);
+        vs[(g * L + t) * D + d] = orc_double_to_bf16(vn[g * D + d]);
+      }
+    /* steps 3 and 4 */
+    for (int64_t h = 0; h < Hq; ++h) {
+      const int64_t g = h / (Hq / Hk);
+      double m = -INFINITY;
+      for (int64_t j = 0; j <= t; ++j) {
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d) acc += q[h * D + d] * orc_bf16_to_double(ks[(g * L + j) * D + d]);
+        sc[j] = acc / sqrt((double)D);
+        if (sc[j] > m) m = sc[j];
+      }
+      double den = 0.0;
+      for (int64_t j = 0; j <= t; ++j) {
+        sc[j] = exp(sc[j] - m);       /* softmax, shifted by the maximum (the same ratio) */
+        den += sc[j];
+      }
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t j = 0; j <= t; ++j) acc += sc[j] * orc_bf16_to_double(vs[(g * L + j) * D + d]);
+        ob[h * D + d] = acc / den;
+      }
+    }
+    pos[slot] = (int32_t)(t + 1);
+  }
+  if (o_out) memcpy(o_out, o, sizeof(double) * (size_t)(B * Ko));
+  /* step 5 */
+  gemv(&wc, w_o, s_o, K, Ko, c->q_gamma_o, o, out, B);
+  for (int32_t b = 0; b < B; ++b)
+    for (int64_t i = 0; i < K; ++i)
+      y[b * K + i] = live[b] ? (residual ? x[b * K + i] : 0.0) + out[b * K + i] : NAN;
+  free(live);
+  free(sc);
+  free(out);
+  free(o);
+  free(qkv);
+  return 0;
+}
+
 /* ---- SSD token update (steps 6 and 7 for one head) ---- */
 
 static void ssd_token(int32_t P, int32_t N, double dt, double A, double D, const double *x,

@@ -116,6 +116,39 @@ void orc_ssd_quadratic(int32_t T, int32_t H, int32_t P, int32_t N, int32_t G, co
 int orc_head_argmax(int32_t wtype, int32_t q_group, double gamma, int64_t vocab, int64_t K, const void *w,
                     const uint16_t *s, const double *h, int32_t B, double *logits, int32_t *token);
 
+/* Attention layer of the hybrid backbone, one decode token per session (blog page
+ * "NemotronLabs VoiceChat 11B" overview, "Key design decisions" item 2: Mamba layers
+ * alternate with attention layers; its "Known limitations": a 2-minute audio context; the
+ * SGLang-Omni cookbook page, "Known limitations": the backbone and its KV cache run in
+ * bfloat16). The pages print no attention equation; the steps are standard scaled
+ * dot-product attention with grouped key/value heads and no positional term:
+ *   1. qkv = W_qkv u, rows [q: n_q heads x D | k: n_kv x D | v: n_kv x D], no bias
+ *   2. k and v rounded to bfloat16 (nearest, ties to even) and stored at position pos of
+ *      the session's cache [n_kv][max_len][D]
+ *   3. query head h reads key/value head g = h / (n_q / n_kv):
+ *      s_j = q_h . K_g[j] / sqrt(D) for j = 0 .. pos (the new entry included)
+ *   4. p = softmax(s); o_h = sum_j p_j V_g[j]
+ *   5. out = W_o o (o head-major, n_q x D), y = out or u + out; pos += 1
+ * A session whose pos is already max_len (or whose slot is out of range) gets NaN outputs
+ * and its cache and pos are not touched. */
+typedef struct {
+  int32_t d_model, n_q, n_kv, head_dim, max_len;
+  int32_t wtype, q_group;          /* weight format of W_qkv and W_o, as for the mixer */
+  double q_gamma_qkv, q_gamma_o;
+} orc_attn_cfg;
+
+/* kc, vc: bf16 bits [n_slots][n_kv][max_len][D]; pos: [n_slots]; x, y: [B][d_model];
+ * qkv_out ([B][(n_q + 2 n_kv) D]) and o_out ([B][n_q D]) receive intermediates if non-NULL.
+ * Returns 0, or -1 on bad arguments. */
+int orc_attn_step(const orc_attn_cfg *c, const void *w_qkv, const uint16_t *s_qkv, const void *w_o,
+                  const uint16_t *s_o, uint16_t *kc, uint16_t *vc, int32_t *pos, int32_t n_slots,
+                  const double *x, double *y, int32_t B, const int32_t *slot_ids, int32_t residual,
+                  double *qkv_out, double *o_out);
+
+/* bfloat16 bits of the value nearest to v (ties to even; beyond the largest finite
+ * bfloat16 by half a step or more: infinity). */
+uint16_t orc_double_to_bf16(double v);
+
 /* Helpers exposed so tests can pin them: element decoders and scalar functions. */
 double orc_bf16_to_double(uint16_t h);
 double orc_fp16_to_double(uint16_t h);

@@ -512,3 +512,138 @@ def test_head_single_row_and_sessions_are_independent():
     for b in range(4):
         one, t1 = oracle.head_argmax("bf16", w, h[b])
         assert np.array_equal(one[0], full[b]) and t1[0] == tok[b]
+
+
+# ---- attention decode step ----
+
+def test_double_to_bf16_rounding_against_hand_values_and_the_generator():
+    cases = {1.0: 0x3F80, 1 + 2 ** -8: 0x3F80, 1 + 3 * 2 ** -8: 0x3F82, -2.0: 0xC000, -0.0: 0x8000,
+             2.0 ** -133: 0x0001, 2.0 ** -134: 0x0000, 3 * 2.0 ** -134: 0x0002, 3.3895e38: 0x7F7F,
+             3.3962e38: 0x7F80, -1e39: 0xFF80, float("inf"): 0x7F80}
+    for v, bits in cases.items():
+        assert oracle.double_to_bf16(v) == bits, (v, hex(oracle.double_to_bf16(v)))
+    assert oracle.double_to_bf16(float("nan")) == 0x7FC0
+    vals = np.random.default_rng(5).standard_normal(4000).astype(np.float32) * np.float32(37.0)
+    ref = synth.f32_to_bf16_bits(vals)
+    assert all(oracle.double_to_bf16(float(v)) == int(r) for v, r in zip(vals, ref))
+
+
+ATT = synth.AttnDims(d_model=64, n_q=6, n_kv=2, head_dim=16, max_len=12, wtype="f32")
+
+
+def _attn(dims, pos, seed=3, w=None, slots=None):
+    w = w if w is not None else synth.make_attn_weights(dims, seed)
+    kc, vc = synth.make_kv_cache(dims, seed + 1, pos)
+    return oracle.AttnLayer(dims, w), w, kc, vc, np.array(pos, np.int32)
+
+
+def _bf(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("wtype,q_group,gamma", [("f32", 16, 1.0), ("bf16", 16, 1.0), ("int8g", 16, 0.25),
+                                                 ("int4g", 32, 1.0), ("int3g", 32, 0.5)])
+def test_attn_projections_match_numpy_matmul(wtype, q_group, gamma):
+    d = ATT.replace(d_model=128, head_dim=32, wtype=wtype, q_group=q_group, q_gamma_qkv=gamma, q_gamma_o=gamma)
+    lay, w, kc, vc, pos = _attn(d, [5, 0, 11])
+    x = np.random.default_rng(2).standard_normal((3, d.d_model))
+    y, tr = lay.step(kc, vc, pos, x, trace=True)
+    dims = synth.TINY.replace(wtype=wtype, q_group=q_group, q_gamma_in=gamma, q_gamma_out=gamma)
+    Wqkv = decoded(dims, {"w_in": w["w_qkv"], "s_in": w["s_qkv"]}, "w_in")
+    Wo = decoded(dims, {"w_out": w["w_o"], "s_out": w["s_o"]}, "w_out")
+    assert rel(tr["qkv"], x @ Wqkv.T) < RTOL
+    assert rel(y, tr["o"] @ Wo.T) < RTOL
+
+
+def test_attn_first_position_returns_the_rounded_new_value():
+    lay, w, kc, vc, pos = _attn(ATT, [0, 0])
+    x = np.random.default_rng(4).standard_normal((2, ATT.d_model))
+    _, tr = lay.step(kc, vc, pos, x, trace=True)
+    D, Hq, Hk = ATT.head_dim, ATT.n_q, ATT.n_kv
+    for b in range(2):
+        v_new = tr["qkv"][b, (Hq + Hk) * D:]
+        k_new = tr["qkv"][b, Hq * D:(Hq + Hk) * D]
+        for h in range(Hq):
+            g = h // (Hq // Hk)
+            expect = _bf(synth.f32_to_bf16_bits(v_new[g * D:(g + 1) * D].astype(np.float32)))
+            assert np.array_equal(tr["o"][b, h * D:(h + 1) * D], expect)
+        assert np.array_equal(_bf(kc[b, :, 0, :]).ravel(), _bf(synth.f32_to_bf16_bits(k_new.astype(np.float32))))
+    assert np.array_equal(pos, [1, 1])
+
+
+def test_attn_zero_queries_average_every_value_up_to_the_new_one():
+    w = synth.make_attn_weights(ATT, 3)
+    w["w_qkv"] = w["w_qkv"].copy()
+    w["w_qkv"][:ATT.n_q * ATT.head_dim] = 0.0                  # q = 0: all scores 0
+    lay, _, kc, vc, pos = _attn(ATT, [7, 3, 11], w=w)
+    x = np.random.default_rng(6).standard_normal((3, ATT.d_model))
+    _, tr = lay.step(kc, vc, pos, x, trace=True)
+    D, Hq, Hk = ATT.head_dim, ATT.n_q, ATT.n_kv
+    for b, t in enumerate([7, 3, 11]):
+        for h in range(Hq):
+            g = h // (Hq // Hk)
+            V = _bf(vc[b, g, :t + 1, :])                        # includes the entry just written
+            assert rel(tr["o"][b, h * D:(h + 1) * D], V.mean(axis=0)) < RTOL
+
+
+def test_attn_dominant_key_selects_its_value():
+    d = ATT.replace(n_q=2, n_kv=2)                               # one query head per key head
+    lay, w, kc, vc, pos = _attn(d, [9])
+    x = np.random.default_rng(7).standard_normal((1, d.d_model))
+    q = x @ np.asarray(w["w_qkv"], np.float64)[:d.n_q * d.head_dim].T
+    D = d.head_dim
+    for g, j in ((0, 4), (1, 0)):
+        qg = q[0, g * D:(g + 1) * D]
+        kc[0, g, j] = synth.f32_to_bf16_bits((60.0 * qg / np.linalg.norm(qg)).astype(np.float32))
+    _, tr = lay.step(kc, vc, pos, x, trace=True)
+    for g, j in ((0, 4), (1, 0)):
+        assert rel(tr["o"][0, g * D:(g + 1) * D], _bf(vc[0, g, j])) < 1e-9
+
+
+def test_attn_is_invariant_to_permuting_cached_positions_and_shares_kv_within_a_group():
+    w = synth.make_attn_weights(ATT, 8)
+    w["w_qkv"] = w["w_qkv"].copy()
+    D = ATT.head_dim
+    w["w_qkv"][1 * D:2 * D] = w["w_qkv"][0:D]                    # heads 0 and 1 (group 0): same q
+    w["w_qkv"][3 * D:4 * D] = w["w_qkv"][0:D]                    # head 3 (group 1): same q, other K/V
+    lay, _, kc, vc, pos = _attn(ATT, [10], w=w)
+    x = np.random.default_rng(9).standard_normal((1, ATT.d_model))
+    perm = np.random.default_rng(10).permutation(10)
+    kc2, vc2, pos2 = kc.copy(), vc.copy(), pos.copy()
+    kc2[0, :, :10] = kc[0][:, perm]
+    vc2[0, :, :10] = vc[0][:, perm]
+    _, t1 = lay.step(kc, vc, pos, x, trace=True)
+    _, t2 = lay.step(kc2, vc2, pos2, x, trace=True)
+    assert rel(t2["o"], t1["o"]) < 1e-13
+    o = t1["o"][0]
+    assert np.array_equal(o[0:D], o[D:2 * D])
+    assert rel(o[3 * D:4 * D], o[0:D]) > 1e-3
+
+
+def test_attn_two_positions_is_a_logistic_mix():
+    from scipy.special import expit
+    lay, w, kc, vc, pos = _attn(ATT, [1])
+    x = np.random.default_rng(11).standard_normal((1, ATT.d_model))
+    _, tr = lay.step(kc, vc, pos, x, trace=True)
+    D = ATT.head_dim
+    for h in range(ATT.n_q):
+        g = h // (ATT.n_q // ATT.n_kv)
+        q = tr["qkv"][0, h * D:(h + 1) * D]
+        s0, s1 = (_bf(kc[0, g, j]) @ q / math.sqrt(D) for j in (0, 1))
+        expect = expit(s0 - s1) * _bf(vc[0, g, 0]) + expit(s1 - s0) * _bf(vc[0, g, 1])
+        assert rel(tr["o"][0, h * D:(h + 1) * D], expect) < 1e-12
+
+
+def test_attn_residual_full_cache_and_bad_slots():
+    lay, w, kc, vc, pos = _attn(ATT, [4, ATT.max_len, 2])
+    x = np.random.default_rng(12).standard_normal((4, ATT.d_model))
+    k0, v0 = kc.copy(), vc.copy()
+    y = lay.step(kc, vc, pos, x, slot_ids=[0, 1, 7, 2], residual=True)
+    assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2]))        # full cache, slot out of range
+    assert np.array_equal(pos, [5, ATT.max_len, 3])
+    assert np.array_equal(kc[1], k0[1]) and np.array_equal(vc[1], v0[1])
+    changed = np.argwhere(kc != k0)
+    assert set(map(tuple, changed[:, [0, 2]])) <= {(0, 4), (2, 2)}
+    lay2, _, kc2, vc2, pos2 = _attn(ATT, [4, ATT.max_len, 2])
+    y2 = lay2.step(kc2, vc2, pos2, x[[0, 3]], slot_ids=[0, 2])
+    assert rel(y[[0, 3]] - x[[0, 3]], y2) < 1e-13
