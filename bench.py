@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--config", type=int, default=1,
                     help="workload: 1 (default), 2 (32 sessions), 3 (27-layer int8 stack), 4 (prefill + 4 sessions), "
                          "5 (int4 g64 weights, 1 session), 6 (int3 g64 weights, 1 session), "
-                         "7 (text and function output heads with greedy argmax, 1 session)")
+                         "7 (text and function output heads with greedy argmax, 1 session), "
+                         "8 (attention layer with a bf16 KV cache of 1000+ positions, 1 session)")
     ap.add_argument("--copies", type=int, default=0,
                     help="identical weight copies used in turn (0: enough for >= 590 MB)")
     ap.add_argument("--no-graph", action="store_true", help="time plain launches only")
@@ -165,6 +166,8 @@ def main():
         del src, dst
     if args.config in synth.HEAD_WORKLOADS:
         return bench_heads(args, synth.HEAD_WORKLOADS[args.config])
+    if args.config in synth.ATTN_WORKLOADS:
+        return bench_attn(args, synth.ATTN_WORKLOADS[args.config])
     wl = synth.workload(args.config)
     dims, B = wl.dims, wl.batch
     print("[bench] workload %s: generating inputs" % wl.name, file=sys.stderr, flush=True)
@@ -426,6 +429,182 @@ def head_cpu_baseline_and_parity(args, wl, host_w, hs_np, toks):
     total = n * wl.heads * wl.batch
     return base, {"frames": n, "tokens_equal": same, "tokens": total, "worst_rel_logit_gap": worst,
                   "tol_rel_logit_gap": 1e-5, "ok": bool(worst <= 1e-5)}
+
+
+ATTN_METRIC = "Attention-layer decode steps/s + achieved HBM GB/s (% peak), 9B-shaped layer, bf16 KV cache"
+ATTN_PHASES = ["qkv_gemv", "attn_split", "attn_combine", "o_gemv"]
+
+
+def attn_bytes(wl, mean_len):
+    """Algorithmic HBM bytes per launch of each kernel of the attention step and of the whole
+    step at a mean of `mean_len` attended positions: weights, cache rows read once, the new
+    rows written, activations in and out; the chunk partials are scratch."""
+    d, B = wl.dims, wl.batch
+    wb = {"f32": 4, "bf16": 2, "int8g": 1, "int4g": 0.5, "int3g": 0.375}[d.wtype]
+    scales = {"int8g": 2, "int4g": 4, "int3g": 4}.get(d.wtype, 0)
+
+    def w(rows, K):
+        return int(rows * K * wb) + (rows * (K // d.q_group) * scales if scales else 0)
+
+    qkv = w(d.qkv_rows, d.d_model) + B * d.d_model * 4 + B * d.qkv_rows * 4
+    cache = int(2 * B * d.n_kv * mean_len * d.head_dim * 2)
+    split = B * d.qkv_rows * 4 + cache + 2 * B * d.n_kv * d.head_dim * 2
+    combine = B * d.o_dim * 4
+    o = w(d.d_model, d.o_dim) + B * d.o_dim * 4 + 2 * B * d.d_model * 4
+    step = (w(d.qkv_rows, d.d_model) + w(d.d_model, d.o_dim) + cache + 2 * B * d.n_kv * d.head_dim * 2 +
+            2 * B * d.d_model * 4)
+    return {"qkv_gemv": qkv, "attn_split": split, "attn_combine": combine, "o_gemv": o, "step": step}
+
+
+def bench_attn(args, wl):
+    """Steps/s of the attention layer: per step one token for `batch` sessions (QKV GEMV, the
+    cache append and grouped-query attention over the cached positions, O GEMV + residual)."""
+    import numpy as np
+    import torch
+    from full_duplex_speech_mamba2_amd import m2, synth
+
+    dev = torch.device("cuda:0")
+    d, B, S = wl.dims, wl.batch, wl.slot_sets
+    print("[bench] workload %s: generating inputs" % wl.name, file=sys.stderr, flush=True)
+    w = synth.make_attn_weights(d, wl.seed)
+    pos0_np = np.full(B * S, wl.start_pos, np.int32)
+    kc_np, vc_np = synth.make_kv_cache(d, wl.seed, pos0_np)
+    ncopy = args.copies
+    if ncopy <= 0:
+        per = attn_bytes(wl, 0)["qkv_gemv"] + attn_bytes(wl, 0)["o_gemv"]
+        ncopy = max(2, -(-590_000_000 // per))
+    layers = [m2.Attn(d, w, dev) for _ in range(ncopy)]
+    kc = torch.from_numpy(kc_np.view(np.int16)).to(dev)
+    vc = torch.from_numpy(vc_np.view(np.int16)).to(dev)
+    pos0 = torch.from_numpy(pos0_np).to(dev)
+    pos = pos0.clone()
+    sets = torch.arange(B * S, dtype=torch.int32, device=dev).reshape(S, B).contiguous()
+    xs_np = synth.make_attn_inputs(d, wl.seed, wl.steps, B)
+    xs = torch.from_numpy(xs_np).to(dev)
+    ys = torch.empty_like(xs)
+    ws = layers[0].workspace(B)
+    nx, nl = xs.shape[0], len(layers)
+    if args.steps // S > d.max_len - wl.start_pos:
+        raise SystemExit("--steps %d would fill the caches (at most %d)" % (args.steps, S * (d.max_len - wl.start_pos)))
+
+    def run(t0, n):
+        for t in range(t0, t0 + n):
+            layers[t % nl].step(kc, vc, pos, xs[t % nx], ys[t % nx], slot_ids=sets[t % S], residual=True, ws=ws)
+
+    run(0, min(args.warmup, S * (d.max_len - wl.start_pos)))
+    pos.copy_(pos0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run(0, args.steps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / args.steps
+    if not bool(torch.isfinite(ys[:min(nx, args.steps)]).all()):
+        raise SystemExit("attention bench: a session ran out of cache positions (NaN outputs)")
+    ms_graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                run(0, args.steps)
+        torch.cuda.current_stream().wait_stream(st)
+        pos.copy_(pos0)
+        g.replay()
+        pos.copy_(pos0)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / args.steps
+        del g
+    ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
+    sps = 1000.0 / ms
+    mean_len = wl.start_pos + 1 + (args.steps / S - 1) / 2.0
+
+    kp = min(max(10, args.prof_steps), S * (d.max_len - wl.start_pos))
+    hip = hip_runtime()
+    evs = [[hip_event(hip) for _ in range(5)] for _ in range(kp)]
+    pos.copy_(pos0)
+    torch.cuda.synchronize()
+    for t in range(kp):
+        layers[t % nl].step_timed(kc, vc, pos, xs[t % nx], ys[t % nx], evs[t], slot_ids=sets[t % S], residual=True,
+                                  ws=ws)
+    torch.cuda.synchronize()
+    dur_us = {n: 1000.0 * float(np.mean([hip_elapsed_ms(hip, e[i], e[i + 1]) for e in evs]))
+              for i, n in enumerate(ATTN_PHASES)}
+    for row in evs:
+        for e in row:
+            hip.hipEventDestroy(e)
+    kb = attn_bytes(wl, mean_len)
+    kb_prof = attn_bytes(wl, wl.start_pos + 1 + (kp / S - 1) / 2.0)
+    dom = max(ATTN_PHASES, key=lambda n: kb_prof[n])
+    achieved = kb_prof[dom] / (dur_us[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_for(dom, wl.name),
+                "algorithmic_bytes": kb_prof[dom], "avg_duration_us": round(dur_us[dom], 2)}
+    out = {
+        "metric": ATTN_METRIC, "value": round(sps, 1), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "d_model": d.d_model, "n_q": d.n_q, "n_kv": d.n_kv,
+                   "head_dim": d.head_dim, "max_len": d.max_len, "batch": B, "weight_dtype": d.wtype,
+                   "kv_dtype": "bf16", "start_positions": wl.start_pos, "mean_attended": round(mean_len, 1),
+                   "slot_sets": S, "weight_copies": nl,
+                   "timing": "graph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"},
+        "achieved_GBps": round(kb["step"] * sps / 1e9, 1),
+        "hbm_peak_frac": round(kb["step"] * sps / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_algorithmic_bytes": kb["step"],
+        "ms_per_step_eager": round(ms_eager, 5),
+        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
+        "kernel_us": {n: round(v, 2) for n, v in dur_us.items()},
+        "roofline": roofline, "cpu_baseline": None, "parity": None,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"], out["parity"] = attn_cpu_baseline_and_parity(args, wl, w, kc_np, vc_np, pos0_np, xs_np)
+    print(json.dumps(out), flush=True)
+
+
+def attn_cpu_baseline_and_parity(args, wl, w, kc_np, vc_np, pos0_np, xs_np):
+    """Time the oracle on the first steps (bounded by --cpu-seconds) and compare the GPU
+    path's outputs for the same steps, from the same caches, with it."""
+    import numpy as np
+    import torch
+    import oracle
+    from full_duplex_speech_mamba2_amd import m2
+    d, B, S = wl.dims, wl.batch, wl.slot_sets
+    lay = oracle.AttnLayer(d, w)
+    kc, vc, pos = kc_np.copy(), vc_np.copy(), pos0_np.copy()
+    ys_o = []
+    t0 = time.perf_counter()
+    n = 0
+    while n < xs_np.shape[0] and (n < 2 or time.perf_counter() - t0 < args.cpu_seconds):
+        ys_o.append(lay.step(kc, vc, pos, xs_np[n], slot_ids=np.arange(B, dtype=np.int32) + (n % S) * B,
+                             residual=True))
+        n += 1
+    wall = time.perf_counter() - t0
+    base = {"value": round(n / wall, 3), "unit": "steps/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "first %d steps of %s (batch %d), fp64 C oracle, %.1f s wall" % (n, wl.name, B, wall)}
+    at = m2.Attn(d, w)
+    kd = torch.from_numpy(kc_np.view(np.int16)).cuda()
+    vd = torch.from_numpy(vc_np.view(np.int16)).cuda()
+    pd = torch.from_numpy(pos0_np.copy()).cuda()
+    xd = torch.from_numpy(xs_np[:n]).cuda()
+    yd = torch.empty_like(xd)
+    for t in range(n):
+        sl = torch.arange(B, dtype=torch.int32, device="cuda") + (t % S) * B
+        at.step(kd, vd, pd, xd[t], yd[t], slot_ids=sl, residual=True)
+    torch.cuda.synchronize()
+    yg = yd.cpu().numpy().astype(np.float64)
+    yo = np.array(ys_o)
+    e_out = float(np.max(np.max(np.abs(yg - yo), axis=-1) / np.max(np.abs(yo), axis=-1)))
+    return base, {"steps": n, "e_out": e_out, "tol_out": 1e-3, "ok": bool(e_out <= 1e-3),
+                  "positions_equal": bool(np.array_equal(pd.cpu().numpy(), pos))}
 
 
 def prefill_flops(dims, B, T, Q):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libm2.so")
-SOURCES = ["m2_api.cpp", "decode.hip", "prefill.hip"]
+SOURCES = ["m2_api.cpp", "decode.hip", "prefill.hip", "attention.hip"]
 ARCH = os.environ.get("M2_OFFLOAD_ARCH", "gfx950")
 
 

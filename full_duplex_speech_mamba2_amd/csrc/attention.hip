@@ -1,0 +1,359 @@
+// Attention layers of the hybrid Mamba-2/attention backbone: one decode token per
+// session with a bf16 KV cache (blog page "NemotronLabs VoiceChat 11B", "Key design
+// decisions" item 2 and "Known limitations": attention layers between the Mamba layers,
+// a 2-minute context; SGLang-Omni cookbook page, "Known limitations": the backbone and
+// its KV cache run in bfloat16).
+//
+// One step, four kernels on the caller's stream:
+//   qkv GEMV         qkv = W_qkv u (the mixer's GEMV kernels with a plain epilogue)
+//   attn_split       per (64-position chunk, key/value head, session): the chunk's scores
+//                    for every query head of the group, their softmax terms relative to
+//                    the chunk maximum, and the weighted sum of the chunk's values; the new
+//                    key and value (rounded to bf16) stand in for the cache row at the
+//                    session's position and are stored there by the chunk that holds it
+//   attn_combine     per (query head, session): rescales the chunk partials to the common
+//                    maximum, normalises, and advances the session's position (chunks past
+//                    the session's length are marked empty by attn_split)
+//   o GEMV           y = W_o o (+ u)
+// Scores are kept in log2 units (q pre-scaled by log2(e)/sqrt(D)) so that every
+// exponential is one exp2.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "m2_internal.h"
+
+namespace m2d {
+namespace {
+
+constexpr int kC = 64;      // cache positions per split workgroup
+constexpr int kT = 256;     // threads per split workgroup
+
+struct AttnArgs {
+  const float *qkv;         // [B][(Hq + 2 Hk) D]
+  uint16_t *kc, *vc;        // [n_slots][Hk][max_len][D] bf16 bits
+  int32_t *pos;             // [n_slots]
+  const int32_t *slots;     // [B] or null (session b uses slot b)
+  int n_slots, B, Hq, Hk, max_len, nsplit;
+  float scale;              // log2(e) / sqrt(D)
+  float *part_o;            // [B][Hq][nsplit][D]: sum over the chunk of 2^(s_j - m) v_j
+  float2 *part_ml;          // [B][Hq][nsplit]: (m, sum over the chunk of 2^(s_j - m))
+  int *lens;                // [B]: positions attended (pos + 1), -1 for a session not run
+  float *o;                 // [B][Hq D]
+};
+
+// bf16 bits of the nearest value (ties to even); NaN -> 0x7FC0.
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void unpack8(const uint4 &r, float *f) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float4 &a, const float4 &b) {
+  uint4 r;
+  r.x = to_bf16(a.x) | (to_bf16(a.y) << 16);
+  r.y = to_bf16(a.z) | (to_bf16(a.w) << 16);
+  r.z = to_bf16(b.x) | (to_bf16(b.y) << 16);
+  r.w = to_bf16(b.z) | (to_bf16(b.w) << 16);
+  return r;
+}
+
+__device__ __forceinline__ uint4 select4(bool c, const uint4 &a, const uint4 &b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
+// Thread layout: LPP = D/8 consecutive lanes share a cache row (8 bf16 = 16 bytes each, so
+// one load instruction of a wave reads 64/LPP whole rows); the workgroup's kT/LPP position
+// groups take positions pg, pg + NPG, ... of the chunk. Every cache load of a thread is
+// issued before anything else.
+template <int D, int HPG>
+__global__ __launch_bounds__(kT) void attn_split_kernel(AttnArgs a) {
+  constexpr int LPP = D / 8;
+  constexpr int NPG = kT / LPP;
+  constexpr int PPT = kC / NPG;
+  constexpr int WPB = kT / 64;
+  static_assert(64 % LPP == 0 && kC % NPG == 0 && PPT >= 1, "layout");
+  __shared__ float qs[HPG][D];
+  __shared__ float sc[HPG][kC];
+  __shared__ float red[WPB][HPG][D];
+  __shared__ float2 ml[HPG];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int dg = tid % LPP, pg = tid / LPP;
+  const int slot = a.slots ? a.slots[b] : b;
+  const bool sok = slot >= 0 && slot < a.n_slots;
+  const int p = sok ? a.pos[slot] : -1;
+  const bool live = sok && p >= 0 && p < a.max_len;
+  if (split == 0 && g == 0 && tid == 0) a.lens[b] = live ? p + 1 : -1;
+  const int j0 = split * kC;
+  if (!live) return;                                 // uniform over the workgroup
+  if (j0 > p) {                                      // a chunk past the session's length: empty
+    if (tid < HPG) a.part_ml[((size_t)b * a.Hq + (size_t)g * HPG + tid) * a.nsplit + split] = make_float2(-INFINITY, 0.0f);
+    return;
+  }
+
+  const size_t cache_off = ((size_t)slot * a.Hk + g) * (size_t)a.max_len * D;
+  const uint16_t *kg = a.kc + cache_off;
+  const uint16_t *vg = a.vc + cache_off;
+  uint4 kr[PPT], vr[PPT];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int j = min(j0 + pg + NPG * i, p);          // past the last position: a valid row, masked below
+    kr[i] = *reinterpret_cast<const uint4 *>(kg + (size_t)j * D + dg * 8);
+    vr[i] = *reinterpret_cast<const uint4 *>(vg + (size_t)j * D + dg * 8);
+  }
+  const float *qkv = a.qkv + (size_t)b * (a.Hq + 2 * a.Hk) * D;
+  const float *kn = qkv + (size_t)(a.Hq + g) * D + dg * 8;
+  const float *vn = kn + (size_t)a.Hk * D;
+  const uint4 knew = pack8(*reinterpret_cast<const float4 *>(kn), *reinterpret_cast<const float4 *>(kn + 4));
+  const uint4 vnew = pack8(*reinterpret_cast<const float4 *>(vn), *reinterpret_cast<const float4 *>(vn + 4));
+  for (int i = tid; i < HPG * D; i += kT) qs[i / D][i % D] = qkv[(size_t)g * HPG * D + i] * a.scale;
+  __syncthreads();
+
+  // scores of the thread's positions for every query head of the group
+  float qv[HPG][8];
+#pragma unroll
+  for (int h = 0; h < HPG; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[h][e] = qs[h][dg * 8 + e];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int jl = pg + NPG * i, j = j0 + jl;
+    float kf[8];
+    unpack8(select4(j == p, knew, kr[i]), kf);
+    float s[HPG];
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) {
+      float t = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t = fmaf(qv[h][e], kf[e], t);
+      s[h] = t;
+    }
+#pragma unroll
+    for (int off = LPP / 2; off >= 1; off >>= 1)
+#pragma unroll
+      for (int h = 0; h < HPG; ++h) s[h] += __shfl_xor(s[h], off, 64);
+    if (dg == 0)
+#pragma unroll
+      for (int h = 0; h < HPG; ++h) sc[h][jl] = j <= p ? s[h] : -INFINITY;
+  }
+  __syncthreads();
+
+  // per head: the chunk maximum, the terms 2^(s - m) and their sum (one wave per head)
+  for (int h = wave; h < HPG; h += WPB) {
+    const float s = sc[h][lane];
+    float m = s;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const float e = exp2f(s - m);
+    float l = e;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off, 64);
+    sc[h][lane] = e;
+    if (lane == 0) ml[h] = make_float2(m, l);
+  }
+  __syncthreads();
+
+  // weighted values: the thread's 8 dimensions over its positions, then over position groups
+  float acc[HPG][8];
+#pragma unroll
+  for (int h = 0; h < HPG; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int jl = pg + NPG * i, j = j0 + jl;
+    float vf[8];
+    unpack8(select4(j == p, vnew, vr[i]), vf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vf[e] = j <= p ? vf[e] : 0.0f;   // rows past p may hold anything
+#pragma unroll
+    for (int h = 0; h < HPG; ++h) {
+      const float w = sc[h][jl];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
+    }
+  }
+#pragma unroll
+  for (int off = LPP; off < 64; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < HPG; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+  if (lane < LPP)
+#pragma unroll
+    for (int h = 0; h < HPG; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][h][lane * 8 + e] = acc[h][e];
+  __syncthreads();
+  const size_t hq0 = (size_t)b * a.Hq + (size_t)g * HPG;
+  for (int i = tid; i < HPG * D; i += kT) {
+    const int h = i / D, d = i % D;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WPB; ++w) v += red[w][h][d];
+    a.part_o[((hq0 + h) * a.nsplit + split) * D + d] = v;
+  }
+  if (tid < HPG) a.part_ml[(hq0 + tid) * a.nsplit + split] = ml[tid];
+  // the chunk holding the session's position stores the new key and value there
+  if (p < j0 + kC && pg == 0) {
+    *reinterpret_cast<uint4 *>(a.kc + cache_off + (size_t)p * D + dg * 8) = knew;
+    *reinterpret_cast<uint4 *>(a.vc + cache_off + (size_t)p * D + dg * 8) = vnew;
+  }
+}
+
+// One workgroup of D threads per (query head, session). The chunk statistics are copied to
+// LDS with one vector load per thread and this thread's dimension of the first 32 chunks'
+// partials is requested in the same round trip; chunks past the session's length carry
+// m = -inf and are skipped by selection, so their stale partials never enter. The session's
+// length is needed only at the end.
+template <int D>
+__global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
+  constexpr int NB = 32;
+  __shared__ float2 mls[1024];                     // nsplit <= 1024 (max_len <= 65536)
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int L = a.lens[b];
+  const size_t hq = (size_t)b * a.Hq + h;
+  const float2 *ml = a.part_ml + hq * a.nsplit;
+  const float *po = a.part_o + hq * a.nsplit * D + d;
+  const int ns = a.nsplit;
+  float v[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) v[i] = po[(size_t)min(i, ns - 1) * D];
+  for (int s = d; s < ns; s += D) mls[s] = ml[s];
+  __syncthreads();
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, mls[s].x);
+  float l = 0.0f, acc = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += NB) {
+    if (s0 > 0)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) v[i] = po[(size_t)min(s0 + i, ns - 1) * D];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const float2 e = mls[min(s0 + i, ns - 1)];
+      const bool use = s0 + i < ns && e.x != -INFINITY;
+      const float w = exp2f(e.x - M);
+      l = use ? fmaf(w, e.y, l) : l;
+      acc = use ? fmaf(w, v[i], acc) : acc;
+    }
+  }
+  float *o = a.o + hq * D;
+  o[d] = L < 0 ? __builtin_nanf("") : acc / l;
+  if (L >= 0 && h == 0 && d == 0) a.pos[a.slots ? a.slots[b] : b] = L;
+}
+
+template <int D, int HPG>
+hipError_t launch_split(const AttnArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_split_kernel<D, HPG>), dim3(a.nsplit, a.Hk, a.B), dim3(kT), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split_d(const AttnArgs &a, int hpg, hipStream_t stream) {
+  switch (hpg) {
+    case 1: return launch_split<D, 1>(a, stream);
+    case 2: return launch_split<D, 2>(a, stream);
+    case 3: return launch_split<D, 3>(a, stream);
+    case 4: return launch_split<D, 4>(a, stream);
+    case 5: return launch_split<D, 5>(a, stream);
+    case 6: return launch_split<D, 6>(a, stream);
+    case 7: return launch_split<D, 7>(a, stream);
+    default: return launch_split<D, 8>(a, stream);
+  }
+}
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct AttnWs {
+  float *qkv, *o, *part_o;
+  float2 *part_ml;
+  int *lens;
+  size_t bytes;
+};
+
+AttnWs attn_ws_layout(const m2_attn_s &A, int B, void *base) {
+  const m2_attn_config &c = A.cfg;
+  char *p = static_cast<char *>(base);
+  AttnWs w{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char *r = p ? p + off : nullptr;
+    off += al256(n);
+    return r;
+  };
+  w.qkv = reinterpret_cast<float *>(take(sizeof(float) * (size_t)B * A.qkv_rows));
+  w.o = reinterpret_cast<float *>(take(sizeof(float) * (size_t)B * A.o_dim));
+  w.part_o = reinterpret_cast<float *>(take(sizeof(float) * (size_t)B * c.n_q * A.nsplit * c.head_dim));
+  w.part_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * (size_t)B * c.n_q * A.nsplit));
+  w.lens = reinterpret_cast<int *>(take(sizeof(int) * (size_t)B));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+int attn_nsplit(int max_len) { return (max_len + kC - 1) / kC; }
+
+size_t attn_ws_bytes(const m2_attn_s &A, int batch) { return attn_ws_layout(A, batch, nullptr).bytes; }
+
+hipError_t launch_attn_step(const m2_attn_s &A, uint16_t *kc, uint16_t *vc, int32_t *pos, int n_slots,
+                            const float *x, float *y, int batch, const int32_t *slots, int flags, void *ws,
+                            hipStream_t stream, hipEvent_t const *events) {
+  const m2_attn_config &c = A.cfg;
+  auto mark = [&](int i) -> hipError_t {
+    return (events && events[i]) ? hipEventRecord(events[i], stream) : hipSuccess;
+  };
+  const AttnWs w = attn_ws_layout(A, batch, ws);
+  hipError_t e = mark(0);
+  if (e == hipSuccess)
+    e = launch_gemv_plain(c.wtype, A.w.w_qkv, A.w.s_qkv, A.qkv_rows, c.d_model, c.q_group, c.q_gamma_qkv, x,
+                          batch, w.qkv, nullptr, stream);
+  if (e == hipSuccess) e = mark(1);
+  if (e != hipSuccess) return e;
+  AttnArgs a{};
+  a.qkv = w.qkv;
+  a.kc = kc;
+  a.vc = vc;
+  a.pos = pos;
+  a.slots = slots;
+  a.n_slots = n_slots;
+  a.B = batch;
+  a.Hq = c.n_q;
+  a.Hk = c.n_kv;
+  a.max_len = c.max_len;
+  a.nsplit = A.nsplit;
+  a.scale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  a.part_o = w.part_o;
+  a.part_ml = w.part_ml;
+  a.lens = w.lens;
+  a.o = w.o;
+  const int hpg = c.n_q / c.n_kv;
+  e = c.head_dim == 128 ? launch_split_d<128>(a, hpg, stream) : launch_split_d<64>(a, hpg, stream);
+  if (e == hipSuccess) e = mark(2);
+  if (e != hipSuccess) return e;
+  if (c.head_dim == 128)
+    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(c.n_q, batch), dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(c.n_q, batch), dim3(64), 0, stream, a);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = mark(3);
+  if (e == hipSuccess)
+    e = launch_gemv_plain(c.wtype, A.w.w_o, A.w.s_o, c.d_model, A.o_dim, c.q_group, c.q_gamma_o, w.o, batch, y,
+                          (flags & M2_RESIDUAL) ? x : nullptr, stream);
+  if (e == hipSuccess) e = mark(4);
+  return e;
+}
+
+}  // namespace m2d

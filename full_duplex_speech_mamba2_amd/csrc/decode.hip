@@ -1793,6 +1793,35 @@ hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, h
   return hipGetLastError();
 }
 
+hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, int K, int q_group, float gamma,
+                             const float *act, int batch, float *y, const float *resid, hipStream_t stream) {
+  const bool quantized = wtype == M2_W_INT8G || wtype == M2_W_INT4G || wtype == M2_W_INT3G;
+  const int epc = wtype == M2_W_F32 ? 4 : wtype == M2_W_BF16 ? 8 : wtype == M2_W_INT8G ? 16 : 32;
+  GemvArgs a{};
+  a.W = W;
+  a.S = S;
+  a.rows = rows;
+  a.K = K;
+  a.q_shift = quantized ? log2i(q_group / epc) : 30;
+  a.gamma = quantized ? gamma : 1.0f;
+  a.act = act;
+  a.B = batch;
+  a.y = y;
+  a.resid = resid;
+  a.slots = nullptr;
+  a.n_slots = batch;
+  // 1-2 sessions, 2- and 4-byte weights: the in_proj configuration (5 nontemporal loads in
+  // flight); otherwise the decode step's choice for out_proj.
+  if (batch <= 2 && (wtype == M2_W_BF16 || wtype == M2_W_F32) && wave_lds_bytes(a, batch, PRO_PLAIN) <= kWaveLdsMax) {
+    if (wtype == M2_W_BF16)
+      return batch == 1 ? launch_wave<M2_W_BF16, 1, 512, 5, 1, PRO_PLAIN, EPI_OUT>(a, stream)
+                        : launch_wave<M2_W_BF16, 2, 512, 5, 1, PRO_PLAIN, EPI_OUT>(a, stream);
+    return batch == 1 ? launch_wave<M2_W_F32, 1, 512, 5, 1, PRO_PLAIN, EPI_OUT>(a, stream)
+                      : launch_wave<M2_W_F32, 2, 512, 5, 1, PRO_PLAIN, EPI_OUT>(a, stream);
+  }
+  return dispatch_wt<PRO_PLAIN, EPI_OUT>(wtype, a, stream);
+}
+
 size_t head_ws_bytes(int vocab) { return sizeof(float2) * 4 * (size_t)((vocab + 7) / 8); }
 
 hipError_t launch_head(const m2_head_config &c, const void *w, const void *scales, const float *h, int batch,

@@ -284,6 +284,92 @@ int m2_head_argmax_timed(const m2_head_config *cfg, const void *w, const void *s
   return head_impl(cfg, w, scales, h, batch, token, logits, ws, ws_bytes, stream, events);
 }
 
+static int check_attn(const m2_attn_config *c) {
+  if (!c) return fail(M2_ERR_NULL, "attention config is NULL");
+  if (c->wtype != M2_W_F32 && c->wtype != M2_W_BF16 && c->wtype != M2_W_INT8G && c->wtype != M2_W_INT4G &&
+      c->wtype != M2_W_INT3G)
+    return fail(M2_ERR_DTYPE, "unknown wtype %d", c->wtype);
+  if (c->n_q < 1 || c->n_kv < 1 || c->n_q % c->n_kv)
+    return fail(M2_ERR_SHAPE, "n_q %d must be a positive multiple of n_kv %d", c->n_q, c->n_kv);
+  if (c->n_q / c->n_kv > 8) return fail(M2_ERR_UNSUPPORTED, "more than 8 query heads per key/value head");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(M2_ERR_UNSUPPORTED, "head_dim %d: 64 and 128 are supported", c->head_dim);
+  if (c->max_len < 1 || c->max_len > 65536) return fail(M2_ERR_SHAPE, "max_len %d outside [1, 65536]", c->max_len);
+  const int epc = c->wtype == M2_W_F32 ? 4 : c->wtype == M2_W_BF16 ? 8 : c->wtype == M2_W_INT8G ? 16 : 32;
+  const int o_dim = c->n_q * c->head_dim;
+  if (c->d_model <= 0 || c->d_model % epc || o_dim % epc)
+    return fail(M2_ERR_SHAPE, "d_model %d and n_q*head_dim %d must be positive multiples of %d", c->d_model, o_dim,
+                epc);
+  if (c->wtype == M2_W_INT8G || c->wtype == M2_W_INT4G || c->wtype == M2_W_INT3G) {
+    const int qmin = c->wtype == M2_W_INT8G ? 16 : 32;
+    if (c->q_group < qmin || (c->q_group & (c->q_group - 1)) || c->d_model % c->q_group || o_dim % c->q_group)
+      return fail(M2_ERR_SHAPE, "q_group %d must be a power of two >= %d dividing d_model and n_q*head_dim",
+                  c->q_group, qmin);
+  }
+  return M2_OK;
+}
+
+int m2_attn_create(const m2_attn_config *cfg, const m2_attn_weights *w, m2_attn *out) {
+  if (!out) return fail(M2_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  int rc = check_attn(cfg);
+  if (rc) return rc;
+  if (!w || !w->w_qkv || !w->w_o) return fail(M2_ERR_NULL, "w_qkv and w_o are required");
+  const bool quantized = cfg->wtype == M2_W_INT8G || cfg->wtype == M2_W_INT4G || cfg->wtype == M2_W_INT3G;
+  if (quantized && (!w->s_qkv || !w->s_o)) return fail(M2_ERR_NULL, "quantized weights need s_qkv and s_o");
+  if (!aligned16(w->w_qkv) || !aligned16(w->w_o) || (quantized && (!aligned16(w->s_qkv) || !aligned16(w->s_o))))
+    return fail(M2_ERR_ALIGN, "attention weights and scales must be 16-byte aligned");
+  m2_attn_s *A = new (std::nothrow) m2_attn_s();
+  if (!A) return fail(M2_ERR_SHAPE, "out of host memory");
+  A->cfg = *cfg;
+  A->w = *w;
+  A->qkv_rows = (cfg->n_q + 2 * cfg->n_kv) * cfg->head_dim;
+  A->o_dim = cfg->n_q * cfg->head_dim;
+  A->nsplit = m2d::attn_nsplit(cfg->max_len);
+  *out = A;
+  return ok();
+}
+
+void m2_attn_destroy(m2_attn a) { delete a; }
+
+size_t m2_attn_workspace(m2_attn a, int32_t batch) {
+  if (!a || batch <= 0) return 0;
+  return m2d::attn_ws_bytes(*a, batch);
+}
+
+static int attn_impl(m2_attn a, void *k_cache, void *v_cache, int32_t *pos, int32_t n_slots, const float *x,
+                     float *y, int32_t batch, const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes,
+                     void *stream, void *const *events) {
+  if (!a || !k_cache || !v_cache || !pos || !x || !y) return fail(M2_ERR_NULL, "a required pointer is NULL");
+  if (batch <= 0) return fail(M2_ERR_SHAPE, "batch must be positive");
+  if (n_slots < 1) return fail(M2_ERR_SLOT, "n_slots must be positive");
+  if (!slot_ids && batch > n_slots) return fail(M2_ERR_SLOT, "batch %d exceeds n_slots %d", batch, n_slots);
+  if (flags & ~M2_RESIDUAL) return fail(M2_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(x) || !aligned16(y) ||
+      (reinterpret_cast<uintptr_t>(pos) & 3u))
+    return fail(M2_ERR_ALIGN, "caches, x and y must be 16-byte aligned, pos 4-byte aligned");
+  const size_t need = m2d::attn_ws_bytes(*a, batch);
+  if (!ws || ws_bytes < need)
+    return fail(M2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(M2_ERR_ALIGN, "workspace must be 16-byte aligned");
+  hipError_t e = m2d::launch_attn_step(*a, static_cast<uint16_t *>(k_cache), static_cast<uint16_t *>(v_cache), pos,
+                                       n_slots, x, y, batch, slot_ids, flags, ws, static_cast<hipStream_t>(stream),
+                                       reinterpret_cast<hipEvent_t const *>(events));
+  if (e != hipSuccess) return fail(M2_ERR_HIP, "attention step launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int m2_attn_step(m2_attn a, void *k_cache, void *v_cache, int32_t *pos, int32_t n_slots, const float *x, float *y,
+                 int32_t batch, const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream) {
+  return attn_impl(a, k_cache, v_cache, pos, n_slots, x, y, batch, slot_ids, flags, ws, ws_bytes, stream, nullptr);
+}
+
+int m2_attn_step_timed(m2_attn a, void *k_cache, void *v_cache, int32_t *pos, int32_t n_slots, const float *x,
+                       float *y, int32_t batch, const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes,
+                       void *stream, void *const *events) {
+  return attn_impl(a, k_cache, v_cache, pos, n_slots, x, y, batch, slot_ids, flags, ws, ws_bytes, stream, events);
+}
+
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk) {
   if (!layer || batch <= 0 || seqlen <= 0 || chunk < 16 || chunk > 256 || chunk % 16) return 0;
   return m2d::prefill_ws_bytes(*layer, batch, seqlen, chunk);

@@ -32,6 +32,14 @@ struct m2_state_s {
   float *conv;      // [n_slots][d_conv-1][conv_dim]
 };
 
+struct m2_attn_s {
+  m2_attn_config cfg;
+  m2_attn_weights w;
+  int qkv_rows;     // (n_q + 2 n_kv) head_dim
+  int o_dim;        // n_q head_dim
+  int nsplit;       // 64-position chunks of max_len
+};
+
 namespace m2d {
 
 // Workspace carve-up of one decode step for `batch` sessions.
@@ -61,6 +69,18 @@ size_t head_ws_bytes(int vocab);
 hipError_t launch_head(const m2_head_config &c, const void *w, const void *scales, const float *h, int batch,
                        int32_t *token, float *logits, void *ws, hipStream_t stream,
                        hipEvent_t const *events = nullptr);
+
+// y[b] = gamma W act[b] (+ resid[b]) for a [rows][K] matrix in any weight format, with the
+// decode step's GEMV kernels (plain epilogue).
+hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, int K, int q_group, float gamma,
+                             const float *act, int batch, float *y, const float *resid, hipStream_t stream);
+
+// Attention decode step (m2_attn_step).
+int attn_nsplit(int max_len);
+size_t attn_ws_bytes(const m2_attn_s &A, int batch);
+hipError_t launch_attn_step(const m2_attn_s &A, uint16_t *kc, uint16_t *vc, int32_t *pos, int n_slots,
+                            const float *x, float *y, int batch, const int32_t *slots, int flags, void *ws,
+                            hipStream_t stream, hipEvent_t const *events = nullptr);
 
 // Prefill
 size_t prefill_ws_bytes(const m2_layer_s &L, int batch, int seqlen, int chunk);

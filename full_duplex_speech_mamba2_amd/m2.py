@@ -42,6 +42,16 @@ class HeadConfig(C.Structure):
                 ("q_group", C.c_int32), ("q_gamma", C.c_float)]
 
 
+class AttnConfig(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("n_q", C.c_int32), ("n_kv", C.c_int32), ("head_dim", C.c_int32),
+                ("max_len", C.c_int32), ("wtype", C.c_int32), ("q_group", C.c_int32),
+                ("q_gamma_qkv", C.c_float), ("q_gamma_o", C.c_float)]
+
+
+class AttnWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("w_qkv", "s_qkv", "w_o", "s_o")]
+
+
 class Weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("w_in", "s_in", "w_out", "s_out", "conv_w", "conv_b",
                                           "dt_bias", "A_log", "D", "norm_w")]
@@ -72,6 +82,15 @@ _lib.m2_head_workspace.argtypes = [_P, _i32]
 _lib.m2_head_workspace.restype = C.c_size_t
 _lib.m2_head_argmax.argtypes = [_P, _P, _P, _P, _i32, _P, _P, _P, C.c_size_t, _P]
 _lib.m2_head_argmax_timed.argtypes = [_P, _P, _P, _P, _i32, _P, _P, _P, C.c_size_t, _P, _P]
+_lib.m2_attn_create.argtypes = [_P, _P, _P]
+_lib.m2_attn_destroy.argtypes = [_P]
+_lib.m2_attn_destroy.restype = None
+_lib.m2_attn_workspace.argtypes = [_P, _i32]
+_lib.m2_attn_workspace.restype = C.c_size_t
+_lib.m2_attn_step.argtypes = [_P, _P, _P, _P, _i32, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P]
+_lib.m2_attn_step_timed.argtypes = [_P, _P, _P, _P, _i32, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P, _P]
+for _f in ("m2_attn_create", "m2_attn_step", "m2_attn_step_timed"):
+    getattr(_lib, _f).restype = C.c_int
 for _f in ("m2_layer_create", "m2_state_sizes", "m2_state_create", "m2_state_zero", "m2_step",
            "m2_step_timed", "m2_prefill", "m2_head_argmax", "m2_head_argmax_timed"):
     getattr(_lib, _f).restype = C.c_int
@@ -306,3 +325,77 @@ class Head:
         _check(_lib.m2_head_argmax_timed(C.byref(self.cfg), _ptr(self.w), _ptr(self.s), _ptr(h), B, _ptr(token),
                                          None, _ptr(ws), ws.numel(), _stream(stream), ev))
         return token
+
+
+def attn_config(dims) -> AttnConfig:
+    return AttnConfig(dims.d_model, dims.n_q, dims.n_kv, dims.head_dim, dims.max_len, WTYPE[dims.wtype],
+                      dims.q_group, float(dims.q_gamma_qkv), float(dims.q_gamma_o))
+
+
+class Attn:
+    """An attention-layer handle (m2_attn) over device copies of W_qkv and W_o."""
+
+    def __init__(self, dims, weights: Dict[str, object], device="cuda"):
+        self.dims = dims
+        self.device = torch.device(device)
+        self.tensors = {k: to_device(v, self.device) for k, v in weights.items()}
+        self.cfg = attn_config(dims)
+        self.wstruct = AttnWeights(*[_ptr(self.tensors.get(k)) for k in ("w_qkv", "s_qkv", "w_o", "s_o")])
+        h = C.c_void_p()
+        _check(_lib.m2_attn_create(C.byref(self.cfg), C.byref(self.wstruct), C.byref(h)))
+        self.handle = h
+        self._ws: Dict[int, torch.Tensor] = {}
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            _lib.m2_attn_destroy(h)
+            self.handle = None
+
+    def workspace(self, batch: int) -> torch.Tensor:
+        ws = self._ws.get(batch)
+        if ws is None:
+            n = int(_lib.m2_attn_workspace(self.handle, batch))
+            if n == 0:
+                raise M2Error(M2_ERR_SHAPE, "no workspace size for batch %d" % batch)
+            ws = self._ws[batch] = torch.empty(n, dtype=torch.uint8, device=self.device)
+        return ws
+
+    def new_cache(self, n_slots: int):
+        """Zeroed device caches k, v (bf16 bits as int16) [n_slots][n_kv][max_len][D] and pos."""
+        d = self.dims
+        shape = (n_slots, d.n_kv, d.max_len, d.head_dim)
+        return (torch.zeros(shape, dtype=torch.int16, device=self.device),
+                torch.zeros(shape, dtype=torch.int16, device=self.device),
+                torch.zeros(n_slots, dtype=torch.int32, device=self.device))
+
+    def _args(self, kc, vc, pos, x, y, slot_ids, residual, ws, stream):
+        d = self.dims
+        B = x.shape[0]
+        _act(x, (B, d.d_model))
+        _act(y, x.shape)
+        n_slots = pos.numel()
+        shape = (n_slots, d.n_kv, d.max_len, d.head_dim)
+        for c in (kc, vc):
+            if c.dtype not in (torch.int16, torch.bfloat16) or not c.is_contiguous() or tuple(c.shape) != shape:
+                raise ValueError("kv cache must be a contiguous 16-bit tensor of shape %s" % (shape,))
+        _tokens(pos, n_slots)
+        if slot_ids is not None:
+            _tokens(slot_ids, B)
+        if ws is None:
+            ws = self.workspace(B)
+        return (self.handle, _ptr(kc), _ptr(vc), _ptr(pos), n_slots, _ptr(x), _ptr(y), B, _ptr(slot_ids),
+                M2_RESIDUAL if residual else 0, _ptr(ws), ws.numel(), _stream(stream))
+
+    def step(self, kc, vc, pos, x, y=None, slot_ids=None, residual=False, ws=None, stream=None):
+        """One token for x [B][d_model]; appends to the caches and advances pos in place."""
+        if y is None:
+            y = torch.empty_like(x)
+        _check(_lib.m2_attn_step(*self._args(kc, vc, pos, x, y, slot_ids, residual, ws, stream)))
+        return y
+
+    def step_timed(self, kc, vc, pos, x, y, events, slot_ids=None, residual=False, ws=None, stream=None):
+        """step() recording five events: before, and after each of its four kernels."""
+        ev = (C.c_void_p * 5)(*[getattr(e, "cuda_event", e) for e in events])
+        _check(_lib.m2_attn_step_timed(*self._args(kc, vc, pos, x, y, slot_ids, residual, ws, stream), ev))
+        return y

@@ -180,6 +180,26 @@ class HeadWorkload:
     seed: int = 0
 
 
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """Attention-layer decode for `batch` sessions whose caches hold `start_pos` positions
+    when timing starts; consecutive steps take consecutive sets of sessions (slot_sets
+    disjoint sets, so every set's cache advances once per slot_sets steps)."""
+    name: str
+    dims: AttnDims
+    batch: int
+    steps: int
+    start_pos: int
+    slot_sets: int
+    seed: int = 0
+
+
+ATTN_WORKLOADS: Dict[int, AttnWorkload] = {
+    8: AttnWorkload("attn_9b_bf16_b1_ctx1000_decode", ATTN_9B, batch=1, steps=750, start_pos=1000,
+                    slot_sets=8, seed=8),
+}
+
+
 # The pages give no vocabulary size: 131072 rows per head is a configured reading, with the
 # function head taken to be a second head of the text head's shape.
 HEAD_WORKLOADS: Dict[int, HeadWorkload] = {

@@ -210,6 +210,60 @@ int m2_head_argmax_timed(const m2_head_config *cfg, const void *w, const void *s
                          int32_t batch, int32_t *token, float *logits, void *ws, size_t ws_bytes,
                          void *stream, void *const *events);
 
+/* Attention layers of the hybrid backbone (blog page "NemotronLabs VoiceChat 11B" overview,
+ * "Key design decisions" item 2: Mamba layers alternate with attention layers; its "Known
+ * limitations": a 2-minute audio context; SGLang-Omni cookbook page, "Known limitations":
+ * the backbone and its KV cache run in bfloat16). One decode token per session:
+ *   qkv = W_qkv u, rows [q: n_q heads x D | k: n_kv heads x D | v: n_kv heads x D] (no bias)
+ *   the new k and v, rounded to bf16 (nearest, ties to even), are stored at position pos of
+ *   the session's cache; query head h reads key/value head g = h / (n_q / n_kv):
+ *   s_j = q_h . K_g[j] / sqrt(D), j = 0 .. pos; o_h = sum_j softmax(s)_j V_g[j]
+ *   y = W_o o (o head-major), or u + W_o o under M2_RESIDUAL; pos += 1.
+ * A session whose slot id is out of range or whose pos is already max_len gets NaN outputs
+ * and its cache and pos are left as they were. */
+typedef struct {
+  int32_t d_model;          /* a multiple of 4 (f32), 8 (bf16), 16 (int8) or 32 (low-bit) */
+  int32_t n_q;              /* query heads; a multiple of n_kv, at most 8 per key/value head */
+  int32_t n_kv;             /* key/value heads */
+  int32_t head_dim;         /* D: 64 or 128 */
+  int32_t max_len;          /* cache positions per session, 1 .. 65536 */
+  int32_t wtype;            /* m2_wtype of W_qkv and W_o */
+  int32_t q_group;          /* quantized types: as m2_config.q_group; divides d_model and n_q D */
+  float q_gamma_qkv;        /* quantized types: per-tensor multipliers (1 = none) */
+  float q_gamma_o;
+} m2_attn_config;
+
+typedef struct {
+  const void *w_qkv;        /* [(n_q + 2 n_kv) D][d_model], formats as m2_weights.w_in */
+  const void *s_qkv;        /* quantized types: scales as m2_weights.s_in, else NULL */
+  const void *w_o;          /* [d_model][n_q D] */
+  const void *s_o;
+} m2_attn_weights;
+
+typedef struct m2_attn_s *m2_attn;   /* borrows the m2_attn_weights pointers; immutable */
+
+int m2_attn_create(const m2_attn_config *cfg, const m2_attn_weights *w, m2_attn *out);
+void m2_attn_destroy(m2_attn a);
+
+/* Workspace bytes m2_attn_step needs for `batch` sessions (0 if batch <= 0). */
+size_t m2_attn_workspace(m2_attn a, int32_t batch);
+
+/* One decode token for `batch` sessions. k_cache, v_cache: device bf16 bits
+ * [n_slots][n_kv][max_len][D], 16-byte aligned, caller-owned; pos: device int32 [n_slots]
+ * (tokens already cached per slot), advanced in place; x, y: fp32 [batch][d_model] (y may
+ * alias x); session b uses slot slot_ids[b] (device int32 [batch]) or b if NULL; flags:
+ * M2_RESIDUAL. Asynchronous on `stream`; errors as m2_status. */
+int m2_attn_step(m2_attn a, void *k_cache, void *v_cache, int32_t *pos, int32_t n_slots, const float *x,
+                 float *y, int32_t batch, const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/* m2_attn_step that also records hipEvent_t events[0..4] on `stream`: before the qkv GEMV
+ * and after each of its four kernels (qkv GEMV, split attention, combine, o GEMV). For
+ * per-kernel timing; NULL events are skipped. */
+int m2_attn_step_timed(m2_attn a, void *k_cache, void *v_cache, int32_t *pos, int32_t n_slots,
+                       const float *x, float *y, int32_t batch, const int32_t *slot_ids, int32_t flags,
+                       void *ws, size_t ws_bytes, void *stream, void *const *events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -211,3 +211,41 @@ def test_head_timed_call_takes_at_most_four_sessions():
         m2.M2_ERR_UNSUPPORTED
     assert L.m2_head_argmax_timed(C.byref(cfg), None, None, FAKE, 4, FAKE, None, FAKE, need, None, ev) == \
         m2.M2_ERR_NULL
+
+
+def test_attention_rejects_bad_configs_and_calls_without_launching():
+    L = m2.lib()
+    good = synth.AttnDims(d_model=256, n_q=8, n_kv=2, head_dim=64, max_len=100)
+
+    def create_attn(dims, w=None):
+        cfg = m2.attn_config(dims)
+        h = C.c_void_p()
+        wq = w or m2.AttnWeights(FAKE, FAKE if dims.wtype in ("int8g", "int4g", "int3g") else None, FAKE,
+                                 FAKE if dims.wtype in ("int8g", "int4g", "int3g") else None)
+        return L.m2_attn_create(C.byref(cfg), C.byref(wq), C.byref(h)), h
+
+    for bad, status in [(good.replace(n_q=6, n_kv=4), m2.M2_ERR_SHAPE), (good.replace(n_q=18, n_kv=2), m2.M2_ERR_UNSUPPORTED),
+                        (good.replace(head_dim=96), m2.M2_ERR_UNSUPPORTED), (good.replace(max_len=0), m2.M2_ERR_SHAPE),
+                        (good.replace(max_len=70000), m2.M2_ERR_SHAPE), (good.replace(d_model=260), m2.M2_ERR_SHAPE),
+                        (good.replace(wtype="int4g", q_group=16), m2.M2_ERR_SHAPE),
+                        (good.replace(wtype="int8g", q_group=512), m2.M2_ERR_SHAPE)]:
+        rc, _ = create_attn(bad)
+        assert rc == status, (bad, rc)
+    rc, _ = create_attn(good.replace(wtype="int4g", q_group=64), m2.AttnWeights(FAKE, None, FAKE, None))
+    assert rc == m2.M2_ERR_NULL
+    rc, _ = create_attn(good, m2.AttnWeights(FAKE + 8, None, FAKE, None))
+    assert rc == m2.M2_ERR_ALIGN
+    rc, h = create_attn(good)
+    assert rc == 0
+    need = L.m2_attn_workspace(h, 3)
+    # qkv (3 x 768) + o (3 x 512) floats, partials of 2 chunks x 8 heads x 3 sessions, lengths
+    assert need >= 4 * 3 * (768 + 512) + 4 * 3 * 8 * 2 * 64 + 8 * 3 * 8 * 2 and L.m2_attn_workspace(h, 0) == 0
+    step = lambda **k: L.m2_attn_step(*[k.get(n, v) for n, v in [
+        ("a", h), ("kc", FAKE), ("vc", FAKE), ("pos", FAKE), ("n", 4), ("x", FAKE), ("y", FAKE * 2), ("b", 3),
+        ("sl", None), ("fl", 0), ("ws", FAKE), ("wn", need), ("st", None)]])
+    assert step(kc=None) == m2.M2_ERR_NULL and step(pos=None) == m2.M2_ERR_NULL and step(a=None) == m2.M2_ERR_NULL
+    assert step(b=0) == m2.M2_ERR_SHAPE and step(b=5) == m2.M2_ERR_SLOT and step(n=0) == m2.M2_ERR_SLOT
+    assert step(fl=2) == m2.M2_ERR_UNSUPPORTED and step(kc=FAKE + 2) == m2.M2_ERR_ALIGN
+    assert step(pos=FAKE + 2) == m2.M2_ERR_ALIGN and step(wn=need - 1) == m2.M2_ERR_WORKSPACE
+    assert step(ws=FAKE + 8) == m2.M2_ERR_ALIGN
+    L.m2_attn_destroy(h)
