@@ -46,7 +46,8 @@ def parse():
                     help="workload: 1 (default), 2 (32 sessions), 3 (27-layer int8 stack), 4 (prefill + 4 sessions), "
                          "5 (int4 g64 weights, 1 session), 6 (int3 g64 weights, 1 session), "
                          "7 (text and function output heads with greedy argmax, 1 session), "
-                         "8 (attention layer with a bf16 KV cache of 1000+ positions, 1 session)")
+                         "8 (attention layer with a bf16 KV cache of 1000+ positions, 1 session), "
+                         "9 (hybrid stack of 27 Mamba-2 and 4 attention layers, one call per step, 1 session)")
     ap.add_argument("--copies", type=int, default=0,
                     help="identical weight copies used in turn (0: enough for >= 590 MB)")
     ap.add_argument("--no-graph", action="store_true", help="time plain launches only")
@@ -135,6 +136,48 @@ def hold_gpu(ms: float) -> None:
     torch.cuda._sleep(int(ms * 2.4e6))          # cycles at 2.4 GHz
 
 
+def graph_ms_per_step(run, steps, launches_per_step, before_replay=None):
+    """Milliseconds per step of `steps` steps replayed from HIP graphs. The steps are captured
+    as one graph of at most ~16k launches (replayed as often as it fits) plus one graph for
+    the remainder, so a deep stack does not build a graph of hundreds of thousands of
+    nodes. before_replay (untimed) runs before the warm replay and before the timed one."""
+    import torch
+    chunk = max(1, min(steps, 16384 // max(1, launches_per_step)))
+    reps, rem = divmod(steps, chunk)
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                run(0, n)
+        torch.cuda.current_stream().wait_stream(st)
+        return g
+
+    ga = capture(chunk)
+    gb = capture(rem) if rem else None
+
+    def replay_all():
+        for _ in range(reps):
+            ga.replay()
+        if gb is not None:
+            gb.replay()
+
+    if before_replay:
+        before_replay()
+    replay_all()
+    if before_replay:
+        before_replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    replay_all()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def traffic_for(kernel_name, workload):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on the
     current kernel source (the summary stores the source hash); else None."""
@@ -176,6 +219,8 @@ def main():
         return bench_heads(args, synth.HEAD_WORKLOADS[args.config])
     if args.config in synth.ATTN_WORKLOADS:
         return bench_attn(args, synth.ATTN_WORKLOADS[args.config])
+    if args.config in synth.STACK_WORKLOADS:
+        return bench_stack(args, synth.STACK_WORKLOADS[args.config])
     wl = synth.workload(args.config)
     dims, B = wl.dims, wl.batch
     print("[bench] workload %s: generating inputs" % wl.name, file=sys.stderr, flush=True)
@@ -230,24 +275,10 @@ def main():
     torch.cuda.synchronize()
     ms_eager = e0.elapsed_time(e1) / args.steps
 
-    # timed region 2: the same steps captured once into a HIP graph and replayed
+    # timed region 2: the same steps captured into HIP graphs and replayed
     ms_graph = None
     if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                run(0, args.steps)
-        torch.cuda.current_stream().wait_stream(s)
-        g.replay()                      # warm replay
-        torch.cuda.synchronize()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms_graph = e0.elapsed_time(e1) / args.steps
-        del g
+        ms_graph = graph_ms_per_step(run, args.steps, 4 * wl.layers)
 
     ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
     steps_per_s = 1000.0 / ms
@@ -356,21 +387,7 @@ def bench_heads(args, wl):
     ms_eager = e0.elapsed_time(e1) / args.steps
     ms_graph = None
     if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        st = torch.cuda.Stream()
-        st.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(st):
-            with torch.cuda.graph(g, stream=st):
-                run(0, args.steps)
-        torch.cuda.current_stream().wait_stream(st)
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms_graph = e0.elapsed_time(e1) / args.steps
-        del g
+        ms_graph = graph_ms_per_step(run, args.steps, 2 * len(heads))
     ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
     fps = 1000.0 / ms
 
@@ -514,23 +531,7 @@ def bench_attn(args, wl):
         raise SystemExit("attention bench: a session ran out of cache positions (NaN outputs)")
     ms_graph = None
     if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        st = torch.cuda.Stream()
-        st.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(st):
-            with torch.cuda.graph(g, stream=st):
-                run(0, args.steps)
-        torch.cuda.current_stream().wait_stream(st)
-        pos.copy_(pos0)
-        g.replay()
-        pos.copy_(pos0)
-        torch.cuda.synchronize()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms_graph = e0.elapsed_time(e1) / args.steps
-        del g
+        ms_graph = graph_ms_per_step(run, args.steps, 4, before_replay=lambda: pos.copy_(pos0))
     ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
     sps = 1000.0 / ms
     mean_len = wl.start_pos + 1 + (args.steps / S - 1) / 2.0
@@ -616,6 +617,116 @@ def attn_cpu_baseline_and_parity(args, wl, w, kc_np, vc_np, pos0_np, xs_np):
     e_out = float(np.max(np.max(np.abs(yg - yo), axis=-1) / np.max(np.abs(yo), axis=-1)))
     return base, {"steps": n, "e_out": e_out, "tol_out": 1e-3, "ok": bool(e_out <= 1e-3),
                   "positions_equal": bool(np.array_equal(pd.cpu().numpy(), pos))}
+
+
+STACK_METRIC = "Hybrid stack decode steps/s + achieved HBM GB/s (% peak), 27 Mamba-2 + 4 attention layers, 9B-shaped"
+
+
+def bench_stack(args, wl):
+    """Steps/s of a hybrid stack stepped by m2_stack_step: per step one token for `batch`
+    sessions through every layer of the pattern (residual chain)."""
+    import numpy as np
+    import torch
+    from full_duplex_speech_mamba2_amd import m2, synth
+
+    dev = torch.device("cuda:0")
+    B, S = wl.batch, wl.slot_sets
+    n_slots = B * S
+    print("[bench] workload %s: generating %d layers" % (wl.name, len(wl.pattern)), file=sys.stderr, flush=True)
+    pos0_np = np.full(n_slots, wl.start_pos, np.int32)
+    entries, pos_list, pos0 = [], [], torch.from_numpy(pos0_np).to(dev)
+    for i, k in enumerate(wl.pattern):
+        if k == "M":
+            lay = m2.Layer(wl.mixer, synth.make_layer_weights(wl.mixer, wl.seed, i), dev)
+            entries.append((lay, m2.State(lay, n_slots)))
+        else:
+            at = m2.Attn(wl.attn, synth.make_attn_weights(wl.attn, wl.seed, i), dev)
+            kc, vc = synth.make_kv_cache(wl.attn, wl.seed, pos0_np, i)
+            st = (torch.from_numpy(kc.view(np.int16)).to(dev), torch.from_numpy(vc.view(np.int16)).to(dev),
+                  pos0.clone())
+            pos_list.append(st[2])
+            entries.append((at, st))
+    stack = m2.Stack(entries, n_slots)
+    print("[bench] layers on the device; warming up", file=sys.stderr, flush=True)
+    sets = torch.arange(n_slots, dtype=torch.int32, device=dev).reshape(S, B).contiguous()
+    xs = torch.from_numpy(synth.make_inputs(wl.mixer, wl.seed, wl.steps, B)).to(dev)
+    ys = torch.empty_like(xs)
+    ws = stack.workspace(B)
+    nx = xs.shape[0]
+    if args.steps // S > wl.attn.max_len - wl.start_pos:
+        raise SystemExit("--steps %d would fill the caches" % args.steps)
+
+    def reset():
+        for p_ in pos_list:
+            p_.copy_(pos0)
+
+    def run(t0, n):
+        for t in range(t0, t0 + n):
+            stack.step(xs[t % nx], ys[t % nx], slot_ids=sets[t % S], ws=ws)
+
+    run(0, min(args.warmup, S * (wl.attn.max_len - wl.start_pos)))
+    reset()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run(0, args.steps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / args.steps
+    if not bool(torch.isfinite(ys[:min(nx, args.steps)]).all()):
+        raise SystemExit("stack bench: non-finite outputs")
+    print("[bench] eager %.3f ms/step; capturing graphs" % ms_eager, file=sys.stderr, flush=True)
+    ms_graph = None
+    if not args.no_graph:
+        ms_graph = graph_ms_per_step(run, args.steps, 4 * len(wl.pattern) + 1, before_replay=reset)
+    print("[bench] graph %s ms/step" % ms_graph, file=sys.stderr, flush=True)
+    ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
+    sps = 1000.0 / ms
+    mean_len = wl.start_pos + 1 + (args.steps / S - 1) / 2.0
+    n_m, n_a = wl.pattern.count("M"), wl.pattern.count("A")
+    awl = synth.AttnWorkload(wl.name, wl.attn, B, wl.steps, wl.start_pos, S)
+    step_bytes = n_m * kernel_bytes(wl.mixer, B)["step"] + n_a * attn_bytes(awl, mean_len)["step"]
+
+    # per-kernel durations of the first mixer layer, residual as in the stack (HIP events)
+    kp = max(10, args.prof_steps)
+    hip = hip_runtime()
+    evs = [[hip_event(hip) for _ in range(4)] for _ in range(kp)]
+    lay0, st0 = entries[0]
+    torch.cuda.synchronize()
+    hold_gpu(150.0)
+    for t in range(kp):
+        m2.step_timed(lay0, st0, xs[t % nx], ys[t % nx], evs[t], slot_ids=sets[t % S], residual=True, ws=ws)
+    torch.cuda.synchronize()
+    dur_us = {n: 1000.0 * float(np.mean([hip_elapsed_ms(hip, e[i], e[i + 1]) for e in evs]))
+              for i, n in enumerate(PHASES)}
+    for row in evs:
+        for e in row:
+            hip.hipEventDestroy(e)
+    kb = kernel_bytes(wl.mixer, B)
+    achieved = kb["gemv_in"] / (dur_us["gemv_in"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": "gemv_in", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_for("gemv_in", "mamba2_9b_bf16_b1_decode750"),
+                "algorithmic_bytes": kb["gemv_in"], "avg_duration_us": round(dur_us["gemv_in"], 2)}
+    out = {
+        "metric": STACK_METRIC, "value": round(sps, 2), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "pattern": wl.pattern, "mixer_layers": n_m, "attention_layers": n_a,
+                   "d_model": wl.mixer.d_model, "batch": B, "weight_dtype": wl.mixer.wtype, "kv_dtype": "bf16",
+                   "start_positions": wl.start_pos, "mean_attended": round(mean_len, 1), "slot_sets": S,
+                   "timing": "graph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"},
+        "achieved_GBps": round(step_bytes * sps / 1e9, 1),
+        "hbm_peak_frac": round(step_bytes * sps / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_algorithmic_bytes": step_bytes,
+        "frame_budget_ms": 80.0,
+        "ms_per_step_eager": round(ms_eager, 4),
+        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 4),
+        "kernel_us_first_mixer": {n: round(v, 2) for n, v in dur_us.items()},
+        "roofline": roofline, "cpu_baseline": None, "parity": None,
+    }
+    print(json.dumps(out), flush=True)
 
 
 def prefill_flops(dims, B, T, Q):

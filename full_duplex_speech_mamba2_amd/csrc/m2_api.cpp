@@ -5,7 +5,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <new>
+#include <vector>
 
 #include "m2_internal.h"
 
@@ -368,6 +370,84 @@ int m2_attn_step_timed(m2_attn a, void *k_cache, void *v_cache, int32_t *pos, in
                        float *y, int32_t batch, const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes,
                        void *stream, void *const *events) {
   return attn_impl(a, k_cache, v_cache, pos, n_slots, x, y, batch, slot_ids, flags, ws, ws_bytes, stream, events);
+}
+
+struct m2_stack_s {
+  std::vector<m2_stack_layer> layers;
+  int n_slots;
+  int d_model;
+};
+
+int m2_stack_create(const m2_stack_layer *layers, int32_t n_layers, int32_t n_slots, m2_stack *out) {
+  if (!out) return fail(M2_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  if (!layers || n_layers < 1) return fail(M2_ERR_SHAPE, "a stack needs at least one layer");
+  if (n_slots < 1) return fail(M2_ERR_SLOT, "n_slots must be positive");
+  int d_model = -1;
+  for (int i = 0; i < n_layers; ++i) {
+    const m2_stack_layer &l = layers[i];
+    if (!l.layer) return fail(M2_ERR_NULL, "layer %d is NULL", i);
+    int dm;
+    if (l.kind == M2_LAYER_MIXER) {
+      const m2_state st = static_cast<m2_state>(l.state);
+      if (!st) return fail(M2_ERR_NULL, "mixer layer %d has no state", i);
+      if (st->n_slots < n_slots) return fail(M2_ERR_SLOT, "mixer layer %d: state of %d slots", i, st->n_slots);
+      dm = static_cast<m2_layer>(l.layer)->cfg.d_model;
+    } else if (l.kind == M2_LAYER_ATTN) {
+      if (!l.k_cache || !l.v_cache || !l.pos) return fail(M2_ERR_NULL, "attention layer %d needs caches and pos", i);
+      dm = static_cast<m2_attn>(l.layer)->cfg.d_model;
+    } else {
+      return fail(M2_ERR_SHAPE, "layer %d: unknown kind %d", i, l.kind);
+    }
+    if (d_model >= 0 && dm != d_model) return fail(M2_ERR_SHAPE, "layer %d: d_model %d, not %d", i, dm, d_model);
+    d_model = dm;
+  }
+  m2_stack_s *S = new (std::nothrow) m2_stack_s();
+  if (!S) return fail(M2_ERR_SHAPE, "out of host memory");
+  S->layers.assign(layers, layers + n_layers);
+  S->n_slots = n_slots;
+  S->d_model = d_model;
+  *out = S;
+  return ok();
+}
+
+void m2_stack_destroy(m2_stack s) { delete s; }
+
+size_t m2_stack_workspace(m2_stack s, int32_t batch) {
+  if (!s || batch <= 0) return 0;
+  size_t need = 0;
+  for (const m2_stack_layer &l : s->layers) {
+    const size_t n = l.kind == M2_LAYER_MIXER ? m2_step_workspace(static_cast<m2_layer>(l.layer), batch)
+                                              : m2_attn_workspace(static_cast<m2_attn>(l.layer), batch);
+    if (n == 0) return 0;
+    need = std::max(need, n);
+  }
+  return need;
+}
+
+int m2_stack_step(m2_stack s, const float *x, float *y, int32_t batch, const int32_t *slot_ids, void *ws,
+                  size_t ws_bytes, void *stream) {
+  if (!s || !x || !y) return fail(M2_ERR_NULL, "stack, x and y are required");
+  if (batch <= 0) return fail(M2_ERR_SHAPE, "batch must be positive");
+  if (batch > s->n_slots) return fail(M2_ERR_SLOT, "batch %d exceeds n_slots %d", batch, s->n_slots);
+  if (!aligned16(x) || !aligned16(y)) return fail(M2_ERR_ALIGN, "x and y must be 16-byte aligned");
+  const size_t need = m2_stack_workspace(s, batch);
+  if (!ws || ws_bytes < need)
+    return fail(M2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (x != y) {
+    hipError_t e = hipMemcpyAsync(y, x, sizeof(float) * (size_t)batch * s->d_model, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return fail(M2_ERR_HIP, "stack input copy: %s", hipGetErrorString(e));
+  }
+  for (const m2_stack_layer &l : s->layers) {
+    const int rc = l.kind == M2_LAYER_MIXER
+                       ? step_impl(static_cast<m2_layer>(l.layer), static_cast<m2_state>(l.state), y, y, batch,
+                                   slot_ids, M2_RESIDUAL, ws, ws_bytes, stream, nullptr)
+                       : attn_impl(static_cast<m2_attn>(l.layer), l.k_cache, l.v_cache, l.pos, s->n_slots, y, y,
+                                   batch, slot_ids, M2_RESIDUAL, ws, ws_bytes, stream, nullptr);
+    if (rc != M2_OK) return rc;
+  }
+  return ok();
 }
 
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk) {

@@ -89,7 +89,13 @@ _lib.m2_attn_workspace.argtypes = [_P, _i32]
 _lib.m2_attn_workspace.restype = C.c_size_t
 _lib.m2_attn_step.argtypes = [_P, _P, _P, _P, _i32, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P]
 _lib.m2_attn_step_timed.argtypes = [_P, _P, _P, _P, _i32, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P, _P]
-for _f in ("m2_attn_create", "m2_attn_step", "m2_attn_step_timed"):
+_lib.m2_stack_create.argtypes = [_P, _i32, _i32, _P]
+_lib.m2_stack_destroy.argtypes = [_P]
+_lib.m2_stack_destroy.restype = None
+_lib.m2_stack_workspace.argtypes = [_P, _i32]
+_lib.m2_stack_workspace.restype = C.c_size_t
+_lib.m2_stack_step.argtypes = [_P, _P, _P, _i32, _P, _P, C.c_size_t, _P]
+for _f in ("m2_attn_create", "m2_attn_step", "m2_attn_step_timed", "m2_stack_create", "m2_stack_step"):
     getattr(_lib, _f).restype = C.c_int
 for _f in ("m2_layer_create", "m2_state_sizes", "m2_state_create", "m2_state_zero", "m2_step",
            "m2_step_timed", "m2_prefill", "m2_head_argmax", "m2_head_argmax_timed"):
@@ -398,4 +404,66 @@ class Attn:
         """step() recording five events: before, and after each of its four kernels."""
         ev = (C.c_void_p * 5)(*[getattr(e, "cuda_event", e) for e in events])
         _check(_lib.m2_attn_step_timed(*self._args(kc, vc, pos, x, y, slot_ids, residual, ws, stream), ev))
+        return y
+
+
+M2_LAYER_MIXER, M2_LAYER_ATTN = 0, 1
+
+
+class StackLayer(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("layer", C.c_void_p), ("state", C.c_void_p), ("k_cache", C.c_void_p),
+                ("v_cache", C.c_void_p), ("pos", C.c_void_p)]
+
+
+class Stack:
+    """A hybrid layer stack (m2_stack) stepped by one call. entries: (Layer, State) for a
+    mixer, (Attn, (k_cache, v_cache, pos)) for an attention layer; references are kept."""
+
+    def __init__(self, entries, n_slots: int):
+        self.entries = list(entries)
+        table = (StackLayer * len(self.entries))()
+        d_model = None
+        for i, (lay, st) in enumerate(self.entries):
+            if isinstance(lay, Layer):
+                table[i] = StackLayer(M2_LAYER_MIXER, lay.handle.value, st.handle.value, None, None, None)
+            else:
+                kc, vc, pos = st
+                table[i] = StackLayer(M2_LAYER_ATTN, lay.handle.value, None, _ptr(kc), _ptr(vc), _ptr(pos))
+            d_model = lay.dims.d_model
+        self.d_model = d_model
+        self.device = self.entries[0][0].device
+        h = C.c_void_p()
+        _check(_lib.m2_stack_create(table, len(self.entries), n_slots, C.byref(h)))
+        self.handle = h
+        self._ws: Dict[int, torch.Tensor] = {}
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            _lib.m2_stack_destroy(h)
+            self.handle = None
+
+    def workspace(self, batch: int) -> torch.Tensor:
+        ws = self._ws.get(batch)
+        if ws is None:
+            n = int(_lib.m2_stack_workspace(self.handle, batch))
+            if n == 0:
+                raise M2Error(M2_ERR_SHAPE, "no workspace size for batch %d" % batch)
+            ws = self._ws[batch] = torch.empty(n, dtype=torch.uint8, device=self.device)
+        return ws
+
+    def step(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, slot_ids: Optional[torch.Tensor] = None,
+             ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """One token through every layer (residual chain); returns y [B][d_model]."""
+        B = x.shape[0]
+        _act(x, (B, self.d_model))
+        if y is None:
+            y = torch.empty_like(x)
+        _act(y, x.shape)
+        if slot_ids is not None:
+            _tokens(slot_ids, B)
+        if ws is None:
+            ws = self.workspace(B)
+        _check(_lib.m2_stack_step(self.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids), _ptr(ws), ws.numel(),
+                                  _stream(stream)))
         return y

@@ -200,6 +200,32 @@ ATTN_WORKLOADS: Dict[int, AttnWorkload] = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class StackWorkload:
+    """A hybrid stack stepped as one call: `pattern` lists the layers in order (M: Mamba-2
+    mixer, A: attention); attention caches hold `start_pos` positions when timing starts and
+    consecutive steps take consecutive sets of sessions (slot_sets sets)."""
+    name: str
+    mixer: MixerDims
+    attn: AttnDims
+    pattern: str
+    batch: int
+    steps: int
+    start_pos: int
+    slot_sets: int
+    seed: int = 0
+
+
+# 27 Mamba-2 mixers and 4 attention layers spread through the stack: a configured reading of
+# the 9B hybrid backbone (its MLP layers are not part of this path).
+HYBRID_9B_PATTERN = "MMMMMMMAMMMMMMMAMMMMMMMAMMMMMMA"
+
+STACK_WORKLOADS: Dict[int, StackWorkload] = {
+    9: StackWorkload("hybrid_27m4a_9b_bf16_b1_decode", NINE_B, ATTN_9B, HYBRID_9B_PATTERN, batch=1, steps=750,
+                     start_pos=1000, slot_sets=8, seed=9),
+}
+
+
 # The pages give no vocabulary size: 131072 rows per head is a configured reading, with the
 # function head taken to be a second head of the text head's shape.
 HEAD_WORKLOADS: Dict[int, HeadWorkload] = {

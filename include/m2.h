@@ -264,6 +264,38 @@ int m2_attn_step_timed(m2_attn a, void *k_cache, void *v_cache, int32_t *pos, in
                        const float *x, float *y, int32_t batch, const int32_t *slot_ids, int32_t flags,
                        void *ws, size_t ws_bytes, void *stream, void *const *events);
 
+/* A hybrid layer stack (blog page "NemotronLabs VoiceChat 11B" overview, "Key design
+ * decisions" item 2: Mamba layers alternate with attention layers) stepped by one call: a
+ * table of layers in order, each a mixer (m2_layer + its m2_state) or an attention layer
+ * (m2_attn + its KV cache and positions). One step for `batch` sessions is the residual
+ * chain u_0 = x, u_{l+1} = u_l + layer_l(u_l), y = u_L, enqueued layer by layer on `stream`
+ * (capturable into one graph by the caller). Every layer must have the same d_model; all
+ * layers' states and caches hold n_slots session slots addressed by the same slot ids. */
+enum { M2_LAYER_MIXER = 0, M2_LAYER_ATTN = 1 };
+
+typedef struct {
+  int32_t kind;             /* M2_LAYER_MIXER or M2_LAYER_ATTN */
+  void *layer;              /* m2_layer or m2_attn (borrowed) */
+  void *state;              /* mixer: its m2_state (borrowed); attention: NULL */
+  void *k_cache, *v_cache;  /* attention: the layer's caches, as m2_attn_step; mixer: NULL */
+  int32_t *pos;             /* attention: the layer's positions [n_slots]; mixer: NULL */
+} m2_stack_layer;
+
+typedef struct m2_stack_s *m2_stack;
+
+/* Copies the table (not what it points to). Errors: a NULL or unknown entry, layers of
+ * different d_model, a mixer state with fewer than n_slots slots. */
+int m2_stack_create(const m2_stack_layer *layers, int32_t n_layers, int32_t n_slots, m2_stack *out);
+void m2_stack_destroy(m2_stack s);
+
+/* Workspace bytes m2_stack_step needs for `batch` sessions: the largest of its layers'. */
+size_t m2_stack_workspace(m2_stack s, int32_t batch);
+
+/* One step of every layer in order for `batch` sessions: x, y fp32 [batch][d_model] (y may
+ * alias x); session b uses slot slot_ids[b] (device int32 [batch]) or b if NULL. */
+int m2_stack_step(m2_stack s, const float *x, float *y, int32_t batch, const int32_t *slot_ids, void *ws,
+                  size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

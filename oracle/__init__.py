@@ -315,3 +315,15 @@ class AttnLayer:
 
 def double_to_bf16(v: float) -> int:
     return int(lib().orc_double_to_bf16(float(v)))
+
+
+def stack_step(entries, x, slot_ids=None):
+    """A hybrid stack's step as the residual chain u_{l+1} = u_l + layer_l(u_l): entries are
+    (Layer, (ssm, conv)) or (AttnLayer, (kc, vc, pos)), their states updated in place."""
+    u = _f64(x)
+    for lay, st in entries:
+        if isinstance(lay, AttnLayer):
+            u = lay.step(st[0], st[1], st[2], u, slot_ids=slot_ids, residual=True)
+        else:
+            u = lay.step(st[0], st[1], u, slot_ids=slot_ids, residual=True)
+    return u

@@ -249,3 +249,45 @@ def test_attention_rejects_bad_configs_and_calls_without_launching():
     assert step(pos=FAKE + 2) == m2.M2_ERR_ALIGN and step(wn=need - 1) == m2.M2_ERR_WORKSPACE
     assert step(ws=FAKE + 8) == m2.M2_ERR_ALIGN
     L.m2_attn_destroy(h)
+
+
+def test_stack_rejects_bad_tables_and_calls_without_launching():
+    L = m2.lib()
+    rc, lay = create(GOOD)
+    assert rc == 0
+    st = C.c_void_p()
+    assert L.m2_state_create(lay, 2, FAKE, FAKE, C.byref(st)) == 0
+    ad = synth.AttnDims(d_model=256, n_q=4, n_kv=2, head_dim=64, max_len=64)
+    ah = C.c_void_p()
+    assert L.m2_attn_create(C.byref(m2.attn_config(ad)), C.byref(m2.AttnWeights(FAKE, None, FAKE, None)),
+                            C.byref(ah)) == 0
+    ah2 = C.c_void_p()
+    assert L.m2_attn_create(C.byref(m2.attn_config(ad.replace(d_model=512))),
+                            C.byref(m2.AttnWeights(FAKE, None, FAKE, None)), C.byref(ah2)) == 0
+    M = lambda: m2.StackLayer(m2.M2_LAYER_MIXER, lay.value, st.value, None, None, None)
+    A = lambda h=ah: m2.StackLayer(m2.M2_LAYER_ATTN, h.value, None, FAKE, FAKE, FAKE)
+
+    def make(entries, n_slots=2):
+        t = (m2.StackLayer * len(entries))(*entries)
+        h = C.c_void_p()
+        return L.m2_stack_create(t, len(entries), n_slots, C.byref(h)), h
+
+    assert make([M(), A(), M()])[0] == 0
+    assert make([M(), A(ah2)])[0] == m2.M2_ERR_SHAPE                     # d_model 256 then 512
+    assert make([M()], n_slots=3)[0] == m2.M2_ERR_SLOT                   # state holds 2 slots
+    assert make([m2.StackLayer(5, lay.value, st.value, None, None, None)])[0] == m2.M2_ERR_SHAPE
+    assert make([m2.StackLayer(m2.M2_LAYER_ATTN, ah.value, None, FAKE, None, FAKE)])[0] == m2.M2_ERR_NULL
+    assert make([m2.StackLayer(m2.M2_LAYER_MIXER, lay.value, None, None, None, None)])[0] == m2.M2_ERR_NULL
+    assert L.m2_stack_create(None, 1, 2, C.byref(C.c_void_p())) == m2.M2_ERR_SHAPE
+    rc, sh = make([M(), A(), M()])
+    need = L.m2_stack_workspace(sh, 2)
+    assert need == max(L.m2_step_workspace(lay, 2), L.m2_attn_workspace(ah, 2)) and need > 0
+    assert L.m2_stack_step(sh, FAKE, FAKE * 2, 3, None, FAKE, need, None) == m2.M2_ERR_SLOT
+    assert L.m2_stack_step(sh, FAKE, FAKE * 2, 2, None, FAKE, need - 1, None) == m2.M2_ERR_WORKSPACE
+    assert L.m2_stack_step(sh, FAKE + 4, FAKE * 2, 2, None, FAKE, need, None) == m2.M2_ERR_ALIGN
+    assert L.m2_stack_step(None, FAKE, FAKE * 2, 2, None, FAKE, need, None) == m2.M2_ERR_NULL
+    L.m2_stack_destroy(sh)
+    L.m2_attn_destroy(ah)
+    L.m2_attn_destroy(ah2)
+    L.m2_state_destroy(st)
+    L.m2_layer_destroy(lay)
