@@ -47,7 +47,8 @@ def parse():
                          "5 (int4 g64 weights, 1 session), 6 (int3 g64 weights, 1 session), "
                          "7 (text and function output heads with greedy argmax, 1 session), "
                          "8 (attention layer with a bf16 KV cache of 1000+ positions, 1 session), "
-                         "9 (hybrid stack of 27 Mamba-2 and 4 attention layers, one call per step, 1 session)")
+                         "9 (hybrid stack of 27 Mamba-2 and 4 attention layers, one call per step, 1 session), "
+                         "10 (attention layer, 32 sessions)")
     ap.add_argument("--copies", type=int, default=0,
                     help="identical weight copies used in turn (0: enough for >= 590 MB)")
     ap.add_argument("--no-graph", action="store_true", help="time plain launches only")

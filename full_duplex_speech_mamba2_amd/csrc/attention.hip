@@ -19,6 +19,7 @@
 // exponential is one exp2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -277,7 +278,7 @@ hipError_t launch_split_d(const AttnArgs &a, int hpg, hipStream_t stream) {
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct AttnWs {
-  float *qkv, *o, *part_o;
+  float *qkv, *o, *part_o, *gemv_part;
   float2 *part_ml;
   int *lens;
   size_t bytes;
@@ -298,6 +299,9 @@ AttnWs attn_ws_layout(const m2_attn_s &A, int B, void *base) {
   w.part_o = reinterpret_cast<float *>(take(sizeof(float) * (size_t)B * c.n_q * A.nsplit * c.head_dim));
   w.part_ml = reinterpret_cast<float2 *>(take(sizeof(float2) * (size_t)B * c.n_q * A.nsplit));
   w.lens = reinterpret_cast<int *>(take(sizeof(int) * (size_t)B));
+  const size_t gp = std::max(gemv_plain_part_bytes(c.wtype, c.q_group, A.qkv_rows, c.d_model, B),
+                             gemv_plain_part_bytes(c.wtype, c.q_group, c.d_model, A.o_dim, B));
+  w.gemv_part = gp ? reinterpret_cast<float *>(take(gp)) : nullptr;
   w.bytes = off;
   return w;
 }
@@ -319,7 +323,7 @@ hipError_t launch_attn_step(const m2_attn_s &A, uint16_t *kc, uint16_t *vc, int3
   hipError_t e = mark(0);
   if (e == hipSuccess)
     e = launch_gemv_plain(c.wtype, A.w.w_qkv, A.w.s_qkv, A.qkv_rows, c.d_model, c.q_group, c.q_gamma_qkv, x,
-                          batch, w.qkv, nullptr, stream);
+                          batch, w.qkv, nullptr, w.gemv_part, stream);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return e;
   AttnArgs a{};
@@ -351,7 +355,7 @@ hipError_t launch_attn_step(const m2_attn_s &A, uint16_t *kc, uint16_t *vc, int3
   if (e == hipSuccess) e = mark(3);
   if (e == hipSuccess)
     e = launch_gemv_plain(c.wtype, A.w.w_o, A.w.s_o, c.d_model, A.o_dim, c.q_group, c.q_gamma_o, w.o, batch, y,
-                          (flags & M2_RESIDUAL) ? x : nullptr, stream);
+                          (flags & M2_RESIDUAL) ? x : nullptr, w.gemv_part, stream);
   if (e == hipSuccess) e = mark(4);
   return e;
 }

@@ -1793,8 +1793,20 @@ hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, h
   return hipGetLastError();
 }
 
+bool gemv_plain_uses_mfma(int wtype, int q_group, int batch) {
+  if (batch < 3 || batch > 32) return false;
+  return wtype == M2_W_BF16 || (wtype == M2_W_INT8G && (q_group == 128 || q_group == 256));
+}
+
+size_t gemv_plain_part_bytes(int wtype, int q_group, int rows, int K, int batch) {
+  if (!gemv_plain_uses_mfma(wtype, q_group, batch)) return 0;
+  const MfmaPlan p = mfma_plan(rows, K, batch, 0);
+  return sizeof(float) * (size_t)p.ks * batch * rows;
+}
+
 hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, int K, int q_group, float gamma,
-                             const float *act, int batch, float *y, const float *resid, hipStream_t stream) {
+                             const float *act, int batch, float *y, const float *resid, float *part,
+                             hipStream_t stream) {
   const bool quantized = wtype == M2_W_INT8G || wtype == M2_W_INT4G || wtype == M2_W_INT3G;
   const int epc = wtype == M2_W_F32 ? 4 : wtype == M2_W_BF16 ? 8 : wtype == M2_W_INT8G ? 16 : 32;
   GemvArgs a{};
@@ -1810,6 +1822,27 @@ hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, 
   a.resid = resid;
   a.slots = nullptr;
   a.n_slots = batch;
+  // 3-32 sessions with bf16 (or int8 g128/g256) weights: the MFMA GEMV over K chunks, then
+  // the reduction with the plain epilogue (as the decode step's MFMA plan, without RMS).
+  if (gemv_plain_uses_mfma(wtype, q_group, batch)) {
+    const MfmaPlan p = mfma_plan(rows, K, batch, 0);
+    MfmaArgs m{};
+    m.W = W;
+    m.S = static_cast<const __half *>(S);
+    m.rows = rows;
+    m.K = K;
+    m.q_group = wtype == M2_W_INT8G ? q_group : K;
+    m.kchunk = p.kchunk;
+    m.act = act;
+    m.B = batch;
+    m.part = part;
+    hipError_t e = wtype == M2_W_BF16 ? launch_mfma<M2_W_BF16, false>(m, p, stream)
+                                      : launch_mfma<M2_W_INT8G, false>(m, p, stream);
+    if (e != hipSuccess) return e;
+    const int n = rows * batch;
+    hipLaunchKernelGGL(gemv_mfma_reduce_kernel<EPI_OUT>, dim3((n + 255) / 256), dim3(256), 0, stream, a, part, p.ks);
+    return hipGetLastError();
+  }
   // 1-2 sessions, 2- and 4-byte weights: the in_proj configuration (5 nontemporal loads in
   // flight); otherwise the decode step's choice for out_proj.
   if (batch <= 2 && (wtype == M2_W_BF16 || wtype == M2_W_F32) && wave_lds_bytes(a, batch, PRO_PLAIN) <= kWaveLdsMax) {

@@ -71,9 +71,13 @@ hipError_t launch_head(const m2_head_config &c, const void *w, const void *scale
                        hipEvent_t const *events = nullptr);
 
 // y[b] = gamma W act[b] (+ resid[b]) for a [rows][K] matrix in any weight format, with the
-// decode step's GEMV kernels (plain epilogue).
+// decode step's GEMV kernels (plain epilogue); `part` holds gemv_plain_part_bytes of
+// K-chunk partial sums when the MFMA GEMV is used (3-32 sessions, bf16 or int8 g128/g256).
+bool gemv_plain_uses_mfma(int wtype, int q_group, int batch);
+size_t gemv_plain_part_bytes(int wtype, int q_group, int rows, int K, int batch);
 hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, int K, int q_group, float gamma,
-                             const float *act, int batch, float *y, const float *resid, hipStream_t stream);
+                             const float *act, int batch, float *y, const float *resid, float *part,
+                             hipStream_t stream);
 
 // Attention decode step (m2_attn_step).
 int attn_nsplit(int max_len);

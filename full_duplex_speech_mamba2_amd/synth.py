@@ -197,6 +197,8 @@ class AttnWorkload:
 ATTN_WORKLOADS: Dict[int, AttnWorkload] = {
     8: AttnWorkload("attn_9b_bf16_b1_ctx1000_decode", ATTN_9B, batch=1, steps=750, start_pos=1000,
                     slot_sets=8, seed=8),
+    10: AttnWorkload("attn_9b_bf16_b32_ctx1000_decode", ATTN_9B, batch=32, steps=100, start_pos=1000,
+                     slot_sets=8, seed=10),
 }
 
 

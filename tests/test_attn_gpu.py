@@ -88,9 +88,10 @@ SMALL = synth.AttnDims(d_model=256, n_q=4, n_kv=2, head_dim=64, max_len=200)
 
 @pytest.mark.parametrize("batch", [1, 2, 3, 5])
 @pytest.mark.parametrize("wtype,q_group,gamma", [("f32", 16, 1.0), ("bf16", 16, 1.0), ("int8g", 64, 0.0625),
-                                                 ("int4g", 32, 1.0), ("int3g", 64, 1.0)])
+                                                 ("int8g", 128, 0.0625), ("int4g", 32, 1.0), ("int3g", 64, 1.0)])
 def test_attn_formats_and_chunk_edges(wtype, q_group, gamma, batch):
-    """Positions at and across the 64-position chunk edges (0, 1, 63, 64, 130); 3 steps."""
+    """Positions at and across the 64-position chunk edges (0, 1, 63, 64, 130); 3 steps. From
+    3 sessions, bf16 and int8 g128 projections take the MFMA GEMV."""
     d = SMALL.replace(wtype=wtype, q_group=q_group, q_gamma_qkv=gamma, q_gamma_o=gamma)
     pos = np.array([0, 63, 1, 130, 64][:batch], np.int32)
     w = synth.make_attn_weights(d, 21)
