@@ -29,6 +29,7 @@
 
 #include <climits>
 
+#include "lanes.h"
 #include "m2_internal.h"
 
 namespace m2d {
@@ -465,10 +466,7 @@ __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
     }
   }
 #pragma unroll
-  for (int bb = 0; bb < BT; ++bb) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc[bb] += __shfl_xor(acc[bb], off, 64);
-  }
+  for (int bb = 0; bb < BT; ++bb) acc[bb] = group_reduce<64>(acc[bb]);
   if (EPI == EPI_OUT && a.conv_cache)
     conv_cache_shift(a, (size_t)blockIdx.x * TPB + tid, (size_t)gridDim.x * TPB);
   if (!row_ok || lane >= nb) return;
@@ -656,8 +654,7 @@ __global__ __launch_bounds__(kLbThreads) void gemv_lowbit_kernel(GemvArgs a) {
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int bb = 0; bb < BT; ++bb)
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc[r][bb] += __shfl_xor(acc[r][bb], off, 64);
+        acc[r][bb] = group_reduce<64>(acc[r][bb]);
     if (lane < nb) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
@@ -767,10 +764,7 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
   }
 
 #pragma unroll
-  for (int bb = 0; bb < BT; ++bb) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) acc[bb] += __shfl_xor(acc[bb], off, 16);
-  }
+  for (int bb = 0; bb < BT; ++bb) acc[bb] = group_reduce<16>(acc[bb]);
   float val = 0.0f;
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb)
@@ -914,7 +908,7 @@ __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b,
     r = fmaf(sv.y, Cq.y, r);
     r = fmaf(sv.z, Cq.z, r);
     r = fmaf(sv.w, Cq.w, r);
-    for (int off = lpr >> 1; off >= 1; off >>= 1) r += __shfl_xor(r, off, 64);
+    r = group_sum_rt(r, lpr);
     if (q == 0 && p >= 0) {
       const int ch = h * a.P + p;
       const float yv = fmaf(Dh, xp, r);
@@ -930,7 +924,7 @@ __device__ __forceinline__ void ssd_item(const SsdArgs &a, int h, int ps, int b,
       if (prow[k] >= 0) st_stream(S + (size_t)prow[k] * lpr + q, st[k]);
   }
   // sum of squares of this item's rows, in a fixed order
-  for (int off = 32; off >= 1; off >>= 1) ssacc += __shfl_xor(ssacc, off, 64);
+  ssacc = group_reduce<64>(ssacc);
   if (lane == 0) wsum[wave] = ssacc;
   __syncthreads();
   if (wave == 0 && lane == 0) {
@@ -1168,9 +1162,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaArgs a) {
         const int b = pair / ngc, g = g0 + pair % ngc;
         for (int q = j; q < per; q += 8) sum += a.ss[(size_t)b * a.n_partials + g * per + q];
       }
-      sum += __shfl_xor(sum, 1, 8);
-      sum += __shfl_xor(sum, 2, 8);
-      sum += __shfl_xor(sum, 4, 8);
+      sum = group_reduce<8>(sum);
       if (pair < a.B * ngc && j == 0) rn_s[pair] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
     }
     __syncthreads();
@@ -1516,8 +1508,7 @@ __global__ __launch_bounds__(512) void head_wave_kernel(HeadArgs a) {
   }
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc[bb] += __shfl_xor(acc[bb], off, 64);
+    acc[bb] = group_reduce<64>(acc[bb]);
   }
   if (lane < BT) {
     float val = 0.0f;
