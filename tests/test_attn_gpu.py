@@ -166,3 +166,14 @@ def test_attn_timed_step_matches():
         outs.append((y.cpu(), kd.cpu(), pd.cpu()))
     assert all(torch.equal(a, b) for a, b in zip(*outs))
     assert all(ev[i].elapsed_time(ev[i + 1]) > 0 for i in range(4))
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_attn_long_cache_combines_more_than_32_chunks(batch):
+    """3000 positions = 47 chunks: the combine takes two passes of 32 chunks."""
+    d = synth.AttnDims(d_model=256, n_q=4, n_kv=1, head_dim=128, max_len=3000)
+    pos = np.array([2999, 2100, 40][:batch], np.int32)
+    w = synth.make_attn_weights(d, 40)
+    kc, vc = synth.make_kv_cache(d, 41, pos)
+    xs = synth.make_attn_inputs(d, 42, 2, batch)
+    _check("long", d, w, kc, vc, pos, xs)
