@@ -1,4 +1,5 @@
-/* CPU oracle for the Mamba-2 mixer layer: plain fp64 loops.
+/* CPU oracle for the Mamba-2 mixer layer (and, further below, the attention layer and
+ * the output heads of the same backbone): plain fp64 loops.
  *
  * TEST INFRASTRUCTURE ONLY. This code is the slow, obviously correct definition
  * that the HIP path is checked against. Only the tests, the smoke check and the
