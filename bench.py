@@ -199,7 +199,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
