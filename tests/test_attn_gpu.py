@@ -177,3 +177,14 @@ def test_attn_long_cache_combines_more_than_32_chunks(batch):
     kc, vc = synth.make_kv_cache(d, 41, pos)
     xs = synth.make_attn_inputs(d, 42, 2, batch)
     _check("long", d, w, kc, vc, pos, xs)
+
+
+@pytest.mark.parametrize("n_q,n_kv", [(4, 4), (16, 2)])
+def test_attn_group_sizes_d64(n_q, n_kv):
+    """head_dim 64: 8 lanes share a cache row (the half-row reductions), 1 and 8 query heads per group."""
+    d = synth.AttnDims(d_model=256, n_q=n_q, n_kv=n_kv, head_dim=64, max_len=200)
+    pos = np.array([0, 199, 64, 127], np.int32)
+    w = synth.make_attn_weights(d, 43)
+    kc, vc = synth.make_kv_cache(d, 44, pos)
+    xs = synth.make_attn_inputs(d, 45, 2, 4)
+    _check("d64", d, w, kc, vc, pos, xs)

@@ -131,3 +131,36 @@ def test_stack_graph_replays_match_eager_steps():
             _ = (xs * 2).sum().item()                       # eager work between replays
         outs.append(res + [ents[1][1][2].clone()])
     assert all(torch.equal(a, b) for a, b in zip(*outs))
+
+
+def test_stack_of_quantized_layers_matches_oracle_chain():
+    """int8 g64 mixers and 4-bit g32 attention layers in one stack (slots, 4 steps)."""
+    import torch
+    from full_duplex_speech_mamba2_amd import m2
+    mix = MIX.replace(wtype="int8g", q_group=64, q_gamma_in=0.0625, q_gamma_out=0.0625)
+    att = ATT.replace(wtype="int4g", q_group=32)
+    host, ents, olay = [], [], []
+    for i, k in enumerate("MAM"):
+        if k == "M":
+            w = synth.make_layer_weights(mix, 70, layer=i)
+            ssm, conv = synth.make_state(mix, 71, N_SLOTS, 0.1, layer=i)
+            lay = m2.Layer(mix, w)
+            ents.append((lay, m2.State(lay, N_SLOTS, torch.from_numpy(ssm).cuda(), torch.from_numpy(conv).cuda())))
+            ol = oracle.Layer(mix, w)
+            olay.append((ol, ol.new_state(N_SLOTS, ssm, conv)))
+        else:
+            w = synth.make_attn_weights(att, 72, layer=i)
+            kc, vc = synth.make_kv_cache(att, 73, POS0, layer=i)
+            ents.append((m2.Attn(att, w), (torch.from_numpy(kc.view(np.int16).copy()).cuda(),
+                                           torch.from_numpy(vc.view(np.int16).copy()).cuda(),
+                                           torch.from_numpy(POS0.copy()).cuda())))
+            olay.append((oracle.AttnLayer(att, w), (kc.copy(), vc.copy(), POS0.copy())))
+    stack = m2.Stack(ents, N_SLOTS)
+    xs = synth.make_inputs(mix, 74, 4, 2)
+    slots = np.array([1, 2], np.int32)
+    sd = torch.from_numpy(slots).cuda()
+    ys = [stack.step(torch.from_numpy(xs[t]).cuda(), slot_ids=sd).cpu().numpy() for t in range(xs.shape[0])]
+    yo = [oracle.stack_step(olay, xs[t], slot_ids=slots) for t in range(xs.shape[0])]
+    e = max(_rel(a, b) for a, b in zip(ys, yo))
+    print("[stack] quantized e_out=%.3e" % e, flush=True)
+    assert e <= 2e-3
