@@ -108,18 +108,32 @@ __global__ __launch_bounds__(kT) void attn_split_kernel(AttnArgs a) {
   const size_t cache_off = ((size_t)slot * a.Hk + g) * (size_t)a.max_len * D;
   const uint16_t *kg = a.kc + cache_off;
   const uint16_t *vg = a.vc + cache_off;
-  uint4 kr[PPT], vr[PPT];
+  // keys: LPP lanes per row (16 bytes each); values: each wave takes positions wave,
+  // wave + WPB, ... and each lane DPL dimensions of the row, so a load instruction reads one
+  // whole row and the weighted sum over positions stays in the lane
+  constexpr int DPL = D / 64, VPW = kC / WPB;
+  uint4 kr[PPT];
+  uint32_t vr[VPW];
 #pragma unroll
   for (int i = 0; i < PPT; ++i) {
     const int j = min(j0 + pg + NPG * i, p);          // past the last position: a valid row, masked below
     kr[i] = *reinterpret_cast<const uint4 *>(kg + (size_t)j * D + dg * 8);
-    vr[i] = *reinterpret_cast<const uint4 *>(vg + (size_t)j * D + dg * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < VPW; ++i) {
+    const int j = min(j0 + wave + WPB * i, p);
+    const uint16_t *vp = vg + (size_t)j * D + lane * DPL;
+    vr[i] = DPL == 2 ? *reinterpret_cast<const uint32_t *>(vp) : (uint32_t)*vp;
   }
   const float *qkv = a.qkv + (size_t)b * (a.Hq + 2 * a.Hk) * D;
   const float *kn = qkv + (size_t)(a.Hq + g) * D + dg * 8;
   const float *vn = kn + (size_t)a.Hk * D;
   const uint4 knew = pack8(*reinterpret_cast<const float4 *>(kn), *reinterpret_cast<const float4 *>(kn + 4));
   const uint4 vnew = pack8(*reinterpret_cast<const float4 *>(vn), *reinterpret_cast<const float4 *>(vn + 4));
+  const float *vnl = qkv + (size_t)(a.Hq + a.Hk + g) * D + lane * DPL;   // the new value, this lane's dims
+  float vfresh[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) vfresh[e] = __uint_as_float(to_bf16(vnl[e]) << 16);
   for (int i = tid; i < HPG * D; i += kT) qs[i / D][i % D] = qkv[(size_t)g * HPG * D + i] * a.scale;
   __syncthreads();
 
@@ -161,35 +175,32 @@ __global__ __launch_bounds__(kT) void attn_split_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // weighted values: the thread's 8 dimensions over its positions, then over position groups
-  float acc[HPG][8];
+  // weighted values: the lane's DPL dimensions over the wave's positions, then over the waves
+  float acc[HPG][DPL];
 #pragma unroll
   for (int h = 0; h < HPG; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int jl = pg + NPG * i, j = j0 + jl;
-    float vf[8];
-    unpack8(select4(j == p, vnew, vr[i]), vf);
+  for (int i = 0; i < VPW; ++i) {
+    const int jl = wave + WPB * i, j = j0 + jl;
+    float vf[DPL];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vf[e] = j <= p ? vf[e] : 0.0f;   // rows past p may hold anything
+    for (int e = 0; e < DPL; ++e) {
+      const float c = __uint_as_float(e == 0 ? vr[i] << 16 : vr[i] & 0xFFFF0000u);
+      vf[e] = j >= p ? vfresh[e] : c;             // the new row at p; past p (weight 0) also finite
+    }
 #pragma unroll
     for (int h = 0; h < HPG; ++h) {
       const float w = sc[h][jl];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
+      for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(w, vf[e], acc[h][e]);
     }
   }
 #pragma unroll
   for (int h = 0; h < HPG; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = across_groups_sum<LPP>(acc[h][e]);
-  if (lane < LPP)
-#pragma unroll
-    for (int h = 0; h < HPG; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[wave][h][lane * 8 + e] = acc[h][e];
+    for (int e = 0; e < DPL; ++e) red[wave][h][lane * DPL + e] = acc[h][e];
   __syncthreads();
   const size_t hq0 = (size_t)b * a.Hq + (size_t)g * HPG;
   for (int i = tid; i < HPG * D; i += kT) {
