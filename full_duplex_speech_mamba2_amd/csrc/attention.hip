@@ -32,6 +32,11 @@ namespace {
 constexpr int kC = 64;      // cache positions per split workgroup
 constexpr int kT = 256;     // threads per split workgroup
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 struct AttnArgs {
   const float *qkv;         // [B][(Hq + 2 Hk) D]
   uint16_t *kc, *vc;        // [n_slots][Hk][max_len][D] bf16 bits
@@ -52,47 +57,28 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ void unpack8(const uint4 &r, float *f) {
-  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
-
-__device__ __forceinline__ uint4 pack8(const float4 &a, const float4 &b) {
-  uint4 r;
-  r.x = to_bf16(a.x) | (to_bf16(a.y) << 16);
-  r.y = to_bf16(a.z) | (to_bf16(a.w) << 16);
-  r.z = to_bf16(b.x) | (to_bf16(b.y) << 16);
-  r.w = to_bf16(b.z) | (to_bf16(b.w) << 16);
-  return r;
-}
-
-__device__ __forceinline__ uint4 select4(bool c, const uint4 &a, const uint4 &b) {
-  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
-}
-
-// Thread layout: LPP = D/8 consecutive lanes share a cache row (8 bf16 = 16 bytes each, so
-// one load instruction of a wave reads 64/LPP whole rows); the workgroup's kT/LPP position
-// groups take positions pg, pg + NPG, ... of the chunk. Every cache load of a thread is
-// issued before anything else.
+// Scores on the matrix cores: wave w takes the chunk's positions 16w .. 16w + 15 as the A
+// operand of bf16 16x16x32 MFMAs (lane l holds 8 dimensions of position l % 16, octet l / 16,
+// loaded straight from the cache) and the group's queries as the B operand (head l % 16, the
+// same octet), split into bf16 hi and lo parts (q = hi + lo to 2^-16 relative; keys are exact
+// in bf16), two MFMAs per 32-dimension step; the product tile gives head l % 16 the scores
+// of positions 4 (l / 16) + r in register r. Values: each wave takes positions w, w + 4, ...
+// and each lane D/64 dimensions of a row, so a load instruction reads one whole row and the
+// weighted sum over positions stays in the lane. Every cache load is issued first.
 template <int D, int HPG>
 __global__ __launch_bounds__(kT) void attn_split_kernel(AttnArgs a) {
-  constexpr int LPP = D / 8;
-  constexpr int NPG = kT / LPP;
-  constexpr int PPT = kC / NPG;
-  constexpr int WPB = kT / 64;
-  static_assert(64 % LPP == 0 && kC % NPG == 0 && PPT >= 1, "layout");
-  __shared__ float qs[HPG][D];
+  constexpr int WPB = kT / 64, KS = D / 32;
+  constexpr int DPL = D / 64, VPW = kC / WPB;
+  static_assert(kC == 16 * WPB && HPG <= 16, "layout");
+  constexpr int QLD = D + 8;                         // padded row: 16 lanes hit distinct banks
   __shared__ float sc[HPG][kC];
   __shared__ float red[WPB][HPG][D];
   __shared__ float2 ml[HPG];
+  __shared__ unsigned short qhl[2][16][QLD];          // scaled queries as bf16 hi and lo, rows >= HPG zero
+  __shared__ unsigned short kns[D];                   // the new key in bf16
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int dg = tid % LPP, pg = tid / LPP;
   const int slot = a.slots ? a.slots[b] : b;
   const bool sok = slot >= 0 && slot < a.n_slots;
   const int p = sok ? a.pos[slot] : -1;
@@ -108,17 +94,13 @@ __global__ __launch_bounds__(kT) void attn_split_kernel(AttnArgs a) {
   const size_t cache_off = ((size_t)slot * a.Hk + g) * (size_t)a.max_len * D;
   const uint16_t *kg = a.kc + cache_off;
   const uint16_t *vg = a.vc + cache_off;
-  // keys: LPP lanes per row (16 bytes each); values: each wave takes positions wave,
-  // wave + WPB, ... and each lane DPL dimensions of the row, so a load instruction reads one
-  // whole row and the weighted sum over positions stays in the lane
-  constexpr int DPL = D / 64, VPW = kC / WPB;
-  uint4 kr[PPT];
-  uint32_t vr[VPW];
+  const int r16 = lane & 15, oct = lane >> 4;
+  const int jk = j0 + 16 * wave + r16;               // this lane's key row
+  u32x4v kr[KS];
 #pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int j = min(j0 + pg + NPG * i, p);          // past the last position: a valid row, masked below
-    kr[i] = *reinterpret_cast<const uint4 *>(kg + (size_t)j * D + dg * 8);
-  }
+  for (int ks = 0; ks < KS; ++ks)
+    kr[ks] = *reinterpret_cast<const u32x4v *>(kg + (size_t)min(jk, p) * D + 32 * ks + 8 * oct);
+  uint32_t vr[VPW];
 #pragma unroll
   for (int i = 0; i < VPW; ++i) {
     const int j = min(j0 + wave + WPB * i, p);
@@ -126,41 +108,46 @@ __global__ __launch_bounds__(kT) void attn_split_kernel(AttnArgs a) {
     vr[i] = DPL == 2 ? *reinterpret_cast<const uint32_t *>(vp) : (uint32_t)*vp;
   }
   const float *qkv = a.qkv + (size_t)b * (a.Hq + 2 * a.Hk) * D;
-  const float *kn = qkv + (size_t)(a.Hq + g) * D + dg * 8;
-  const float *vn = kn + (size_t)a.Hk * D;
-  const uint4 knew = pack8(*reinterpret_cast<const float4 *>(kn), *reinterpret_cast<const float4 *>(kn + 4));
-  const uint4 vnew = pack8(*reinterpret_cast<const float4 *>(vn), *reinterpret_cast<const float4 *>(vn + 4));
+  const float *kn = qkv + (size_t)(a.Hq + g) * D;                   // the new key
   const float *vnl = qkv + (size_t)(a.Hq + a.Hk + g) * D + lane * DPL;   // the new value, this lane's dims
+  // queries split by truncation (hi = the top 16 bits, lo = the top 16 bits of the rest:
+  // q = hi + lo to 2^-16 relative), the new key rounded to nearest even as it is stored
+  for (int i = tid; i < 16 * D; i += kT) {
+    const int h = i / D, d = i - h * D;
+    const float v = h < HPG ? qkv[(size_t)(g * HPG + h) * D + d] * a.scale : 0.0f;
+    const uint32_t hb = __float_as_uint(v) & 0xFFFF0000u;
+    qhl[0][h][d] = (unsigned short)(hb >> 16);
+    qhl[1][h][d] = (unsigned short)(__float_as_uint(v - __uint_as_float(hb)) >> 16);
+  }
+  for (int i = tid; i < D; i += kT) kns[i] = (unsigned short)to_bf16(kn[i]);
+  __syncthreads();
+  bf16x8 qhi[KS], qlo[KS];
+  u32x4v knew[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qhi[ks] = *reinterpret_cast<const bf16x8 *>(&qhl[0][r16][32 * ks + 8 * oct]);
+    qlo[ks] = *reinterpret_cast<const bf16x8 *>(&qhl[1][r16][32 * ks + 8 * oct]);
+    knew[ks] = *reinterpret_cast<const u32x4v *>(&kns[32 * ks + 8 * oct]);
+  }
   float vfresh[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) vfresh[e] = __uint_as_float(to_bf16(vnl[e]) << 16);
-  for (int i = tid; i < HPG * D; i += kT) qs[i / D][i % D] = qkv[(size_t)g * HPG * D + i] * a.scale;
-  __syncthreads();
 
-  // scores of the thread's positions for every query head of the group
-  float qv[HPG][8];
+  // scores: rows at and past p take the new key (finite; past p they are masked)
+  f32x4v c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int h = 0; h < HPG; ++h)
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4v kk = jk >= p ? knew[ks] : kr[ks];
+    const bf16x8 av = __builtin_bit_cast(bf16x8, kk);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qhi[ks], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qlo[ks], c, 0, 0, 0);
+  }
+  if (r16 < HPG) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[h][e] = qs[h][dg * 8 + e];
-#pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int jl = pg + NPG * i, j = j0 + jl;
-    float kf[8];
-    unpack8(select4(j == p, knew, kr[i]), kf);
-    float s[HPG];
-#pragma unroll
-    for (int h = 0; h < HPG; ++h) {
-      float t = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) t = fmaf(qv[h][e], kf[e], t);
-      s[h] = t;
+    for (int r = 0; r < 4; ++r) {
+      const int jl = 16 * wave + 4 * oct + r;
+      sc[r16][jl] = j0 + jl <= p ? c[r] : -INFINITY;
     }
-#pragma unroll
-    for (int h = 0; h < HPG; ++h) s[h] = group_reduce<LPP>(s[h]);
-    if (dg == 0)
-#pragma unroll
-      for (int h = 0; h < HPG; ++h) sc[h][jl] = j <= p ? s[h] : -INFINITY;
   }
   __syncthreads();
 
@@ -211,10 +198,21 @@ __global__ __launch_bounds__(kT) void attn_split_kernel(AttnArgs a) {
     a.part_o[((hq0 + h) * a.nsplit + split) * D + d] = v;
   }
   if (tid < HPG) a.part_ml[(hq0 + tid) * a.nsplit + split] = ml[tid];
-  // the chunk holding the session's position stores the new key and value there
-  if (p < j0 + kC && pg == 0) {
-    *reinterpret_cast<uint4 *>(a.kc + cache_off + (size_t)p * D + dg * 8) = knew;
-    *reinterpret_cast<uint4 *>(a.vc + cache_off + (size_t)p * D + dg * 8) = vnew;
+  // the chunk holding the session's position stores the new key (the lanes whose key row
+  // is p, 8 dimensions per step each) and the new value (wave 0, D/64 dimensions per lane)
+  if (jk == p) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      *reinterpret_cast<u32x4v *>(a.kc + cache_off + (size_t)p * D + 32 * ks + 8 * oct) = knew[ks];
+  }
+  if (p < j0 + kC && wave == 0) {
+    uint32_t vb = 0;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) vb |= (__float_as_uint(vfresh[e]) >> 16) << (16 * e);
+    if (DPL == 2)
+      *reinterpret_cast<uint32_t *>(a.vc + cache_off + (size_t)p * D + lane * 2) = vb;
+    else
+      a.vc[cache_off + (size_t)p * D + lane] = (uint16_t)vb;
   }
 }
 
