@@ -1053,7 +1053,12 @@ __device__ __forceinline__ void mfma_store_x(const MfmaArgs &a, int kt, int tid,
     const int b = i / (kMKT / 4), k4 = (i - b * (kMKT / 4)) * 4;
     f32x4 vv = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
     if (RMS) {
-      const float r = b < a.B ? rn_s[b * ngc + (kt + k4) / a.ng - g0] : 0.0f;
+      // Past the end of K (a ragged last tile) the activation is 0 and the group index
+      // would leave the chunk's groups (into the next session's factors, or LDS never
+      // written here); clamped, the factor is this session's own last one, so 0 * r is 0
+      // unless this very session's factors are NaN (an out-of-range slot).
+      const int gi = min((kt + k4) / a.ng - g0, ngc - 1);
+      const float r = b < a.B ? rn_s[b * ngc + gi] : 0.0f;
       vv *= r;
     }
     // hi = bf16(v) and lo = bf16(v - hi), both rounded to nearest even

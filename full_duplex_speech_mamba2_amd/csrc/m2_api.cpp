@@ -185,16 +185,18 @@ size_t m2_step_workspace(m2_layer layer, int32_t batch) {
   return m2d::step_ws_layout(*layer, batch, nullptr).bytes;
 }
 
+// A state made for one layer serves another of the same state shape.
+static bool same_state_shape(const m2_config &a, const m2_config &b) {
+  return a.n_heads == b.n_heads && a.head_dim == b.head_dim && a.d_state == b.d_state && a.n_groups == b.n_groups &&
+         a.d_conv == b.d_conv;
+}
+
 static int step_impl(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
                      const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream,
                      void *const *events) {
   if (!layer || !st) return fail(M2_ERR_NULL, "layer or state is NULL");
-  if (st->layer != layer) {
-    const m2_config &a = st->layer->cfg, &b = layer->cfg;
-    if (a.n_heads != b.n_heads || a.head_dim != b.head_dim || a.d_state != b.d_state ||
-        a.n_groups != b.n_groups || a.d_conv != b.d_conv)
-      return fail(M2_ERR_SHAPE, "state was created for a layer of another shape");
-  }
+  if (st->layer != layer && !same_state_shape(st->layer->cfg, layer->cfg))
+    return fail(M2_ERR_SHAPE, "state was created for a layer of another shape");
   if (!x || !y) return fail(M2_ERR_NULL, "x and y are required");
   if (!aligned16(x) || !aligned16(y)) return fail(M2_ERR_ALIGN, "x and y must be 16-byte aligned");
   if (batch <= 0) return fail(M2_ERR_SHAPE, "batch must be positive");
@@ -388,13 +390,20 @@ int m2_stack_create(const m2_stack_layer *layers, int32_t n_layers, int32_t n_sl
     const m2_stack_layer &l = layers[i];
     if (!l.layer) return fail(M2_ERR_NULL, "layer %d is NULL", i);
     int dm;
+    // every check a layer's step would make on its own arguments is made here, so that
+    // m2_stack_step cannot fail part-way through the chain (after earlier layers ran)
     if (l.kind == M2_LAYER_MIXER) {
       const m2_state st = static_cast<m2_state>(l.state);
       if (!st) return fail(M2_ERR_NULL, "mixer layer %d has no state", i);
       if (st->n_slots < n_slots) return fail(M2_ERR_SLOT, "mixer layer %d: state of %d slots", i, st->n_slots);
-      dm = static_cast<m2_layer>(l.layer)->cfg.d_model;
+      const m2_layer ml = static_cast<m2_layer>(l.layer);
+      if (!same_state_shape(st->layer->cfg, ml->cfg))
+        return fail(M2_ERR_SHAPE, "mixer layer %d: state was created for a layer of another shape", i);
+      dm = ml->cfg.d_model;
     } else if (l.kind == M2_LAYER_ATTN) {
       if (!l.k_cache || !l.v_cache || !l.pos) return fail(M2_ERR_NULL, "attention layer %d needs caches and pos", i);
+      if (!aligned16(l.k_cache) || !aligned16(l.v_cache) || (reinterpret_cast<uintptr_t>(l.pos) & 3u))
+        return fail(M2_ERR_ALIGN, "attention layer %d: caches must be 16-byte aligned, pos 4-byte aligned", i);
       dm = static_cast<m2_attn>(l.layer)->cfg.d_model;
     } else {
       return fail(M2_ERR_SHAPE, "layer %d: unknown kind %d", i, l.kind);
@@ -434,6 +443,7 @@ int m2_stack_step(m2_stack s, const float *x, float *y, int32_t batch, const int
   const size_t need = m2_stack_workspace(s, batch);
   if (!ws || ws_bytes < need)
     return fail(M2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+  if (!aligned16(ws)) return fail(M2_ERR_ALIGN, "workspace must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (x != y) {
     hipError_t e = hipMemcpyAsync(y, x, sizeof(float) * (size_t)batch * s->d_model, hipMemcpyDeviceToDevice, st);

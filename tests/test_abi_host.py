@@ -279,6 +279,19 @@ def test_stack_rejects_bad_tables_and_calls_without_launching():
     assert make([m2.StackLayer(m2.M2_LAYER_ATTN, ah.value, None, FAKE, None, FAKE)])[0] == m2.M2_ERR_NULL
     assert make([m2.StackLayer(m2.M2_LAYER_MIXER, lay.value, None, None, None, None)])[0] == m2.M2_ERR_NULL
     assert L.m2_stack_create(None, 1, 2, C.byref(C.c_void_p())) == m2.M2_ERR_SHAPE
+    # checks a layer's own step would make run at create, so a step never stops part-way
+    bad_kc = m2.StackLayer(m2.M2_LAYER_ATTN, ah.value, None, FAKE + 8, FAKE, FAKE)
+    bad_pos = m2.StackLayer(m2.M2_LAYER_ATTN, ah.value, None, FAKE, FAKE, FAKE + 2)
+    assert make([M(), A(), bad_kc])[0] == m2.M2_ERR_ALIGN                # misaligned cache in layer 2
+    assert make([M(), A(), bad_pos])[0] == m2.M2_ERR_ALIGN
+    rc, other = create(GOOD.replace(d_state=32))
+    assert rc == 0
+    st_other = C.c_void_p()
+    assert L.m2_state_create(other, 2, FAKE, FAKE, C.byref(st_other)) == 0
+    assert make([M(), m2.StackLayer(m2.M2_LAYER_MIXER, lay.value, st_other.value, None, None, None)])[0] \
+        == m2.M2_ERR_SHAPE                                                # state of another shape
+    L.m2_state_destroy(st_other)
+    L.m2_layer_destroy(other)
     rc, sh = make([M(), A(), M()])
     need = L.m2_stack_workspace(sh, 2)
     assert need == max(L.m2_step_workspace(lay, 2), L.m2_attn_workspace(ah, 2)) and need > 0
@@ -286,6 +299,7 @@ def test_stack_rejects_bad_tables_and_calls_without_launching():
     assert L.m2_stack_step(sh, FAKE, FAKE * 2, 2, None, FAKE, need - 1, None) == m2.M2_ERR_WORKSPACE
     assert L.m2_stack_step(sh, FAKE + 4, FAKE * 2, 2, None, FAKE, need, None) == m2.M2_ERR_ALIGN
     assert L.m2_stack_step(None, FAKE, FAKE * 2, 2, None, FAKE, need, None) == m2.M2_ERR_NULL
+    assert L.m2_stack_step(sh, FAKE, FAKE * 2, 2, None, FAKE + 4, need, None) == m2.M2_ERR_ALIGN
     L.m2_stack_destroy(sh)
     L.m2_attn_destroy(ah)
     L.m2_attn_destroy(ah2)

@@ -42,7 +42,8 @@ RAGGED = synth.MixerDims(d_model=272, n_heads=6, head_dim=24, d_state=32, n_grou
 @pytest.mark.parametrize("wtype", ["f32", "bf16", "int8g"])
 @pytest.mark.parametrize("variant", ["plain", "slots_residual", "norm_all", "conv2", "conv5_n64"])
 def test_ragged_shapes(wtype, variant, batch):
-    """Batches of 1 and 2 take the fused in_proj + SSD kernel, 3 the three-kernel plan."""
+    """Batches of 1 and 2 take the one-wave-per-row VALU GEMVs; 3 takes the MFMA GEMVs
+    (bf16 and int8 g16 here: int8 at q_group 16 stays on the tiled VALU GEMV)."""
     dims = RAGGED.replace(wtype=wtype, q_group=16, q_gamma_in=0.0625, q_gamma_out=0.1)
     B, slots, n_slots, residual, steps = batch, None, batch, False, 9
     if variant == "slots_residual":
@@ -123,6 +124,38 @@ def test_out_of_range_slot_gives_nan_and_touches_nothing():
     assert np.all(np.isfinite(yh[0])) and np.all(np.isnan(yh[1]))
     assert np.array_equal(st.ssm.cpu().numpy()[0], ssm0[0])
     assert np.array_equal(st.conv.cpu().numpy()[0], conv0[0])
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "int8g"])
+def test_mfma_bad_slot_leaves_neighbours_finite(wtype):
+    """bf16, 3 sessions: the MFMA plan with K = d_inner = 144, not a multiple of the 256-wide tile:
+    the out_proj activations past K are zero and their RMS factor must come from the same
+    session. A session on an out-of-range slot has NaN factors; its neighbours' outputs
+    stay finite and match the oracle, and its own are all NaN."""
+    import torch
+    from full_duplex_speech_mamba2_amd import m2
+    dims = RAGGED.replace(wtype=wtype, q_group=16)     # int8 g16: the tiled VALU GEMVs
+    w = synth.make_layer_weights(dims, 151)
+    xs = synth.make_inputs(dims, 152, 3, 3)
+    ssm0, conv0 = synth.make_state(dims, 153, 3, 0.1)
+    lay = m2.Layer(dims, w)
+    st = m2.State(lay, 3, torch.from_numpy(ssm0).cuda(), torch.from_numpy(conv0).cuda())
+    slots = np.array([0, 9, 1], np.int32)
+    sd = torch.from_numpy(slots).cuda()
+    xd = torch.from_numpy(xs).cuda()
+    yd = torch.empty_like(xd)
+    for t in range(xs.shape[0]):
+        m2.step(lay, st, xd[t], yd[t], slot_ids=sd)
+    torch.cuda.synchronize()
+    yg = yd.cpu().numpy()
+    assert np.all(np.isnan(yg[:, 1]))
+    good = [0, 2]
+    assert np.all(np.isfinite(yg[:, good]))
+    yo, so, co = oracle_decode(dims, w, xs, ssm0, conv0, slot_ids=slots, sessions=good)
+    eo = e_out(yg[:, good], yo)
+    es = e_state(st.ssm.cpu().numpy()[[0, 1]], so[[0, 1]])
+    print("[parity] mfma-bad-slot-%s plan=%d e_out=%.3e e_state=%.3e" % (wtype, lay.step_plan(3), eo, es), flush=True)
+    assert eo <= TOL_OUT and es <= TOL_STATE
 
 
 def test_state_zero_selected_slots():

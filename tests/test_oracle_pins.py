@@ -647,3 +647,74 @@ def test_attn_residual_full_cache_and_bad_slots():
     lay2, _, kc2, vc2, pos2 = _attn(ATT, [4, ATT.max_len, 2])
     y2 = lay2.step(kc2, vc2, pos2, x[[0, 3]], slot_ids=[0, 2])
     assert rel(y[[0, 3]] - x[[0, 3]], y2) < 1e-13
+
+
+# ---------------------------------------------------------------- the hybrid stack
+
+def _stack_parts(seed):
+    """An M-A-M chain on d_model 64: two mixers with their own weights and states, one
+    attention layer with its cache; 3 session slots, random states and caches."""
+    r = np.random.default_rng(seed)
+    m0, _ = _layer(SMALL_G2, seed=seed)
+    m2_, _ = _layer(SMALL_G2, seed=seed + 1)
+    att = oracle.AttnLayer(ATT, synth.make_attn_weights(ATT, seed + 2))
+    st0 = m0.new_state(3, r.standard_normal((3, 4, 8, 16)), r.standard_normal((3, 3, SMALL_G2.conv_dim)))
+    st2 = m2_.new_state(3, r.standard_normal((3, 4, 8, 16)), r.standard_normal((3, 3, SMALL_G2.conv_dim)))
+    kc, vc = synth.make_kv_cache(ATT, seed + 3, np.array([3, 0, 7], np.int32))
+    return [(m0, st0), (att, (kc, vc, np.array([3, 0, 7], np.int32))), (m2_, st2)]
+
+
+def _copy_parts(parts):
+    return [(lay, tuple(a.copy() for a in st)) for lay, st in parts]
+
+
+def test_stack_step_is_the_residual_chain_of_its_layers():
+    """oracle.stack_step against the chain written out: u1 = x + M0(x), u2 = u1 + A(u1),
+    y = u2 + M2(u2), each layer called on its own without the residual flag. The layers
+    differ, so a dropped residual or a permuted order gives another result (checked)."""
+    x = np.random.default_rng(40).standard_normal((3, SMALL_G2.d_model))
+    slots = np.array([1, 2, 0], np.int32)
+    parts = _stack_parts(41)
+    ref = _copy_parts(parts)
+    (m0, s0), (att, sa), (m2_, s2) = ref
+    u1 = x + m0.step(s0[0], s0[1], x, slot_ids=slots)
+    u2 = u1 + att.step(sa[0], sa[1], sa[2], u1, slot_ids=slots)
+    y_ref = u2 + m2_.step(s2[0], s2[1], u2, slot_ids=slots)
+    got = _copy_parts(parts)
+    y = oracle.stack_step(got, x, slot_ids=slots)
+    assert rel(y, y_ref) < 1e-14
+    for (_, a), (_, b) in zip(got, ref):            # every layer's state advanced the same way
+        for u, v in zip(a, b):
+            assert np.array_equal(u, v)
+    # the same layers without residuals, or in another order, give something else
+    alt = _copy_parts(parts)
+    (n0, t0), (nat, ta), (n2, t2) = alt
+    v = n0.step(t0[0], t0[1], x, slot_ids=slots)
+    v = nat.step(ta[0], ta[1], ta[2], v, slot_ids=slots)
+    v = n2.step(t2[0], t2[1], v, slot_ids=slots)
+    assert rel(v, y_ref) > 1e-2
+    rev = _copy_parts(parts)
+    assert rel(oracle.stack_step(rev[::-1], x, slot_ids=slots), y_ref) > 1e-2
+
+
+def test_stack_step_follows_the_slot_ids():
+    """Session b on slot perm[b] through every layer: permuting the sessions' inputs and
+    slot ids together permutes the outputs and leaves every state and cache the same."""
+    x = np.random.default_rng(42).standard_normal((3, SMALL_G2.d_model))
+    parts = _stack_parts(43)
+    a = _copy_parts(parts)
+    ya = oracle.stack_step(a, x)                     # identity slots
+    perm = np.array([2, 0, 1], np.int32)
+    b = _copy_parts(parts)
+    yb = oracle.stack_step(b, x[perm], slot_ids=perm)
+    assert np.array_equal(yb, ya[perm])
+    for (_, u), (_, v) in zip(a, b):
+        for p, q in zip(u, v):
+            assert np.array_equal(p, q)
+    # a slot id forwarded to one layer only (the others on identity) breaks the equality
+    c = _copy_parts(parts)
+    (m0, s0), (att, sa), (m2_, s2) = c
+    u = x[perm] + m0.step(s0[0], s0[1], x[perm], slot_ids=perm)
+    u = u + att.step(sa[0], sa[1], sa[2], u)
+    u = u + m2_.step(s2[0], s2[1], u, slot_ids=perm)
+    assert rel(u, ya[perm]) > 1e-2

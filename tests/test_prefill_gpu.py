@@ -117,3 +117,46 @@ def test_lowbit_prefill(wtype):
     x = synth.make_prompt(dims, 152, 2, 70)
     ssm0, conv0 = synth.make_state(dims, 153, 2, 0.1)
     _check("lowbit-%s" % wtype, dims, w, x, ssm0, conv0, 32)
+
+
+def test_prefill_dt_zero_keeps_state_and_A_to_minus_inf_resets_it():
+    """The chunked scan's limits through m2_prefill (37 tokens, chunks of 16, the last
+    partial), from a random state: dt = 0 (softplus underflows) makes every decay exp(0) = 1
+    and every input term 0, so the state is bitwise unchanged and y = C.S + D x; A -> -inf
+    makes every decay across tokens 0, so the final state is dt x B^T of the last token
+    alone, with no trace of the initial state or of earlier tokens."""
+    dims = SMALL
+    x = synth.make_prompt(dims, 161, 2, 37)
+    ssm0, conv0 = synth.make_state(dims, 162, 2, 0.1)
+    w = synth.make_layer_weights(dims, 163)
+    w["dt_bias"] = np.full(dims.n_heads, -1e4, np.float32)
+    yg, sg, cg, _ = gpu_prefill(dims, w, x, ssm0, conv0, 16)
+    assert np.array_equal(sg, ssm0)
+    yo, so, co = oracle_prefill(dims, w, x, ssm0, conv0)
+    eo, ec = e_out(yg, yo), e_conv(cg, co)
+    print("[parity] prefill dt=0 e_out=%.3e e_conv=%.3e" % (eo, ec), flush=True)
+    assert eo <= TOL_OUT and ec <= TOL_STATE
+
+    w2 = synth.make_layer_weights(dims, 163)
+    w2["A_log"] = np.full(dims.n_heads, np.log(1e30), np.float32)
+    yg2, sg2, cg2, _ = gpu_prefill(dims, w2, x, ssm0, conv0, 16)
+    yo2, so2, co2 = oracle_prefill(dims, w2, x, ssm0, conv0)
+    # the last token alone, from a zero state with the conv cache the first 36 tokens left,
+    # gives the same final state: nothing of the initial state or earlier tokens remains
+    cache36 = oracle_prefill(dims, w2, x[:, :-1], ssm0, conv0)[2]
+    _, so_last, _ = oracle_prefill(dims, w2, x[:, -1:], np.zeros_like(ssm0), cache36)
+    eo2, es2 = e_out(yg2, yo2), e_state(sg2, so2)
+    print("[parity] prefill A->-inf e_out=%.3e e_state=%.3e" % (eo2, es2), flush=True)
+    assert eo2 <= TOL_OUT and es2 <= 1e-5
+    assert e_state(so2, so_last) <= 1e-12
+
+
+@pytest.mark.parametrize("T", [255, 256, 257])
+def test_9b_prefill_chunk_edges_from_random_state(T):
+    """The 9B-shaped layer at one token short of, exactly at, and one past the 256-token
+    chunk, 2 sessions from random states and caches; every state element compared."""
+    dims = synth.NINE_B
+    w = synth.make_layer_weights(dims, 1)
+    x = synth.make_prompt(dims, 170 + T, 2, T)
+    ssm0, conv0 = synth.make_state(dims, 171, 2, 0.1)
+    _check("9b-T%d" % T, dims, w, x, ssm0, conv0, 256)
