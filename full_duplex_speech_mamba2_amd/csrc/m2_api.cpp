@@ -6,6 +6,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -191,9 +192,10 @@ static bool same_state_shape(const m2_config &a, const m2_config &b) {
          a.d_conv == b.d_conv;
 }
 
+// check_only: every argument check except the workspace's, then return without launching.
 static int step_impl(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
                      const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream,
-                     void *const *events) {
+                     void *const *events, bool check_only = false) {
   if (!layer || !st) return fail(M2_ERR_NULL, "layer or state is NULL");
   if (st->layer != layer && !same_state_shape(st->layer->cfg, layer->cfg))
     return fail(M2_ERR_SHAPE, "state was created for a layer of another shape");
@@ -204,6 +206,7 @@ static int step_impl(m2_layer layer, m2_state st, const float *x, float *y, int3
   if (flags & ~M2_RESIDUAL) return fail(M2_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   if (!(flags & M2_RESIDUAL) && x == y)
     return fail(M2_ERR_SHAPE, "y may alias x only with M2_RESIDUAL");
+  if (check_only) return M2_OK;
   const size_t need = m2_step_workspace(layer, batch);
   if (!ws || ws_bytes < need)
     return fail(M2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
@@ -225,6 +228,54 @@ int m2_step_timed(m2_layer layer, m2_state st, const float *x, float *y, int32_t
                   const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream,
                   void *const *events) {
   return step_impl(layer, st, x, y, batch, slot_ids, flags, ws, ws_bytes, stream, events);
+}
+
+// m2_step_noalloc's workspace: one array per GPU, in the code object's zero-filled device
+// memory, alive until the process ends. Host code never names it in a launch or a copy:
+// the array's name is a host-side stand-in, so every use goes through the device address
+// hipGetSymbolAddress returns, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[M2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_for_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(M2_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(M2_ERR_UNSUPPORTED, "device %d above %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(M2_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return M2_OK;
+}
+}  // namespace
+
+size_t m2_noalloc_scratch_bytes(void) { return M2_NOALLOC_SCRATCH_BYTES; }
+
+int m2_step_noalloc(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
+                    const int32_t *slot_ids, int32_t flags, void *stream) {
+  if (!layer || !st) return fail(M2_ERR_NULL, "layer or state is NULL");
+  if (batch <= 0) return fail(M2_ERR_SHAPE, "batch must be positive");
+  const size_t need = m2_step_workspace(layer, batch);
+  if (need > M2_NOALLOC_SCRATCH_BYTES)
+    return fail(M2_ERR_WORKSPACE, "a step of %d sessions needs %zu bytes of scratch; the static scratch holds %zu",
+                batch, need, (size_t)M2_NOALLOC_SCRATCH_BYTES);
+  // the host checks that need no device run first, so that a rejected call makes no HIP call
+  int rc = step_impl(layer, st, x, y, batch, slot_ids, flags, nullptr, 0, stream, nullptr, /*check_only=*/true);
+  if (rc != M2_OK) return rc;
+  void *ws = nullptr;
+  rc = scratch_for_current_device(&ws);
+  if (rc != M2_OK) return rc;
+  return step_impl(layer, st, x, y, batch, slot_ids, flags, ws, M2_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int m2_step_plan(m2_layer layer, int32_t batch) {

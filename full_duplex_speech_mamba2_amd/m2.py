@@ -73,6 +73,9 @@ _lib.m2_step_workspace.argtypes = [_P, _i32]
 _lib.m2_step_workspace.restype = C.c_size_t
 _lib.m2_step.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P]
 _lib.m2_step_timed.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P, _P]
+_lib.m2_step_noalloc.argtypes = [_P, _P, _P, _P, _i32, _P, _i32, _P]
+_lib.m2_step_noalloc.restype = C.c_int
+_lib.m2_noalloc_scratch_bytes.restype = C.c_size_t
 _lib.m2_step_plan.argtypes = [_P, _i32]
 _lib.m2_step_plan.restype = C.c_int
 _lib.m2_prefill_workspace.argtypes = [_P, _i32, _i32, _i32]
@@ -251,6 +254,24 @@ def step(layer: Layer, state: State, x: torch.Tensor, y: Optional[torch.Tensor] 
     _check(_lib.m2_step(layer.handle, state.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids),
                         M2_RESIDUAL if residual else 0, _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def step_noalloc(layer: Layer, state: State, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                 slot_ids: Optional[torch.Tensor] = None, residual: bool = False, stream=None) -> torch.Tensor:
+    """step() through m2_step_noalloc: the library's static per-GPU scratch serves as the
+    workspace (no workspace tensor); returns y [B][d_model]."""
+    B = x.shape[0]
+    _act(x, (B, layer.dims.d_model))
+    if y is None:
+        y = torch.empty_like(x)
+    _act(y, x.shape)
+    _check(_lib.m2_step_noalloc(layer.handle, state.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids),
+                                M2_RESIDUAL if residual else 0, _stream(stream)))
+    return y
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(_lib.m2_noalloc_scratch_bytes())
 
 
 def step_timed(layer: Layer, state: State, x: torch.Tensor, y: torch.Tensor, events,

@@ -156,6 +156,20 @@ int m2_step_timed(m2_layer layer, m2_state st, const float *x, float *y, int32_t
                   const int32_t *slot_ids, int32_t flags, void *ws, size_t ws_bytes, void *stream,
                   void *const *events);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): m2_step with no workspace argument. Its
+ * workspace is a static device array of M2_NOALLOC_SCRATCH_BYTES per GPU, held by the
+ * library until the process ends and shared by every call on that GPU; the first call on a
+ * device looks up the array's device address (no allocation). It makes no allocating call.
+ * Steps whose m2_step_workspace exceeds the array fail with M2_ERR_WORKSPACE (at the 9B
+ * shape: up to 32 sessions fit). Calls that overlap on one GPU (other streams, other
+ * threads) race on the array: serialise them. Arguments, results and errors otherwise as
+ * m2_step. */
+#define M2_NOALLOC_SCRATCH_BYTES (16u << 20)
+size_t m2_noalloc_scratch_bytes(void);
+int m2_step_noalloc(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
+                    const int32_t *slot_ids, int32_t flags, void *stream);
+
 /* How m2_step runs `batch` sessions. Both plans have three phases, the ones
  * m2_step_timed's events delimit: in_proj | conv + SSD update + readout + gate |
  * RMSNorm + out_proj.

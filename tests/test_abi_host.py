@@ -305,3 +305,25 @@ def test_stack_rejects_bad_tables_and_calls_without_launching():
     L.m2_attn_destroy(ah2)
     L.m2_state_destroy(st)
     L.m2_layer_destroy(lay)
+
+
+def test_step_noalloc_rejects_without_launching():
+    """m2_step_noalloc makes its host checks (including the scratch size) before any HIP
+    call: at the 9B shape 200 sessions need more than the static scratch."""
+    L = m2.lib()
+    assert L.m2_noalloc_scratch_bytes() == 16 << 20
+    rc, lay = create(synth.NINE_B)
+    assert rc == 0
+    st = C.c_void_p()
+    assert L.m2_state_create(lay, 300, FAKE, FAKE, C.byref(st)) == 0
+    assert L.m2_step_workspace(lay, 200) > L.m2_noalloc_scratch_bytes() >= L.m2_step_workspace(lay, 32)
+    assert L.m2_step_noalloc(lay, st, FAKE, FAKE * 2, 200, None, 0, None) == m2.M2_ERR_WORKSPACE
+    assert b"scratch" in L.m2_last_error()
+    assert L.m2_step_noalloc(None, st, FAKE, FAKE * 2, 1, None, 0, None) == m2.M2_ERR_NULL
+    assert L.m2_step_noalloc(lay, st, FAKE, FAKE * 2, 0, None, 0, None) == m2.M2_ERR_SHAPE
+    assert L.m2_step_noalloc(lay, st, FAKE + 4, FAKE * 2, 1, None, 0, None) == m2.M2_ERR_ALIGN
+    assert L.m2_step_noalloc(lay, st, FAKE, FAKE, 1, None, 0, None) == m2.M2_ERR_SHAPE     # y aliases x
+    assert L.m2_step_noalloc(lay, st, FAKE, FAKE * 2, 1, None, 4, None) == m2.M2_ERR_UNSUPPORTED
+    assert L.m2_step_noalloc(lay, st, FAKE, FAKE * 2, 301, None, 0, None) == m2.M2_ERR_WORKSPACE
+    L.m2_state_destroy(st)
+    L.m2_layer_destroy(lay)
