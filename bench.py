@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0,
                     help="identical weight copies used in turn (0: enough for >= 590 MB)")
     ap.add_argument("--no-graph", action="store_true", help="time plain launches only")
+    ap.add_argument("--persistent", action="store_true",
+                    help="single-layer decode workloads: plan 2 (the persistent SSD + out_proj kernel)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity")
     ap.add_argument("--prof-steps", type=int, default=200, help="steps of the per-kernel event pass")
@@ -137,13 +139,56 @@ def hold_gpu(ms: float) -> None:
     torch.cuda._sleep(int(ms * 2.4e6))          # cycles at 2.4 GHz
 
 
-def graph_ms_per_step(run, steps, launches_per_step, before_replay=None):
-    """Milliseconds per step of `steps` steps replayed from HIP graphs. The steps are captured
-    as one graph of at most ~16k launches (replayed as often as it fits) plus one graph for
-    the remainder, so a deep stack does not build a graph of hundreds of thousands of
-    nodes. before_replay (untimed) runs before the warm replay and before the timed one."""
+REPEATS = 5
+
+
+def hold_ms(steps):
+    """Length of the spin kernel that precedes a timed region: long enough for the host to
+    enqueue `steps` steps behind it (about 40 us of host time per step, at least 5 ms)."""
+    return max(5.0, 0.04 * steps)
+
+
+def eager_ms_per_step(run, t0, steps, before=None):
+    """Median over REPEATS of the milliseconds per step of `steps` plain-launch steps, each
+    repeat bracketed by events on torch's current stream (where the steps run), the GPU held
+    by a spin kernel while the host enqueues them. Returns (median, all repeats)."""
+    import numpy as np
     import torch
-    chunk = max(1, min(steps, 16384 // max(1, launches_per_step)))
+    out = []
+    for _ in range(REPEATS):
+        if before:
+            before()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_gpu(hold_ms(steps))
+        e0.record()
+        run(t0, steps)
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return float(np.median(out)), out
+
+
+# Launches per captured graph. A graph of ~294k kernel nodes (3000 steps of a 31-layer stack)
+# ended the process in a host segmentation fault during capture: the host-side graph grows
+# by a node object (with its kernel arguments copied) per captured launch, plus the
+# dependency edges, so one graph of that size holds several GB of host structures in the
+# runtime; the stack is captured in graphs of at most this many launches instead, replayed
+# in turn, and a larger request is refused with an error rather than attempted.
+MAX_GRAPH_LAUNCHES = 16384
+
+
+def graph_ms_per_step(run, steps, launches_per_step, before_replay=None):
+    """Median over REPEATS of the milliseconds per step of `steps` steps replayed from HIP
+    graphs. The steps are captured as graphs of at most MAX_GRAPH_LAUNCHES launches
+    (replayed as often as they fit) plus one for the remainder. before_replay (untimed) runs
+    before the warm replay and before every timed one. Returns (median, all repeats)."""
+    import numpy as np
+    import torch
+    if launches_per_step > MAX_GRAPH_LAUNCHES:
+        raise ValueError("one step has %d launches, above the %d a captured graph may hold"
+                         % (launches_per_step, MAX_GRAPH_LAUNCHES))
+    chunk = max(1, min(steps, MAX_GRAPH_LAUNCHES // max(1, launches_per_step)))
     reps, rem = divmod(steps, chunk)
 
     def capture(n):
@@ -168,15 +213,19 @@ def graph_ms_per_step(run, steps, launches_per_step, before_replay=None):
     if before_replay:
         before_replay()
     replay_all()
-    if before_replay:
-        before_replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    replay_all()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    out = []
+    for _ in range(REPEATS):
+        if before_replay:
+            before_replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_gpu(hold_ms(reps + 1))
+        e0.record()
+        replay_all()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return float(np.median(out)), out
 
 
 def traffic_for(kernel_name, workload):
@@ -256,7 +305,7 @@ def main():
     def run(t0, n):
         for t in range(t0, t0 + n):
             if wl.layers == 1:
-                m2.step(layers[t % nl], st, xs[t % nx], ys[t % nx], ws=ws)
+                m2.step(layers[t % nl], st, xs[t % nx], ys[t % nx], ws=ws, persistent=args.persistent)
             else:
                 u = ys[t % nx]
                 u.copy_(xs[t % nx])
@@ -267,23 +316,17 @@ def main():
     run(0, args.warmup)
     torch.cuda.synchronize()
 
-    # timed region 1: plain launches on torch's current stream
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    run(args.warmup, args.steps)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_eager = e0.elapsed_time(e1) / args.steps
+    # timed region 1: plain launches on torch's current stream (median of REPEATS)
+    ms_eager, rep_eager = eager_ms_per_step(run, args.warmup, args.steps)
 
     # timed region 2: the same steps captured into HIP graphs and replayed
-    ms_graph = None
+    ms_graph, rep_graph = None, None
     if not args.no_graph:
-        ms_graph = graph_ms_per_step(run, args.steps, 4 * wl.layers)
+        ms_graph, rep_graph = graph_ms_per_step(run, args.steps, 4 * wl.layers)
 
     ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
     steps_per_s = 1000.0 / ms
-    plan = layers[0].step_plan(B)
+    plan = layers[0].step_plan(B, persistent=args.persistent)
     kb = kernel_bytes(dims, B)
 
     # per-kernel durations: HIP events recorded between the step's kernels on the stream they
@@ -296,11 +339,19 @@ def main():
     for t in range(kp):
         # per-kernel times of one layer (the stack's first layer, residual as in the stack)
         m2.step_timed(layers[t % nl] if wl.layers == 1 else layers[0], st, xs[t % nx], ys[t % nx], evs[t],
-                      residual=wl.layers > 1, ws=ws)
+                      residual=wl.layers > 1, ws=ws, persistent=args.persistent and wl.layers == 1)
     torch.cuda.synchronize()
-    names = PHASES
-    dur_us = {n: 1000.0 * float(np.mean([hip_elapsed_ms(hip, evs[t][i], evs[t][i + 1]) for t in range(kp)]))
-              for i, n in enumerate(names)}
+    if plan == 2:
+        # in_proj, then the SSD and out_proj in one persistent kernel
+        names = ["gemv_in", "ssd_out_fused"]
+        kb["ssd_out_fused"] = kb["ssd_step"] + kb["gemv_out"]
+        dur_us = {"gemv_in": 1000.0 * float(np.mean([hip_elapsed_ms(hip, evs[t][0], evs[t][1]) for t in range(kp)])),
+                  "ssd_out_fused": 1000.0 * float(np.mean([hip_elapsed_ms(hip, evs[t][1], evs[t][3])
+                                                           for t in range(kp)]))}
+    else:
+        names = PHASES
+        dur_us = {n: 1000.0 * float(np.mean([hip_elapsed_ms(hip, evs[t][i], evs[t][i + 1]) for t in range(kp)]))
+                  for i, n in enumerate(names)}
     for row in evs:
         for e in row:
             hip.hipEventDestroy(e)
@@ -328,7 +379,11 @@ def main():
         "session_tokens_per_s": round(B * steps_per_s, 1),
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
+        "repeats_ms_per_step": {"eager": [round(v, 5) for v in rep_eager],
+                                "graph": None if rep_graph is None else [round(v, 5) for v in rep_graph],
+                                "statistic": "median of %d repeats of %d steps" % (REPEATS, args.steps)},
         "kernel_us": {n: round(v, 2) for n, v in dur_us.items()},
+        "kernel_us_source": "HIP events on the kernels' stream, mean over %d steps" % kp,
         "roofline": roofline,
         "cpu_baseline": None,
         "parity": None,
@@ -380,15 +435,10 @@ def bench_heads(args, wl):
 
     run(0, args.warmup)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    run(args.warmup, args.steps)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_eager = e0.elapsed_time(e1) / args.steps
+    ms_eager, _ = eager_ms_per_step(run, args.warmup, args.steps)
     ms_graph = None
     if not args.no_graph:
-        ms_graph = graph_ms_per_step(run, args.steps, 2 * len(heads))
+        ms_graph, _ = graph_ms_per_step(run, args.steps, 2 * len(heads))
     ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
     fps = 1000.0 / ms
 
@@ -522,17 +572,12 @@ def bench_attn(args, wl):
     run(0, min(args.warmup, S * (d.max_len - wl.start_pos)))
     pos.copy_(pos0)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    run(0, args.steps)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_eager = e0.elapsed_time(e1) / args.steps
+    ms_eager, _ = eager_ms_per_step(run, 0, args.steps, before=lambda: pos.copy_(pos0))
     if not bool(torch.isfinite(ys[:min(nx, args.steps)]).all()):
         raise SystemExit("attention bench: a session ran out of cache positions (NaN outputs)")
     ms_graph = None
     if not args.no_graph:
-        ms_graph = graph_ms_per_step(run, args.steps, 4, before_replay=lambda: pos.copy_(pos0))
+        ms_graph, _ = graph_ms_per_step(run, args.steps, 4, before_replay=lambda: pos.copy_(pos0))
     ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
     sps = 1000.0 / ms
     mean_len = wl.start_pos + 1 + (args.steps / S - 1) / 2.0
@@ -668,18 +713,13 @@ def bench_stack(args, wl):
     run(0, min(args.warmup, S * (wl.attn.max_len - wl.start_pos)))
     reset()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    run(0, args.steps)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_eager = e0.elapsed_time(e1) / args.steps
+    ms_eager, _ = eager_ms_per_step(run, 0, args.steps, before=reset)
     if not bool(torch.isfinite(ys[:min(nx, args.steps)]).all()):
         raise SystemExit("stack bench: non-finite outputs")
     print("[bench] eager %.3f ms/step; capturing graphs" % ms_eager, file=sys.stderr, flush=True)
     ms_graph = None
     if not args.no_graph:
-        ms_graph = graph_ms_per_step(run, args.steps, 4 * len(wl.pattern) + 1, before_replay=reset)
+        ms_graph, _ = graph_ms_per_step(run, args.steps, 4 * len(wl.pattern) + 1, before_replay=reset)
     print("[bench] graph %s ms/step" % ms_graph, file=sys.stderr, flush=True)
     ms = min(ms_eager, ms_graph) if ms_graph is not None else ms_eager
     sps = 1000.0 / ms
@@ -773,6 +813,44 @@ def time_prefill(args, wl, layer, st, dev):
             "workspace_bytes": int(ws.numel())}
 
 
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def single_thread_oracle(lay, wl, xs_np, ssm0, conv0):
+    """The oracle on one thread: the whole tiny workload (16 steps) and one step of this
+    workload, each timed once; the thread count is restored afterwards."""
+    import numpy as np
+    import oracle
+    from full_duplex_speech_mamba2_amd import synth
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        tw = synth.workload(0)
+        tl = oracle.Layer(tw.dims, synth.make_layer_weights(tw.dims, tw.weight_seed))
+        ts, tc = tl.new_state(tw.batch)
+        txs = synth.make_inputs(tw.dims, tw.seed, tw.steps, tw.batch)
+        t0 = time.perf_counter()
+        for t in range(tw.steps):
+            tl.step(ts, tc, txs[t])
+        tiny = time.perf_counter() - t0
+        so, co = lay.new_state(wl.batch, ssm0, conv0)
+        t0 = time.perf_counter()
+        lay.step(so, co, xs_np[0])
+        one = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
+    return {"tiny_16_steps_s": round(tiny, 5), "tiny_steps_per_s": round(tw.steps / tiny, 1),
+            "one_step_s": round(one, 4), "steps_per_s": round(1.0 / one, 3), "threads": 1}
+
+
 def cpu_baseline_and_parity(args, wl, w, xs_np, ssm0, conv0):
     """Time the oracle on the first steps of the workload (bounded by --cpu-seconds) and compare
     the GPU path's outputs for those steps, from the same initial state, with it."""
@@ -793,9 +871,10 @@ def cpu_baseline_and_parity(args, wl, w, xs_np, ssm0, conv0):
         n += 1
     wall = time.perf_counter() - t0
     base = {"value": round(n / wall, 3), "unit": "steps/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "first %d decode steps of %s (batch %d), fp64 C oracle, %.1f s wall"
                       % (n, wl.name, B, wall)}
+    base["single_thread"] = single_thread_oracle(lay, wl, xs_np, ssm0, conv0)
 
     gl = m2.Layer(dims, w)
     gs = m2.State(gl, B, torch.from_numpy(ssm0).cuda(), torch.from_numpy(conv0).cuda())

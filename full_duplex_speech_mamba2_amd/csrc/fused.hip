@@ -1,0 +1,366 @@
+// SSD and out_proj of the decode step in one persistent launch, on gfx950 (one session,
+// bf16 weights): the step's plan 2, after the in_proj GEMV of decode.hip.
+//
+// The step is bound by streaming the two projection matrices from HBM (page
+// "NemotronLabs VoiceChat 11B: GPTQ 3-bit LLM, MLX", introduction: the LLM step is limited
+// by memory bandwidth). With one kernel for the SSD update and one for out_proj, the HBM
+// stream stops between in_proj and out_proj for the whole SSD kernel, a short kernel bound
+// by the latency of its state loads, and again while out_proj's first loads are in flight.
+// Here the workgroups of one kernel, all resident at once (two per CU), issue the loads of
+// their SSD item (state tile, gate and conv inputs), then the first third of their out_proj
+// weights, which stream in while the item is computed; they arrive at one grid-wide barrier
+// (the SSD's output v and its sums of squares complete), issue the second third while they
+// wait, and finish out_proj. (Loads complete in issue order as far as a wave's wait counts
+// go, so weights requested before the item's own inputs would delay the item.)
+//
+//   SSD      workgroup w takes item w (head, range of head rows) as the three-kernel step's
+//            SSD kernel does; its barriers order LDS only, so the weight loads stay in
+//            flight; v and the sums of squares are stored past the per-XCD caches; the
+//            updated state tile is written after the workgroup has arrived at the barrier
+//            (nothing in the launch reads it again).
+//   out_proj workgroup w owns a contiguous block of at most 9 rows and wave j of it the j-th
+//            eighth of every row's chunks, so every wave moves the same bytes; v is staged
+//            with coalesced loads past the caches, scaled by its RMS factor, into LDS; the 8
+//            waves' row sums meet in LDS and are added in a fixed order; the conv-cache
+//            shift runs here too (the SSD, its last reader, has finished).
+//
+// Grid barrier: each wave waits for its stores to complete and counts itself in LDS; wave 0
+// then adds the workgroup's arrival to a global counter (zeroed by the in_proj kernel before
+// this launch), polls it and releases the other waves through an LDS flag, so only wave 0
+// waits on memory. The data crossing the barrier bypasses the per-XCD caches (loads and
+// stores with the sc1 policy), so no cache write-back or invalidation is needed. Every wait
+// is bounded: were the grid not all resident the kernel would still finish (and raise a
+// flag) instead of hanging. Measured forms, not kept: the in_proj GEMV in the same kernel
+// (a third phase, a second barrier) ran at 5 TB/s against 6.3 for its own kernel, since a
+// persistent grid's fixed row assignment leaves slow waves no one takes work from; and
+// barriers that wrote back and invalidated the L2 (plain accesses to the shared data).
+#include "decode_common.h"
+
+namespace m2d {
+namespace {
+
+constexpr int kFThreads = 512;
+constexpr int kFWaves = kFThreads / 64;
+constexpr int kFJC = 3;        // out_proj: chunks per lane of a wave's eighth of a row (<= 192 chunks)
+constexpr int kFRB = 3;        // out_proj: rows per batch of loads
+constexpr int kFRMax = 9;      // out_proj: rows per workgroup (3 batches)
+constexpr int kFMaxI = 2;      // SSD: state slices per wave (items of up to 16 wave instructions)
+constexpr int kFGroups = 4;    // out_proj: RMS groups an eighth of a row may touch
+// Bounds of the barrier waits, in polls: LDS polls take ~0.1 us, global ones about a memory
+// latency (~1 us); a wave waiting on LDS outlasts wave 0's two waits together.
+constexpr unsigned kLdsSpin = 1u << 22;
+constexpr unsigned kGlobalSpin = 1u << 18;
+constexpr int kBufOutOfRange = 0x7ffffff0;   // a buffer offset past every resource: the load returns 0
+
+typedef float f32x4b __attribute__((ext_vector_type(4)));
+
+struct FusedArgs {
+  GemvArgs go;
+  SsdArgs sa;
+  unsigned *bar;       // [0] workgroups arrived (zeroed before the launch); [1] set if a wait ran out
+  int items;           // SSD items: H * psplit (one session)
+};
+
+struct BarCtl {
+  unsigned arrived;    // waves 1..7 arrived, counted over the launch
+  unsigned go;         // number of the last barrier wave 0 has passed
+};
+
+// LDS words polled by the waves of one workgroup (relaxed atomics, so that they stay LDS
+// instructions and a poll never waits for the wave's global loads in flight)
+__device__ __forceinline__ unsigned lds_load(unsigned *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Grid-wide barrier number `gen` of the launch: every global store a wave made before it is
+// complete before any wave passes it. `after_arrival()` is called once by every wave after
+// its workgroup's arrival is counted, before the wave waits -- except wave 0, which polls
+// memory (each poll waits for all of the wave's earlier memory operations): it calls it
+// once the barrier is passed.
+template <typename F>
+__device__ __forceinline__ void grid_barrier(const FusedArgs &f, BarCtl *ctl, unsigned gen, int wave, int lane,
+                                             F &&after_arrival) {
+  // this wave's stores complete: a workgroup-scope release does not wait for them (waves of
+  // a workgroup share the L1), and an agent-scope one would also write back the L2, which
+  // data stored past the caches does not need; so an explicit wait for every counter
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (wave != 0) {
+    if (lane == 0) __hip_atomic_fetch_add(&ctl->arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    after_arrival();
+    for (unsigned n = 0; lds_load(&ctl->go) < gen && n < 4 * kLdsSpin; ++n) __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return;
+  }
+  for (unsigned n = 0; lds_load(&ctl->arrived) < gen * (kFWaves - 1) && n < kLdsSpin; ++n)
+    __builtin_amdgcn_s_sleep(1);
+  if (lane == 0) __hip_atomic_fetch_add(f.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) {
+    const unsigned target = gen * gridDim.x;
+    unsigned n = 0;
+    while (__hip_atomic_load(f.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      if (++n > kGlobalSpin) {
+        __hip_atomic_store(f.bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (lane == 0) __hip_atomic_store(&ctl->go, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  after_arrival();
+}
+
+// ---------------------------------------------------------------------------
+// out_proj rows [r0, r0 + nr) of this workgroup, this wave's chunks [s0, s1) of them. The
+// weights are read through a buffer resource over W_out: a row past the block or a chunk
+// past the eighth takes an offset past the resource, which returns zeros without a memory
+// access.
+struct OutBatch {
+  u32x4 w[kFRB][kFJC];
+};
+
+__device__ __forceinline__ void out_batch_load(__amdgpu_buffer_rsrc_t wr, int NC, int r0, int nr, int batch, int s0,
+                                               int s1, int lane, OutBatch &o) {
+#pragma unroll
+  for (int i = 0; i < kFRB; ++i) {
+    const int rl = batch * kFRB + i;
+#pragma unroll
+    for (int j = 0; j < kFJC; ++j) {
+      const int c = s0 + lane + 64 * j;
+      const int off = (rl < nr && c < s1) ? ((r0 + rl) * NC + c) * 16 : kBufOutOfRange;
+      const f32x4b v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);   // nontemporal
+      o.w[i][j] = u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+    }
+  }
+}
+
+// act: the RMS-scaled activations in LDS, [K]
+__device__ __forceinline__ void out_batch_run(int batch, int s0, int s1, int lane, const OutBatch &o,
+                                              const float *act, float (&acc)[kFRMax]) {
+#pragma unroll
+  for (int i = 0; i < kFRB; ++i) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kFJC; ++j) {
+      const int c = s0 + lane + 64 * j;
+      if (c < s1) s += chunk_dot<M2_W_BF16>(o.w[i][j], act + 8 * c);
+    }
+    acc[batch * kFRB + i] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 16 waves per CU (two workgroups): at most 128 VGPRs
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void fused_ssd_out_kernel(FusedArgs f) {
+  extern __shared__ float lds[];
+  __shared__ BarCtl ctl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwg = gridDim.x;
+  const GemvArgs &go = f.go;
+  const SsdArgs &sa = f.sa;
+  if (tid == 0) {
+    ctl.arrived = 0;
+    ctl.go = 0;
+  }
+  const int slot = go.slots ? go.slots[0] : 0;          // the session's slot, read once
+  const bool sok = slot >= 0 && slot < go.n_slots;
+
+  // the SSD item's state tile first, then the first two batches of out_proj rows
+  const bool has_item = (int)blockIdx.x < f.items;
+  const int item = has_item ? (int)blockIdx.x : f.items - 1;   // without one: a copy of the last, not written
+  const int h = item / sa.psplit, ps = item - h * sa.psplit;
+  SsdTile<kFMaxI> tile;
+  ssd_load<kFWaves, kFMaxI>(sa, h, ps, slot, wave, lane, tile);
+  const int r0 = (int)(((long)blockIdx.x * go.rows) / nwg);
+  const int nr = (int)(((long)(blockIdx.x + 1) * go.rows) / nwg) - r0;
+  const int NC = go.K / 8, per_w = (NC + kFWaves - 1) / kFWaves;
+  const int s0 = min(wave * per_w, NC), s1 = min(s0 + per_w, NC);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(go.W), (short)0,
+                                                                      go.rows * NC * 16, 0x00020000);
+  OutBatch ob0, ob1;
+
+  // ---- SSD item (the workgroup barriers inside order LDS only); once its own loads are
+  // all issued, the first out_proj rows
+  float *wsum = lds;
+  float *cx = lds + 16;
+  ssd_finish<kFWaves, kFMaxI, false, true>(sa, h, ps, 0, slot, wave, lane, tile, wsum, cx, has_item, [&] {
+    // every slice register of the tile counts as used here, also on paths where the item
+    // leaves it untouched, so that the compiler waits for the tile's loads now (not for
+    // the weight loads issued next), and not again at the tile's store
+#pragma unroll
+    for (int k = 0; k < kFMaxI; ++k)
+      asm volatile("" : "+v"(tile.st[k].x), "+v"(tile.st[k].y), "+v"(tile.st[k].z), "+v"(tile.st[k].w));
+    out_batch_load(wr, NC, r0, nr, 0, s0, s1, lane, ob0);
+  });
+
+  // ---- grid barrier: v and the sums of squares complete; after arriving, the state tile
+  // and the next out_proj rows
+  grid_barrier(f, &ctl, 1, wave, lane, [&] {
+    ssd_store<kFMaxI>(sa, h, has_item ? slot : -1, lane, tile);
+    out_batch_load(wr, NC, r0, nr, 1, s0, s1, lane, ob1);
+  });
+
+  // ---- out_proj (+ residual), conv-cache shift
+  conv_cache_shift(go, (size_t)blockIdx.x * kFThreads + tid, (size_t)nwg * kFThreads);
+  if (nr <= 0) return;
+  float *act = lds;                                  // [K]: this wave's eighth, scaled
+  float *red = lds + go.K;                           // [kFWaves][kFRMax]
+  float acc[kFRMax];
+#pragma unroll
+  for (int i = 0; i < kFRMax; ++i) acc[i] = 0.0f;
+  if (s1 > s0) {
+    // RMS factors of the groups this wave's chunks touch: the group's partial sums of
+    // squares over the lanes, reduced in a fixed order
+    const int g_lo = (8 * s0) / go.ng, g_hi = (8 * s1 - 1) / go.ng;
+    const int per = go.n_partials / go.n_norm;
+    float rf[kFGroups];
+#pragma unroll
+    for (int gq = 0; gq < kFGroups; ++gq) {
+      const int g = min(g_lo + gq, g_hi);
+      float sum = 0.0f;
+      for (int p = lane; p < per; p += 64) sum += ldc<true>(go.ss + g * per + p);
+      sum = group_reduce<64>(sum);
+      rf[gq] = 1.0f / sqrtf(sum / (float)go.ng + go.eps);
+    }
+    // v of the eighth: coalesced 16-byte loads past the caches, scaled, into LDS
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(go.act), (short)0,
+                                                                        go.K * 4, 0x00020000);
+    for (int i = 2 * s0 + lane; i < 2 * s1; i += 64) {
+      const f32x4b v = __builtin_amdgcn_raw_buffer_load_b128(vr, i * 16, 0, 16);   // sc1: coherent
+      const int q = (4 * i) / go.ng - g_lo;
+      float fq = rf[0];
+#pragma unroll
+      for (int gq = 1; gq < kFGroups; ++gq) fq = q == gq ? rf[gq] : fq;
+      *reinterpret_cast<float4 *>(act + 4 * i) = make_float4(v.x * fq, v.y * fq, v.z * fq, v.w * fq);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);         // LDS writes of this wave before its reads
+    out_batch_run(0, s0, s1, lane, ob0, act, acc);
+    out_batch_load(wr, NC, r0, nr, 2, s0, s1, lane, ob0);
+    out_batch_run(1, s0, s1, lane, ob1, act, acc);
+    out_batch_run(2, s0, s1, lane, ob0, act, acc);
+#pragma unroll
+    for (int i = 0; i < kFRMax; ++i) acc[i] = group_reduce<64>(acc[i]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < kFRMax; ++i) red[wave * kFRMax + i] = acc[i];
+  }
+  __syncthreads();
+  if (tid < nr) {
+    const int row = r0 + tid;
+    const float rv = go.resid ? go.resid[row] : 0.0f;
+    float s = 0.0f;
+    for (int w = 0; w < kFWaves; ++w) s += red[w * kFRMax + tid];
+    s *= go.gamma;
+    go.y[row] = sok ? s + rv : __builtin_nanf("");
+  }
+}
+
+size_t fused_lds_bytes(const m2_layer_s &L) {
+  const size_t b = 16 + 2 * (size_t)L.cfg.d_state + L.prange;         // wsum | conv outputs
+  const size_t c = (size_t)L.d_inner + kFWaves * kFRMax;              // scaled activations | row sums
+  return sizeof(float) * std::max(b, c);
+}
+
+}  // namespace
+
+// The grid of the persistent kernel on the current device: two workgroups per CU, if the
+// kernel's occupancy allows two (0: it cannot run here). Cached per device and LDS size.
+int fused_grid(const m2_layer_s &L) {
+  static int cus[64] = {0}, occ[64][2] = {{0}};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cus[dev] = n;
+  }
+  const size_t lds = fused_lds_bytes(L);
+  if (occ[dev][1] != (int)lds) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fused_ssd_out_kernel, kFThreads, lds) != hipSuccess)
+      return 0;
+    occ[dev][0] = nb;
+    occ[dev][1] = (int)lds;
+  }
+  return occ[dev][0] >= 2 ? 2 * cus[dev] : 0;
+}
+
+// Whether the layer's shapes fit plan 2 at this grid size (one session, bf16).
+bool fused_fits(const m2_layer_s &L, int grid) {
+  const m2_config &c = L.cfg;
+  if (c.wtype != M2_W_BF16 || grid <= 0) return false;
+  if (c.d_model % 8 || L.d_inner % 8 || c.d_model > 24576) return false;   // in_proj x in LDS
+  const long nco = L.d_inner / 8, per_w = (nco + kFWaves - 1) / kFWaves;
+  if (per_w > 64 * kFJC) return false;                                // out_proj eighth of a row
+  if ((c.d_model + grid - 1) / grid > kFRMax) return false;           // out_proj rows per workgroup
+  if ((long)c.d_model * nco * 16 >= kBufOutOfRange) return false;     // W_out within one buffer resource
+  if (c.n_heads * L.psplit > grid) return false;                      // one SSD item per workgroup
+  const int rpi = 64 / (c.d_state / 4);
+  if ((L.prange + rpi - 1) / rpi > kFWaves * kFMaxI) return false;    // slices per wave
+  for (int w = 0; w < kFWaves; ++w) {                                 // RMS groups per eighth
+    const long s0 = std::min(w * per_w, nco), s1 = std::min(s0 + per_w, nco);
+    if (s1 > s0 && (8 * s1 - 1) / L.ng - (8 * s0) / L.ng + 1 > kFGroups) return false;
+  }
+  return true;
+}
+
+hipError_t launch_fused_step(const m2_layer_s &L, const m2_state_s &S, const float *x, float *y,
+                             const int32_t *slots, int flags, const StepWs &ws, int grid, hipStream_t stream) {
+  const m2_config &c = L.cfg;
+  FusedArgs f{};
+  SsdArgs &sa = f.sa;
+  sa.zx = ws.zx;
+  sa.zx_stride = L.zx_stride;
+  sa.d_inner = L.d_inner;
+  sa.conv_dim = L.conv_dim;
+  sa.H = c.n_heads;
+  sa.P = c.head_dim;
+  sa.N = c.d_state;
+  sa.G = c.n_groups;
+  sa.hpg = L.hpg;
+  sa.ssm = S.ssm;
+  sa.conv_cache = S.conv;
+  sa.conv_w = L.w.conv_w;
+  sa.conv_b = L.w.conv_b;
+  sa.d_conv = c.d_conv;
+  sa.A_log = L.w.A_log;
+  sa.D = L.w.D;
+  sa.norm_w = L.w.norm_w;
+  sa.vw = ws.v;
+  sa.ss = ws.ss;
+  sa.prange = L.prange;
+  sa.psplit = L.psplit;
+  sa.n_partials = L.n_partials;
+  sa.slots = slots;
+  sa.n_slots = S.n_slots;
+  GemvArgs &go = f.go;
+  go.W = L.w.w_out;
+  go.rows = c.d_model;
+  go.K = L.d_inner;
+  go.gamma = 1.0f;
+  go.act = ws.v;
+  go.B = 1;
+  go.ss = ws.ss;
+  go.ng = L.ng;
+  go.n_partials = L.n_partials;
+  go.n_norm = L.n_norm;
+  go.eps = c.norm_eps;
+  go.y = y;
+  go.resid = (flags & M2_RESIDUAL) ? x : nullptr;
+  go.slots = slots;
+  go.n_slots = S.n_slots;
+  go.zx = ws.zx;
+  go.zx_stride = L.zx_stride;
+  go.d_inner = L.d_inner;
+  go.conv_dim = L.conv_dim;
+  go.d_conv = c.d_conv;
+  go.conv_cache = S.conv;
+  f.bar = ws.bar;
+  f.items = c.n_heads * L.psplit;
+  hipLaunchKernelGGL(fused_ssd_out_kernel, dim3(grid), dim3(kFThreads), fused_lds_bytes(L), stream, f);
+  return hipGetLastError();
+}
+
+}  // namespace m2d

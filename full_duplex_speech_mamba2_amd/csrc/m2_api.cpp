@@ -203,7 +203,7 @@ static int step_impl(m2_layer layer, m2_state st, const float *x, float *y, int3
   if (!aligned16(x) || !aligned16(y)) return fail(M2_ERR_ALIGN, "x and y must be 16-byte aligned");
   if (batch <= 0) return fail(M2_ERR_SHAPE, "batch must be positive");
   if (batch > st->n_slots) return fail(M2_ERR_SLOT, "batch %d exceeds n_slots %d", batch, st->n_slots);
-  if (flags & ~M2_RESIDUAL) return fail(M2_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (flags & ~(M2_RESIDUAL | M2_PERSISTENT)) return fail(M2_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   if (!(flags & M2_RESIDUAL) && x == y)
     return fail(M2_ERR_SHAPE, "y may alias x only with M2_RESIDUAL");
   if (check_only) return M2_OK;
@@ -281,6 +281,11 @@ int m2_step_noalloc(m2_layer layer, m2_state st, const float *x, float *y, int32
 int m2_step_plan(m2_layer layer, int32_t batch) {
   if (!layer || batch <= 0) return -1;
   return m2d::step_plan(*layer, batch);
+}
+
+int m2_step_plan_flags(m2_layer layer, int32_t batch, int32_t flags) {
+  if (!layer || batch <= 0 || (flags & ~(M2_RESIDUAL | M2_PERSISTENT))) return -1;
+  return m2d::step_plan(*layer, batch, flags);
 }
 
 static int check_head(const m2_head_config *c) {

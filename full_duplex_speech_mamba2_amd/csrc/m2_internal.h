@@ -48,6 +48,7 @@ struct StepWs {
   float *v;         // [B][d_inner]: gated SSD output
   float *ss;        // [B][n_partials]: sums of squares of v per partial range
   float *part;      // MFMA GEMVs: K-chunk partial sums [KS][B][rows]
+  unsigned *bar;    // one-launch step: grid-barrier counters (256 bytes)
   size_t bytes;
 };
 StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base);
@@ -56,9 +57,17 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
                        const int32_t *slots, int flags, const StepWs &ws, hipStream_t stream,
                        hipEvent_t const *events = nullptr);
 
-// Kernel plan of a decode step of `batch` sessions (m2_step_plan).
-enum { kPlanValu = 0, kPlanMfma = 1 };
-int step_plan(const m2_layer_s &L, int batch);
+// Kernel plan of a decode step of `batch` sessions (m2_step_plan); flags may hold
+// M2_PERSISTENT, which asks for plan 2 where it applies.
+enum { kPlanValu = 0, kPlanMfma = 1, kPlanFused = 2 };
+int step_plan(const m2_layer_s &L, int batch, int flags = 0);
+
+// Plan 2's persistent SSD + out_proj kernel (fused.hip): the grid it runs with on the
+// current device (0: it cannot), whether the layer's shapes fit it, and its launch.
+int fused_grid(const m2_layer_s &L);
+bool fused_fits(const m2_layer_s &L, int grid);
+hipError_t launch_fused_step(const m2_layer_s &L, const m2_state_s &S, const float *x, float *y,
+                             const int32_t *slots, int flags, const StepWs &ws, int grid, hipStream_t stream);
 // Whether a step of `batch` sessions runs its projections as MFMA GEMVs.
 bool step_uses_mfma(const m2_layer_s &L, int batch);
 

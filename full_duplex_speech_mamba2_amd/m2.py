@@ -27,6 +27,7 @@ _lib = C.CDLL(LIB_PATH)
 M2_OK, M2_ERR_NULL, M2_ERR_SHAPE, M2_ERR_DTYPE, M2_ERR_ALIGN = 0, -1, -2, -3, -4
 M2_ERR_WORKSPACE, M2_ERR_SLOT, M2_ERR_UNSUPPORTED, M2_ERR_HIP = -5, -6, -7, -8
 M2_RESIDUAL = 1
+M2_PERSISTENT = 2
 WTYPE = {"f32": 0, "bf16": 1, "int8g": 2, "int4g": 3, "int3g": 4}
 
 
@@ -78,6 +79,8 @@ _lib.m2_step_noalloc.restype = C.c_int
 _lib.m2_noalloc_scratch_bytes.restype = C.c_size_t
 _lib.m2_step_plan.argtypes = [_P, _i32]
 _lib.m2_step_plan.restype = C.c_int
+_lib.m2_step_plan_flags.argtypes = [_P, _i32, _i32]
+_lib.m2_step_plan_flags.restype = C.c_int
 _lib.m2_prefill_workspace.argtypes = [_P, _i32, _i32, _i32]
 _lib.m2_prefill_workspace.restype = C.c_size_t
 _lib.m2_prefill.argtypes = [_P, _P, _P, _P, _i32, _i32, _i32, _P, _i32, _P, C.c_size_t, _P]
@@ -177,9 +180,10 @@ class Layer:
     def step_workspace_bytes(self, batch: int) -> int:
         return int(_lib.m2_step_workspace(self.handle, batch))
 
-    def step_plan(self, batch: int) -> int:
-        """0: VALU GEMVs; 1: MFMA GEMVs around the SSD kernel (m2_step_plan)."""
-        return int(_lib.m2_step_plan(self.handle, batch))
+    def step_plan(self, batch: int, persistent: bool = False) -> int:
+        """0: VALU GEMVs; 1: MFMA GEMVs around the SSD kernel; 2: in_proj GEMV, then the
+        persistent SSD + out_proj kernel (only with persistent=True) (m2_step_plan_flags)."""
+        return int(_lib.m2_step_plan_flags(self.handle, batch, _flags(False, persistent)))
 
     def prefill_workspace_bytes(self, batch: int, seqlen: int, chunk: int) -> int:
         return int(_lib.m2_prefill_workspace(self.handle, batch, seqlen, chunk))
@@ -240,10 +244,15 @@ def _tokens(t: torch.Tensor, n: int) -> torch.Tensor:
     return t
 
 
+def _flags(residual: bool, persistent: bool = False) -> int:
+    return (M2_RESIDUAL if residual else 0) | (M2_PERSISTENT if persistent else 0)
+
+
 def step(layer: Layer, state: State, x: torch.Tensor, y: Optional[torch.Tensor] = None,
          slot_ids: Optional[torch.Tensor] = None, residual: bool = False,
-         ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """One decode token for x.shape[0] sessions; returns y [B][d_model]."""
+         ws: Optional[torch.Tensor] = None, stream=None, persistent: bool = False) -> torch.Tensor:
+    """One decode token for x.shape[0] sessions; returns y [B][d_model]. persistent: plan 2
+    (the persistent SSD + out_proj kernel) where it applies."""
     B = x.shape[0]
     _act(x, (B, layer.dims.d_model))
     if y is None:
@@ -252,7 +261,7 @@ def step(layer: Layer, state: State, x: torch.Tensor, y: Optional[torch.Tensor] 
     if ws is None:
         ws = layer.workspace("step", B)
     _check(_lib.m2_step(layer.handle, state.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids),
-                        M2_RESIDUAL if residual else 0, _ptr(ws), ws.numel(), _stream(stream)))
+                        _flags(residual, persistent), _ptr(ws), ws.numel(), _stream(stream)))
     return y
 
 
@@ -276,7 +285,7 @@ def noalloc_scratch_bytes() -> int:
 
 def step_timed(layer: Layer, state: State, x: torch.Tensor, y: torch.Tensor, events,
                slot_ids: Optional[torch.Tensor] = None, residual: bool = False,
-               ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+               ws: Optional[torch.Tensor] = None, stream=None, persistent: bool = False) -> torch.Tensor:
     """step() that records the four events in `events` around its three kernels. Each is a
     raw hipEvent_t handle (int) or a torch.cuda.Event that has been recorded once (so that
     its HIP event exists)."""
@@ -287,7 +296,7 @@ def step_timed(layer: Layer, state: State, x: torch.Tensor, y: torch.Tensor, eve
         ws = layer.workspace("step", B)
     ev = (C.c_void_p * 4)(*[getattr(e, "cuda_event", e) for e in events])
     _check(_lib.m2_step_timed(layer.handle, state.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids),
-                              M2_RESIDUAL if residual else 0, _ptr(ws), ws.numel(), _stream(stream), ev))
+                              _flags(residual, persistent), _ptr(ws), ws.numel(), _stream(stream), ev))
     return y
 
 

@@ -78,7 +78,10 @@ typedef enum {
 } m2_wtype;
 
 /* flags */
-enum { M2_RESIDUAL = 1 };   /* y = x + mixer(x); y may alias x */
+enum {
+  M2_RESIDUAL = 1,          /* y = x + mixer(x); y may alias x */
+  M2_PERSISTENT = 2         /* m2_step: run plan 2 where it applies (see m2_step_plan) */
+};
 
 typedef struct {
   int32_t d_model;          /* model width (K of in_proj); multiple of 16 */
@@ -170,15 +173,26 @@ size_t m2_noalloc_scratch_bytes(void);
 int m2_step_noalloc(m2_layer layer, m2_state st, const float *x, float *y, int32_t batch,
                     const int32_t *slot_ids, int32_t flags, void *stream);
 
-/* How m2_step runs `batch` sessions. Both plans have three phases, the ones
- * m2_step_timed's events delimit: in_proj | conv + SSD update + readout + gate |
- * RMSNorm + out_proj.
+/* How m2_step runs `batch` sessions. Every plan has three phases: in_proj | conv + SSD
+ * update + readout + gate | RMSNorm + out_proj.
  *   0  VALU GEMVs: one kernel per phase
  *   1  MFMA GEMVs (batch 3..32 with bf16 weights, or int8 weights whose q_group is
  *      a multiple of 32 up to 256): in_proj GEMV + reduction | SSD | RMS factors +
  *      out_proj GEMV + reduction
- * Returns -1 for a NULL layer or batch <= 0. */
+ *   2  only when asked for with M2_PERSISTENT (slower than plan 0 on MI355X), for one
+ *      session with bf16 weights on a device where two workgroups of the persistent kernel
+ *      fit on every CU (shapes up to d_model 2 x CUs x 9 = 4608 on 256 CUs, d_inner 12288,
+ *      and n_heads x head_dim / prange no larger than 2 x CUs): the in_proj GEMV of plan 0,
+ *      then the SSD update and out_proj in one persistent kernel whose workgroups meet at
+ *      one grid-wide barrier, out_proj's weights in flight across it.
+ * m2_step_timed's events delimit the phases of plans 0 and 1; with plan 2, events[2] and
+ * events[3] are both recorded after the persistent kernel. m2_step_plan gives the plan
+ * without flags (never 2). Returns -1 for a NULL layer or batch <= 0. */
 int m2_step_plan(m2_layer layer, int32_t batch);
+
+/* The plan m2_step runs for `batch` sessions with these flags (2 where M2_PERSISTENT is set
+ * and plan 2 applies on the current device; -1 as m2_step_plan, or for unknown flags). */
+int m2_step_plan_flags(m2_layer layer, int32_t batch, int32_t flags);
 
 /* Workspace bytes m2_prefill needs. */
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk);

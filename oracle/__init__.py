@@ -83,6 +83,8 @@ def lib():
             getattr(_lib, f).argtypes = [C.c_double]
             getattr(_lib, f).restype = C.c_double
         _lib.orc_num_threads.restype = C.c_int
+        _lib.orc_set_num_threads.argtypes = [C.c_int]
+        _lib.orc_set_num_threads.restype = None
         _lib.orc_head_argmax.argtypes = [i32, i32, C.c_double, C.c_int64, C.c_int64, P, P, P, i32, P, P]
         _lib.orc_head_argmax.restype = C.c_int
         _lib.orc_attn_step.argtypes = [P, P, P, P, P, P, P, P, i32, P, P, i32, P, i32, P, P]
@@ -94,6 +96,11 @@ def lib():
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (timing on one core)."""
+    lib().orc_set_num_threads(int(n))
 
 
 def _ptr(a):

@@ -72,6 +72,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Threads of the parallel loops that follow (n >= 1), for timing the oracle on one core. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ---- weights ---- */
 
 /* Row `row` of a [rows][K] weight matrix as doubles. */

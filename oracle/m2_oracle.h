@@ -158,6 +158,7 @@ double orc_silu(double x);
 
 /* Number of OpenMP threads the oracle runs with (1 without OpenMP). */
 int orc_num_threads(void);
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

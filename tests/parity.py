@@ -65,8 +65,9 @@ def oracle_decode(dims, weights, xs, ssm0, conv0, slot_ids=None, residual=False,
     return ys, ssm, conv
 
 
-def gpu_decode(dims, weights, xs, ssm0, conv0, slot_ids=None, residual=False, graph=False):
-    """Run m2_step over xs [steps][B][d_model] on cuda:0; returns numpy ys, ssm, conv."""
+def gpu_decode(dims, weights, xs, ssm0, conv0, slot_ids=None, residual=False, graph=False, persistent=False):
+    """Run m2_step over xs [steps][B][d_model] on cuda:0; returns numpy ys, ssm, conv
+    (persistent: plan 2, the persistent SSD + out_proj kernel, where it applies)."""
     import torch
     from full_duplex_speech_mamba2_amd import m2
     lay = m2.Layer(dims, weights)
@@ -76,6 +77,6 @@ def gpu_decode(dims, weights, xs, ssm0, conv0, slot_ids=None, residual=False, gr
     yd = torch.empty_like(xd)
     sl = None if slot_ids is None else torch.from_numpy(np.asarray(slot_ids, np.int32)).cuda()
     for t in range(xs.shape[0]):
-        m2.step(lay, st, xd[t], yd[t], slot_ids=sl, residual=residual)
+        m2.step(lay, st, xd[t], yd[t], slot_ids=sl, residual=residual, persistent=persistent)
     torch.cuda.synchronize()
     return yd.cpu().numpy(), st.ssm.cpu().numpy(), st.conv.cpu().numpy()

@@ -57,15 +57,17 @@ def e_conv_sampled(C, cpos, csamples, cmax):
     return float(np.max(d / max(float(cmax), 1e-30)))
 
 
-def test_9b_bf16_single_session_750_steps():
+@pytest.mark.parametrize("persistent", [False, True])
+def test_9b_bf16_single_session_750_steps(persistent):
+    """The headline workload on the three-kernel plan (as timed) and on plan 2."""
     wl = synth.workload(1)
     w = synth.make_layer_weights(wl.dims, wl.weight_seed)
     xs = synth.make_inputs(wl.dims, wl.seed, wl.steps, wl.batch)
     ssm0, conv0 = synth.make_state(wl.dims, wl.seed, wl.batch, wl.state_var)
-    yg, sg, cg = gpu_decode(wl.dims, w, xs, ssm0, conv0)
+    yg, sg, cg = gpu_decode(wl.dims, w, xs, ssm0, conv0, persistent=persistent)
     yo, so, co = oracle_decode(wl.dims, w, xs, ssm0, conv0)
     eo, es, ec = e_out(yg, yo), e_state(sg, so), e_conv(cg, co)
-    _report(wl.name, e_out=eo, e_state=es, e_conv=ec)
+    _report(wl.name + (" persistent" if persistent else ""), e_out=eo, e_state=es, e_conv=ec)
     assert eo <= TOL_OUT and es <= TOL_STATE and ec <= TOL_STATE
 
 
