@@ -58,7 +58,7 @@ __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
   }
   EpiIn epi{};
   if (row_ok && lane < nb) epi = epilogue_prefetch<EPI>(a, row, lane);
-  if (EPI == EPI_INPROJ && a.bar_clear && blockIdx.x == 0 && tid < 2) a.bar_clear[tid] = 0u;
+  if (EPI == EPI_INPROJ && a.bar_clear && blockIdx.x == 0 && tid < kBarWords) a.bar_clear[tid * kBarStride] = 0u;
 
   float *act_s = lds;
   if (PRO == PRO_NORM) {
@@ -1119,7 +1119,7 @@ StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base) {
   w.ss = p ? reinterpret_cast<float *>(p + off) : nullptr;
   off += ss;
   w.bar = p ? reinterpret_cast<unsigned *>(p + off) : nullptr;
-  off += 256;
+  off += align256(kBarBytes);
   if (step_uses_mfma(L, batch)) {
     const MfmaPlan pi = mfma_plan(L.d_in_proj, L.cfg.d_model, batch, 0);
     const MfmaPlan po = mfma_plan(L.cfg.d_model, L.d_inner, batch, L.ng);

@@ -54,6 +54,17 @@ __device__ __forceinline__ void stc(float *p, float v) {
   else *p = v;
 }
 
+// Grid-barrier words of the persistent SSD + out_proj kernel, one per 128-byte line (their
+// atomics and polls then go to different memory channels): a counter per group of
+// workgroups (blockIdx % 8, the XCD the dispatcher sends a workgroup to), the count of
+// groups complete, a release flag per group, and a flag raised when a bounded wait ran out.
+// All zero before the kernel starts (the in_proj kernel before it zeroes them).
+constexpr int kBarStride = 32;          // words per line
+constexpr int kBarGroups = 8;
+constexpr int kBarCount = 0, kBarTop = kBarGroups, kBarFlag = kBarGroups + 1, kBarError = 2 * kBarGroups + 1;
+constexpr int kBarWords = 2 * kBarGroups + 2;
+constexpr int kBarBytes = kBarWords * kBarStride * 4;
+
 // A workgroup barrier that orders LDS accesses only: unlike __syncthreads it does not wait
 // for the waves' global loads in flight (weights requested for a later phase).
 __device__ __forceinline__ void lds_barrier() {
@@ -235,7 +246,7 @@ struct GemvArgs {
   const float *resid;     // [B][rows] or null
   const int32_t *slots;
   int n_slots;
-  unsigned *bar_clear;    // in_proj: a grid-barrier counter pair for the kernel after it, zeroed here (or null)
+  unsigned *bar_clear;    // in_proj: the grid-barrier words of the kernel after it, zeroed here (or null)
 };
 
 // ---------------------------------------------------------------------------

@@ -25,9 +25,12 @@
 //            shift runs here too (the SSD, its last reader, has finished).
 //
 // Grid barrier: each wave waits for its stores to complete and counts itself in LDS; wave 0
-// then adds the workgroup's arrival to a global counter (zeroed by the in_proj kernel before
-// this launch), polls it and releases the other waves through an LDS flag, so only wave 0
-// waits on memory. The data crossing the barrier bypasses the per-XCD caches (loads and
+// then counts the workgroup in its group's counter (8 groups, so that no address takes the
+// atomics of the whole grid, which serialise at the memory), the group's last workgroup
+// counts the group, the last group raises every group's flag; wave 0 polls its group's flag
+// (words zeroed by the in_proj kernel before this launch) and releases the other waves
+// through an LDS flag, so only wave 0 waits on memory. (With one counter for all 512
+// workgroups the barrier took ~20 us.) The data crossing the barrier bypasses the per-XCD caches (loads and
 // stores with the sc1 policy), so no cache write-back or invalidation is needed. Every wait
 // is bounded: were the grid not all resident the kernel would still finish (and raise a
 // flag) instead of hanging. Measured forms, not kept: the in_proj GEMV in the same kernel
@@ -42,8 +45,8 @@ namespace {
 constexpr int kFThreads = 512;
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kFJC = 3;        // out_proj: chunks per lane of a wave's eighth of a row (<= 192 chunks)
-constexpr int kFRB = 3;        // out_proj: rows per batch of loads
-constexpr int kFRMax = 9;      // out_proj: rows per workgroup (3 batches)
+constexpr int kFRMax = 9;      // out_proj: rows per workgroup
+constexpr int kFDepth = 4;     // out_proj: rows of a wave in flight while one is multiplied
 constexpr int kFMaxI = 2;      // SSD: state slices per wave (items of up to 16 wave instructions)
 constexpr int kFGroups = 4;    // out_proj: RMS groups an eighth of a row may touch
 // Bounds of the barrier waits, in polls: LDS polls take ~0.1 us, global ones about a memory
@@ -57,7 +60,7 @@ typedef float f32x4b __attribute__((ext_vector_type(4)));
 struct FusedArgs {
   GemvArgs go;
   SsdArgs sa;
-  unsigned *bar;       // [0] workgroups arrived (zeroed before the launch); [1] set if a wait ran out
+  unsigned *bar;       // the grid-barrier words (kBar*, zeroed before the launch)
   int items;           // SSD items: H * psplit (one session)
 };
 
@@ -94,16 +97,28 @@ __device__ __forceinline__ void grid_barrier(const FusedArgs &f, BarCtl *ctl, un
   }
   for (unsigned n = 0; lds_load(&ctl->arrived) < gen * (kFWaves - 1) && n < kLdsSpin; ++n)
     __builtin_amdgcn_s_sleep(1);
-  if (lane == 0) __hip_atomic_fetch_add(f.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // two levels, so that no address takes more than a group's worth of atomics: the last
+  // workgroup of a group counts the group complete, the last group releases every group
   if (lane == 0) {
-    const unsigned target = gen * gridDim.x;
+    const int grp = blockIdx.x % kBarGroups;
+    const unsigned members = (gridDim.x - grp + kBarGroups - 1) / kBarGroups;
+    const unsigned groups = gridDim.x < kBarGroups ? gridDim.x : kBarGroups;
+    unsigned *flag = f.bar + (kBarFlag + grp) * kBarStride;
+    if (__hip_atomic_fetch_add(f.bar + (kBarCount + grp) * kBarStride, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) == gen * members - 1) {
+      if (__hip_atomic_fetch_add(f.bar + kBarTop * kBarStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          gen * groups - 1) {
+        for (unsigned q = 0; q < groups; ++q)
+          __hip_atomic_store(f.bar + (kBarFlag + q) * kBarStride, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
     unsigned n = 0;
-    while (__hip_atomic_load(f.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
       if (++n > kGlobalSpin) {
-        __hip_atomic_store(f.bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(f.bar + kBarError * kBarStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(2);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -115,39 +130,31 @@ __device__ __forceinline__ void grid_barrier(const FusedArgs &f, BarCtl *ctl, un
 // out_proj rows [r0, r0 + nr) of this workgroup, this wave's chunks [s0, s1) of them. The
 // weights are read through a buffer resource over W_out: a row past the block or a chunk
 // past the eighth takes an offset past the resource, which returns zeros without a memory
-// access.
-struct OutBatch {
-  u32x4 w[kFRB][kFJC];
+// access, so every load is unconditional and the compiler's wait counts stay exact.
+struct OutRow {
+  u32x4 w[kFJC];
 };
 
-__device__ __forceinline__ void out_batch_load(__amdgpu_buffer_rsrc_t wr, int NC, int r0, int nr, int batch, int s0,
-                                               int s1, int lane, OutBatch &o) {
+__device__ __forceinline__ void out_row_load(__amdgpu_buffer_rsrc_t wr, int NC, int r0, int nr, int rl, int s0,
+                                             int s1, int lane, OutRow &o) {
 #pragma unroll
-  for (int i = 0; i < kFRB; ++i) {
-    const int rl = batch * kFRB + i;
-#pragma unroll
-    for (int j = 0; j < kFJC; ++j) {
-      const int c = s0 + lane + 64 * j;
-      const int off = (rl < nr && c < s1) ? ((r0 + rl) * NC + c) * 16 : kBufOutOfRange;
-      const f32x4b v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);   // nontemporal
-      o.w[i][j] = u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
-    }
+  for (int j = 0; j < kFJC; ++j) {
+    const int c = s0 + lane + 64 * j;
+    const int off = (rl < nr && c < s1) ? ((r0 + rl) * NC + c) * 16 : kBufOutOfRange;
+    const f32x4b v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+    o.w[j] = u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
   }
 }
 
 // act: the RMS-scaled activations in LDS, [K]
-__device__ __forceinline__ void out_batch_run(int batch, int s0, int s1, int lane, const OutBatch &o,
-                                              const float *act, float (&acc)[kFRMax]) {
+__device__ __forceinline__ float out_row_dot(int s0, int s1, int lane, const OutRow &o, const float *act) {
+  float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kFRB; ++i) {
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kFJC; ++j) {
-      const int c = s0 + lane + 64 * j;
-      if (c < s1) s += chunk_dot<M2_W_BF16>(o.w[i][j], act + 8 * c);
-    }
-    acc[batch * kFRB + i] = s;
+  for (int j = 0; j < kFJC; ++j) {
+    const int c = s0 + lane + 64 * j;
+    if (c < s1) s += chunk_dot<M2_W_BF16>(o.w[j], act + 8 * c);
   }
+  return s;
 }
 
 // ---------------------------------------------------------------------------
@@ -178,10 +185,11 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
   const int s0 = min(wave * per_w, NC), s1 = min(s0 + per_w, NC);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(go.W), (short)0,
                                                                       go.rows * NC * 16, 0x00020000);
-  OutBatch ob0, ob1;
+  OutRow rows[kFDepth + 1];                          // a ring: row k in rows[k % (kFDepth + 1)]
 
   // ---- SSD item (the workgroup barriers inside order LDS only); once its own loads are
-  // all issued, the first out_proj rows
+  // all issued, the first out_proj row (more would only queue behind the HBM's capacity and
+  // hold up the issue of the item's work)
   float *wsum = lds;
   float *cx = lds + 16;
   ssd_finish<kFWaves, kFMaxI, false, true>(sa, h, ps, 0, slot, wave, lane, tile, wsum, cx, has_item, [&] {
@@ -191,15 +199,11 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
 #pragma unroll
     for (int k = 0; k < kFMaxI; ++k)
       asm volatile("" : "+v"(tile.st[k].x), "+v"(tile.st[k].y), "+v"(tile.st[k].z), "+v"(tile.st[k].w));
-    out_batch_load(wr, NC, r0, nr, 0, s0, s1, lane, ob0);
+    out_row_load(wr, NC, r0, nr, 0, s0, s1, lane, rows[0]);
   });
 
   // ---- grid barrier: v and the sums of squares complete; after arriving, the state tile
-  // and the next out_proj rows
-  grid_barrier(f, &ctl, 1, wave, lane, [&] {
-    ssd_store<kFMaxI>(sa, h, has_item ? slot : -1, lane, tile);
-    out_batch_load(wr, NC, r0, nr, 1, s0, s1, lane, ob1);
-  });
+  grid_barrier(f, &ctl, 1, wave, lane, [&] { ssd_store<kFMaxI>(sa, h, has_item ? slot : -1, lane, tile); });
 
   // ---- out_proj (+ residual), conv-cache shift
   conv_cache_shift(go, (size_t)blockIdx.x * kFThreads + tid, (size_t)nwg * kFThreads);
@@ -209,36 +213,54 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
   float acc[kFRMax];
 #pragma unroll
   for (int i = 0; i < kFRMax; ++i) acc[i] = 0.0f;
+  const float rv = (tid < nr && go.resid) ? go.resid[r0 + tid] : 0.0f;
   if (s1 > s0) {
-    // RMS factors of the groups this wave's chunks touch: the group's partial sums of
-    // squares over the lanes, reduced in a fixed order
+    // first the loads the staging of v needs (the partial sums of squares of the groups this
+    // wave's chunks touch, v of its eighth, coalesced, both past the caches), then the next
+    // out_proj rows: waiting for the former then never waits for the latter
     const int g_lo = (8 * s0) / go.ng, g_hi = (8 * s1 - 1) / go.ng;
     const int per = go.n_partials / go.n_norm;
-    float rf[kFGroups];
+    float sq[kFGroups];
 #pragma unroll
     for (int gq = 0; gq < kFGroups; ++gq) {
       const int g = min(g_lo + gq, g_hi);
       float sum = 0.0f;
       for (int p = lane; p < per; p += 64) sum += ldc<true>(go.ss + g * per + p);
-      sum = group_reduce<64>(sum);
-      rf[gq] = 1.0f / sqrtf(sum / (float)go.ng + go.eps);
+      sq[gq] = sum;
     }
-    // v of the eighth: coalesced 16-byte loads past the caches, scaled, into LDS
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(go.act), (short)0,
                                                                         go.K * 4, 0x00020000);
-    for (int i = 2 * s0 + lane; i < 2 * s1; i += 64) {
-      const f32x4b v = __builtin_amdgcn_raw_buffer_load_b128(vr, i * 16, 0, 16);   // sc1: coherent
-      const int q = (4 * i) / go.ng - g_lo;
-      float fq = rf[0];
+    constexpr int kV = 2 * 64 * kFJC / 64;           // float4s of v per lane (an eighth of <= 192 chunks)
+    f32x4b vv[kV];
 #pragma unroll
-      for (int gq = 1; gq < kFGroups; ++gq) fq = q == gq ? rf[gq] : fq;
-      *reinterpret_cast<float4 *>(act + 4 * i) = make_float4(v.x * fq, v.y * fq, v.z * fq, v.w * fq);
+    for (int k = 0; k < kV; ++k) {
+      const int i4 = 2 * s0 + lane + 64 * k;
+      vv[k] = __builtin_amdgcn_raw_buffer_load_b128(vr, i4 < 2 * s1 ? i4 * 16 : kBufOutOfRange, 0, 16);   // sc1
+    }
+#pragma unroll
+    for (int k = 1; k <= kFDepth; ++k) out_row_load(wr, NC, r0, nr, k, s0, s1, lane, rows[k]);
+    float rf[kFGroups];
+#pragma unroll
+    for (int gq = 0; gq < kFGroups; ++gq) rf[gq] = 1.0f / sqrtf(group_reduce<64>(sq[gq]) / (float)go.ng + go.eps);
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+      const int i4 = 2 * s0 + lane + 64 * k;
+      if (i4 < 2 * s1) {
+        const int q = (4 * i4) / go.ng - g_lo;
+        float fq = rf[0];
+#pragma unroll
+        for (int gq = 1; gq < kFGroups; ++gq) fq = q == gq ? rf[gq] : fq;
+        *reinterpret_cast<float4 *>(act + 4 * i4) = make_float4(vv[k].x * fq, vv[k].y * fq, vv[k].z * fq, vv[k].w * fq);
+      }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);         // LDS writes of this wave before its reads
-    out_batch_run(0, s0, s1, lane, ob0, act, acc);
-    out_batch_load(wr, NC, r0, nr, 2, s0, s1, lane, ob0);
-    out_batch_run(1, s0, s1, lane, ob1, act, acc);
-    out_batch_run(2, s0, s1, lane, ob0, act, acc);
+    // rows in order, kFDepth of them in flight
+#pragma unroll
+    for (int k = 0; k < kFRMax; ++k) {
+      acc[k] = out_row_dot(s0, s1, lane, rows[k % (kFDepth + 1)], act);
+      if (k + kFDepth + 1 < kFRMax)
+        out_row_load(wr, NC, r0, nr, k + kFDepth + 1, s0, s1, lane, rows[(k + kFDepth + 1) % (kFDepth + 1)]);
+    }
 #pragma unroll
     for (int i = 0; i < kFRMax; ++i) acc[i] = group_reduce<64>(acc[i]);
   }
@@ -249,7 +271,6 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
   __syncthreads();
   if (tid < nr) {
     const int row = r0 + tid;
-    const float rv = go.resid ? go.resid[row] : 0.0f;
     float s = 0.0f;
     for (int w = 0; w < kFWaves; ++w) s += red[w * kFRMax + tid];
     s *= go.gamma;

@@ -48,7 +48,7 @@ struct StepWs {
   float *v;         // [B][d_inner]: gated SSD output
   float *ss;        // [B][n_partials]: sums of squares of v per partial range
   float *part;      // MFMA GEMVs: K-chunk partial sums [KS][B][rows]
-  unsigned *bar;    // one-launch step: grid-barrier counters (256 bytes)
+  unsigned *bar;    // plan 2: the persistent kernel's grid-barrier words
   size_t bytes;
 };
 StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base);
