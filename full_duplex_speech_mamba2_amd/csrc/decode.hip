@@ -26,6 +26,7 @@
 //   gemv_tiled  any batch: 16-lane row groups, K split inside the workgroup,
 //               activations staged in K tiles for tiles of 4 sessions.
 #include "decode_common.h"
+#include <algorithm>
 
 namespace m2d {
 namespace {
@@ -430,70 +431,120 @@ __global__ __launch_bounds__(NW * 64) void ssd_step_kernel(SsdArgs a) {
 
 // ---------------------------------------------------------------------------
 // gemv_mfma: batch 3..32 with bf16 weights, or int8 weights with q_group 128 or
-// 256. A workgroup of 8 waves owns 128 rows (16 per wave) over one K chunk
-// (blockIdx.y) of whole 256-wide tiles and writes its partial sums
-// part[chunk][b][row]. Per 32-wide k-step: A = 16 weight rows x 32 k straight
-// from HBM (one 16- or 8-byte load per lane and step), B = 32 k x 16 sessions
-// from LDS as bf16 hi + lo (an fp32 value is hi + lo to 2^-16 relative; bf16 and
-// int8 weights are exact in bf16), two 16x16x32 bf16 MFMAs per product. The tiles
-// are software-pipelined: while one tile's MFMAs run, the next tile's weights are
-// in flight into a second register set and its activations into registers, which
-// are then converted into the second LDS buffer; one barrier per tile. With RMS
-// (out_proj) the workgroup first forms the RMS factors of the norm groups its
-// chunk covers from the sums of squares (fixed order) and scales the activations
-// by them while staging. gemv_mfma_reduce sums the chunks in a fixed order and
-// applies the row epilogue, so results do not depend on scheduling.
+// 256. Work is cut stream-K fashion: a unit is one 128-row block x one 256-wide k tile,
+// units are numbered row block by row block, and workgroup g of G takes units
+// [g U / G, (g + 1) U / G). G is two workgroups per CU (the number resident at once) but
+// at least the number of row blocks, so every workgroup gets the same work to within one
+// unit and its run spans at most two row blocks; it writes one partial sum per row block
+// it touches (its first at partial g, a second one, which begins inside its run, at
+// partial G + row block), and gemv_mfma_reduce adds a row block's partials in workgroup
+// order, so results do not depend on scheduling. Within a workgroup, 8 waves
+// own 16 rows each. Per 32-wide k-step: A = 16 weight rows x 32 k straight from HBM
+// (one 16- or 8-byte load per lane and step), B = 32 k x 16 sessions from LDS as bf16
+// hi + lo (an fp32 value is hi + lo to 2^-16 relative; bf16 and int8 weights are exact
+// in bf16), two 16x16x32 bf16 MFMAs per product. The units are software-pipelined:
+// each k-step's weight registers are refilled with the same k-step of the next unit as
+// soon as its MFMAs are issued (8 loads per lane in flight: more only queue behind the
+// HBM's capacity and slow the stream), the next unit's activations are loaded into
+// registers meanwhile and converted into the second LDS buffer; one barrier per unit.
+// Weights come either row-major or as 16-row panels (m2_pack_panels), in which one
+// k-step of a 16-row panel is the 1 KB (bf16; 512 B int8) of the lanes' A fragments in
+// lane order: a load instruction then reads whole cache lines instead of 64 (32) bytes
+// of each of 16 rows, and goes out nontemporal. Every global load goes through a buffer
+// resource: a row past the matrix, a session past the batch or a k past K takes an
+// out-of-range offset and reads zeros, so the unit loop has no branch around a load and
+// each wait is for exactly the load whose value comes next. With RMS (out_proj) the
+// workgroup first forms the RMS factors of the norm groups its units cover from the
+// sums of squares (fixed order) and scales the activations by them while staging.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMKT = 256;          // K tile
+constexpr int kMKT = 256;          // k tile
 constexpr int kMLD = kMKT + 8;     // LDS row stride (bf16)
 constexpr int kMRows = 128;        // rows per workgroup (8 waves x 16)
 
 struct MfmaArgs {
-  const void *W;
-  const __half *S;
-  int rows, K, q_group, kchunk;
+  const void *W;                   // row-major [rows][K], or 16-row panels
+  const __half *S;                 // int8: fp16 scales [rows][K / q_group]
+  int rows, K, q_group;
+  int T;                           // k tiles per row block: ceil(K / 256)
+  int U;                           // units: row blocks x T
+  int nks;                         // panels: 32-wide k-steps per panel, ceil(K / 32)
   const float *act;                // [B][K]
   int B;
   // RMS prologue (out_proj): act[b][k] *= 1/sqrt(sum_j ss[b][g*per + j] / ng + eps), g = k / ng
   const float *ss;
   int n_partials, n_norm, ng;
   float eps;
-  float *part;                     // [KS][B][rows]
+  int ngt;                         // RMS factors held per session in LDS
+  float *part;                     // [G + row blocks][B][128]
 };
 
-// Raw weights of one tile for one lane: 8 k-steps of 8 values.
+// Raw weights of one unit for one lane: 8 k-steps of 8 values.
 template <int WT> struct MRaw;
 template <> struct MRaw<M2_W_BF16> { bf16x8 v[8]; };
 template <> struct MRaw<M2_W_INT8G> { uint2 v[8]; };
 
-template <int WT>
-__device__ __forceinline__ void mfma_load_w(const MfmaArgs &a, int arow, int kt, int klen, int kq, MRaw<WT> &w) {
-  const bool arow_ok = arow < a.rows;
-#pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const bool ok = arow_ok && 32 * st + kq < klen;
-    const size_t off = (size_t)arow * a.K + kt + 32 * st + kq;
-    if constexpr (WT == M2_W_BF16)
-      w.v[st] = ok ? *reinterpret_cast<const bf16x8 *>(static_cast<const unsigned short *>(a.W) + off) : bf16x8{};
-    else
-      w.v[st] = ok ? *reinterpret_cast<const uint2 *>(static_cast<const int8_t *>(a.W) + off) : make_uint2(0u, 0u);
+template <int WT> constexpr int mfma_esz() { return WT == M2_W_BF16 ? 2 : 1; }
+template <int WT> constexpr int mfma_frag() { return 8 * mfma_esz<WT>(); }   // bytes per lane and k-step
+
+// Weight resource of row block rb. Offsets stay below 2^31 (checked on the host).
+template <int WT, bool PANEL>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mfma_wres(const MfmaArgs &a, int rb) {
+  char *base = const_cast<char *>(static_cast<const char *>(a.W));
+  if constexpr (PANEL) {
+    const int npan = (a.rows + 15) / 16;
+    const int np = min(kMRows / 16, npan - rb * (kMRows / 16));
+    const int pbytes = a.nks * 64 * mfma_frag<WT>();
+    return __builtin_amdgcn_make_buffer_rsrc(base + (size_t)rb * (kMRows / 16) * pbytes, (short)0, np * pbytes,
+                                             0x00020000);
+  } else {
+    const int nr = min(kMRows, a.rows - rb * kMRows);
+    return __builtin_amdgcn_make_buffer_rsrc(base + (size_t)rb * kMRows * a.K * mfma_esz<WT>(), (short)0,
+                                             nr * a.K * mfma_esz<WT>(), 0x00020000);
   }
 }
 
-// int8 scales of the tile's q_group groups (at most 2) for this lane's 4 C rows.
-__device__ __forceinline__ void mfma_load_s(const MfmaArgs &a, int rbase, int lane, int kt, float (&sc)[2][4]) {
+// This lane's byte offset of k-step 0 within its row block's resource.
+template <int WT, bool PANEL>
+__device__ __forceinline__ int mfma_lbase(const MfmaArgs &a, int wave, int lane) {
+  if constexpr (PANEL) return (wave * a.nks * 64 + lane) * mfma_frag<WT>();
+  else return (wave * 16 + (lane & 15)) * a.K * mfma_esz<WT>();
+}
+
+// One k-step of weights for this lane at k (its 8 values start there); zeros at k >= K
+// or past the block's rows.
+template <int WT, bool PANEL>
+__device__ __forceinline__ void mfma_ld(__amdgpu_buffer_rsrc_t wr, int lb, int k, int K, MRaw<WT> &w, int st) {
+  const int off = k < K ? lb + (PANEL ? (k >> 5) * 64 * mfma_frag<WT>() : k * mfma_esz<WT>()) : kBufOutOfRange;
+  constexpr int aux = PANEL ? 2 : 0;     // panels: nontemporal
+  if constexpr (WT == M2_W_BF16) {
+    w.v[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, aux));
+  } else {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, off, 0, aux);
+    w.v[st] = make_uint2(v.x, v.y);
+  }
+}
+
+// int8 scales of a unit's q_group groups (at most 2) for this lane's 4 C rows (rows
+// r4 .. r4 + 3 of the matrix); zero for a group that starts at or past K. Kept as fp16
+// bits until the tile applies them: converted here, the conversion would wait for the
+// loads at once.
+__device__ __forceinline__ void mfma_load_s(const MfmaArgs &a, __amdgpu_buffer_rsrc_t sr, int r4, int kt,
+                                            unsigned short (&sc)[2][4]) {
   const int ngrp = a.K / a.q_group;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int g = (kt + q * a.q_group) / a.q_group;
+    const int k0 = kt + q * a.q_group;
+    const bool ok = q * a.q_group < kMKT && k0 < a.K;
+    const int g = k0 / a.q_group;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rr = rbase + (lane >> 4) * 4 + r;
-      sc[q][r] = (rr < a.rows && g < ngrp && q * a.q_group < kMKT) ? __half2float(a.S[(size_t)rr * ngrp + g]) : 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const int off = ok ? ((r4 + i) * ngrp + g) * 2 : kBufOutOfRange;
+      sc[q][i] = __builtin_amdgcn_raw_buffer_load_b16(sr, off, 0, 0);
     }
   }
 }
@@ -503,32 +554,47 @@ template <> __device__ __forceinline__ bf16x8 mfma_a<M2_W_BF16>(const MRaw<M2_W_
 // int8 -> bf16 is exact; the conversions vectorise to byte-select converts and packed
 // bf16 converts (1.5 instructions per value).
 template <> __device__ __forceinline__ bf16x8 mfma_a<M2_W_INT8G>(const MRaw<M2_W_INT8G> &w, int st) {
+  // the empty asm keeps each k-step's conversion at its k-step: without it the
+  // instruction scheduler converts all eight at the top of the tile, which waits there for
+  // the last of the tile's weight loads
+  uint2 v = w.v[st];
+  asm volatile("" : "+v"(v.x), "+v"(v.y));
   f32x8 f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const unsigned wd = e < 4 ? w.v[st].x : w.v[st].y;
+    const unsigned wd = e < 4 ? v.x : v.y;
     f[e] = (float)((int32_t)(wd << (24 - 8 * (e & 3))) >> 24);
   }
   return __builtin_convertvector(f, bf16x8);
 }
 
-// Activations of one tile (NBT*16 sessions x 256 k, zero-filled) into registers.
+// Activations of one k tile (NBT*16 sessions x 256 k; zeros past the batch and past K)
+// into registers.
 template <int NBT>
-__device__ __forceinline__ void mfma_load_x(const MfmaArgs &a, int kt, int klen, int tid, float4 (&xv)[NBT * 2]) {
+__device__ __forceinline__ void mfma_load_x(const MfmaArgs &a, __amdgpu_buffer_rsrc_t xr, int kt, int tid,
+                                            float4 (&xv)[NBT * 2]) {
 #pragma unroll
   for (int q = 0; q < NBT * 2; ++q) {
     const int i = tid + 512 * q;
     const int b = i / (kMKT / 4), k4 = (i - b * (kMKT / 4)) * 4;
-    xv[q] = (b < a.B && k4 < klen) ? *reinterpret_cast<const float4 *>(a.act + (size_t)b * a.K + kt + k4)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int off = kt + k4 < a.K ? (b * a.K + kt + k4) * 4 : kBufOutOfRange;
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+    xv[q] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
   }
 }
 
-// ... scaled by the RMS factors (RMS) and stored as bf16 hi / lo.
+// The RMS factors a workgroup holds: groups [g0, g1] of its first row block's k range,
+// then [0, h1] of the second's (if its units reach into a second row block).
+struct RmsMap {
+  int g0, g1, h1, nA;
+};
+
+// ... scaled by the RMS factors (RMS; `first`: the unit is in the workgroup's first row
+// block) and stored as bf16 hi / lo.
 template <int NBT, bool RMS>
 __device__ __forceinline__ void mfma_store_x(const MfmaArgs &a, int kt, int tid, const float4 (&xv)[NBT * 2],
-                                             unsigned short *xh, unsigned short *xl, const float *rn_s, int g0,
-                                             int ngc) {
+                                             unsigned short *xh, unsigned short *xl, const float *rn_s,
+                                             const RmsMap &m, bool first) {
 #pragma unroll
   for (int q = 0; q < NBT * 2; ++q) {
     const int i = tid + 512 * q;
@@ -536,11 +602,12 @@ __device__ __forceinline__ void mfma_store_x(const MfmaArgs &a, int kt, int tid,
     f32x4 vv = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
     if (RMS) {
       // Past the end of K (a ragged last tile) the activation is 0 and the group index
-      // would leave the chunk's groups (into the next session's factors, or LDS never
-      // written here); clamped, the factor is this session's own last one, so 0 * r is 0
-      // unless this very session's factors are NaN (an out-of-range slot).
-      const int gi = min((kt + k4) / a.ng - g0, ngc - 1);
-      const float r = b < a.B ? rn_s[b * ngc + gi] : 0.0f;
+      // would leave the range of held factors; clamped, the factor is this session's own
+      // last one, so 0 * r is 0 unless this very session's factors are NaN (an
+      // out-of-range slot).
+      const int g = (kt + k4) / a.ng;
+      const int gi = first ? min(g, m.g1) - m.g0 : m.nA + min(g, m.h1);
+      const float r = b < a.B ? rn_s[b * a.ngt + gi] : 0.0f;
       vv *= r;
     }
     // hi = bf16(v) and lo = bf16(v - hi), both rounded to nearest even
@@ -551,160 +618,200 @@ __device__ __forceinline__ void mfma_store_x(const MfmaArgs &a, int kt, int tid,
   }
 }
 
-// The MFMAs of one tile; each k-step's weight registers are refilled with the same
-// k-step of the next tile (kn < k_end) as soon as its MFMAs are issued, so 8 loads
-// per lane stay in flight without a second register set.
-template <int WT, int NBT>
-__device__ __forceinline__ void mfma_tile(const MfmaArgs &a, MRaw<WT> &w, const float (&sc)[2][4], int klen,
-                                          int lane, int kq, const unsigned short *xh, const unsigned short *xl,
-                                          f32x4 (&acc)[NBT], int arow, int kn, int k_end) {
-  const bool arow_ok = arow < a.rows;
-  const int nlen = min(kMKT, k_end - kn);
-  auto refill = [&](int st) {
-    if (kn < k_end) {
-      const bool ok = arow_ok && 32 * st + kq < nlen;
-      const size_t off = (size_t)arow * a.K + kn + 32 * st + kq;
-      if constexpr (WT == M2_W_BF16)
-        w.v[st] = ok ? *reinterpret_cast<const bf16x8 *>(static_cast<const unsigned short *>(a.W) + off) : bf16x8{};
-      else
-        w.v[st] = ok ? *reinterpret_cast<const uint2 *>(static_cast<const int8_t *>(a.W) + off) : make_uint2(0u, 0u);
+// The MFMAs of one unit; with REFILL each k-step's weight registers are refilled with
+// the same k-step of the next unit (resource wn, k tile kn) as soon as its MFMAs are
+// issued. int8: SPG k-steps form one scale group (q_group / 32), whose products are
+// gathered and then scaled.
+template <int WT, bool PANEL, int NBT, int SPG, bool REFILL>
+__device__ __forceinline__ void mfma_tile(MRaw<WT> &w, const unsigned short (&sc)[2][4], int lane, int kq,
+                                          const unsigned short *xh, const unsigned short *xl, f32x4 (&acc)[NBT],
+                                          __amdgpu_buffer_rsrc_t wn, int lb, int kn, int K) {
+  f32x4 gacc[NBT];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    if (WT == M2_W_INT8G && st % SPG == 0) {
+#pragma unroll
+      for (int j = 0; j < NBT; ++j) gacc[j] = f32x4{};
     }
-  };
-  if (WT == M2_W_BF16) {
+    const bf16x8 av = mfma_a<WT>(w, st);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (32 * st < klen) {
-        const bf16x8 av = mfma_a<WT>(w, st);
-#pragma unroll
-        for (int j = 0; j < NBT; ++j) {
-          const int b = 16 * j + (lane & 15);
-          const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&xh[b * kMLD + 32 * st + kq]);
-          const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&xl[b * kMLD + 32 * st + kq]);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[j], 0, 0, 0);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[j], 0, 0, 0);
-        }
-      }
-      refill(st);
+    for (int j = 0; j < NBT; ++j) {
+      const int b = 16 * j + (lane & 15);
+      const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&xh[b * kMLD + 32 * st + kq]);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&xl[b * kMLD + 32 * st + kq]);
+      f32x4 &d = WT == M2_W_BF16 ? acc[j] : gacc[j];
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, d, 0, 0, 0);
     }
-  } else {
-    // one scale group = q_group / 32 k-steps (4 or 8): its products gathered, then scaled
-    const int spg = a.q_group / 32;
-    f32x4 gacc[NBT];
+    if (WT == M2_W_INT8G && st % SPG == SPG - 1) {
+      const int q = st / SPG;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (32 * st < klen) {
-        if (st % spg == 0) {
+      for (int j = 0; j < NBT; ++j)
 #pragma unroll
-          for (int j = 0; j < NBT; ++j) gacc[j] = f32x4{};
-        }
-        const bf16x8 av = mfma_a<WT>(w, st);
-#pragma unroll
-        for (int j = 0; j < NBT; ++j) {
-          const int b = 16 * j + (lane & 15);
-          const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&xh[b * kMLD + 32 * st + kq]);
-          const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&xl[b * kMLD + 32 * st + kq]);
-          gacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, gacc[j], 0, 0, 0);
-          gacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, gacc[j], 0, 0, 0);
-        }
-        if (st % spg == spg - 1 || 32 * (st + 1) >= klen) {
-          const int q = st / spg;
-#pragma unroll
-          for (int j = 0; j < NBT; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(q == 0 ? sc[0][r] : sc[1][r], gacc[j][r], acc[j][r]);
-        }
-      }
-      refill(st);
+        for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(__half2float(__ushort_as_half(sc[q][i])), gacc[j][i], acc[j][i]);
+    }
+    if (REFILL) {
+      // issued here, not clustered at the unit's end by the scheduler: each load then has
+      // a whole unit's time to arrive
+      mfma_ld<WT, PANEL>(wn, lb, kn + 32 * st + kq, K, w, st);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-template <int WT, int NBT, bool RMS>
-__global__ __launch_bounds__(512) void gemv_mfma_kernel(MfmaArgs a) {
+// This lane's accumulators to partial `pi`: lane l, register i -> block row
+// wave*16 + (l/16)*4 + i, session 16 j + l % 16.
+template <int NBT>
+__device__ __forceinline__ void mfma_flush(const MfmaArgs &a, int pi, int lr4, int lane, f32x4 (&acc)[NBT]) {
+  float *part = a.part + (size_t)pi * a.B * kMRows;
+#pragma unroll
+  for (int j = 0; j < NBT; ++j) {
+    const int b = 16 * j + (lane & 15);
+    if (b < a.B) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[(size_t)b * kMRows + lr4 + i] = acc[j][i];
+    }
+    acc[j] = f32x4{};
+  }
+}
+
+// Two workgroups per CU (16 waves): at most 128 VGPRs.
+template <int WT, bool PANEL, int NBT, bool RMS, int SPG>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_mfma_kernel(MfmaArgs a) {
   extern __shared__ unsigned short xs[];            // [2 buffers][hi, lo][NBT*16][kMLD], then rn
   constexpr int XB = NBT * 16 * kMLD;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rbase = blockIdx.x * kMRows + wave * 16;
-  const int arow = rbase + (lane & 15);             // A-operand row of this lane
-  const int k_begin = blockIdx.y * a.kchunk, k_end = min(a.K, k_begin + a.kchunk);
-  const int kq = (lane >> 4) * 8;                   // this lane's 8 k within a 32-wide step
+  const int G = gridDim.x;
+  const int u0 = (int)((long)blockIdx.x * a.U / G), u1 = (int)((long)(blockIdx.x + 1) * a.U / G);
+  if (u0 >= u1) return;
+  const int lr4 = wave * 16 + (lane >> 4) * 4;       // block row of this lane's first result
+  const int kq = (lane >> 4) * 8;                    // this lane's 8 k within a 32-wide step
+  const int lb = mfma_lbase<WT, PANEL>(a, wave, lane);
   float *rn_s = reinterpret_cast<float *>(xs + 4 * XB);
-  const int g0 = RMS ? k_begin / a.ng : 0;
-  const int ngc = RMS ? (k_end - 1) / a.ng - g0 + 1 : 1;
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.act), (short)0, a.B * a.K * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__half *>(a.S), (short)0, WT == M2_W_INT8G ? a.rows * (a.K / a.q_group) * 2 : 0, 0x00020000);
 
+  int rb = u0 / a.T, t = u0 - rb * a.T;
+  const int rbA = rb;
+  __amdgpu_buffer_rsrc_t wr = mfma_wres<WT, PANEL>(a, rb);
   MRaw<WT> w;
-  float s0[2][4] = {}, s1[2][4] = {};
+  unsigned short s0[2][4] = {}, s1[2][4] = {};
   float4 xv[NBT * 2];
-  mfma_load_w<WT>(a, arow, k_begin, min(kMKT, k_end - k_begin), kq, w);
-  if (WT == M2_W_INT8G) mfma_load_s(a, rbase, lane, k_begin, s0);
-  mfma_load_x<NBT>(a, k_begin, min(kMKT, k_end - k_begin), tid, xv);
+  // activations first, so that staging them waits for them alone
+  mfma_load_x<NBT>(a, xr, t * kMKT, tid, xv);
+  if (WT == M2_W_INT8G) mfma_load_s(a, sr, rb * kMRows + lr4, t * kMKT, s0);
+#pragma unroll
+  for (int st = 0; st < 8; ++st) mfma_ld<WT, PANEL>(wr, lb, t * kMKT + 32 * st + kq, a.K, w, st);
+
+  RmsMap m{};
   if (RMS) {
-    // RMS factors of the chunk's groups: 8 lanes per (session, group), strided sums
-    // combined in a fixed order
+    // the groups of the first row block's k range [t * 256, end) and of the second's
+    // [0, end); their RMS factors: 8 lanes per (session, group), strided sums combined in
+    // a fixed order
+    const int ul = u1 - 1, rbl = ul / a.T, tl = ul - rbl * a.T;
+    const int kA1 = min(a.K, (rbl == rbA ? tl + 1 : a.T) * kMKT);
+    m.g0 = t * kMKT / a.ng;
+    m.g1 = (kA1 - 1) / a.ng;
+    m.nA = m.g1 - m.g0 + 1;
+    m.h1 = rbl > rbA ? (min(a.K, (tl + 1) * kMKT) - 1) / a.ng : -1;
+    const int nh = m.nA + m.h1 + 1;
     const int per = a.n_partials / a.n_norm;
-    for (int base = 0; base < a.B * ngc * 8; base += 512) {
+    for (int base = 0; base < a.B * nh * 8; base += 512) {
       const int i = base + tid, pair = i >> 3, j = i & 7;
       float sum = 0.0f;
-      if (pair < a.B * ngc) {
-        const int b = pair / ngc, g = g0 + pair % ngc;
+      const int b = pair / max(nh, 1), slot = pair - b * nh;
+      if (pair < a.B * nh) {
+        const int g = slot < m.nA ? m.g0 + slot : slot - m.nA;
         for (int q = j; q < per; q += 8) sum += a.ss[(size_t)b * a.n_partials + g * per + q];
       }
       sum = group_reduce<8>(sum);
-      if (pair < a.B * ngc && j == 0) rn_s[pair] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
+      if (pair < a.B * nh && j == 0) rn_s[b * a.ngt + slot] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
     }
-    __syncthreads();
+    lds_barrier();
   }
-  mfma_store_x<NBT, RMS>(a, k_begin, tid, xv, xs, xs + XB, rn_s, g0, ngc);
-  __syncthreads();
+  mfma_store_x<NBT, RMS>(a, t * kMKT, tid, xv, xs, xs + XB, rn_s, m, true);
+  lds_barrier();
 
   f32x4 acc[NBT];
 #pragma unroll
   for (int j = 0; j < NBT; ++j) acc[j] = f32x4{};
   int buf = 0;
-  for (int kt = k_begin; kt < k_end; kt += kMKT) {
-    const int kn = kt + kMKT;
-    if (kn < k_end) {
-      mfma_load_x<NBT>(a, kn, min(kMKT, k_end - kn), tid, xv);
-      if (WT == M2_W_INT8G) mfma_load_s(a, rbase, lane, kn, s1);
-    }
-    mfma_tile<WT, NBT>(a, w, s0, min(kMKT, k_end - kt), lane, kq, xs + 2 * buf * XB, xs + (2 * buf + 1) * XB, acc,
-                       arow, kn, k_end);
-    if (kn >= k_end) break;
-    mfma_store_x<NBT, RMS>(a, kn, tid, xv, xs + 2 * (buf ^ 1) * XB, xs + (2 * (buf ^ 1) + 1) * XB, rn_s, g0, ngc);
+  // Every unit but the last: the next unit's activations and scales, this unit's MFMAs
+  // with the next unit's weight loads, the next activations staged; the last unit runs
+  // after the loop (with an exit test between loads and their use the compiler sinks the
+  // loads past it).
+  for (int u = u0; u < u1 - 1; ++u) {
+    const int rbn = (u + 1) / a.T, tn = u + 1 - rbn * a.T;
+    const __amdgpu_buffer_rsrc_t wn = rbn == rb ? wr : mfma_wres<WT, PANEL>(a, rbn);
+    mfma_load_x<NBT>(a, xr, tn * kMKT, tid, xv);
+    if (WT == M2_W_INT8G) mfma_load_s(a, sr, rbn * kMRows + lr4, tn * kMKT, s1);
+    __builtin_amdgcn_sched_barrier(0);
+    unsigned short *const xc = xs + 2 * buf * XB, *const xn = xs + 2 * (buf ^ 1) * XB;
+    mfma_tile<WT, PANEL, NBT, SPG, true>(w, s0, lane, kq, xc, xc + XB, acc, wn, lb, tn * kMKT, a.K);
+    mfma_store_x<NBT, RMS>(a, tn * kMKT, tid, xv, xn, xn + XB, rn_s, m, rbn == rbA);
+    if (rbn != rb) mfma_flush<NBT>(a, rb == rbA ? (int)blockIdx.x : G + rb, lr4, lane, acc);
     if (WT == M2_W_INT8G) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s0[q][r] = s1[q][r];
+        for (int i = 0; i < 4; ++i) s0[q][i] = s1[q][i];
     }
-    __syncthreads();
+    lds_barrier();
     buf ^= 1;
+    rb = rbn;
+    wr = wn;
   }
-  // lane l, reg r -> row rbase + (l/16)*4 + r, session 16 j + l % 16
-  float *part = a.part + (size_t)blockIdx.y * a.B * a.rows;
-#pragma unroll
-  for (int j = 0; j < NBT; ++j) {
-    const int b = 16 * j + (lane & 15);
-    if (b >= a.B) continue;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rr = rbase + (lane >> 4) * 4 + r;
-      if (rr < a.rows) part[(size_t)b * a.rows + rr] = acc[j][r];
-    }
-  }
+  mfma_tile<WT, PANEL, NBT, SPG, false>(w, s0, lane, kq, xs + 2 * buf * XB, xs + (2 * buf + 1) * XB, acc, wr, lb, 0,
+                                        a.K);
+  mfma_flush<NBT>(a, rb == rbA ? (int)blockIdx.x : G + rb, lr4, lane, acc);
 }
 
-// Sum of the K-chunk partials in chunk order, then the row epilogue.
+// Sum of a row block's partials in workgroup order, then the row epilogue. The
+// workgroups of row block rb are those holding its first and its last unit and all
+// between; rb is the first row block of each but (possibly) the first of them, whose
+// partial of rb is then G + rb.
 template <int EPI>
-__global__ void gemv_mfma_reduce_kernel(GemvArgs a, const float *part, int ks) {
+__global__ void gemv_mfma_reduce_kernel(GemvArgs a, const float *part, int T, int G) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (EPI == EPI_OUT && a.conv_cache) conv_cache_shift(a, idx, (size_t)gridDim.x * blockDim.x);
   if (idx >= a.rows * a.B) return;
   const int b = idx / a.rows, row = idx - b * a.rows;
   const EpiIn e = epilogue_prefetch<EPI>(a, row, b);
+  const int rb = row / kMRows, lr = row - rb * kMRows;
+  const long U = (long)((a.rows + kMRows - 1) / kMRows) * T;
+  // the workgroup holding unit u is the last g with g U / G <= u: floor(((u + 1) G - 1) / U)
+  const int gf = (int)((((long)rb * T + 1) * G - 1) / U), gl = (int)((((long)rb * T + T) * G - 1) / U);
   float v = 0.0f;
-  for (int s = 0; s < ks; ++s) v += part[((size_t)s * a.B + b) * a.rows + row];
+  for (int g = gf; g <= gl; ++g) {
+    const int rbg = (int)((long)g * U / G / T);
+    v += part[((size_t)(rbg == rb ? g : G + rb) * a.B + b) * kMRows + lr];
+  }
   gemv_epilogue<EPI>(a, row, b, v, e);
+}
+
+// 16-row panels of a row-major [rows][K] matrix of ESZ-byte elements: fragment (p, s, l)
+// (E = 8 ESZ bytes at ((p S + s) 64 + l) E, S = ceil(K / 32)) holds row 16 p + l % 16,
+// k = 32 s + 8 (l / 16) .. + 8; rows past the matrix and k past K are zeros. One thread per
+// fragment; element by element, so any K and alignment of a row work.
+template <int ESZ>
+__global__ void pack_panels_kernel(const unsigned char *w, int rows, int K, unsigned char *out, long nfrag) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nfrag) return;
+  const int S = (K + 31) / 32;
+  const int l = (int)(i & 63);
+  const long ps = i >> 6;
+  const int s = (int)(ps % S), p = (int)(ps / S);
+  const int row = 16 * p + (l & 15), k0 = 32 * s + 8 * (l >> 4);
+  unsigned char *o = out + i * 8 * ESZ;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = k0 + e;
+    const bool ok = row < rows && k < K;
+#pragma unroll
+    for (int b = 0; b < ESZ; ++b) o[e * ESZ + b] = ok ? w[((size_t)row * K + k) * ESZ + b] : 0;
+  }
 }
 
 __global__ void state_zero_kernel(float *ssm, float *conv, size_t ssm_per, size_t conv_per,
@@ -843,54 +950,88 @@ hipError_t dispatch_wt(int wtype, const GemvArgs &a, hipStream_t stream) {
 // most as many workgroups as are resident at once on the 256 CUs of an MI355X (2
 // per CU), so that no second, partial round of workgroups forms a tail.
 struct MfmaPlan {
-  int ks, kchunk, nbt;
+  int G, T, U, nbt, ngt;
   size_t lds;
 };
+
+// Stream-K plan: U units of one 128-row block x one 256-wide k tile over G workgroups,
+// two per CU of the 256-CU gfx950 parts (VGPRs and LDS allow two resident), at least one
+// per row block (so that a workgroup's run of units spans at most two row blocks) and
+// at most one per unit. The plan needs no HIP call, so workspace sizes can be computed
+// on the host alone.
+constexpr int kMfmaGrid = 512;
 
 MfmaPlan mfma_plan(int rows, int K, int B, int ng) {
   MfmaPlan p;
   p.nbt = B <= 16 ? 1 : 2;
-  const int rb = (rows + kMRows - 1) / kMRows;
-  const int ntiles = (K + kMKT - 1) / kMKT;
-  const int target = 512;                              // 2 resident workgroups per CU
-  int ks = target / rb;
-  if (ks > ntiles) ks = ntiles;
-  if (ks < 1) ks = 1;
-  const int tiles_per = (ntiles + ks - 1) / ks;
-  p.kchunk = tiles_per * kMKT;
-  p.ks = (K + p.kchunk - 1) / p.kchunk;
-  const int ngc = ng > 0 ? p.kchunk / ng + 2 : 0;      // norm groups a chunk can touch
-  p.lds = 4 * sizeof(unsigned short) * (size_t)p.nbt * 16 * kMLD + sizeof(float) * (size_t)B * ngc;
+  const int rbn = (rows + kMRows - 1) / kMRows;
+  p.T = (K + kMKT - 1) / kMKT;
+  p.U = rbn * p.T;
+  p.G = std::min(p.U, std::max(kMfmaGrid, rbn));
+  const int upw = (p.U + p.G - 1) / p.G;               // units per workgroup, at most
+  p.ngt = ng > 0 ? upw * kMKT / ng + 4 : 0;            // norm groups its two k ranges can touch
+  p.lds = 4 * sizeof(unsigned short) * (size_t)p.nbt * 16 * kMLD + sizeof(float) * (size_t)B * p.ngt;
   return p;
 }
 
-template <int WT, int NBT, bool RMS>
+size_t mfma_part_floats(const MfmaPlan &p, int B) { return (size_t)(p.G + p.U / p.T) * B * kMRows; }
+
+template <int WT, bool PANEL, int NBT, bool RMS, int SPG>
 hipError_t launch_mfma_k(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
-  auto *k = gemv_mfma_kernel<WT, NBT, RMS>;
+  auto *k = gemv_mfma_kernel<WT, PANEL, NBT, RMS, SPG>;
   hipError_t e = allow_lds(k, p.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((m.rows + kMRows - 1) / kMRows, p.ks), dim3(512), p.lds, stream, m);
+  hipLaunchKernelGGL(k, dim3(p.G), dim3(512), p.lds, stream, m);
   return hipGetLastError();
 }
 
-template <int WT, bool RMS>
-hipError_t launch_mfma(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
-  return p.nbt == 1 ? launch_mfma_k<WT, 1, RMS>(m, p, stream) : launch_mfma_k<WT, 2, RMS>(m, p, stream);
+template <int WT, bool PANEL, bool RMS, int SPG>
+hipError_t launch_mfma_nbt(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
+  return p.nbt == 1 ? launch_mfma_k<WT, PANEL, 1, RMS, SPG>(m, p, stream)
+                    : launch_mfma_k<WT, PANEL, 2, RMS, SPG>(m, p, stream);
 }
 
-// One MFMA GEMV + reduce for the arguments of a gemv_* launch; out_proj (EPI_OUT)
-// also forms the RMS factors from g.ss.
+// The kernels' buffer offsets (a row block of W or of its panels, the activations [B][K],
+// the scales, with the out-of-range marker above all) must stay below 2^31.
+template <int WT, bool PANEL, bool RMS>
+hipError_t launch_mfma(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
+  const long esz = WT == M2_W_BF16 ? 2 : 1;
+  const long kpad = PANEL ? (long)(m.K + 31) / 32 * 32 : m.K;
+  if ((long)kMRows * kpad * esz >= kBufOutOfRange || (long)m.B * m.K * 4 >= kBufOutOfRange ||
+      (long)m.rows * (m.K / m.q_group) * 2 >= kBufOutOfRange)
+    return hipErrorInvalidValue;
+  if constexpr (WT == M2_W_BF16) {
+    return launch_mfma_nbt<WT, PANEL, RMS, 8>(m, p, stream);
+  } else {
+    if (m.q_group == 128) return launch_mfma_nbt<WT, PANEL, RMS, 4>(m, p, stream);
+    if (m.q_group == 256) return launch_mfma_nbt<WT, PANEL, RMS, 8>(m, p, stream);
+    return hipErrorInvalidValue;
+  }
+}
+
+template <bool RMS>
+hipError_t launch_mfma_wt(int wtype, bool panel, const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
+  if (wtype == M2_W_BF16)
+    return panel ? launch_mfma<M2_W_BF16, true, RMS>(m, p, stream) : launch_mfma<M2_W_BF16, false, RMS>(m, p, stream);
+  return panel ? launch_mfma<M2_W_INT8G, true, RMS>(m, p, stream) : launch_mfma<M2_W_INT8G, false, RMS>(m, p, stream);
+}
+
+// One MFMA GEMV + reduce for the arguments of a gemv_* launch, from the 16-row panels of
+// the weights when given; out_proj (EPI_OUT) also forms the RMS factors from g.ss.
 template <int EPI>
-hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, float *part, hipStream_t stream) {
+hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, const void *panels, float *part,
+                         hipStream_t stream) {
   constexpr bool RMS = EPI == EPI_OUT;
   const MfmaPlan p = mfma_plan(g.rows, g.K, g.B, RMS ? g.ng : 0);
   MfmaArgs m{};
-  m.W = g.W;
+  m.W = panels ? panels : g.W;
   m.S = static_cast<const __half *>(g.S);
   m.rows = g.rows;
   m.K = g.K;
   m.q_group = c.wtype == M2_W_INT8G ? c.q_group : g.K;
-  m.kchunk = p.kchunk;
+  m.T = p.T;
+  m.U = p.U;
+  m.nks = (g.K + 31) / 32;
   m.act = g.act;
   m.B = g.B;
   m.ss = g.ss;
@@ -898,12 +1039,12 @@ hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, float *part, hip
   m.n_norm = g.n_norm;
   m.ng = g.ng;
   m.eps = g.eps;
+  m.ngt = p.ngt;
   m.part = part;
-  hipError_t e = c.wtype == M2_W_BF16 ? launch_mfma<M2_W_BF16, RMS>(m, p, stream)
-                                      : launch_mfma<M2_W_INT8G, RMS>(m, p, stream);
+  hipError_t e = launch_mfma_wt<RMS>(c.wtype, panels != nullptr, m, p, stream);
   if (e != hipSuccess) return e;
   const int n = g.rows * g.B;
-  hipLaunchKernelGGL(gemv_mfma_reduce_kernel<EPI>, dim3((n + 255) / 256), dim3(256), 0, stream, g, part, p.ks);
+  hipLaunchKernelGGL(gemv_mfma_reduce_kernel<EPI>, dim3((n + 255) / 256), dim3(256), 0, stream, g, part, p.T, p.G);
   return hipGetLastError();
 }
 
@@ -1123,7 +1264,7 @@ StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base) {
   if (step_uses_mfma(L, batch)) {
     const MfmaPlan pi = mfma_plan(L.d_in_proj, L.cfg.d_model, batch, 0);
     const MfmaPlan po = mfma_plan(L.cfg.d_model, L.d_inner, batch, L.ng);
-    const size_t n_in = (size_t)pi.ks * batch * L.d_in_proj, n_out = (size_t)po.ks * batch * L.cfg.d_model;
+    const size_t n_in = mfma_part_floats(pi, batch), n_out = mfma_part_floats(po, batch);
     w.part = p ? reinterpret_cast<float *>(p + off) : nullptr;
     off += align256(sizeof(float) * (n_in > n_out ? n_in : n_out));
   }
@@ -1192,7 +1333,7 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
     return e;
   }
   const bool mfma = plan == kPlanMfma;
-  e = mfma ? run_mfma_gemv<EPI_INPROJ>(c, gi, ws.part, stream)
+  e = mfma ? run_mfma_gemv<EPI_INPROJ>(c, gi, L.w.w_in_panels, ws.part, stream)
            : dispatch_wt<PRO_PLAIN, EPI_INPROJ>(c.wtype, gi, stream);
   if (e == hipSuccess) e = mark(1);
   if (e != hipSuccess) return e;
@@ -1253,7 +1394,7 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return e;
   if (mfma) {
-    e = run_mfma_gemv<EPI_OUT>(c, go, ws.part, stream);
+    e = run_mfma_gemv<EPI_OUT>(c, go, L.w.w_out_panels, ws.part, stream);
   } else {
     e = dispatch_wt<PRO_NORM, EPI_OUT>(c.wtype, go, stream);
   }
@@ -1275,6 +1416,24 @@ int step_plan(const m2_layer_s &L, int batch, int flags) {
 bool step_uses_mfma(const m2_layer_s &L, int batch) { return step_plan(L, batch) == kPlanMfma; }
 
 
+size_t panels_bytes(int wtype, int rows, int K) {
+  if ((wtype != M2_W_BF16 && wtype != M2_W_INT8G) || rows <= 0 || K <= 0) return 0;
+  const size_t esz = wtype == M2_W_BF16 ? 2 : 1;
+  return (size_t)((rows + 15) / 16) * ((K + 31) / 32) * 64 * 8 * esz;
+}
+
+hipError_t launch_pack_panels(int wtype, const void *w, int rows, int K, void *out, hipStream_t stream) {
+  const long nfrag = (long)((rows + 15) / 16) * ((K + 31) / 32) * 64;
+  const dim3 grid((unsigned)((nfrag + 255) / 256));
+  if (wtype == M2_W_BF16)
+    hipLaunchKernelGGL(pack_panels_kernel<2>, grid, dim3(256), 0, stream, static_cast<const unsigned char *>(w), rows,
+                       K, static_cast<unsigned char *>(out), nfrag);
+  else
+    hipLaunchKernelGGL(pack_panels_kernel<1>, grid, dim3(256), 0, stream, static_cast<const unsigned char *>(w), rows,
+                       K, static_cast<unsigned char *>(out), nfrag);
+  return hipGetLastError();
+}
+
 hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, hipStream_t stream) {
   const m2_layer_s &L = *S.layer;
   const size_t ssm_per = (size_t)L.d_inner * L.cfg.d_state;
@@ -1294,7 +1453,7 @@ bool gemv_plain_uses_mfma(int wtype, int q_group, int batch) {
 size_t gemv_plain_part_bytes(int wtype, int q_group, int rows, int K, int batch) {
   if (!gemv_plain_uses_mfma(wtype, q_group, batch)) return 0;
   const MfmaPlan p = mfma_plan(rows, K, batch, 0);
-  return sizeof(float) * (size_t)p.ks * batch * rows;
+  return sizeof(float) * mfma_part_floats(p, batch);
 }
 
 hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, int K, int q_group, float gamma,
@@ -1325,15 +1484,17 @@ hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, 
     m.rows = rows;
     m.K = K;
     m.q_group = wtype == M2_W_INT8G ? q_group : K;
-    m.kchunk = p.kchunk;
+    m.T = p.T;
+    m.U = p.U;
+    m.nks = (K + 31) / 32;
     m.act = act;
     m.B = batch;
     m.part = part;
-    hipError_t e = wtype == M2_W_BF16 ? launch_mfma<M2_W_BF16, false>(m, p, stream)
-                                      : launch_mfma<M2_W_INT8G, false>(m, p, stream);
+    hipError_t e = launch_mfma_wt<false>(wtype, false, m, p, stream);
     if (e != hipSuccess) return e;
     const int n = rows * batch;
-    hipLaunchKernelGGL(gemv_mfma_reduce_kernel<EPI_OUT>, dim3((n + 255) / 256), dim3(256), 0, stream, a, part, p.ks);
+    hipLaunchKernelGGL(gemv_mfma_reduce_kernel<EPI_OUT>, dim3((n + 255) / 256), dim3(256), 0, stream, a, part, p.T,
+                       p.G);
     return hipGetLastError();
   }
   // 1-2 sessions, 2- and 4-byte weights: the in_proj configuration (5 nontemporal loads in

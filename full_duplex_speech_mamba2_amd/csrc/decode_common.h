@@ -29,6 +29,11 @@ constexpr int kLdsFloatsPerBatch = 12288;   // tiled kernel: activation tile bud
 // conflict that costs it nothing measurable; padding its rows made it slower, so it keeps
 // them dense.
 __host__ __device__ constexpr int lds_pad(int k) { return k + 4 * (k >> 6); }
+
+// A buffer offset past every resource the kernels build: a raw buffer load there returns
+// zeros without a memory access, so a load that must not read can still be issued without
+// a branch, and the compiler's wait counts for the loads around it stay exact.
+constexpr int kBufOutOfRange = 0x7ffffff0;
 __host__ __device__ constexpr int lds_padded(int K) { return lds_pad(K - 1) + 1; }   // a multiple of 4 for K % 4 == 0
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }

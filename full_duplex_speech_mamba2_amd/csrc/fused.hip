@@ -53,7 +53,6 @@ constexpr int kFGroups = 4;    // out_proj: RMS groups an eighth of a row may to
 // latency (~1 us); a wave waiting on LDS outlasts wave 0's two waits together.
 constexpr unsigned kLdsSpin = 1u << 22;
 constexpr unsigned kGlobalSpin = 1u << 18;
-constexpr int kBufOutOfRange = 0x7ffffff0;   // a buffer offset past every resource: the load returns 0
 
 typedef float f32x4b __attribute__((ext_vector_type(4)));
 

@@ -92,6 +92,22 @@ int m2_abi_version(void) { return M2_ABI_VERSION; }
 
 const char *m2_last_error(void) { return g_err; }
 
+size_t m2_panels_bytes(int32_t wtype, int32_t rows, int32_t K) {
+  if (rows > (1 << 24) || K > (1 << 24)) return 0;
+  return m2d::panels_bytes(wtype, rows, K);
+}
+
+int m2_pack_panels(int32_t wtype, const void *w, int32_t rows, int32_t K, void *out, void *stream) {
+  if (wtype != M2_W_BF16 && wtype != M2_W_INT8G) return fail(M2_ERR_DTYPE, "panels: wtype must be bf16 or int8");
+  if (rows <= 0 || K <= 0 || rows > (1 << 24) || K > (1 << 24))
+    return fail(M2_ERR_SHAPE, "panels: rows and K must be in [1, 2^24]");
+  if (!w || !out) return fail(M2_ERR_NULL, "panels: w and out must not be NULL");
+  if (!aligned16(out)) return fail(M2_ERR_ALIGN, "panels: out must be 16-byte aligned");
+  const hipError_t e = m2d::launch_pack_panels(wtype, w, rows, K, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(M2_ERR_HIP, "panel pack launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int m2_layer_create(const m2_config *cfg, const m2_weights *w, m2_layer *out) {
   if (!out) return fail(M2_ERR_NULL, "out is NULL");
   *out = nullptr;
@@ -111,6 +127,10 @@ int m2_layer_create(const m2_config *cfg, const m2_weights *w, m2_layer *out) {
     return fail(M2_ERR_ALIGN, "s_in and s_out must be 16-byte aligned");
   for (int i = 2; i < 8; ++i)
     if (!aligned16(req[i])) return fail(M2_ERR_ALIGN, "%s must be 16-byte aligned", names[i]);
+  if ((w->w_in_panels || w->w_out_panels) && cfg->wtype != M2_W_BF16 && cfg->wtype != M2_W_INT8G)
+    return fail(M2_ERR_DTYPE, "panel copies exist for bf16 and int8 weights only");
+  if (!aligned16(w->w_in_panels) || !aligned16(w->w_out_panels))
+    return fail(M2_ERR_ALIGN, "w_in_panels and w_out_panels must be 16-byte aligned");
 
   m2_layer_s *L = new (std::nothrow) m2_layer_s();
   if (!L) return fail(M2_ERR_SHAPE, "out of host memory");

@@ -72,6 +72,10 @@ hipError_t launch_fused_step(const m2_layer_s &L, const m2_state_s &S, const flo
 bool step_uses_mfma(const m2_layer_s &L, int batch);
 
 hipError_t launch_state_zero(const m2_state_s &S, const int32_t *slots, int n, hipStream_t stream);
+// 16-row panel copies of a [rows][K] bf16 or int8 matrix (the batched decode GEMVs' weight
+// layout): their size (0 for other types), and the packing kernel.
+size_t panels_bytes(int wtype, int rows, int K);
+hipError_t launch_pack_panels(int wtype, const void *w, int rows, int K, void *out, hipStream_t stream);
 
 // Output heads: greedy argmax of W h (m2_head_argmax).
 size_t head_ws_bytes(int vocab);

@@ -55,7 +55,8 @@ class AttnWeights(C.Structure):
 
 class Weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("w_in", "s_in", "w_out", "s_out", "conv_w", "conv_b",
-                                          "dt_bias", "A_log", "D", "norm_w")]
+                                          "dt_bias", "A_log", "D", "norm_w", "w_in_panels",
+                                          "w_out_panels")]
 
 
 _P = C.c_void_p
@@ -63,6 +64,9 @@ _i32 = C.c_int32
 _lib.m2_abi_version.restype = C.c_int
 _lib.m2_last_error.restype = C.c_char_p
 _lib.m2_layer_create.argtypes = [_P, _P, _P]
+_lib.m2_panels_bytes.argtypes = [_i32, _i32, _i32]
+_lib.m2_panels_bytes.restype = C.c_size_t
+_lib.m2_pack_panels.argtypes = [_i32, _P, _i32, _i32, _P, _P]
 _lib.m2_layer_destroy.argtypes = [_P]
 _lib.m2_layer_destroy.restype = None
 _lib.m2_state_sizes.argtypes = [_P, _i32, _P, _P]
@@ -155,17 +159,43 @@ def to_device(a, device="cuda") -> Optional[torch.Tensor]:
     return torch.from_numpy(a).to(device)
 
 
-class Layer:
-    """A mixer layer handle over device copies of its weights (the handle borrows them)."""
+def panels_bytes(wtype: str, rows: int, k: int) -> int:
+    """Bytes of the 16-row panel copy of a [rows][k] matrix (m2_panels_bytes; 0 if none)."""
+    return int(_lib.m2_panels_bytes(WTYPE[wtype], rows, k))
 
-    def __init__(self, dims, weights: Dict[str, object], device="cuda"):
+
+def pack_panels(wtype: str, w: torch.Tensor, rows: int, k: int) -> torch.Tensor:
+    """The 16-row panel copy of the device row-major matrix w, written by m2_pack_panels on
+    the current stream (a uint8 tensor of panels_bytes)."""
+    n = panels_bytes(wtype, rows, k)
+    out = torch.empty(n, dtype=torch.uint8, device=w.device)
+    _check(_lib.m2_pack_panels(WTYPE[wtype], _ptr(w), rows, k, _ptr(out),
+                               C.c_void_p(torch.cuda.current_stream(w.device).cuda_stream)))
+    return out
+
+
+class Layer:
+    """A mixer layer handle over device copies of its weights (the handle borrows them).
+
+    With panels (the default, bf16 and int8 weights only) the layer also holds the 16-row
+    panel copies of W_in and W_out (m2_pack_panels), which the batched decode step's
+    matrix-core GEMVs read; panels=False leaves them out (those GEMVs then read the
+    row-major weights)."""
+
+    def __init__(self, dims, weights: Dict[str, object], device="cuda", panels: bool = True):
         self.dims = dims
         self.device = torch.device(device)
         self.tensors = {k: to_device(v, self.device) for k, v in weights.items()}
         self.cfg = config_from_dims(dims)
+        if panels and dims.wtype in ("bf16", "int8g"):
+            d_inner = dims.n_heads * dims.head_dim
+            d_in_proj = 2 * d_inner + 2 * dims.n_groups * dims.d_state + dims.n_heads
+            for name, rows, k in (("w_in", d_in_proj, dims.d_model), ("w_out", dims.d_model, d_inner)):
+                self.tensors[name + "_panels"] = pack_panels(dims.wtype, self.tensors[name], rows, k)
+            torch.cuda.current_stream(self.device).synchronize()
         self.wstruct = Weights(*[_ptr(self.tensors.get(k)) for k in
                                  ("w_in", "s_in", "w_out", "s_out", "conv_w", "conv_b", "dt_bias",
-                                  "A_log", "D", "norm_w")])
+                                  "A_log", "D", "norm_w", "w_in_panels", "w_out_panels")])
         h = C.c_void_p()
         _check(_lib.m2_layer_create(C.byref(self.cfg), C.byref(self.wstruct), C.byref(h)))
         self.handle = h

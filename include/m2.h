@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define M2_ABI_VERSION 1
+#define M2_ABI_VERSION 2
 
 typedef enum {
   M2_OK = 0,
@@ -113,6 +113,11 @@ typedef struct {
   const float *A_log;       /* [H]: A = -exp(A_log) */
   const float *D;           /* [H] */
   const float *norm_w;      /* [d_inner] */
+  /* Optional (NULL: not used): w_in / w_out of a bf16 or int8 layer repacked into 16-row
+     panels by m2_pack_panels. The batched decode step (3 to 32 sessions) then reads these
+     instead of w_in / w_out; every other path reads w_in / w_out. */
+  const void *w_in_panels;  /* m2_panels_bytes(wtype, d_in_proj, d_model) bytes */
+  const void *w_out_panels; /* m2_panels_bytes(wtype, d_model, d_inner) bytes */
 } m2_weights;
 
 typedef struct m2_layer_s *m2_layer;  /* borrows the m2_weights pointers; immutable */
@@ -127,6 +132,23 @@ const char *m2_last_error(void);
 /* Validate cfg and w and create a layer handle (host memory only; no HIP call). */
 int m2_layer_create(const m2_config *cfg, const m2_weights *w, m2_layer *out);
 void m2_layer_destroy(m2_layer layer);
+
+/* Panel layout of the projections W_in and W_out (the zxbcdt = W_in u and out = W_out yn
+ * products above) for the batched decode step, whose matrix-core GEMVs take 16 rows x 32
+ * columns per instruction: the matrix is cut into panels of 16 rows (the last one padded
+ * with zero rows), each stored as ceil(K/32) steps of 32 columns (the last padded with
+ * zeros); step s of panel p is 64 fragments of 8 consecutive elements in fragment order,
+ * fragment l holding row 16p + l%16, columns 32s + 8(l/16) .. +7, so that one load
+ * instruction of a wave reads whole cache lines.
+ * m2_panels_bytes: the size of the panel copy of a [rows][K] matrix of wtype (M2_W_BF16 or
+ * M2_W_INT8G); 0 for other types or rows, K <= 0.
+ * m2_pack_panels: enqueue on `stream` the kernel that writes the panel copy of the device
+ * row-major matrix w ([rows][K], wtype; any alignment) into out (device, m2_panels_bytes
+ * bytes, 16-byte aligned, not overlapping w). Int8 scales are not repacked. Returns
+ * M2_ERR_DTYPE for other types, M2_ERR_SHAPE for rows or K <= 0 or above 2^24,
+ * M2_ERR_NULL / M2_ERR_ALIGN for the pointers, M2_ERR_HIP if the launch fails. */
+size_t m2_panels_bytes(int32_t wtype, int32_t rows, int32_t K);
+int m2_pack_panels(int32_t wtype, const void *w, int32_t rows, int32_t K, void *out, void *stream);
 
 /* Bytes of the per-layer state buffers for n_slots sessions:
  *   ssm  fp32 [n_slots][H][P][N]           (N contiguous)

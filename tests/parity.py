@@ -65,12 +65,14 @@ def oracle_decode(dims, weights, xs, ssm0, conv0, slot_ids=None, residual=False,
     return ys, ssm, conv
 
 
-def gpu_decode(dims, weights, xs, ssm0, conv0, slot_ids=None, residual=False, graph=False, persistent=False):
+def gpu_decode(dims, weights, xs, ssm0, conv0, slot_ids=None, residual=False, graph=False, persistent=False,
+               panels=True):
     """Run m2_step over xs [steps][B][d_model] on cuda:0; returns numpy ys, ssm, conv
-    (persistent: plan 2, the persistent SSD + out_proj kernel, where it applies)."""
+    (persistent: plan 2, the persistent SSD + out_proj kernel, where it applies; panels:
+    the layer holds the 16-row panel copies the batched GEMVs read)."""
     import torch
     from full_duplex_speech_mamba2_amd import m2
-    lay = m2.Layer(dims, weights)
+    lay = m2.Layer(dims, weights, panels=panels)
     st = m2.State(lay, ssm0.shape[0], torch.from_numpy(np.ascontiguousarray(ssm0, np.float32)).cuda(),
                   torch.from_numpy(np.ascontiguousarray(conv0, np.float32)).cuda())
     xd = torch.from_numpy(np.ascontiguousarray(xs, np.float32)).cuda()

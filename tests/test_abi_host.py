@@ -37,7 +37,7 @@ def test_single_hip_runtime_mapped():
 
 
 def test_abi_version():
-    assert m2.abi_version() == 1
+    assert m2.abi_version() == 2
 
 
 def fake_weights(int8=False):
@@ -327,3 +327,37 @@ def test_step_noalloc_rejects_without_launching():
     assert L.m2_step_noalloc(lay, st, FAKE, FAKE * 2, 301, None, 0, None) == m2.M2_ERR_WORKSPACE
     L.m2_state_destroy(st)
     L.m2_layer_destroy(lay)
+
+
+def test_panels_sizes_and_rejections_without_launching():
+    """m2_panels_bytes: ceil(rows/16) panels x ceil(K/32) k-steps x 64 fragments of 8
+    elements; m2_pack_panels and m2_layer_create check their arguments on the host."""
+    lib = m2.lib()
+    assert lib.m2_panels_bytes(1, 37, 100) == 3 * 4 * 64 * 8 * 2
+    assert lib.m2_panels_bytes(2, 908, 384) == 57 * 12 * 64 * 8
+    assert lib.m2_panels_bytes(1, 22656, 4480) == 22656 * 4480 * 2          # no padding at the 9B shape
+    for wt, r, k in ((0, 16, 32), (3, 16, 32), (4, 16, 32), (1, 0, 32), (1, 16, -1)):
+        assert lib.m2_panels_bytes(wt, r, k) == 0
+    assert lib.m2_pack_panels(0, FAKE, 16, 32, FAKE, None) == m2.M2_ERR_DTYPE
+    assert lib.m2_pack_panels(4, FAKE, 16, 32, FAKE, None) == m2.M2_ERR_DTYPE
+    assert lib.m2_pack_panels(1, FAKE, 0, 32, FAKE, None) == m2.M2_ERR_SHAPE
+    assert lib.m2_pack_panels(2, FAKE, 16, 1 << 25, FAKE, None) == m2.M2_ERR_SHAPE
+    assert lib.m2_pack_panels(1, None, 16, 32, FAKE, None) == m2.M2_ERR_NULL
+    assert lib.m2_pack_panels(1, FAKE, 16, 32, None, None) == m2.M2_ERR_NULL
+    assert lib.m2_pack_panels(1, FAKE, 16, 32, FAKE + 8, None) == m2.M2_ERR_ALIGN
+    w = fake_weights()
+    w.w_in_panels = FAKE
+    assert create(GOOD.replace(wtype="f32"), w)[0] == m2.M2_ERR_DTYPE
+    w = fake_weights(True)
+    w.w_out_panels = FAKE
+    assert create(GOOD.replace(wtype="int4g", q_group=64), w)[0] == m2.M2_ERR_DTYPE
+    w = fake_weights()
+    w.w_out_panels = FAKE + 8
+    assert create(GOOD, w)[0] == m2.M2_ERR_ALIGN
+    for wt, scales in (("bf16", False), ("int8g", True)):
+        w = fake_weights(scales)
+        w.w_in_panels = FAKE
+        w.w_out_panels = FAKE + 16
+        rc, h = create(GOOD.replace(wtype=wt), w)
+        assert rc == m2.M2_OK
+        lib.m2_layer_destroy(h)

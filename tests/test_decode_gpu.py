@@ -12,8 +12,8 @@ def _report(tag, eo, es, ec):
     print("[parity] %s e_out=%.3e e_state=%.3e e_conv=%.3e" % (tag, eo, es, ec), flush=True)
 
 
-def _check(tag, dims, w, xs, ssm0, conv0, slot_ids=None, residual=False, sessions=None):
-    yg, sg, cg = gpu_decode(dims, w, xs, ssm0, conv0, slot_ids=slot_ids, residual=residual)
+def _check(tag, dims, w, xs, ssm0, conv0, slot_ids=None, residual=False, sessions=None, panels=True):
+    yg, sg, cg = gpu_decode(dims, w, xs, ssm0, conv0, slot_ids=slot_ids, residual=residual, panels=panels)
     yo, so, co = oracle_decode(dims, w, xs, ssm0, conv0, slot_ids=slot_ids, residual=residual,
                                sessions=sessions)
     if sessions is not None:
@@ -179,9 +179,11 @@ def test_state_zero_selected_slots():
 MID = synth.MixerDims(d_model=512, n_heads=16, head_dim=32, d_state=64, n_groups=4, wtype="bf16")
 
 
+@pytest.mark.parametrize("panels", [True, False])
 @pytest.mark.parametrize("wtype", ["bf16", "int8g"])
 @pytest.mark.parametrize("batch", [3, 8, 32])
-def test_mfma_batched_gemv(wtype, batch):
+def test_mfma_batched_gemv(wtype, batch, panels):
+    """The stream-K MFMA GEMVs from the 16-row panel copies and from the row-major weights."""
     dims = MID.replace(wtype=wtype, q_group=128, q_gamma_in=float(np.float32(1 / np.sqrt(512))),
                        q_gamma_out=float(np.float32(1 / np.sqrt(512))))
     w = synth.make_layer_weights(dims, 91)
@@ -189,16 +191,27 @@ def test_mfma_batched_gemv(wtype, batch):
     n_slots = batch + 3
     ssm0, conv0 = synth.make_state(dims, 93, n_slots, 0.1)
     slots = np.random.default_rng(94).permutation(n_slots)[:batch].astype(np.int32)
-    _check("mfma-%s-b%d" % (wtype, batch), dims, w, xs, ssm0, conv0, slot_ids=slots, residual=True)
+    _check("mfma-%s-b%d-%s" % (wtype, batch, "panels" if panels else "rows"), dims, w, xs, ssm0, conv0,
+           slot_ids=slots, residual=True, panels=panels)
 
 
-def test_mfma_ragged_rows_and_k():
-    # rows and K not multiples of the 64-row block or the 256-wide K tile
-    dims = synth.MixerDims(d_model=336, n_heads=6, head_dim=16, d_state=32, n_groups=2, wtype="bf16")
+@pytest.mark.parametrize("panels", [True, False])
+@pytest.mark.parametrize("wtype", ["bf16", "int8g"])
+def test_mfma_ragged_rows_and_k(wtype, panels):
+    """Rows and K not multiples of the 128-row block, the 16-row panel or the 256-wide k
+    tile: bf16 in_proj 326 x 336 (K not a multiple of the 32-wide k-step either) and
+    out_proj 336 x 96; int8 (groups of 128) in_proj 908 x 384 and out_proj 384 x 384, whose
+    last k tile holds one whole scale group."""
+    if wtype == "bf16":
+        dims = synth.MixerDims(d_model=336, n_heads=6, head_dim=16, d_state=32, n_groups=2, wtype=wtype)
+    else:
+        dims = synth.MixerDims(d_model=384, n_heads=12, head_dim=32, d_state=32, n_groups=2, wtype=wtype,
+                               q_group=128, q_gamma_in=0.0625, q_gamma_out=0.1)
     w = synth.make_layer_weights(dims, 95)
     xs = synth.make_inputs(dims, 96, 4, 5)
     ssm0, conv0 = synth.make_state(dims, 97, 5, 0.1)
-    _check("mfma-ragged", dims, w, xs, ssm0, conv0)
+    _check("mfma-ragged-%s-%s" % (wtype, "panels" if panels else "rows"), dims, w, xs, ssm0, conv0,
+           panels=panels)
 
 
 @pytest.mark.parametrize("d_state", [4, 256])
