@@ -433,8 +433,8 @@ __global__ __launch_bounds__(NW * 64) void ssd_step_kernel(SsdArgs a) {
 // gemv_mfma: batch 3..32 with bf16 weights, or int8 weights with q_group 128 or
 // 256. Work is cut stream-K fashion: a unit is one 128-row block x one 256-wide k tile,
 // units are numbered row block by row block, and workgroup g of G takes units
-// [g U / G, (g + 1) U / G). G is two workgroups per CU (the number resident at once) but
-// at least the number of row blocks, so every workgroup gets the same work to within one
+// [g U / G, (g + 1) U / G). G is about one workgroup per CU but at least the number of
+// row blocks, so every workgroup gets the same work to within one
 // unit and its run spans at most two row blocks; it writes one partial sum per row block
 // it touches (its first at partial g, a second one, which begins inside its run, at
 // partial G + row block), and gemv_mfma_reduce adds a row block's partials in workgroup
@@ -675,7 +675,7 @@ __device__ __forceinline__ void mfma_flush(const MfmaArgs &a, int pi, int lr4, i
   }
 }
 
-// Two workgroups per CU (16 waves): at most 128 VGPRs.
+// At most 128 VGPRs (4 waves per SIMD).
 template <int WT, bool PANEL, int NBT, bool RMS, int SPG>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_mfma_kernel(MfmaArgs a) {
   extern __shared__ unsigned short xs[];            // [2 buffers][hi, lo][NBT*16][kMLD], then rn
@@ -770,24 +770,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
 // Sum of a row block's partials in workgroup order, then the row epilogue. The
 // workgroups of row block rb are those holding its first and its last unit and all
-// between; rb is the first row block of each but (possibly) the first of them, whose
-// partial of rb is then G + rb.
-template <int EPI>
-__global__ void gemv_mfma_reduce_kernel(GemvArgs a, const float *part, int T, int G) {
+// between (at most MAXW); rb is the first row block of each but (possibly) the first of
+// them, whose partial of rb is then G + rb. The partials are loaded together (past the
+// last workgroup the offset is out of range and the load gives 0, which adds exactly),
+// then added in order. out_proj: the grid also covers the conv-cache shift.
+template <int EPI, int MAXW>
+__global__ void gemv_mfma_reduce_kernel(GemvArgs a, const float *part, int T, int G, int part_bytes) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (EPI == EPI_OUT && a.conv_cache) conv_cache_shift(a, idx, (size_t)gridDim.x * blockDim.x);
   if (idx >= a.rows * a.B) return;
   const int b = idx / a.rows, row = idx - b * a.rows;
   const EpiIn e = epilogue_prefetch<EPI>(a, row, b);
   const int rb = row / kMRows, lr = row - rb * kMRows;
-  const long U = (long)((a.rows + kMRows - 1) / kMRows) * T;
-  // the workgroup holding unit u is the last g with g U / G <= u: floor(((u + 1) G - 1) / U)
-  const int gf = (int)((((long)rb * T + 1) * G - 1) / U), gl = (int)((((long)rb * T + T) * G - 1) / U);
-  float v = 0.0f;
-  for (int g = gf; g <= gl; ++g) {
-    const int rbg = (int)((long)g * U / G / T);
-    v += part[((size_t)(rbg == rb ? g : G + rb) * a.B + b) * kMRows + lr];
+  const int U = (a.rows + kMRows - 1) / kMRows * T;   // U G < 2^31 (checked on the host)
+  // the workgroup holding unit u is the last g with g U / G <= u: ((u + 1) G - 1) / U
+  const int gf = ((rb * T + 1) * G - 1) / U, gl = ((rb * T + T) * G - 1) / U;
+  const __amdgpu_buffer_rsrc_t pr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(part), (short)0, part_bytes, 0x00020000);
+  float pv[MAXW];
+#pragma unroll
+  for (int i = 0; i < MAXW; ++i) {
+    const int g = gf + i, gg = min(g, G - 1);          // past gl the offset is out of range
+    const int pi = gg * U / G / T == rb ? gg : G + rb;
+    const int off = g <= gl ? ((pi * a.B + b) * kMRows + lr) * 4 : kBufOutOfRange;
+    pv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, off, 0, 0));
   }
+  float v = 0.0f;
+#pragma unroll
+  for (int i = 0; i < MAXW; ++i) v += pv[i];
   gemv_epilogue<EPI>(a, row, b, v, e);
 }
 
@@ -954,12 +964,15 @@ struct MfmaPlan {
   size_t lds;
 };
 
-// Stream-K plan: U units of one 128-row block x one 256-wide k tile over G workgroups,
-// two per CU of the 256-CU gfx950 parts (VGPRs and LDS allow two resident), at least one
-// per row block (so that a workgroup's run of units spans at most two row blocks) and
-// at most one per unit. The plan needs no HIP call, so workspace sizes can be computed
-// on the host alone.
-constexpr int kMfmaGrid = 512;
+// Stream-K plan: U units of one 128-row block x one 256-wide k tile over G workgroups:
+// as few as give every workgroup the same number of units (to within one) with about one
+// per CU of the 256-CU gfx950 parts, at least one per row block (so that a workgroup's run
+// of units spans at most two row blocks) and at most one per unit. One workgroup per CU
+// streamed fastest on MI355X (73 / 146 / 75 us per step at 4 and 32 bf16 sessions and 8
+// int8 sessions, against 77 / 158 / 78 with two per CU and 82 / 161 / 83 with 320 in all);
+// more loads in flight only queue behind the HBM's capacity. The plan needs no HIP call,
+// so workspace sizes can be computed on the host alone.
+constexpr int kMfmaGrid = 256;
 
 MfmaPlan mfma_plan(int rows, int K, int B, int ng) {
   MfmaPlan p;
@@ -967,7 +980,8 @@ MfmaPlan mfma_plan(int rows, int K, int B, int ng) {
   const int rbn = (rows + kMRows - 1) / kMRows;
   p.T = (K + kMKT - 1) / kMKT;
   p.U = rbn * p.T;
-  p.G = std::min(p.U, std::max(kMfmaGrid, rbn));
+  const int per = (p.U + kMfmaGrid - 1) / kMfmaGrid;
+  p.G = std::max((p.U + per - 1) / per, std::min(p.U, rbn));
   const int upw = (p.U + p.G - 1) / p.G;               // units per workgroup, at most
   p.ngt = ng > 0 ? upw * kMKT / ng + 4 : 0;            // norm groups its two k ranges can touch
   p.lds = 4 * sizeof(unsigned short) * (size_t)p.nbt * 16 * kMLD + sizeof(float) * (size_t)B * p.ngt;
@@ -975,6 +989,31 @@ MfmaPlan mfma_plan(int rows, int K, int B, int ng) {
 }
 
 size_t mfma_part_floats(const MfmaPlan &p, int B) { return (size_t)(p.G + p.U / p.T) * B * kMRows; }
+
+// The reduction of a plan's partials (and, out_proj, the conv-cache shift): one thread per
+// output, or per conv element if those are more.
+template <int EPI>
+hipError_t launch_mfma_reduce(const GemvArgs &g, const MfmaPlan &p, float *part, hipStream_t stream) {
+  const long pbytes = (long)mfma_part_floats(p, g.B) * 4;
+  if ((long)p.U * p.G >= (1L << 31) || pbytes >= kBufOutOfRange) return hipErrorInvalidValue;
+  // workgroups of a row block: its T units over runs of at least U / G units each
+  const int minrun = std::max(1, p.U / p.G);
+  const int maxw = (p.T + minrun - 1) / minrun + 1;
+  long n = (long)g.rows * g.B;
+  if (EPI == EPI_OUT && g.conv_cache) n = std::max(n, (long)g.B * g.conv_dim);
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (maxw <= 4)
+    hipLaunchKernelGGL((gemv_mfma_reduce_kernel<EPI, 4>), grid, block, 0, stream, g, part, p.T, p.G, (int)pbytes);
+  else if (maxw <= 8)
+    hipLaunchKernelGGL((gemv_mfma_reduce_kernel<EPI, 8>), grid, block, 0, stream, g, part, p.T, p.G, (int)pbytes);
+  else if (maxw <= 16)
+    hipLaunchKernelGGL((gemv_mfma_reduce_kernel<EPI, 16>), grid, block, 0, stream, g, part, p.T, p.G, (int)pbytes);
+  else if (maxw <= 32)
+    hipLaunchKernelGGL((gemv_mfma_reduce_kernel<EPI, 32>), grid, block, 0, stream, g, part, p.T, p.G, (int)pbytes);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 template <int WT, bool PANEL, int NBT, bool RMS, int SPG>
 hipError_t launch_mfma_k(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
@@ -992,13 +1031,13 @@ hipError_t launch_mfma_nbt(const MfmaArgs &m, const MfmaPlan &p, hipStream_t str
 }
 
 // The kernels' buffer offsets (a row block of W or of its panels, the activations [B][K],
-// the scales, with the out-of-range marker above all) must stay below 2^31.
+// the scales, with the out-of-range marker above all) and U G must stay below 2^31.
 template <int WT, bool PANEL, bool RMS>
 hipError_t launch_mfma(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
   const long esz = WT == M2_W_BF16 ? 2 : 1;
   const long kpad = PANEL ? (long)(m.K + 31) / 32 * 32 : m.K;
   if ((long)kMRows * kpad * esz >= kBufOutOfRange || (long)m.B * m.K * 4 >= kBufOutOfRange ||
-      (long)m.rows * (m.K / m.q_group) * 2 >= kBufOutOfRange)
+      (long)m.rows * (m.K / m.q_group) * 2 >= kBufOutOfRange || (long)p.U * p.G >= (1L << 31))
     return hipErrorInvalidValue;
   if constexpr (WT == M2_W_BF16) {
     return launch_mfma_nbt<WT, PANEL, RMS, 8>(m, p, stream);
@@ -1043,9 +1082,7 @@ hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, const void *pane
   m.part = part;
   hipError_t e = launch_mfma_wt<RMS>(c.wtype, panels != nullptr, m, p, stream);
   if (e != hipSuccess) return e;
-  const int n = g.rows * g.B;
-  hipLaunchKernelGGL(gemv_mfma_reduce_kernel<EPI>, dim3((n + 255) / 256), dim3(256), 0, stream, g, part, p.T, p.G);
-  return hipGetLastError();
+  return launch_mfma_reduce<EPI>(g, p, part, stream);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1492,10 +1529,7 @@ hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, 
     m.part = part;
     hipError_t e = launch_mfma_wt<false>(wtype, false, m, p, stream);
     if (e != hipSuccess) return e;
-    const int n = rows * batch;
-    hipLaunchKernelGGL(gemv_mfma_reduce_kernel<EPI_OUT>, dim3((n + 255) / 256), dim3(256), 0, stream, a, part, p.T,
-                       p.G);
-    return hipGetLastError();
+    return launch_mfma_reduce<EPI_OUT>(a, p, part, stream);
   }
   // 1-2 sessions, 2- and 4-byte weights: the in_proj configuration (5 nontemporal loads in
   // flight); otherwise the decode step's choice for out_proj.

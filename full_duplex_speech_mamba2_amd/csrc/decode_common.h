@@ -339,14 +339,22 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs &a, int row, int b,
 // kernel) has finished. Elements (session, channel) strided over the grid.
 __device__ __forceinline__ void conv_cache_shift(const GemvArgs &a, size_t gtid, size_t gthreads) {
   const size_t total = (size_t)a.B * a.conv_dim;
+  const int nk = a.d_conv - 1;                      // 1..7 cached inputs
   for (size_t i = gtid; i < total; i += gthreads) {
     const int b = (int)(i / a.conv_dim), c = (int)(i - (size_t)b * a.conv_dim);
     const int slot = a.slots ? a.slots[b] : b;
     if (slot < 0 || slot >= a.n_slots) continue;
-    float *cc = a.conv_cache + (size_t)slot * (a.d_conv - 1) * a.conv_dim + c;
-    const float raw = a.zx[(size_t)b * a.zx_stride + a.d_inner + c];
-    for (int k = 0; k + 1 < a.d_conv - 1; ++k) cc[(size_t)k * a.conv_dim] = cc[(size_t)(k + 1) * a.conv_dim];
-    cc[(size_t)(a.d_conv - 2) * a.conv_dim] = raw;
+    float *cc = a.conv_cache + (size_t)slot * nk * a.conv_dim + c;
+    // every old value first, then the stores: a store between the loads would make each
+    // load wait for the one before it
+    float v[7];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) v[k] = k + 1 < nk ? cc[(size_t)(k + 1) * a.conv_dim] : 0.0f;
+    v[6] = a.zx[(size_t)b * a.zx_stride + a.d_inner + c];
+#pragma unroll
+    for (int k = 0; k < 6; ++k)
+      if (k + 1 < nk) cc[(size_t)k * a.conv_dim] = v[k];
+    cc[(size_t)(nk - 1) * a.conv_dim] = v[6];
   }
 }
 

@@ -258,3 +258,43 @@ def test_lowbit_ragged_k(wtype, q_group, d_model, batch):
     xs = synth.make_inputs(dims, 62, 6, batch)
     ssm0, conv0 = synth.make_state(dims, 63, batch, 0.1)
     _check("lowbit-ragged-%s-g%d-k%d-b%d" % (wtype, q_group, d_model, batch), dims, w, xs, ssm0, conv0)
+
+
+@pytest.mark.parametrize("wtype,batch", [("bf16", 8), ("int8g", 5), ("bf16", 32)])
+def test_mfma_plan_graph_replays_match_eager_steps(wtype, batch):
+    """A captured step of the MFMA plan (GEMV + reduction kernels around the SSD kernel),
+    replayed three times with eager work between replays, gives the same bits as eager
+    steps from the same state."""
+    import torch
+    from full_duplex_speech_mamba2_amd import m2
+    dims = MID.replace(wtype=wtype, q_group=128, q_gamma_in=0.0625, q_gamma_out=0.0625)
+    w = synth.make_layer_weights(dims, 171)
+    xs = torch.from_numpy(synth.make_inputs(dims, 172, 3, batch)).cuda()
+    ssm0, conv0 = synth.make_state(dims, 173, batch, 0.1)
+    lay = m2.Layer(dims, w)
+    assert lay.step_plan(batch) == 1
+    runs = []
+    for graph in (False, True):
+        st = m2.State(lay, batch, torch.from_numpy(ssm0).cuda(), torch.from_numpy(conv0).cuda())
+        ws = torch.empty(lay.step_workspace_bytes(batch), dtype=torch.uint8, device="cuda")
+        xin, y = xs[0].clone(), torch.empty_like(xs[0])
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    m2.step(lay, st, xin, y, ws=ws)
+            torch.cuda.current_stream().wait_stream(s)
+        res = []
+        for t in range(3):
+            xin.copy_(xs[t])
+            if graph:
+                g.replay()
+            else:
+                m2.step(lay, st, xin, y, ws=ws)
+            torch.cuda.synchronize()
+            res.append(y.clone())
+            _ = (xs * 2).sum().item()
+        runs.append(res + [st.ssm.clone(), st.conv.clone()])
+    assert all(torch.equal(a, b) for a, b in zip(*runs))
