@@ -61,9 +61,11 @@ _lib = None
 
 
 def lib():
+    """The oracle's C library; M2_ORACLE_LIB names another build of the same source (the
+    sanitizer tests load one built with AddressSanitizer and UBSan)."""
     global _lib
     if _lib is None:
-        _lib = C.CDLL(build())
+        _lib = C.CDLL(os.environ.get("M2_ORACLE_LIB") or build())
         P = C.c_void_p
         i32 = C.c_int32
         _lib.orc_step.argtypes = [P, P, P, P, i32, P, P, i32, P, i32, P]
