@@ -169,12 +169,15 @@ def eager_ms_per_step(run, t0, steps, before=None):
     return float(np.median(out)), out
 
 
-# Launches per captured graph. A graph of ~294k kernel nodes (3000 steps of a 31-layer stack)
-# ended the process in a host segmentation fault during capture: the host-side graph grows
-# by a node object (with its kernel arguments copied) per captured launch, plus the
-# dependency edges, so one graph of that size holds several GB of host structures in the
-# runtime; the stack is captured in graphs of at most this many launches instead, replayed
-# in turn, and a larger request is refused with an error rather than attempted.
+# Launches per captured graph. Capturing 3000 steps of a 31-layer stack as one graph
+# (~294k kernel nodes, one dependency chain) ended the process with a host segmentation fault
+# during capture, before anything ran on the GPU. Only host-side graph state grows with the
+# capture: one node (with a copy of its kernel arguments) and one edge per launch. A fault
+# rather than an allocation failure fits a recursive walk over a chain of that length
+# exhausting a thread's stack better than memory exhaustion; which one it was is not
+# established, and the capture is not repeated. Graphs of at most this many launches (55
+# stack steps) capture and replay correctly, so the steps are captured in such graphs and
+# replayed in turn, and a single step above the limit is refused with an error.
 MAX_GRAPH_LAUNCHES = 16384
 
 
