@@ -462,9 +462,13 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kMKT = 256;          // k tile
-constexpr int kMLD = kMKT + 8;     // LDS row stride (bf16)
 constexpr int kMRows = 128;        // rows per workgroup (8 waves x 16)
+// k tile of a unit, and LDS rows of a tile's activations (KT + 8 bf16). A 512-wide tile
+// for int8 (the same 8 KB per wave in flight as bf16) measured no faster (27-layer int8
+// stack at 8 sessions: 548 against 553 stack steps/s).
+template <int WT> constexpr int mfma_kt() { return 256; }
+template <int WT> constexpr int mfma_ldw() { return mfma_kt<WT>() + 8; }
+constexpr int kMaxScaleGroups = 2; // int8 scale groups in one k tile (q_group >= 128)
 
 struct MfmaArgs {
   const void *W;                   // row-major [rows][K], or 16-row panels
@@ -483,10 +487,10 @@ struct MfmaArgs {
   float *part;                     // [G + row blocks][B][128]
 };
 
-// Raw weights of one unit for one lane: 8 k-steps of 8 values.
+// Raw weights of one unit for one lane: KT / 32 k-steps of 8 values.
 template <int WT> struct MRaw;
-template <> struct MRaw<M2_W_BF16> { bf16x8 v[8]; };
-template <> struct MRaw<M2_W_INT8G> { uint2 v[8]; };
+template <> struct MRaw<M2_W_BF16> { bf16x8 v[mfma_kt<M2_W_BF16>() / 32]; };
+template <> struct MRaw<M2_W_INT8G> { uint2 v[mfma_kt<M2_W_INT8G>() / 32]; };
 
 template <int WT> constexpr int mfma_esz() { return WT == M2_W_BF16 ? 2 : 1; }
 template <int WT> constexpr int mfma_frag() { return 8 * mfma_esz<WT>(); }   // bytes per lane and k-step
@@ -529,17 +533,18 @@ __device__ __forceinline__ void mfma_ld(__amdgpu_buffer_rsrc_t wr, int lb, int k
   }
 }
 
-// int8 scales of a unit's q_group groups (at most 2) for this lane's 4 C rows (rows
-// r4 .. r4 + 3 of the matrix); zero for a group that starts at or past K. Kept as fp16
-// bits until the tile applies them: converted here, the conversion would wait for the
-// loads at once.
+// int8 scales of a unit's q_group groups (at most kMaxScaleGroups) for this lane's 4 C
+// rows (rows r4 .. r4 + 3 of the matrix); zero for a group that starts at or past K. Kept
+// as fp16 bits until the tile applies them: converted here, the conversion would wait for
+// the loads at once.
+template <int KT>
 __device__ __forceinline__ void mfma_load_s(const MfmaArgs &a, __amdgpu_buffer_rsrc_t sr, int r4, int kt,
-                                            unsigned short (&sc)[2][4]) {
+                                            unsigned short (&sc)[kMaxScaleGroups][4]) {
   const int ngrp = a.K / a.q_group;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < kMaxScaleGroups; ++q) {
     const int k0 = kt + q * a.q_group;
-    const bool ok = q * a.q_group < kMKT && k0 < a.K;
+    const bool ok = q * a.q_group < KT && k0 < a.K;
     const int g = k0 / a.q_group;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -568,15 +573,15 @@ template <> __device__ __forceinline__ bf16x8 mfma_a<M2_W_INT8G>(const MRaw<M2_W
   return __builtin_convertvector(f, bf16x8);
 }
 
-// Activations of one k tile (NBT*16 sessions x 256 k; zeros past the batch and past K)
+// Activations of one k tile (NBT*16 sessions x KT k; zeros past the batch and past K)
 // into registers.
-template <int NBT>
+template <int NBT, int KT>
 __device__ __forceinline__ void mfma_load_x(const MfmaArgs &a, __amdgpu_buffer_rsrc_t xr, int kt, int tid,
-                                            float4 (&xv)[NBT * 2]) {
+                                            float4 (&xv)[NBT * KT / 128]) {
 #pragma unroll
-  for (int q = 0; q < NBT * 2; ++q) {
+  for (int q = 0; q < NBT * KT / 128; ++q) {
     const int i = tid + 512 * q;
-    const int b = i / (kMKT / 4), k4 = (i - b * (kMKT / 4)) * 4;
+    const int b = i / (KT / 4), k4 = (i - b * (KT / 4)) * 4;
     const int off = kt + k4 < a.K ? (b * a.K + kt + k4) * 4 : kBufOutOfRange;
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
     xv[q] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
@@ -591,14 +596,15 @@ struct RmsMap {
 
 // ... scaled by the RMS factors (RMS; `first`: the unit is in the workgroup's first row
 // block) and stored as bf16 hi / lo.
-template <int NBT, bool RMS>
-__device__ __forceinline__ void mfma_store_x(const MfmaArgs &a, int kt, int tid, const float4 (&xv)[NBT * 2],
+template <int NBT, int KT, bool RMS>
+__device__ __forceinline__ void mfma_store_x(const MfmaArgs &a, int kt, int tid, const float4 (&xv)[NBT * KT / 128],
                                              unsigned short *xh, unsigned short *xl, const float *rn_s,
                                              const RmsMap &m, bool first) {
+  constexpr int LD = KT + 8;
 #pragma unroll
-  for (int q = 0; q < NBT * 2; ++q) {
+  for (int q = 0; q < NBT * KT / 128; ++q) {
     const int i = tid + 512 * q;
-    const int b = i / (kMKT / 4), k4 = (i - b * (kMKT / 4)) * 4;
+    const int b = i / (KT / 4), k4 = (i - b * (KT / 4)) * 4;
     f32x4 vv = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
     if (RMS) {
       // Past the end of K (a ragged last tile) the activation is 0 and the group index
@@ -613,8 +619,8 @@ __device__ __forceinline__ void mfma_store_x(const MfmaArgs &a, int kt, int tid,
     // hi = bf16(v) and lo = bf16(v - hi), both rounded to nearest even
     const bf16x4 h = __builtin_convertvector(vv, bf16x4);
     const bf16x4 l = __builtin_convertvector(vv - __builtin_convertvector(h, f32x4), bf16x4);
-    *reinterpret_cast<bf16x4 *>(&xh[b * kMLD + k4]) = h;
-    *reinterpret_cast<bf16x4 *>(&xl[b * kMLD + k4]) = l;
+    *reinterpret_cast<bf16x4 *>(&xh[b * LD + k4]) = h;
+    *reinterpret_cast<bf16x4 *>(&xl[b * LD + k4]) = l;
   }
 }
 
@@ -623,12 +629,13 @@ __device__ __forceinline__ void mfma_store_x(const MfmaArgs &a, int kt, int tid,
 // issued. int8: SPG k-steps form one scale group (q_group / 32), whose products are
 // gathered and then scaled.
 template <int WT, bool PANEL, int NBT, int SPG, bool REFILL>
-__device__ __forceinline__ void mfma_tile(MRaw<WT> &w, const unsigned short (&sc)[2][4], int lane, int kq,
+__device__ __forceinline__ void mfma_tile(MRaw<WT> &w, const unsigned short (&sc)[kMaxScaleGroups][4], int lane, int kq,
                                           const unsigned short *xh, const unsigned short *xl, f32x4 (&acc)[NBT],
                                           __amdgpu_buffer_rsrc_t wn, int lb, int kn, int K) {
+  constexpr int KT = mfma_kt<WT>(), LD = KT + 8;
   f32x4 gacc[NBT];
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
+  for (int st = 0; st < KT / 32; ++st) {
     if (WT == M2_W_INT8G && st % SPG == 0) {
 #pragma unroll
       for (int j = 0; j < NBT; ++j) gacc[j] = f32x4{};
@@ -637,8 +644,8 @@ __device__ __forceinline__ void mfma_tile(MRaw<WT> &w, const unsigned short (&sc
 #pragma unroll
     for (int j = 0; j < NBT; ++j) {
       const int b = 16 * j + (lane & 15);
-      const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&xh[b * kMLD + 32 * st + kq]);
-      const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&xl[b * kMLD + 32 * st + kq]);
+      const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&xh[b * LD + 32 * st + kq]);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&xl[b * LD + 32 * st + kq]);
       f32x4 &d = WT == M2_W_BF16 ? acc[j] : gacc[j];
       d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, d, 0, 0, 0);
       d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, d, 0, 0, 0);
@@ -675,11 +682,12 @@ __device__ __forceinline__ void mfma_flush(const MfmaArgs &a, int pi, int lr4, i
   }
 }
 
-// At most 128 VGPRs (4 waves per SIMD).
+// One workgroup of 8 waves per CU (2 waves per SIMD): up to 256 VGPRs a wave.
 template <int WT, bool PANEL, int NBT, bool RMS, int SPG>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv_mfma_kernel(MfmaArgs a) {
-  extern __shared__ unsigned short xs[];            // [2 buffers][hi, lo][NBT*16][kMLD], then rn
-  constexpr int XB = NBT * 16 * kMLD;
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemv_mfma_kernel(MfmaArgs a) {
+  extern __shared__ unsigned short xs[];            // [2 buffers][hi, lo][NBT*16][KT + 8], then rn
+  constexpr int KT = mfma_kt<WT>();
+  constexpr int XB = NBT * 16 * mfma_ldw<WT>();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x;
   const int u0 = (int)((long)blockIdx.x * a.U / G), u1 = (int)((long)(blockIdx.x + 1) * a.U / G);
@@ -697,13 +705,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int rbA = rb;
   __amdgpu_buffer_rsrc_t wr = mfma_wres<WT, PANEL>(a, rb);
   MRaw<WT> w;
-  unsigned short s0[2][4] = {}, s1[2][4] = {};
-  float4 xv[NBT * 2];
+  unsigned short s0[kMaxScaleGroups][4] = {}, s1[kMaxScaleGroups][4] = {};
+  float4 xv[NBT * KT / 128];
   // activations first, so that staging them waits for them alone
-  mfma_load_x<NBT>(a, xr, t * kMKT, tid, xv);
-  if (WT == M2_W_INT8G) mfma_load_s(a, sr, rb * kMRows + lr4, t * kMKT, s0);
+  mfma_load_x<NBT, KT>(a, xr, t * KT, tid, xv);
+  if (WT == M2_W_INT8G) mfma_load_s<KT>(a, sr, rb * kMRows + lr4, t * KT, s0);
 #pragma unroll
-  for (int st = 0; st < 8; ++st) mfma_ld<WT, PANEL>(wr, lb, t * kMKT + 32 * st + kq, a.K, w, st);
+  for (int st = 0; st < KT / 32; ++st) mfma_ld<WT, PANEL>(wr, lb, t * KT + 32 * st + kq, a.K, w, st);
 
   RmsMap m{};
   if (RMS) {
@@ -711,11 +719,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     // [0, end); their RMS factors: 8 lanes per (session, group), strided sums combined in
     // a fixed order
     const int ul = u1 - 1, rbl = ul / a.T, tl = ul - rbl * a.T;
-    const int kA1 = min(a.K, (rbl == rbA ? tl + 1 : a.T) * kMKT);
-    m.g0 = t * kMKT / a.ng;
+    const int kA1 = min(a.K, (rbl == rbA ? tl + 1 : a.T) * KT);
+    m.g0 = t * KT / a.ng;
     m.g1 = (kA1 - 1) / a.ng;
     m.nA = m.g1 - m.g0 + 1;
-    m.h1 = rbl > rbA ? (min(a.K, (tl + 1) * kMKT) - 1) / a.ng : -1;
+    m.h1 = rbl > rbA ? (min(a.K, (tl + 1) * KT) - 1) / a.ng : -1;
     const int nh = m.nA + m.h1 + 1;
     const int per = a.n_partials / a.n_norm;
     for (int base = 0; base < a.B * nh * 8; base += 512) {
@@ -731,7 +739,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     lds_barrier();
   }
-  mfma_store_x<NBT, RMS>(a, t * kMKT, tid, xv, xs, xs + XB, rn_s, m, true);
+  mfma_store_x<NBT, KT, RMS>(a, t * KT, tid, xv, xs, xs + XB, rn_s, m, true);
   lds_barrier();
 
   f32x4 acc[NBT];
@@ -745,16 +753,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   for (int u = u0; u < u1 - 1; ++u) {
     const int rbn = (u + 1) / a.T, tn = u + 1 - rbn * a.T;
     const __amdgpu_buffer_rsrc_t wn = rbn == rb ? wr : mfma_wres<WT, PANEL>(a, rbn);
-    mfma_load_x<NBT>(a, xr, tn * kMKT, tid, xv);
-    if (WT == M2_W_INT8G) mfma_load_s(a, sr, rbn * kMRows + lr4, tn * kMKT, s1);
+    mfma_load_x<NBT, KT>(a, xr, tn * KT, tid, xv);
+    if (WT == M2_W_INT8G) mfma_load_s<KT>(a, sr, rbn * kMRows + lr4, tn * KT, s1);
     __builtin_amdgcn_sched_barrier(0);
     unsigned short *const xc = xs + 2 * buf * XB, *const xn = xs + 2 * (buf ^ 1) * XB;
-    mfma_tile<WT, PANEL, NBT, SPG, true>(w, s0, lane, kq, xc, xc + XB, acc, wn, lb, tn * kMKT, a.K);
-    mfma_store_x<NBT, RMS>(a, tn * kMKT, tid, xv, xn, xn + XB, rn_s, m, rbn == rbA);
+    mfma_tile<WT, PANEL, NBT, SPG, true>(w, s0, lane, kq, xc, xc + XB, acc, wn, lb, tn * KT, a.K);
+    mfma_store_x<NBT, KT, RMS>(a, tn * KT, tid, xv, xn, xn + XB, rn_s, m, rbn == rbA);
     if (rbn != rb) mfma_flush<NBT>(a, rb == rbA ? (int)blockIdx.x : G + rb, lr4, lane, acc);
     if (WT == M2_W_INT8G) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int q = 0; q < kMaxScaleGroups; ++q)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s0[q][i] = s1[q][i];
     }
@@ -974,17 +982,18 @@ struct MfmaPlan {
 // so workspace sizes can be computed on the host alone.
 constexpr int kMfmaGrid = 256;
 
-MfmaPlan mfma_plan(int rows, int K, int B, int ng) {
+MfmaPlan mfma_plan(int wtype, int rows, int K, int B, int ng) {
   MfmaPlan p;
   p.nbt = B <= 16 ? 1 : 2;
+  const int kt = wtype == M2_W_INT8G ? mfma_kt<M2_W_INT8G>() : mfma_kt<M2_W_BF16>();
   const int rbn = (rows + kMRows - 1) / kMRows;
-  p.T = (K + kMKT - 1) / kMKT;
+  p.T = (K + kt - 1) / kt;
   p.U = rbn * p.T;
   const int per = (p.U + kMfmaGrid - 1) / kMfmaGrid;
   p.G = std::max((p.U + per - 1) / per, std::min(p.U, rbn));
   const int upw = (p.U + p.G - 1) / p.G;               // units per workgroup, at most
-  p.ngt = ng > 0 ? upw * kMKT / ng + 4 : 0;            // norm groups its two k ranges can touch
-  p.lds = 4 * sizeof(unsigned short) * (size_t)p.nbt * 16 * kMLD + sizeof(float) * (size_t)B * p.ngt;
+  p.ngt = ng > 0 ? upw * kt / ng + 4 : 0;              // norm groups its two k ranges can touch
+  p.lds = 4 * sizeof(unsigned short) * (size_t)p.nbt * 16 * (kt + 8) + sizeof(float) * (size_t)B * p.ngt;
   return p;
 }
 
@@ -1061,7 +1070,7 @@ template <int EPI>
 hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, const void *panels, float *part,
                          hipStream_t stream) {
   constexpr bool RMS = EPI == EPI_OUT;
-  const MfmaPlan p = mfma_plan(g.rows, g.K, g.B, RMS ? g.ng : 0);
+  const MfmaPlan p = mfma_plan(c.wtype, g.rows, g.K, g.B, RMS ? g.ng : 0);
   MfmaArgs m{};
   m.W = panels ? panels : g.W;
   m.S = static_cast<const __half *>(g.S);
@@ -1299,8 +1308,8 @@ StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base) {
   w.bar = p ? reinterpret_cast<unsigned *>(p + off) : nullptr;
   off += align256(kBarBytes);
   if (step_uses_mfma(L, batch)) {
-    const MfmaPlan pi = mfma_plan(L.d_in_proj, L.cfg.d_model, batch, 0);
-    const MfmaPlan po = mfma_plan(L.cfg.d_model, L.d_inner, batch, L.ng);
+    const MfmaPlan pi = mfma_plan(L.cfg.wtype, L.d_in_proj, L.cfg.d_model, batch, 0);
+    const MfmaPlan po = mfma_plan(L.cfg.wtype, L.cfg.d_model, L.d_inner, batch, L.ng);
     const size_t n_in = mfma_part_floats(pi, batch), n_out = mfma_part_floats(po, batch);
     w.part = p ? reinterpret_cast<float *>(p + off) : nullptr;
     off += align256(sizeof(float) * (n_in > n_out ? n_in : n_out));
@@ -1489,7 +1498,7 @@ bool gemv_plain_uses_mfma(int wtype, int q_group, int batch) {
 
 size_t gemv_plain_part_bytes(int wtype, int q_group, int rows, int K, int batch) {
   if (!gemv_plain_uses_mfma(wtype, q_group, batch)) return 0;
-  const MfmaPlan p = mfma_plan(rows, K, batch, 0);
+  const MfmaPlan p = mfma_plan(wtype, rows, K, batch, 0);
   return sizeof(float) * mfma_part_floats(p, batch);
 }
 
@@ -1514,7 +1523,7 @@ hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, 
   // 3-32 sessions with bf16 (or int8 g128/g256) weights: the MFMA GEMV over K chunks, then
   // the reduction with the plain epilogue (as the decode step's MFMA plan, without RMS).
   if (gemv_plain_uses_mfma(wtype, q_group, batch)) {
-    const MfmaPlan p = mfma_plan(rows, K, batch, 0);
+    const MfmaPlan p = mfma_plan(wtype, rows, K, batch, 0);
     MfmaArgs m{};
     m.W = W;
     m.S = static_cast<const __half *>(S);
