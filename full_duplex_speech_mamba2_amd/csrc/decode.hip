@@ -682,9 +682,46 @@ __device__ __forceinline__ void mfma_flush(const MfmaArgs &a, int pi, int lr4, i
   }
 }
 
-// One workgroup of 8 waves per CU (2 waves per SIMD): up to 256 VGPRs a wave.
-template <int WT, bool PANEL, int NBT, bool RMS, int SPG>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemv_mfma_kernel(MfmaArgs a) {
+// A workgroup that owns a whole row block (EPI >= 0): its sums are final, so each lane
+// applies the row epilogue to its own 4 rows x NBT sessions. The epilogue inputs are
+// loaded before the last tile (unconditional loads, so that the tile's weights need no
+// wait for them) and the results stored after it.
+template <int EPI, int NBT>
+struct MfmaEpi {
+  EpiIn e[NBT][4];
+};
+
+template <int EPI, int NBT>
+__device__ __forceinline__ void mfma_epi_load(const GemvArgs &g, int row0, int lane, MfmaEpi<EPI, NBT> &m) {
+#pragma unroll
+  for (int j = 0; j < NBT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m.e[j][i] = epilogue_load_all<EPI>(g, min(row0 + i, g.rows - 1), min(16 * j + (lane & 15), g.B - 1));
+}
+
+template <int EPI, int NBT>
+__device__ __forceinline__ void mfma_epi_store(const GemvArgs &g, int row0, int lane, const f32x4 (&acc)[NBT],
+                                               const MfmaEpi<EPI, NBT> &m) {
+#pragma unroll
+  for (int j = 0; j < NBT; ++j) {
+    const int b = 16 * j + (lane & 15);
+    if (b < g.B) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (row0 + i < g.rows) gemv_epilogue<EPI>(g, row0 + i, b, acc[j][i], m.e[j][i]);
+    }
+  }
+}
+
+constexpr int kEpiPartials = -1;
+
+// One workgroup of 8 waves per CU (2 waves per SIMD): up to 256 VGPRs a wave. EPI:
+// kEpiPartials (partial sums per workgroup, reduced by gemv_mfma_reduce_kernel) or the
+// row epilogue of g (every workgroup owns exactly one row block: G = U / T).
+template <int WT, bool PANEL, int NBT, bool RMS, int SPG, int EPI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemv_mfma_kernel(MfmaArgs a,
+                                                                                                    GemvArgs g) {
   extern __shared__ unsigned short xs[];            // [2 buffers][hi, lo][NBT*16][KT + 8], then rn
   constexpr int KT = mfma_kt<WT>();
   constexpr int XB = NBT * 16 * mfma_ldw<WT>();
@@ -759,7 +796,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     unsigned short *const xc = xs + 2 * buf * XB, *const xn = xs + 2 * (buf ^ 1) * XB;
     mfma_tile<WT, PANEL, NBT, SPG, true>(w, s0, lane, kq, xc, xc + XB, acc, wn, lb, tn * KT, a.K);
     mfma_store_x<NBT, KT, RMS>(a, tn * KT, tid, xv, xn, xn + XB, rn_s, m, rbn == rbA);
-    if (rbn != rb) mfma_flush<NBT>(a, rb == rbA ? (int)blockIdx.x : G + rb, lr4, lane, acc);
+    if (EPI == kEpiPartials && rbn != rb) mfma_flush<NBT>(a, rb == rbA ? (int)blockIdx.x : G + rb, lr4, lane, acc);
     if (WT == M2_W_INT8G) {
 #pragma unroll
       for (int q = 0; q < kMaxScaleGroups; ++q)
@@ -771,17 +808,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     rb = rbn;
     wr = wn;
   }
-  mfma_tile<WT, PANEL, NBT, SPG, false>(w, s0, lane, kq, xs + 2 * buf * XB, xs + (2 * buf + 1) * XB, acc, wr, lb, 0,
-                                        a.K);
-  mfma_flush<NBT>(a, rb == rbA ? (int)blockIdx.x : G + rb, lr4, lane, acc);
+  if constexpr (EPI == kEpiPartials) {
+    mfma_tile<WT, PANEL, NBT, SPG, false>(w, s0, lane, kq, xs + 2 * buf * XB, xs + (2 * buf + 1) * XB, acc, wr, lb, 0,
+                                          a.K);
+    mfma_flush<NBT>(a, rb == rbA ? (int)blockIdx.x : G + rb, lr4, lane, acc);
+  } else {
+    MfmaEpi<EPI, NBT> me;
+    mfma_epi_load<EPI, NBT>(g, rb * kMRows + lr4, lane, me);
+    mfma_tile<WT, PANEL, NBT, SPG, false>(w, s0, lane, kq, xs + 2 * buf * XB, xs + (2 * buf + 1) * XB, acc, wr, lb, 0,
+                                          a.K);
+    mfma_epi_store<EPI, NBT>(g, rb * kMRows + lr4, lane, acc, me);
+  }
 }
 
 // Sum of a row block's partials in workgroup order, then the row epilogue. The
 // workgroups of row block rb are those holding its first and its last unit and all
-// between (at most MAXW); rb is the first row block of each but (possibly) the first of
-// them, whose partial of rb is then G + rb. The partials are loaded together (past the
-// last workgroup the offset is out of range and the load gives 0, which adds exactly),
-// then added in order. out_proj: the grid also covers the conv-cache shift.
+// between; rb is the first row block of each but (possibly) the first of them, whose
+// partial of rb is then G + rb. The partials are loaded MAXW at a time (past the last
+// workgroup the offset is out of range and the load gives 0, which adds exactly), then
+// added in order. out_proj: the grid also covers the conv-cache shift.
 template <int EPI, int MAXW>
 __global__ void gemv_mfma_reduce_kernel(GemvArgs a, const float *part, int T, int G, int part_bytes) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -795,17 +840,19 @@ __global__ void gemv_mfma_reduce_kernel(GemvArgs a, const float *part, int T, in
   const int gf = ((rb * T + 1) * G - 1) / U, gl = ((rb * T + T) * G - 1) / U;
   const __amdgpu_buffer_rsrc_t pr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(part), (short)0, part_bytes, 0x00020000);
-  float pv[MAXW];
-#pragma unroll
-  for (int i = 0; i < MAXW; ++i) {
-    const int g = gf + i, gg = min(g, G - 1);          // past gl the offset is out of range
-    const int pi = gg * U / G / T == rb ? gg : G + rb;
-    const int off = g <= gl ? ((pi * a.B + b) * kMRows + lr) * 4 : kBufOutOfRange;
-    pv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, off, 0, 0));
-  }
   float v = 0.0f;
+  for (int g0 = gf; g0 <= gl; g0 += MAXW) {
+    float pv[MAXW];
 #pragma unroll
-  for (int i = 0; i < MAXW; ++i) v += pv[i];
+    for (int i = 0; i < MAXW; ++i) {
+      const int g = g0 + i, gg = min(g, G - 1);        // past gl the offset is out of range
+      const int pi = gg * U / G / T == rb ? gg : G + rb;
+      const int off = g <= gl ? ((pi * a.B + b) * kMRows + lr) * 4 : kBufOutOfRange;
+      pv[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < MAXW; ++i) v += pv[i];
+  }
   gemv_epilogue<EPI>(a, row, b, v, e);
 }
 
@@ -969,6 +1016,7 @@ hipError_t dispatch_wt(int wtype, const GemvArgs &a, hipStream_t stream) {
 // per CU), so that no second, partial round of workgroups forms a tail.
 struct MfmaPlan {
   int G, T, U, nbt, ngt;
+  bool whole;          // one workgroup per row block, the row epilogue in the GEMV kernel
   size_t lds;
 };
 
@@ -982,7 +1030,16 @@ struct MfmaPlan {
 // so workspace sizes can be computed on the host alone.
 constexpr int kMfmaGrid = 256;
 
-MfmaPlan mfma_plan(int wtype, int rows, int K, int B, int ng) {
+// With bf16 weights and at least this many row blocks, a workgroup per row block keeps
+// the HBM about as busy as the balanced stream-K grid, and its sums need no second
+// kernel: the in_proj of the 9B-shaped layer (177 row blocks of 4480) ran 1.3 / 2.8 us
+// longer at 4 / 32 sessions than over 246 workgroups, against 4.7 / 6.9 us for the
+// reduction it drops. int8 weights lost 2 us net (their tiles cost more ALU per byte).
+constexpr int kMfmaWholeMinBlocks = 160;
+
+// `whole_ok`: the caller can take the row epilogue in the GEMV kernel (no RMS prologue, no
+// conv-cache shift).
+MfmaPlan mfma_plan(int wtype, int rows, int K, int B, int ng, bool whole_ok) {
   MfmaPlan p;
   p.nbt = B <= 16 ? 1 : 2;
   const int kt = wtype == M2_W_INT8G ? mfma_kt<M2_W_INT8G>() : mfma_kt<M2_W_BF16>();
@@ -990,14 +1047,15 @@ MfmaPlan mfma_plan(int wtype, int rows, int K, int B, int ng) {
   p.T = (K + kt - 1) / kt;
   p.U = rbn * p.T;
   const int per = (p.U + kMfmaGrid - 1) / kMfmaGrid;
-  p.G = std::max((p.U + per - 1) / per, std::min(p.U, rbn));
+  p.whole = whole_ok && ng == 0 && wtype == M2_W_BF16 && rbn >= kMfmaWholeMinBlocks;
+  p.G = p.whole ? rbn : std::max((p.U + per - 1) / per, std::min(p.U, rbn));
   const int upw = (p.U + p.G - 1) / p.G;               // units per workgroup, at most
   p.ngt = ng > 0 ? upw * kt / ng + 4 : 0;              // norm groups its two k ranges can touch
   p.lds = 4 * sizeof(unsigned short) * (size_t)p.nbt * 16 * (kt + 8) + sizeof(float) * (size_t)B * p.ngt;
   return p;
 }
 
-size_t mfma_part_floats(const MfmaPlan &p, int B) { return (size_t)(p.G + p.U / p.T) * B * kMRows; }
+size_t mfma_part_floats(const MfmaPlan &p, int B) { return p.whole ? 0 : (size_t)(p.G + p.U / p.T) * B * kMRows; }
 
 // The reduction of a plan's partials (and, out_proj, the conv-cache shift): one thread per
 // output, or per conv element if those are more.
@@ -1005,7 +1063,8 @@ template <int EPI>
 hipError_t launch_mfma_reduce(const GemvArgs &g, const MfmaPlan &p, float *part, hipStream_t stream) {
   const long pbytes = (long)mfma_part_floats(p, g.B) * 4;
   if ((long)p.U * p.G >= (1L << 31) || pbytes >= kBufOutOfRange) return hipErrorInvalidValue;
-  // workgroups of a row block: its T units over runs of at least U / G units each
+  // workgroups of a row block: its T units over runs of at least U / G units each (more
+  // than 32 are summed in batches of 32)
   const int minrun = std::max(1, p.U / p.G);
   const int maxw = (p.T + minrun - 1) / minrun + 1;
   long n = (long)g.rows * g.B;
@@ -1017,60 +1076,74 @@ hipError_t launch_mfma_reduce(const GemvArgs &g, const MfmaPlan &p, float *part,
     hipLaunchKernelGGL((gemv_mfma_reduce_kernel<EPI, 8>), grid, block, 0, stream, g, part, p.T, p.G, (int)pbytes);
   else if (maxw <= 16)
     hipLaunchKernelGGL((gemv_mfma_reduce_kernel<EPI, 16>), grid, block, 0, stream, g, part, p.T, p.G, (int)pbytes);
-  else if (maxw <= 32)
-    hipLaunchKernelGGL((gemv_mfma_reduce_kernel<EPI, 32>), grid, block, 0, stream, g, part, p.T, p.G, (int)pbytes);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv_mfma_reduce_kernel<EPI, 32>), grid, block, 0, stream, g, part, p.T, p.G, (int)pbytes);
   return hipGetLastError();
 }
 
-template <int WT, bool PANEL, int NBT, bool RMS, int SPG>
-hipError_t launch_mfma_k(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
-  auto *k = gemv_mfma_kernel<WT, PANEL, NBT, RMS, SPG>;
+template <int WT, bool PANEL, int NBT, bool RMS, int SPG, int EPI>
+hipError_t launch_mfma_k(const MfmaArgs &m, const GemvArgs &g, const MfmaPlan &p, hipStream_t stream) {
+  auto *k = gemv_mfma_kernel<WT, PANEL, NBT, RMS, SPG, EPI>;
   hipError_t e = allow_lds(k, p.lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(p.G), dim3(512), p.lds, stream, m);
+  hipLaunchKernelGGL(k, dim3(p.G), dim3(512), p.lds, stream, m, g);
   return hipGetLastError();
 }
 
+// The in-kernel epilogue exists for bf16 weights and the in_proj epilogue only (the plans
+// that choose it).
 template <int WT, bool PANEL, bool RMS, int SPG>
-hipError_t launch_mfma_nbt(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
-  return p.nbt == 1 ? launch_mfma_k<WT, PANEL, 1, RMS, SPG>(m, p, stream)
-                    : launch_mfma_k<WT, PANEL, 2, RMS, SPG>(m, p, stream);
+hipError_t launch_mfma_nbt(const MfmaArgs &m, const GemvArgs &g, int epi, const MfmaPlan &p, hipStream_t stream) {
+  if constexpr (WT == M2_W_BF16 && !RMS) {
+    if (p.whole) {
+      if (epi != EPI_INPROJ) return hipErrorInvalidValue;
+      return p.nbt == 1 ? launch_mfma_k<WT, PANEL, 1, RMS, SPG, EPI_INPROJ>(m, g, p, stream)
+                        : launch_mfma_k<WT, PANEL, 2, RMS, SPG, EPI_INPROJ>(m, g, p, stream);
+    }
+  }
+  if (p.whole) return hipErrorInvalidValue;
+  return p.nbt == 1 ? launch_mfma_k<WT, PANEL, 1, RMS, SPG, kEpiPartials>(m, g, p, stream)
+                    : launch_mfma_k<WT, PANEL, 2, RMS, SPG, kEpiPartials>(m, g, p, stream);
 }
 
 // The kernels' buffer offsets (a row block of W or of its panels, the activations [B][K],
 // the scales, with the out-of-range marker above all) and U G must stay below 2^31.
 template <int WT, bool PANEL, bool RMS>
-hipError_t launch_mfma(const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
+hipError_t launch_mfma(const MfmaArgs &m, const GemvArgs &g, int epi, const MfmaPlan &p, hipStream_t stream) {
   const long esz = WT == M2_W_BF16 ? 2 : 1;
   const long kpad = PANEL ? (long)(m.K + 31) / 32 * 32 : m.K;
   if ((long)kMRows * kpad * esz >= kBufOutOfRange || (long)m.B * m.K * 4 >= kBufOutOfRange ||
       (long)m.rows * (m.K / m.q_group) * 2 >= kBufOutOfRange || (long)p.U * p.G >= (1L << 31))
     return hipErrorInvalidValue;
   if constexpr (WT == M2_W_BF16) {
-    return launch_mfma_nbt<WT, PANEL, RMS, 8>(m, p, stream);
+    return launch_mfma_nbt<WT, PANEL, RMS, 8>(m, g, epi, p, stream);
   } else {
-    if (m.q_group == 128) return launch_mfma_nbt<WT, PANEL, RMS, 4>(m, p, stream);
-    if (m.q_group == 256) return launch_mfma_nbt<WT, PANEL, RMS, 8>(m, p, stream);
+    if (m.q_group == 128) return launch_mfma_nbt<WT, PANEL, RMS, 4>(m, g, epi, p, stream);
+    if (m.q_group == 256) return launch_mfma_nbt<WT, PANEL, RMS, 8>(m, g, epi, p, stream);
     return hipErrorInvalidValue;
   }
 }
 
+// `g`, `epi`: the row epilogue of a whole-row-block plan (unused otherwise).
 template <bool RMS>
-hipError_t launch_mfma_wt(int wtype, bool panel, const MfmaArgs &m, const MfmaPlan &p, hipStream_t stream) {
+hipError_t launch_mfma_wt(int wtype, bool panel, const MfmaArgs &m, const GemvArgs &g, int epi, const MfmaPlan &p,
+                          hipStream_t stream) {
   if (wtype == M2_W_BF16)
-    return panel ? launch_mfma<M2_W_BF16, true, RMS>(m, p, stream) : launch_mfma<M2_W_BF16, false, RMS>(m, p, stream);
-  return panel ? launch_mfma<M2_W_INT8G, true, RMS>(m, p, stream) : launch_mfma<M2_W_INT8G, false, RMS>(m, p, stream);
+    return panel ? launch_mfma<M2_W_BF16, true, RMS>(m, g, epi, p, stream)
+                 : launch_mfma<M2_W_BF16, false, RMS>(m, g, epi, p, stream);
+  return panel ? launch_mfma<M2_W_INT8G, true, RMS>(m, g, epi, p, stream)
+               : launch_mfma<M2_W_INT8G, false, RMS>(m, g, epi, p, stream);
 }
 
 // One MFMA GEMV + reduce for the arguments of a gemv_* launch, from the 16-row panels of
-// the weights when given; out_proj (EPI_OUT) also forms the RMS factors from g.ss.
+// the weights when given; out_proj (EPI_OUT) also forms the RMS factors from g.ss. An
+// in_proj plan of whole row blocks applies the epilogue in the GEMV kernel and needs no
+// reduction.
 template <int EPI>
 hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, const void *panels, float *part,
                          hipStream_t stream) {
   constexpr bool RMS = EPI == EPI_OUT;
-  const MfmaPlan p = mfma_plan(c.wtype, g.rows, g.K, g.B, RMS ? g.ng : 0);
+  const MfmaPlan p = mfma_plan(c.wtype, g.rows, g.K, g.B, RMS ? g.ng : 0, EPI == EPI_INPROJ);
   MfmaArgs m{};
   m.W = panels ? panels : g.W;
   m.S = static_cast<const __half *>(g.S);
@@ -1089,8 +1162,8 @@ hipError_t run_mfma_gemv(const m2_config &c, const GemvArgs &g, const void *pane
   m.eps = g.eps;
   m.ngt = p.ngt;
   m.part = part;
-  hipError_t e = launch_mfma_wt<RMS>(c.wtype, panels != nullptr, m, p, stream);
-  if (e != hipSuccess) return e;
+  hipError_t e = launch_mfma_wt<RMS>(c.wtype, panels != nullptr, m, g, EPI, p, stream);
+  if (e != hipSuccess || p.whole) return e;
   return launch_mfma_reduce<EPI>(g, p, part, stream);
 }
 
@@ -1308,8 +1381,8 @@ StepWs step_ws_layout(const m2_layer_s &L, int batch, void *base) {
   w.bar = p ? reinterpret_cast<unsigned *>(p + off) : nullptr;
   off += align256(kBarBytes);
   if (step_uses_mfma(L, batch)) {
-    const MfmaPlan pi = mfma_plan(L.cfg.wtype, L.d_in_proj, L.cfg.d_model, batch, 0);
-    const MfmaPlan po = mfma_plan(L.cfg.wtype, L.cfg.d_model, L.d_inner, batch, L.ng);
+    const MfmaPlan pi = mfma_plan(L.cfg.wtype, L.d_in_proj, L.cfg.d_model, batch, 0, true);
+    const MfmaPlan po = mfma_plan(L.cfg.wtype, L.cfg.d_model, L.d_inner, batch, L.ng, false);
     const size_t n_in = mfma_part_floats(pi, batch), n_out = mfma_part_floats(po, batch);
     w.part = p ? reinterpret_cast<float *>(p + off) : nullptr;
     off += align256(sizeof(float) * (n_in > n_out ? n_in : n_out));
@@ -1498,7 +1571,7 @@ bool gemv_plain_uses_mfma(int wtype, int q_group, int batch) {
 
 size_t gemv_plain_part_bytes(int wtype, int q_group, int rows, int K, int batch) {
   if (!gemv_plain_uses_mfma(wtype, q_group, batch)) return 0;
-  const MfmaPlan p = mfma_plan(wtype, rows, K, batch, 0);
+  const MfmaPlan p = mfma_plan(wtype, rows, K, batch, 0, false);
   return sizeof(float) * mfma_part_floats(p, batch);
 }
 
@@ -1523,7 +1596,7 @@ hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, 
   // 3-32 sessions with bf16 (or int8 g128/g256) weights: the MFMA GEMV over K chunks, then
   // the reduction with the plain epilogue (as the decode step's MFMA plan, without RMS).
   if (gemv_plain_uses_mfma(wtype, q_group, batch)) {
-    const MfmaPlan p = mfma_plan(wtype, rows, K, batch, 0);
+    const MfmaPlan p = mfma_plan(wtype, rows, K, batch, 0, false);
     MfmaArgs m{};
     m.W = W;
     m.S = static_cast<const __half *>(S);
@@ -1536,7 +1609,7 @@ hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, 
     m.act = act;
     m.B = batch;
     m.part = part;
-    hipError_t e = launch_mfma_wt<false>(wtype, false, m, p, stream);
+    hipError_t e = launch_mfma_wt<false>(wtype, false, m, a, EPI_OUT, p, stream);
     if (e != hipSuccess) return e;
     return launch_mfma_reduce<EPI_OUT>(a, p, part, stream);
   }

@@ -260,6 +260,23 @@ def test_lowbit_ragged_k(wtype, q_group, d_model, batch):
     _check("lowbit-ragged-%s-g%d-k%d-b%d" % (wtype, q_group, d_model, batch), dims, w, xs, ssm0, conv0)
 
 
+@pytest.mark.parametrize("batch,panels", [(5, True), (17, False)])
+def test_mfma_whole_row_block_in_proj(batch, panels):
+    """bf16 in_proj of at least 160 row blocks: one workgroup per 128-row block applies the
+    row epilogue itself (no partial sums). 20714 rows (161 whole blocks and one of 106 rows,
+    which holds the dt rows) x 336 (K not a multiple of the 32-wide k-step); one and two
+    16-session MFMA tiles; slots permuted, residual on."""
+    dims = synth.MixerDims(d_model=336, n_heads=106, head_dim=96, d_state=64, n_groups=2, wtype="bf16")
+    assert dims.d_in_proj == 20714
+    w = synth.make_layer_weights(dims, 181)
+    xs = synth.make_inputs(dims, 182, 4, batch)
+    n_slots = batch + 2
+    ssm0, conv0 = synth.make_state(dims, 183, n_slots, 0.1)
+    slots = np.random.default_rng(184).permutation(n_slots)[:batch].astype(np.int32)
+    _check("mfma-whole-b%d-%s" % (batch, "panels" if panels else "rows"), dims, w, xs, ssm0, conv0,
+           slot_ids=slots, residual=True, panels=panels)
+
+
 @pytest.mark.parametrize("wtype,batch", [("bf16", 8), ("int8g", 5), ("bf16", 32)])
 def test_mfma_plan_graph_replays_match_eager_steps(wtype, batch):
     """A captured step of the MFMA plan (GEMV + reduction kernels around the SSD kernel),
