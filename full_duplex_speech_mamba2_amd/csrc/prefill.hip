@@ -60,7 +60,8 @@ constexpr size_t kGemmLds = sizeof(unsigned short) * 2 * (2 * GBM + GBN) * GLD; 
 struct GemmArgs {
   const float *A;
   int lda;
-  const unsigned short *W;   // bf16 [N][K]
+  const unsigned short *W;   // bf16 [N][K], or its 16-row panels (PANEL)
+  int S;                     // panels: 32-wide k-steps per panel, ceil(K / 32)
   float *C;
   int ldc;
   const float *R;            // residual [M][ldr] or null
@@ -75,6 +76,10 @@ struct GemmArgs {
 // from LDS for 16 MFMAs. LDS (dynamic, 80 KB, so two workgroups per CU): double-
 // buffered A hi, A lo [128][40] and W [256][40] bf16 (rows padded to 80 B). The next
 // K tile's global loads are held in registers while the current one is multiplied.
+// PANEL: W is read from its 16-row panels (m2_pack_panels), where the tile's 32 k of 16
+// rows are one contiguous 1 KB (row-major, each of the 256 rows gives 64 B of a 128-byte
+// line per tile).
+template <bool PANEL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_kernel(GemmArgs g) {
   extern __shared__ unsigned short gsm[];
   unsigned short *sAh = gsm;                          // [2][GBM * GLD]
@@ -113,8 +118,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int q = 0; q < 4; ++q) ra[q] = *reinterpret_cast<const f32x4 *>(arow + ka + 4 * q);
     // the out_proj scale per (row, norm group): one group covers the 16 values (ng % 16 == 0)
     if (rsrow) rsc = rsrow[ka / g.ng];
+    if constexpr (PANEL) {
+      static_assert(GBK == 32 && GBN == 256, "one k-step of 16 panels per tile");
+      // fragment f = tid + 256 q: panel f / 64 of the tile (past the matrix: its last
+      // panel, whose results are never stored), lane f % 64 of the tile's k-step; the
+      // panels are zero past K
+      const int npan = (g.N + 15) / 16, s = k0 >> 5;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) rw[q] = *reinterpret_cast<const u32x4 *>(wrow + min(k0 + 8 * q, g.K - 8));
+      for (int q = 0; q < 4; ++q) {
+        const int f = tid + 256 * q, p = min(n0 / 16 + (f >> 6), npan - 1);
+        rw[q] = *reinterpret_cast<const u32x4 *>(g.W + (((size_t)p * g.S + s) * 64 + (f & 63)) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rw[q] = *reinterpret_cast<const u32x4 *>(wrow + min(k0 + 8 * q, g.K - 8));
+    }
   };
   auto store_tile = [&](int buf, int k0) {
     // hi = bf16(v), lo = bf16(v - hi), both rounded to nearest even (packed converts)
@@ -130,9 +148,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       ph[q] = h;
       pl[q] = __builtin_convertvector(v - __builtin_convertvector(h, f32x8), bf16x8);
     }
-    u32x4 *pw = reinterpret_cast<u32x4 *>(&sW[buf * GBN * GLD + tid * GLD]);
+    if constexpr (PANEL) {
+      // fragment lane l holds row l % 16 of its panel, k 8 (l / 16) .. + 7
 #pragma unroll
-    for (int q = 0; q < 4; ++q) pw[q] = k0 + 8 * q < g.K ? rw[q] : u32x4{0u, 0u, 0u, 0u};
+      for (int q = 0; q < 4; ++q) {
+        const int f = tid + 256 * q, row = 16 * (f >> 6) + (f & 15), col = 8 * ((f & 63) >> 4);
+        *reinterpret_cast<u32x4 *>(&sW[buf * GBN * GLD + row * GLD + col]) = rw[q];
+      }
+    } else {
+      u32x4 *pw = reinterpret_cast<u32x4 *>(&sW[buf * GBN * GLD + tid * GLD]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pw[q] = k0 + 8 * q < g.K ? rw[q] : u32x4{0u, 0u, 0u, 0u};
+    }
   };
 
   f32x16 acc[2][4];
@@ -907,7 +934,9 @@ hipError_t run_gemm(const m2_layer_s &L, bool in_proj, const float *A, int lda, 
     GemmArgs g{};
     g.A = A;
     g.lda = lda;
-    g.W = static_cast<const unsigned short *>(in_proj ? L.w.w_in : L.w.w_out);
+    const void *panels = in_proj ? L.w.w_in_panels : L.w.w_out_panels;
+    g.W = static_cast<const unsigned short *>(panels ? panels : in_proj ? L.w.w_in : L.w.w_out);
+    g.S = (K + 31) / 32;
     g.C = C;
     g.ldc = ldc;
     g.R = R;
@@ -918,10 +947,11 @@ hipError_t run_gemm(const m2_layer_s &L, bool in_proj, const float *A, int lda, 
     g.M = M;
     g.N = N;
     g.K = K;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_bf16_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+    auto *k = panels ? gemm_bf16_kernel<true> : gemm_bf16_kernel<false>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kGemmLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(((N + GBN - 1) / GBN) * ((M + GBM - 1) / GBM)), dim3(256), kGemmLds, stream, g);
+    hipLaunchKernelGGL(k, dim3(((N + GBN - 1) / GBN) * ((M + GBM - 1) / GBM)), dim3(256), kGemmLds, stream, g);
     return hipGetLastError();
   }
   GemmValuArgs g{};
