@@ -179,8 +179,8 @@ class Layer:
 
     With panels (the default, bf16 and int8 weights only) the layer also holds the 16-row
     panel copies of W_in and W_out (m2_pack_panels), which the batched decode step's
-    matrix-core GEMVs read; panels=False leaves them out (those GEMVs then read the
-    row-major weights)."""
+    matrix-core GEMVs and the bf16 prefill GEMMs read; panels=False leaves them out (those
+    kernels then read the row-major weights)."""
 
     def __init__(self, dims, weights: Dict[str, object], device="cuda", panels: bool = True):
         self.dims = dims

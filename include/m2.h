@@ -114,8 +114,9 @@ typedef struct {
   const float *D;           /* [H] */
   const float *norm_w;      /* [d_inner] */
   /* Optional (NULL: not used): w_in / w_out of a bf16 or int8 layer repacked into 16-row
-     panels by m2_pack_panels. The batched decode step (3 to 32 sessions) then reads these
-     instead of w_in / w_out; every other path reads w_in / w_out. */
+     panels by m2_pack_panels. The batched decode step (3 to 32 sessions) and the bf16
+     prefill GEMMs then read these instead of w_in / w_out (same results, bit for bit);
+     every other path reads w_in / w_out. */
   const void *w_in_panels;  /* m2_panels_bytes(wtype, d_in_proj, d_model) bytes */
   const void *w_out_panels; /* m2_panels_bytes(wtype, d_model, d_inner) bytes */
 } m2_weights;
@@ -135,7 +136,7 @@ void m2_layer_destroy(m2_layer layer);
 
 /* Panel layout of the projections W_in and W_out (the zxbcdt = W_in u and out = W_out yn
  * products above) for the batched decode step, whose matrix-core GEMVs take 16 rows x 32
- * columns per instruction: the matrix is cut into panels of 16 rows (the last one padded
+ * columns per instruction, and for the bf16 prefill GEMMs: the matrix is cut into panels of 16 rows (the last one padded
  * with zero rows), each stored as ceil(K/32) steps of 32 columns (the last padded with
  * zeros); step s of panel p is 64 fragments of 8 consecutive elements in fragment order,
  * fragment l holding row 16p + l%16, columns 32s + 8(l/16) .. +7, so that one load

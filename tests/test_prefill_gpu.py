@@ -52,6 +52,28 @@ def test_small_bf16_ragged_lengths(T, chunk):
     _check("small-T%d-c%d" % (T, chunk), SMALL, w, x, ssm0, conv0, chunk)
 
 
+def test_panel_and_row_major_weights_give_identical_prefill():
+    """The bf16 projection GEMMs read W from the 16-row panel copies when the layer holds
+    them, row-major otherwise: the same products in the same order, so bitwise-equal outputs,
+    states and conv caches (K = 272, half a 32-wide k-step past the last whole one; in_proj
+    N = 388, out_proj N = 272: ragged column tiles)."""
+    import torch
+    from full_duplex_speech_mamba2_amd import m2
+    w = synth.make_layer_weights(SMALL, 121)
+    x = synth.make_prompt(SMALL, 122, 2, 70)
+    ssm0, conv0 = synth.make_state(SMALL, 123, 2, 0.1)
+    outs = []
+    for panels in (True, False):
+        lay = m2.Layer(SMALL, w, panels=panels)
+        assert (lay.tensors.get("w_in_panels") is not None) == panels
+        st = m2.State(lay, 2, torch.from_numpy(ssm0).cuda(), torch.from_numpy(conv0).cuda())
+        y = m2.prefill(lay, st, torch.from_numpy(x).cuda(), chunk=32)
+        torch.cuda.synchronize()
+        outs.append((y.cpu().numpy(), st.ssm.cpu().numpy(), st.conv.cpu().numpy()))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
 def test_small_slots_residual_and_all_weight_types():
     for wtype in ("f32", "bf16", "int8g"):
         dims = SMALL.replace(wtype=wtype, q_group=16, q_gamma_in=0.0625, q_gamma_out=0.1)
