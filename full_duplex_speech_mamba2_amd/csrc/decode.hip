@@ -33,7 +33,7 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // gemv_wave: one wave per row, whole-K activations of BT (= batch) sessions in LDS.
-// LDS: act [BT][K] | part [n_partials] | rn [BT][n_norm]
+// LDS: act [BT][K] | rn [BT][n_norm]
 template <int WT, int BT, int TPB, int U, int NT, int PRO, int EPI>
 __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
   extern __shared__ float lds[];
@@ -906,7 +906,7 @@ hipError_t allow_lds(F *kernel, size_t bytes) {
 constexpr size_t kWaveLdsMax = 96 * 1024;
 
 size_t wave_lds_bytes(const GemvArgs &a, int BT, int PRO) {
-  return sizeof(float) * ((size_t)BT * a.K + (PRO == PRO_NORM ? (size_t)a.n_partials + (size_t)BT * a.n_norm : 0));
+  return sizeof(float) * ((size_t)BT * a.K + (PRO == PRO_NORM ? (size_t)BT * a.n_norm : 0));
 }
 
 template <int WT, int BT, int TPB, int U, int NT, int PRO, int EPI>

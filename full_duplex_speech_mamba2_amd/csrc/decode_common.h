@@ -375,44 +375,40 @@ __device__ __forceinline__ void rms_factors(const GemvArgs &a, int b0, int nb, f
   }
 }
 
-// out_proj activation staging in one memory trip: each thread loads its float4s
-// of v * norm_w and one sum-of-squares partial per session together, the RMS
-// factors are formed in LDS, then the float4s are scaled by their group's factor.
-// LDS: act [BT][K] | part [n_partials] | rn [BT][n_norm]. K/4 <= TPB * kNormF4PerThread.
+// out_proj activation staging in one memory trip: each thread loads its float4s of
+// v * norm_w (kept in registers) and, with them, its lanes' share of the sums-of-squares
+// partials; wave w reduces norm groups w, w + W, ... (each lane a strided part of the
+// group's partials, then a cross-lane tree: a fixed order) into their RMS factors, and after
+// one barrier every thread writes its float4s scaled by their group's factor.
+// LDS: act [BT][K] | rn [BT][n_norm]. K/4 <= TPB * kNormF4PerThread.
 template <int BT, int TPB>
 __device__ __forceinline__ void stage_norm_act(const GemvArgs &a, float *lds, int tid) {
-  const int K = a.K;
-  const int nb = min(BT, a.B);
+  constexpr int MAXF = kNormF4PerThread, W = TPB / 64;
+  const int K = a.K, nb = min(BT, a.B), nf = K / 4;
+  const int lane = tid & 63, wave = tid >> 6;
   float *act_s = lds;
-  float *part = lds + BT * K;
-  float *rn = part + a.n_partials;
-  constexpr int MAXF = kNormF4PerThread;
-  const int nf = K / 4;
-  float pv[BT];
+  float *rn = lds + BT * K;
+  float4 v[BT][MAXF];
 #pragma unroll
-  for (int bb = 0; bb < BT; ++bb) {
-    pv[bb] = (bb < nb && tid < a.n_partials) ? a.ss[(size_t)bb * a.n_partials + tid] : 0.0f;
+  for (int bb = 0; bb < BT; ++bb)
 #pragma unroll
     for (int i = 0; i < MAXF; ++i) {
       const int f = tid + TPB * i;
-      if (f < nf)
-        reinterpret_cast<float4 *>(act_s + bb * K)[f] =
-            bb < nb ? reinterpret_cast<const float4 *>(a.act + (size_t)bb * K)[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[bb][i] = (bb < nb && f < nf) ? reinterpret_cast<const float4 *>(a.act + (size_t)bb * K)[f]
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-  }
   const int per = a.n_partials / a.n_norm;
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) {
-    if (tid < a.n_partials) part[tid] = pv[bb];
-    __syncthreads();
-    if (tid < a.n_norm) {
+    const float *ssb = a.ss + (size_t)min(bb, nb - 1) * a.n_partials;
+    for (int g = wave; g < a.n_norm; g += W) {
       float sum = 0.0f;
-      for (int q = 0; q < per; ++q) sum += part[tid * per + q];
-      rn[bb * a.n_norm + tid] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
+      for (int q = lane; q < per; q += 64) sum += ssb[g * per + q];
+      sum = group_reduce<64>(sum);
+      if (lane == 0) rn[bb * a.n_norm + g] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
     }
-    __syncthreads();
   }
-  // each thread rescales the float4s it staged
+  __syncthreads();
   const int ng4 = a.ng / 4;
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb)
@@ -421,9 +417,8 @@ __device__ __forceinline__ void stage_norm_act(const GemvArgs &a, float *lds, in
       const int f = tid + TPB * i;
       if (f < nf) {
         const float r = bb < nb ? rn[bb * a.n_norm + f / ng4] : 0.0f;
-        float4 *p4 = reinterpret_cast<float4 *>(act_s + bb * K) + f;
-        const float4 x = *p4;
-        *p4 = make_float4(x.x * r, x.y * r, x.z * r, x.w * r);
+        const float4 x = v[bb][i];
+        reinterpret_cast<float4 *>(act_s + bb * K)[f] = make_float4(x.x * r, x.y * r, x.z * r, x.w * r);
       }
     }
 }
