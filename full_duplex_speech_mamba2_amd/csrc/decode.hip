@@ -118,7 +118,7 @@ __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
 // any LDS write (the weight loads go out first), then the sum of every 32-element chunk
 // of each session is formed once, for the group bias: w = s q + m gives
 // sum_k w_k x_k = s sum_k q_k x_k + m sum_k x_k.
-// LDS: act [BT][K] | xsum [BT][K/32] (| part [BT][n_partials] | rn [BT][n_norm], out_proj)
+// LDS: act [BT][K] | xsum [BT][K/32] (| rn [BT][n_norm], out_proj)
 constexpr int kLbThreads = 512;
 
 template <int WT, int BT, int PRO>
@@ -127,31 +127,29 @@ __device__ __forceinline__ void lb_stage(const GemvArgs &a, float *lds, int tid)
   constexpr int MAXF = kNormF4PerThread;
   const int K = a.K, nf = K / 4, nb = min(BT, a.B);
   f32x4 v[BT][MAXF];
-  float pv[BT];
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) {
     const int sb = min(bb, nb - 1);
     const f32x4 *src = reinterpret_cast<const f32x4 *>(a.act + (size_t)sb * K);
 #pragma unroll
     for (int i = 0; i < MAXF; ++i) v[bb][i] = src[min(tid + TPB * i, nf - 1)];   // clamped index
-    pv[bb] = PRO != PRO_NORM ? 0.0f : a.ss[(size_t)sb * a.n_partials + min(tid, a.n_partials - 1)];
   }
   const int KP = lds_padded(K);
   float *acts = lds;
   if (PRO == PRO_NORM) {
-    float *part = lds + BT * (KP + K / 32);
-    float *rn = part + BT * a.n_partials;
-    if (tid < a.n_partials) {
+    // the RMS factors: wave w reduces norm groups w, w + 8, ... (each lane a strided part of
+    // the group's partials, then a cross-lane tree: a fixed order)
+    float *rn = lds + BT * (KP + K / 32);
+    const int per = a.n_partials / a.n_norm, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-      for (int bb = 0; bb < BT; ++bb) part[bb * a.n_partials + tid] = pv[bb];
-    }
-    __syncthreads();
-    const int per = a.n_partials / a.n_norm;
-    for (int j = tid; j < BT * a.n_norm; j += TPB) {
-      const int bb = j / a.n_norm, q = j - bb * a.n_norm;
-      float sum = 0.0f;
-      for (int k = 0; k < per; ++k) sum += part[bb * a.n_partials + q * per + k];
-      rn[j] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
+    for (int bb = 0; bb < BT; ++bb) {
+      const float *ssb = a.ss + (size_t)min(bb, nb - 1) * a.n_partials;
+      for (int g = wave; g < a.n_norm; g += TPB / 64) {
+        float sum = 0.0f;
+        for (int q = lane; q < per; q += 64) sum += ssb[g * per + q];
+        sum = group_reduce<64>(sum);
+        if (lane == 0) rn[bb * a.n_norm + g] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
+      }
     }
     __syncthreads();
     const int ng4 = a.ng / 4;
@@ -940,8 +938,7 @@ int pick_kt(int K, int BT) {
 }
 
 size_t lowbit_lds_bytes(const GemvArgs &a, int BT, int PRO) {
-  return sizeof(float) * ((size_t)BT * (lds_padded(a.K) + a.K / 32) +
-                          (PRO == PRO_NORM ? (size_t)BT * (a.n_partials + a.n_norm) : 0));
+  return sizeof(float) * ((size_t)BT * (lds_padded(a.K) + a.K / 32) + (PRO == PRO_NORM ? (size_t)BT * a.n_norm : 0));
 }
 
 template <int WT, int BT, int R, int U, int NT, int PRO, int EPI>
