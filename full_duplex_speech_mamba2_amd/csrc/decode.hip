@@ -467,6 +467,7 @@ constexpr int kMRows = 128;        // rows per workgroup (8 waves x 16)
 template <int WT> constexpr int mfma_kt() { return 256; }
 template <int WT> constexpr int mfma_ldw() { return mfma_kt<WT>() + 8; }
 constexpr int kMaxScaleGroups = 2; // int8 scale groups in one k tile (q_group >= 128)
+constexpr int kRmsLoads = 16;      // out_proj RMS prologue: partial sums a lane requests at once
 
 struct MfmaArgs {
   const void *W;                   // row-major [rows][K], or 16-row panels
@@ -763,14 +764,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int per = a.n_partials / a.n_norm;
     for (int base = 0; base < a.B * nh * 8; base += 512) {
       const int i = base + tid, pair = i >> 3, j = i & 7;
+      const bool ok = pair < a.B * nh;
+      const int pc = ok ? pair : 0;
+      const int b = pc / max(nh, 1), slot = pc - b * nh;
+      const int g = slot < m.nA ? m.g0 + slot : slot - m.nA;
+      const float *sp = a.ss + (size_t)b * a.n_partials + g * per;
       float sum = 0.0f;
-      const int b = pair / max(nh, 1), slot = pair - b * nh;
-      if (pair < a.B * nh) {
-        const int g = slot < m.nA ? m.g0 + slot : slot - m.nA;
-        for (int q = j; q < per; q += 8) sum += a.ss[(size_t)b * a.n_partials + g * per + q];
+      // this lane's partials j, j + 8, ... requested together (indices clamped, values
+      // selected after: a load behind a branch or in a loop waits for everything before it),
+      // added in that order
+      for (int q0 = j; q0 < per; q0 += 8 * kRmsLoads) {
+        float pv[kRmsLoads];
+#pragma unroll
+        for (int k = 0; k < kRmsLoads; ++k) pv[k] = sp[min(q0 + 8 * k, per - 1)];
+#pragma unroll
+        for (int k = 0; k < kRmsLoads; ++k) sum += q0 + 8 * k < per ? pv[k] : 0.0f;
       }
       sum = group_reduce<8>(sum);
-      if (pair < a.B * nh && j == 0) rn_s[b * a.ngt + slot] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
+      if (ok && j == 0) rn_s[b * a.ngt + slot] = 1.0f / sqrtf(sum / (float)a.ng + a.eps);
     }
     lds_barrier();
   }
