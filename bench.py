@@ -53,7 +53,8 @@ def parse():
                     help="identical weight copies used in turn (0: enough for >= 590 MB)")
     ap.add_argument("--no-graph", action="store_true", help="time plain launches only")
     ap.add_argument("--persistent", action="store_true",
-                    help="single-layer decode workloads: plan 2 (the persistent SSD + out_proj kernel)")
+                    help="single-layer decode workloads: plan 2 (the persistent SSD + out_proj kernel); "
+                         "stack workloads: each run of mixer layers in one persistent launch")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline and parity")
     ap.add_argument("--prof-steps", type=int, default=200, help="steps of the per-kernel event pass")
@@ -700,7 +701,11 @@ def bench_stack(args, wl):
     sets = torch.arange(n_slots, dtype=torch.int32, device=dev).reshape(S, B).contiguous()
     xs = torch.from_numpy(synth.make_inputs(wl.mixer, wl.seed, wl.steps, B)).to(dev)
     ys = torch.empty_like(xs)
-    ws = stack.workspace(B)
+    persistent = bool(args.persistent)
+    runs = stack.persistent_runs(B) if persistent else 0
+    if persistent and runs == 0:
+        raise SystemExit("--persistent: the persistent stack step does not apply to %s" % wl.name)
+    ws = stack.workspace(B, persistent)
     nx = xs.shape[0]
     if args.steps // S > wl.attn.max_len - wl.start_pos:
         raise SystemExit("--steps %d would fill the caches" % args.steps)
@@ -711,7 +716,7 @@ def bench_stack(args, wl):
 
     def run(t0, n):
         for t in range(t0, t0 + n):
-            stack.step(xs[t % nx], ys[t % nx], slot_ids=sets[t % S], ws=ws)
+            stack.step(xs[t % nx], ys[t % nx], slot_ids=sets[t % S], ws=ws, persistent=persistent)
 
     run(0, min(args.warmup, S * (wl.attn.max_len - wl.start_pos)))
     reset()
@@ -736,6 +741,7 @@ def bench_stack(args, wl):
     hip = hip_runtime()
     evs = [[hip_event(hip) for _ in range(4)] for _ in range(kp)]
     lay0, st0 = entries[0]
+    ws = stack.workspace(B)
     torch.cuda.synchronize()
     hold_gpu(150.0)
     for t in range(kp):
@@ -760,6 +766,7 @@ def bench_stack(args, wl):
         "config": {"workload": wl.name, "pattern": wl.pattern, "mixer_layers": n_m, "attention_layers": n_a,
                    "d_model": wl.mixer.d_model, "batch": B, "weight_dtype": wl.mixer.wtype, "kv_dtype": "bf16",
                    "start_positions": wl.start_pos, "mean_attended": round(mean_len, 1), "slot_sets": S,
+                   "persistent_runs": runs,
                    "timing": "graph" if (ms_graph is not None and ms_graph <= ms_eager) else "eager"},
         "achieved_GBps": round(step_bytes * sps / 1e9, 1),
         "hbm_peak_frac": round(step_bytes * sps / 1e9 / HBM_PEAK_GBPS, 4),

@@ -58,6 +58,11 @@ __device__ __forceinline__ void stc(float *p, float v) {
   if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else *p = v;
 }
+template <bool COH>
+__device__ __forceinline__ float4 ldc4(const float *p) {
+  if constexpr (COH) return make_float4(ldc<true>(p), ldc<true>(p + 1), ldc<true>(p + 2), ldc<true>(p + 3));
+  else return *reinterpret_cast<const float4 *>(p);
+}
 
 // Grid-barrier words of the persistent SSD + out_proj kernel, one per 128-byte line (their
 // atomics and polls then go to different memory channels): a counter per group of
@@ -337,6 +342,7 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs &a, int row, int b,
 // The conv cache after this step: the last d_conv-1 raw inputs, oldest first.
 // Runs in the out_proj kernels, after every reader of the old cache (the SSD
 // kernel) has finished. Elements (session, channel) strided over the grid.
+template <bool ZC = false>
 __device__ __forceinline__ void conv_cache_shift(const GemvArgs &a, size_t gtid, size_t gthreads) {
   const size_t total = (size_t)a.B * a.conv_dim;
   const int nk = a.d_conv - 1;                      // 1..7 cached inputs
@@ -350,7 +356,7 @@ __device__ __forceinline__ void conv_cache_shift(const GemvArgs &a, size_t gtid,
     float v[7];
 #pragma unroll
     for (int k = 0; k < 6; ++k) v[k] = k + 1 < nk ? cc[(size_t)(k + 1) * a.conv_dim] : 0.0f;
-    v[6] = a.zx[(size_t)b * a.zx_stride + a.d_inner + c];
+    v[6] = ldc<ZC>(a.zx + (size_t)b * a.zx_stride + a.d_inner + c);
 #pragma unroll
     for (int k = 0; k < 6; ++k)
       if (k + 1 < nk) cc[(size_t)k * a.conv_dim] = v[k];
@@ -442,8 +448,10 @@ __device__ __forceinline__ void st_stream(float4 *p, const float4 &v) {
 // Causal conv + SiLU of 4 consecutive conv channels c0..c0+3 of one session
 // (cache slot `slot`): bias + sum_k w[c][k] in(t-K+1+k), the last K-1 inputs from
 // the cache, the newest the raw in_proj output.
+// ZC: zx was written inside the same launch (read past the per-XCD caches).
+template <bool ZC = false>
 __device__ __forceinline__ float4 conv4(const SsdArgs &a, const float *zb, int slot, int c0) {
-  const float4 raw = *reinterpret_cast<const float4 *>(zb + a.d_inner + c0);
+  const float4 raw = ldc4<ZC>(zb + a.d_inner + c0);
   const float4 bias = *reinterpret_cast<const float4 *>(a.conv_b + c0);
   const float *cache = a.conv_cache + (size_t)slot * (a.d_conv - 1) * a.conv_dim + c0;
   const float r[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -536,7 +544,8 @@ struct NoOp {
 
 // mid(): called by every wave once the item's own loads have all been issued and the conv
 // outputs are in LDS (a caller's loads for a later phase, which then cannot delay these).
-template <int NW, int MAXI, bool STORE, bool COH = false, typename Mid = NoOp>
+// ZC: zx was written inside the same launch, so its reads go past the per-XCD caches too.
+template <int NW, int MAXI, bool STORE, bool COH = false, bool ZC = false, typename Mid = NoOp>
 __device__ __forceinline__ void ssd_finish(const SsdArgs &a, int h, int ps, int b, int slot, int wave, int lane,
                                            SsdTile<MAXI> &t, float *wsum, float *cx, bool active = true,
                                            Mid &&mid = Mid()) {
@@ -559,10 +568,10 @@ __device__ __forceinline__ void ssd_finish(const SsdArgs &a, int h, int ps, int 
 #pragma unroll
   for (int k = 0; k < MAXI; ++k) {
     const bool need = q == 0 && t.prow[k] >= 0;
-    zg[k] = need ? zb[h * a.P + t.prow[k]] : 0.0f;
+    zg[k] = need ? ldc<ZC>(zb + h * a.P + t.prow[k]) : 0.0f;
     nw[k] = need ? a.norm_w[h * a.P + t.prow[k]] : 0.0f;
   }
-  const float dt = zb[a.d_inner + a.conv_dim + h];
+  const float dt = ldc<ZC>(zb + a.d_inner + a.conv_dim + h);
   const float dA = expf(-expf(a.A_log[h]) * dt);
   const float Dh = a.D[h];
   // conv outputs, each channel once per workgroup: B and C of the group and the
@@ -573,7 +582,7 @@ __device__ __forceinline__ void ssd_finish(const SsdArgs &a, int h, int ps, int 
       const int c0 = i < n4 ? a.d_inner + g * a.N + 4 * i
                    : i < 2 * n4 ? a.d_inner + (a.G + g) * a.N + 4 * (i - n4)
                    : h * a.P + ps * a.prange + 4 * (i - 2 * n4);
-      reinterpret_cast<float4 *>(cx)[i] = conv4(a, zb, sok ? slot : 0, c0);
+      reinterpret_cast<float4 *>(cx)[i] = conv4<ZC>(a, zb, sok ? slot : 0, c0);
     }
     wg_sync();
   }

@@ -39,6 +39,9 @@
 // barriers that wrote back and invalidated the L2 (plain accesses to the shared data).
 #include "decode_common.h"
 
+#include <algorithm>
+#include <cstring>
+
 namespace m2d {
 namespace {
 
@@ -80,7 +83,7 @@ __device__ __forceinline__ unsigned lds_load(unsigned *p) {
 // memory (each poll waits for all of the wave's earlier memory operations): it calls it
 // once the barrier is passed.
 template <typename F>
-__device__ __forceinline__ void grid_barrier(const FusedArgs &f, BarCtl *ctl, unsigned gen, int wave, int lane,
+__device__ __forceinline__ void grid_barrier(unsigned *bar, BarCtl *ctl, unsigned gen, int wave, int lane,
                                              F &&after_arrival) {
   // this wave's stores complete: a workgroup-scope release does not wait for them (waves of
   // a workgroup share the L1), and an agent-scope one would also write back the L2, which
@@ -102,19 +105,23 @@ __device__ __forceinline__ void grid_barrier(const FusedArgs &f, BarCtl *ctl, un
     const int grp = blockIdx.x % kBarGroups;
     const unsigned members = (gridDim.x - grp + kBarGroups - 1) / kBarGroups;
     const unsigned groups = gridDim.x < kBarGroups ? gridDim.x : kBarGroups;
-    unsigned *flag = f.bar + (kBarFlag + grp) * kBarStride;
-    if (__hip_atomic_fetch_add(f.bar + (kBarCount + grp) * kBarStride, 1u, __ATOMIC_RELAXED,
+    unsigned *flag = bar + (kBarFlag + grp) * kBarStride;
+    unsigned *err = bar + kBarError * kBarStride;
+    if (__hip_atomic_fetch_add(bar + (kBarCount + grp) * kBarStride, 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT) == gen * members - 1) {
-      if (__hip_atomic_fetch_add(f.bar + kBarTop * kBarStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+      if (__hip_atomic_fetch_add(bar + kBarTop * kBarStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
           gen * groups - 1) {
         for (unsigned q = 0; q < groups; ++q)
-          __hip_atomic_store(f.bar + (kBarFlag + q) * kBarStride, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(bar + (kBarFlag + q) * kBarStride, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+    // once any wait has run out (the error word raised), no later barrier waits at all, so
+    // a launch with many barriers still ends after one bound's time
     unsigned n = 0;
-    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen &&
+           __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
       if (++n > kGlobalSpin) {
-        __hip_atomic_store(f.bar + kBarError * kBarStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
@@ -157,24 +164,21 @@ __device__ __forceinline__ float out_row_dot(int s0, int s1, int lane, const Out
 }
 
 // ---------------------------------------------------------------------------
-// 16 waves per CU (two workgroups): at most 128 VGPRs
-__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void fused_ssd_out_kernel(FusedArgs f) {
-  extern __shared__ float lds[];
-  __shared__ BarCtl ctl;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// The SSD item of this workgroup, one grid barrier (number `gen` of the launch), then its
+// out_proj rows (+ residual) and its share of the conv-cache shift. Called by every thread.
+// STACK: inside the persistent stack kernel, where zx, the residual input and y are
+// written and read by other workgroups of the same launch: all of them go past the per-XCD
+// caches (zx and the residual input read, y stored). LDS: fused_lds_bytes; ctl initialised.
+template <bool STACK>
+__device__ __forceinline__ void ssd_out_phase(const GemvArgs &go, const SsdArgs &sa, unsigned *bar, int items,
+                                              BarCtl *ctl, unsigned gen, float *lds, int tid, int lane, int wave) {
   const int nwg = gridDim.x;
-  const GemvArgs &go = f.go;
-  const SsdArgs &sa = f.sa;
-  if (tid == 0) {
-    ctl.arrived = 0;
-    ctl.go = 0;
-  }
   const int slot = go.slots ? go.slots[0] : 0;          // the session's slot, read once
   const bool sok = slot >= 0 && slot < go.n_slots;
 
   // the SSD item's state tile first, then the first two batches of out_proj rows
-  const bool has_item = (int)blockIdx.x < f.items;
-  const int item = has_item ? (int)blockIdx.x : f.items - 1;   // without one: a copy of the last, not written
+  const bool has_item = (int)blockIdx.x < items;
+  const int item = has_item ? (int)blockIdx.x : items - 1;   // without one: a copy of the last, not written
   const int h = item / sa.psplit, ps = item - h * sa.psplit;
   SsdTile<kFMaxI> tile;
   ssd_load<kFWaves, kFMaxI>(sa, h, ps, slot, wave, lane, tile);
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
   // hold up the issue of the item's work)
   float *wsum = lds;
   float *cx = lds + 16;
-  ssd_finish<kFWaves, kFMaxI, false, true>(sa, h, ps, 0, slot, wave, lane, tile, wsum, cx, has_item, [&] {
+  ssd_finish<kFWaves, kFMaxI, false, true, STACK>(sa, h, ps, 0, slot, wave, lane, tile, wsum, cx, has_item, [&] {
     // every slice register of the tile counts as used here, also on paths where the item
     // leaves it untouched, so that the compiler waits for the tile's loads now (not for
     // the weight loads issued next), and not again at the tile's store
@@ -202,17 +206,17 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
   });
 
   // ---- grid barrier: v and the sums of squares complete; after arriving, the state tile
-  grid_barrier(f, &ctl, 1, wave, lane, [&] { ssd_store<kFMaxI>(sa, h, has_item ? slot : -1, lane, tile); });
+  grid_barrier(bar, ctl, gen, wave, lane, [&] { ssd_store<kFMaxI>(sa, h, has_item ? slot : -1, lane, tile); });
 
   // ---- out_proj (+ residual), conv-cache shift
-  conv_cache_shift(go, (size_t)blockIdx.x * kFThreads + tid, (size_t)nwg * kFThreads);
-  if (nr <= 0) return;
+  conv_cache_shift<STACK>(go, (size_t)blockIdx.x * kFThreads + tid, (size_t)nwg * kFThreads);
+  if (nr <= 0) return;                               // uniform over the workgroup
   float *act = lds;                                  // [K]: this wave's eighth, scaled
   float *red = lds + go.K;                           // [kFWaves][kFRMax]
   float acc[kFRMax];
 #pragma unroll
   for (int i = 0; i < kFRMax; ++i) acc[i] = 0.0f;
-  const float rv = (tid < nr && go.resid) ? go.resid[r0 + tid] : 0.0f;
+  const float rv = (tid < nr && go.resid) ? ldc<STACK>(go.resid + r0 + tid) : 0.0f;
   if (s1 > s0) {
     // first the loads the staging of v needs (the partial sums of squares of the groups this
     // wave's chunks touch, v of its eighth, coalesced, both past the caches), then the next
@@ -273,8 +277,152 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
     float s = 0.0f;
     for (int w = 0; w < kFWaves; ++w) s += red[w * kFRMax + tid];
     s *= go.gamma;
-    go.y[row] = sok ? s + rv : __builtin_nanf("");
+    stc<STACK>(go.y + row, sok ? s + rv : __builtin_nanf(""));
   }
+}
+
+// 16 waves per CU (two workgroups): at most 128 VGPRs
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void fused_ssd_out_kernel(FusedArgs f) {
+  extern __shared__ float lds[];
+  __shared__ BarCtl ctl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    ctl.arrived = 0;
+    ctl.go = 0;
+  }
+  ssd_out_phase<false>(f.go, f.sa, f.bar, f.items, &ctl, 1, lds, tid, lane, wave);
+}
+
+// ---------------------------------------------------------------------------
+// The persistent stack step: every Mamba-2 mixer of a run of consecutive layers (one
+// session, bf16) in one launch, three phases per layer with a grid barrier after each:
+// in_proj | SSD (+ the barrier inside ssd_out_phase) | out_proj + residual. Between layers the
+// residual stream u_{l+1} = u_l + mixer_l(u_l) goes through a buffer of its own per layer,
+// as do zx, v and the sums of squares, so that nothing a phase reads was read or written
+// earlier in the launch at another address's behest: each is written once (past the per-XCD
+// caches) and read after a barrier (past them too).
+
+// in_proj of one session, as the three-kernel step's wave GEMV computes it: one wave per
+// row, lane l summing the row's 8-element chunks l, l + 64, ... in order, then the same
+// cross-lane tree and epilogue, so the results are bitwise that kernel's. Wave gw of the
+// grid's nw takes rows gw, gw + nw, ...; the next row's first loads go out before the
+// current row's reduction. x is staged into LDS and zx stored past the per-XCD caches.
+constexpr int kIU = 5;          // chunk loads in flight per lane
+
+__device__ __forceinline__ void inproj_load(const GemvArgs &gi, int row, int NC, int cb, int lane, u32x4 (&w)[kIU]) {
+  const char *wr = static_cast<const char *>(gi.W) + (size_t)(row < gi.rows ? row : 0) * NC * 16;
+#pragma unroll
+  for (int u = 0; u < kIU; ++u) {
+    const int c = cb + 64 * u;
+    w[u] = (row < gi.rows && c < NC) ? load_chunk<M2_W_BF16, 1>(wr, c) : u32x4{};
+  }
+}
+
+__device__ __forceinline__ void inproj_phase(const GemvArgs &gi, float *lds, int tid, int lane, int wave) {
+  const int nw = gridDim.x * kFWaves;
+  const int K = gi.K, NC = K / 8;
+  const int slot = gi.slots ? gi.slots[0] : 0;
+  const bool sok = slot >= 0 && slot < gi.n_slots;
+  int row = blockIdx.x * kFWaves + wave;
+  u32x4 w[kIU];
+  inproj_load(gi, row, NC, lane, lane, w);            // weights do not depend on x: first
+  for (int i = tid; i < K; i += kFThreads) lds[i] = ldc<true>(gi.act + i);
+  __syncthreads();
+  const int dt0 = gi.d_inner + gi.conv_dim;
+  while (row < gi.rows) {                             // uniform over the wave
+    const char *wr = static_cast<const char *>(gi.W) + (size_t)row * NC * 16;
+    float acc = 0.0f;
+    for (int cb = lane;;) {
+#pragma unroll
+      for (int u = 0; u < kIU; ++u) {
+        const int c = cb + 64 * u;
+        if (c < NC) acc = chunk_acc<M2_W_BF16>(w[u], lds + c * 8, QScale{1.0f, 0.0f}, acc);
+      }
+      cb += 64 * kIU;
+      if (cb >= NC) break;
+#pragma unroll
+      for (int u = 0; u < kIU; ++u) {
+        const int c = cb + 64 * u;
+        w[u] = c < NC ? load_chunk<M2_W_BF16, 1>(wr, c) : u32x4{};
+      }
+    }
+    const int next = row + nw;
+    inproj_load(gi, next, NC, lane, lane, w);
+    acc = group_reduce<64>(acc);
+    if (lane == 0) {
+      float val = acc * gi.gamma;
+      if (row >= dt0) val = softplus(val + gi.dt_bias[row - dt0]);
+      stc<true>(gi.zx + row, sok ? val : __builtin_nanf(""));
+    }
+    row = next;
+  }
+}
+
+// One mixer layer of the table: the three phases' arguments with every pointer of the call
+// left out, and the byte offsets of the layer's buffers in the persistent area.
+struct StackRec {
+  GemvArgs gi, go;
+  SsdArgs sa;
+  int items;
+  long long zx_off, v_off, ss_off, u_off;
+};
+
+struct StackArgs {
+  const StackRec *tab;    // device table, one record per layer of the stack
+  int l0, l1;             // the run: layers [l0, l1), all mixers
+  char *area;             // the barrier words, then each layer's buffers
+  float *y;               // the residual stream: the run's input and its output
+  const int32_t *slots;
+  int n_slots;
+};
+
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void stack_persistent_kernel(StackArgs a) {
+  extern __shared__ float lds[];
+  __shared__ BarCtl ctl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    ctl.arrived = 0;
+    ctl.go = 0;
+  }
+  __syncthreads();
+  unsigned *bar = reinterpret_cast<unsigned *>(a.area);
+  unsigned gen = 0;
+  const float *u = a.y;
+  for (int l = a.l0; l < a.l1; ++l) {
+    const StackRec &r = a.tab[l];
+    float *zx = reinterpret_cast<float *>(a.area + r.zx_off);
+    float *v = reinterpret_cast<float *>(a.area + r.v_off);
+    float *ss = reinterpret_cast<float *>(a.area + r.ss_off);
+    float *uo = l + 1 == a.l1 ? a.y : reinterpret_cast<float *>(a.area + r.u_off);
+    GemvArgs gi = r.gi;
+    gi.act = u;
+    gi.zx = zx;
+    gi.slots = a.slots;
+    gi.n_slots = a.n_slots;
+    inproj_phase(gi, lds, tid, lane, wave);
+    grid_barrier(bar, &ctl, ++gen, wave, lane, NoOp());
+    SsdArgs sa = r.sa;
+    sa.zx = zx;
+    sa.vw = v;
+    sa.ss = ss;
+    sa.slots = a.slots;
+    sa.n_slots = a.n_slots;
+    GemvArgs go = r.go;
+    go.act = v;
+    go.ss = ss;
+    go.y = uo;
+    go.resid = u;
+    go.zx = zx;
+    go.slots = a.slots;
+    go.n_slots = a.n_slots;
+    ssd_out_phase<true>(go, sa, bar, r.items, &ctl, ++gen, lds, tid, lane, wave);
+    if (l + 1 < a.l1) grid_barrier(bar, &ctl, ++gen, wave, lane, NoOp());
+    u = uo;
+  }
+}
+
+__global__ void bar_zero_kernel(unsigned *bar) {
+  if ((int)threadIdx.x < kBarWords) bar[threadIdx.x * kBarStride] = 0u;
 }
 
 size_t fused_lds_bytes(const m2_layer_s &L) {
@@ -380,6 +528,121 @@ hipError_t launch_fused_step(const m2_layer_s &L, const m2_state_s &S, const flo
   f.bar = ws.bar;
   f.items = c.n_heads * L.psplit;
   hipLaunchKernelGGL(fused_ssd_out_kernel, dim3(grid), dim3(kFThreads), fused_lds_bytes(L), stream, f);
+  return hipGetLastError();
+}
+
+
+// ---- the persistent stack step (host side)
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t stack_area_head() { return al256(kBarBytes); }
+
+size_t stack_area_layer_bytes(const m2_layer_s &L) {
+  return al256(sizeof(float) * (size_t)L.zx_stride) + al256(sizeof(float) * (size_t)L.d_inner) +
+         al256(sizeof(float) * (size_t)L.n_partials) + al256(sizeof(float) * (size_t)L.cfg.d_model);
+}
+
+size_t stack_rec_bytes() { return sizeof(StackRec); }
+
+void stack_rec_fill(const m2_layer_s &L, const m2_state_s &S, size_t off, void *out) {
+  const m2_config &c = L.cfg;
+  StackRec r{};
+  GemvArgs &gi = r.gi;
+  gi.W = L.w.w_in;
+  gi.rows = L.d_in_proj;
+  gi.K = c.d_model;
+  gi.gamma = 1.0f;
+  gi.B = 1;
+  gi.zx_stride = L.zx_stride;
+  gi.d_inner = L.d_inner;
+  gi.conv_dim = L.conv_dim;
+  gi.d_conv = c.d_conv;
+  gi.dt_bias = L.w.dt_bias;
+  SsdArgs &sa = r.sa;
+  sa.zx_stride = L.zx_stride;
+  sa.d_inner = L.d_inner;
+  sa.conv_dim = L.conv_dim;
+  sa.H = c.n_heads;
+  sa.P = c.head_dim;
+  sa.N = c.d_state;
+  sa.G = c.n_groups;
+  sa.hpg = L.hpg;
+  sa.ssm = S.ssm;
+  sa.conv_cache = S.conv;
+  sa.conv_w = L.w.conv_w;
+  sa.conv_b = L.w.conv_b;
+  sa.d_conv = c.d_conv;
+  sa.A_log = L.w.A_log;
+  sa.D = L.w.D;
+  sa.norm_w = L.w.norm_w;
+  sa.prange = L.prange;
+  sa.psplit = L.psplit;
+  sa.n_partials = L.n_partials;
+  GemvArgs &go = r.go;
+  go.W = L.w.w_out;
+  go.rows = c.d_model;
+  go.K = L.d_inner;
+  go.gamma = 1.0f;
+  go.B = 1;
+  go.ng = L.ng;
+  go.n_partials = L.n_partials;
+  go.n_norm = L.n_norm;
+  go.eps = c.norm_eps;
+  go.zx_stride = L.zx_stride;
+  go.d_inner = L.d_inner;
+  go.conv_dim = L.conv_dim;
+  go.d_conv = c.d_conv;
+  go.conv_cache = S.conv;
+  r.items = c.n_heads * L.psplit;
+  r.zx_off = (long long)off;
+  r.v_off = r.zx_off + (long long)al256(sizeof(float) * (size_t)L.zx_stride);
+  r.ss_off = r.v_off + (long long)al256(sizeof(float) * (size_t)L.d_inner);
+  r.u_off = r.ss_off + (long long)al256(sizeof(float) * (size_t)L.n_partials);
+  std::memcpy(out, &r, sizeof r);
+}
+
+size_t stack_lds_bytes(const m2_layer_s &L) {
+  return std::max(fused_lds_bytes(L), sizeof(float) * (size_t)L.cfg.d_model);
+}
+
+// Two workgroups per CU if the kernel's occupancy at this LDS size allows two (else 0).
+int stack_grid(size_t lds) {
+  static int cus[64] = {0}, occ[64][2] = {{0}};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cus[dev] = n;
+  }
+  if (occ[dev][1] != (int)lds) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, stack_persistent_kernel, kFThreads, lds) != hipSuccess)
+      return 0;
+    occ[dev][0] = nb;
+    occ[dev][1] = (int)lds;
+  }
+  return occ[dev][0] >= 2 ? 2 * cus[dev] : 0;
+}
+
+bool stack_fits(const m2_layer_s &L, int grid) {
+  return fused_fits(L, grid) && L.d_in_proj > 0 && (long)L.d_in_proj * (L.cfg.d_model / 8) * 16 < (1L << 40);
+}
+
+hipError_t launch_stack_run(const void *tab, int l0, int l1, size_t lds, void *area, float *y,
+                            const int32_t *slots, int n_slots, int grid, hipStream_t stream) {
+  StackArgs a{};
+  a.tab = static_cast<const StackRec *>(tab);
+  a.l0 = l0;
+  a.l1 = l1;
+  a.area = static_cast<char *>(area);
+  a.y = y;
+  a.slots = slots;
+  a.n_slots = n_slots;
+  hipLaunchKernelGGL(bar_zero_kernel, dim3(1), dim3(64), 0, stream, reinterpret_cast<unsigned *>(area));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(stack_persistent_kernel, dim3(grid), dim3(kFThreads), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -454,6 +454,11 @@ struct m2_stack_s {
   std::vector<m2_stack_layer> layers;
   int n_slots;
   int d_model;
+  void *dtab = nullptr;     // the persistent kernel's layer table, on the device current at create
+  size_t area = 0;          // bytes of the persistent path's workspace area (a multiple of 256)
+  ~m2_stack_s() {
+    if (dtab) (void)hipFree(dtab);
+  }
 };
 
 int m2_stack_create(const m2_stack_layer *layers, int32_t n_layers, int32_t n_slots, m2_stack *out) {
@@ -492,6 +497,30 @@ int m2_stack_create(const m2_stack_layer *layers, int32_t n_layers, int32_t n_sl
   S->layers.assign(layers, layers + n_layers);
   S->n_slots = n_slots;
   S->d_model = d_model;
+  // the persistent path's area (barrier words, then each mixer's buffers) and its layer
+  // table, which goes to the current device when there is one (without one, the persistent
+  // path never applies and the table is not made)
+  const size_t rb = m2d::stack_rec_bytes();
+  std::vector<unsigned char> tab(rb * (size_t)n_layers, 0);
+  size_t off = m2d::stack_area_head();
+  for (int i = 0; i < n_layers; ++i) {
+    if (layers[i].kind != M2_LAYER_MIXER) continue;
+    const m2_layer ml = static_cast<m2_layer>(layers[i].layer);
+    m2d::stack_rec_fill(*ml, *static_cast<m2_state>(layers[i].state), off, tab.data() + rb * (size_t)i);
+    off += m2d::stack_area_layer_bytes(*ml);
+  }
+  S->area = (off + 255) & ~(size_t)255;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0) {
+    hipError_t e = hipMalloc(&S->dtab, tab.size());
+    if (e == hipSuccess) e = hipMemcpy(S->dtab, tab.data(), tab.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      delete S;
+      return fail(M2_ERR_HIP, "stack layer table: %s", hipGetErrorString(e));
+    }
+  } else {
+    (void)hipGetLastError();
+  }
   *out = S;
   return ok();
 }
@@ -510,30 +539,111 @@ size_t m2_stack_workspace(m2_stack s, int32_t batch) {
   return need;
 }
 
-int m2_stack_step(m2_stack s, const float *x, float *y, int32_t batch, const int32_t *slot_ids, void *ws,
-                  size_t ws_bytes, void *stream) {
+size_t m2_stack_workspace_flags(m2_stack s, int32_t batch, int32_t flags) {
+  if (!s || batch <= 0 || (flags & ~M2_PERSISTENT)) return 0;
+  const size_t base = m2_stack_workspace(s, batch);
+  if (base == 0) return 0;
+  return (flags & M2_PERSISTENT) ? s->area + base : base;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The runs of consecutive mixer layers a step with these flags takes in one persistent
+// launch each: [first, end) pairs, with the run's dynamic LDS bytes and grid.
+struct StackRun {
+  int l0, l1;
+  size_t lds;
+  int grid;
+};
+
+std::vector<StackRun> stack_runs(const m2_stack_s &s, int batch, int flags) {
+  std::vector<StackRun> runs;
+  if (!(flags & M2_PERSISTENT) || batch != 1 || !s.dtab) return runs;
+  const int n = (int)s.layers.size();
+  for (int i = 0; i < n;) {
+    if (s.layers[i].kind != M2_LAYER_MIXER) {
+      ++i;
+      continue;
+    }
+    int j = i;
+    size_t lds = 0;
+    while (j < n && s.layers[j].kind == M2_LAYER_MIXER) {
+      const m2_layer_s &L = *static_cast<m2_layer>(s.layers[j].layer);
+      lds = std::max(lds, m2d::stack_lds_bytes(L));
+      ++j;
+    }
+    const int grid = m2d::stack_grid(lds);
+    bool fits = grid > 0;
+    for (int k = i; k < j && fits; ++k) {
+      const m2_layer_s &L = *static_cast<m2_layer>(s.layers[k].layer);
+      fits = L.cfg.wtype == M2_W_BF16 && m2d::stack_fits(L, grid);
+    }
+    if (fits) runs.push_back(StackRun{i, j, lds, grid});
+    i = j;
+  }
+  return runs;
+}
+
+int stack_step_impl(m2_stack s, const float *x, float *y, int32_t batch, const int32_t *slot_ids, int32_t flags,
+                    void *ws, size_t ws_bytes, void *stream) {
   if (!s || !x || !y) return fail(M2_ERR_NULL, "stack, x and y are required");
   if (batch <= 0) return fail(M2_ERR_SHAPE, "batch must be positive");
   if (batch > s->n_slots) return fail(M2_ERR_SLOT, "batch %d exceeds n_slots %d", batch, s->n_slots);
+  if (flags & ~M2_PERSISTENT) return fail(M2_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
   if (!aligned16(x) || !aligned16(y)) return fail(M2_ERR_ALIGN, "x and y must be 16-byte aligned");
-  const size_t need = m2_stack_workspace(s, batch);
+  const size_t need = m2_stack_workspace_flags(s, batch, flags);
   if (!ws || ws_bytes < need)
     return fail(M2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
   if (!aligned16(ws)) return fail(M2_ERR_ALIGN, "workspace must be 16-byte aligned");
+  // with M2_PERSISTENT the persistent area comes first; the layers' own workspace after it
+  const size_t skip = (flags & M2_PERSISTENT) ? s->area : 0;
+  void *lws = static_cast<char *>(ws) + skip;
+  const size_t lws_bytes = ws_bytes - skip;
+  const std::vector<StackRun> runs = stack_runs(*s, batch, flags);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (x != y) {
     hipError_t e = hipMemcpyAsync(y, x, sizeof(float) * (size_t)batch * s->d_model, hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return fail(M2_ERR_HIP, "stack input copy: %s", hipGetErrorString(e));
   }
-  for (const m2_stack_layer &l : s->layers) {
+  size_t r = 0;
+  for (int i = 0; i < (int)s->layers.size();) {
+    if (r < runs.size() && runs[r].l0 == i) {
+      const StackRun &R = runs[r++];
+      hipError_t e = m2d::launch_stack_run(s->dtab, R.l0, R.l1, R.lds, ws, y, slot_ids, s->n_slots, R.grid, st);
+      if (e != hipSuccess) return fail(M2_ERR_HIP, "persistent stack launch: %s", hipGetErrorString(e));
+      i = R.l1;
+      continue;
+    }
+    const m2_stack_layer &l = s->layers[i++];
     const int rc = l.kind == M2_LAYER_MIXER
                        ? step_impl(static_cast<m2_layer>(l.layer), static_cast<m2_state>(l.state), y, y, batch,
-                                   slot_ids, M2_RESIDUAL, ws, ws_bytes, stream, nullptr)
+                                   slot_ids, M2_RESIDUAL, lws, lws_bytes, stream, nullptr)
                        : attn_impl(static_cast<m2_attn>(l.layer), l.k_cache, l.v_cache, l.pos, s->n_slots, y, y,
-                                   batch, slot_ids, M2_RESIDUAL, ws, ws_bytes, stream, nullptr);
+                                   batch, slot_ids, M2_RESIDUAL, lws, lws_bytes, stream, nullptr);
     if (rc != M2_OK) return rc;
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int m2_stack_step(m2_stack s, const float *x, float *y, int32_t batch, const int32_t *slot_ids, void *ws,
+                  size_t ws_bytes, void *stream) {
+  return stack_step_impl(s, x, y, batch, slot_ids, 0, ws, ws_bytes, stream);
+}
+
+int m2_stack_step_flags(m2_stack s, const float *x, float *y, int32_t batch, const int32_t *slot_ids, int32_t flags,
+                        void *ws, size_t ws_bytes, void *stream) {
+  return stack_step_impl(s, x, y, batch, slot_ids, flags, ws, ws_bytes, stream);
+}
+
+int m2_stack_persistent_runs(m2_stack s, int32_t batch, int32_t flags) {
+  if (!s || batch <= 0 || (flags & ~M2_PERSISTENT)) return -1;
+  return (int)stack_runs(*s, batch, flags).size();
 }
 
 size_t m2_prefill_workspace(m2_layer layer, int32_t batch, int32_t seqlen, int32_t chunk) {

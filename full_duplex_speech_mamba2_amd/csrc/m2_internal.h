@@ -68,6 +68,19 @@ int fused_grid(const m2_layer_s &L);
 bool fused_fits(const m2_layer_s &L, int grid);
 hipError_t launch_fused_step(const m2_layer_s &L, const m2_state_s &S, const float *x, float *y,
                              const int32_t *slots, int flags, const StepWs &ws, int grid, hipStream_t stream);
+// The persistent stack step (fused.hip): one launch runs a run of consecutive mixer layers
+// (one session, bf16). Its workspace area: the barrier words (stack_area_head bytes), then
+// stack_area_layer_bytes per layer; a device table holds one stack_rec_bytes record per
+// layer of the stack (stack_rec_fill writes a mixer's, `off` its buffers' area offset).
+size_t stack_area_head();
+size_t stack_area_layer_bytes(const m2_layer_s &L);
+size_t stack_rec_bytes();
+void stack_rec_fill(const m2_layer_s &L, const m2_state_s &S, size_t off, void *out);
+size_t stack_lds_bytes(const m2_layer_s &L);
+int stack_grid(size_t lds);
+bool stack_fits(const m2_layer_s &L, int grid);
+hipError_t launch_stack_run(const void *tab, int l0, int l1, size_t lds, void *area, float *y,
+                            const int32_t *slots, int n_slots, int grid, hipStream_t stream);
 // Whether a step of `batch` sessions runs its projections as MFMA GEMVs.
 bool step_uses_mfma(const m2_layer_s &L, int batch);
 

@@ -105,7 +105,12 @@ _lib.m2_stack_destroy.restype = None
 _lib.m2_stack_workspace.argtypes = [_P, _i32]
 _lib.m2_stack_workspace.restype = C.c_size_t
 _lib.m2_stack_step.argtypes = [_P, _P, _P, _i32, _P, _P, C.c_size_t, _P]
-for _f in ("m2_attn_create", "m2_attn_step", "m2_attn_step_timed", "m2_stack_create", "m2_stack_step"):
+_lib.m2_stack_workspace_flags.argtypes = [_P, _i32, _i32]
+_lib.m2_stack_workspace_flags.restype = C.c_size_t
+_lib.m2_stack_step_flags.argtypes = [_P, _P, _P, _i32, _P, _i32, _P, C.c_size_t, _P]
+_lib.m2_stack_persistent_runs.argtypes = [_P, _i32, _i32]
+for _f in ("m2_attn_create", "m2_attn_step", "m2_attn_step_timed", "m2_stack_create", "m2_stack_step",
+           "m2_stack_step_flags", "m2_stack_persistent_runs"):
     getattr(_lib, _f).restype = C.c_int
 for _f in ("m2_layer_create", "m2_state_sizes", "m2_state_create", "m2_state_zero", "m2_step",
            "m2_step_timed", "m2_prefill", "m2_head_argmax", "m2_head_argmax_timed"):
@@ -503,18 +508,24 @@ class Stack:
             _lib.m2_stack_destroy(h)
             self.handle = None
 
-    def workspace(self, batch: int) -> torch.Tensor:
-        ws = self._ws.get(batch)
+    def workspace(self, batch: int, persistent: bool = False) -> torch.Tensor:
+        key = (batch, persistent)
+        ws = self._ws.get(key)
         if ws is None:
-            n = int(_lib.m2_stack_workspace(self.handle, batch))
+            n = int(_lib.m2_stack_workspace_flags(self.handle, batch, M2_PERSISTENT if persistent else 0))
             if n == 0:
                 raise M2Error(M2_ERR_SHAPE, "no workspace size for batch %d" % batch)
-            ws = self._ws[batch] = torch.empty(n, dtype=torch.uint8, device=self.device)
+            ws = self._ws[key] = torch.empty(n, dtype=torch.uint8, device=self.device)
         return ws
 
+    def persistent_runs(self, batch: int) -> int:
+        """Persistent launches per step with M2_PERSISTENT (m2_stack_persistent_runs)."""
+        return int(_lib.m2_stack_persistent_runs(self.handle, batch, M2_PERSISTENT))
+
     def step(self, x: torch.Tensor, y: Optional[torch.Tensor] = None, slot_ids: Optional[torch.Tensor] = None,
-             ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-        """One token through every layer (residual chain); returns y [B][d_model]."""
+             ws: Optional[torch.Tensor] = None, stream=None, persistent: bool = False) -> torch.Tensor:
+        """One token through every layer (residual chain); returns y [B][d_model].
+        persistent: each run of mixer layers in one persistent launch where that applies."""
         B = x.shape[0]
         _act(x, (B, self.d_model))
         if y is None:
@@ -523,7 +534,7 @@ class Stack:
         if slot_ids is not None:
             _tokens(slot_ids, B)
         if ws is None:
-            ws = self.workspace(B)
-        _check(_lib.m2_stack_step(self.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids), _ptr(ws), ws.numel(),
-                                  _stream(stream)))
+            ws = self.workspace(B, persistent)
+        _check(_lib.m2_stack_step_flags(self.handle, _ptr(x), _ptr(y), B, _ptr(slot_ids),
+                                        M2_PERSISTENT if persistent else 0, _ptr(ws), ws.numel(), _stream(stream)))
         return y

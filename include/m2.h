@@ -334,8 +334,10 @@ typedef struct {
 
 typedef struct m2_stack_s *m2_stack;
 
-/* Copies the table (not what it points to). Errors: a NULL or unknown entry, layers of
- * different d_model, a mixer state with fewer than n_slots slots. */
+/* Copies the table (not what it points to). Where a GPU is present it also copies the
+ * mixers' arguments into a small table on the current device (for m2_stack_step_flags);
+ * m2_stack_destroy frees it. Errors: a NULL or unknown entry, layers of different d_model, a
+ * mixer state with fewer than n_slots slots, M2_ERR_HIP if that table cannot be made. */
 int m2_stack_create(const m2_stack_layer *layers, int32_t n_layers, int32_t n_slots, m2_stack *out);
 void m2_stack_destroy(m2_stack s);
 
@@ -346,6 +348,32 @@ size_t m2_stack_workspace(m2_stack s, int32_t batch);
  * alias x); session b uses slot slot_ids[b] (device int32 [batch]) or b if NULL. */
 int m2_stack_step(m2_stack s, const float *x, float *y, int32_t batch, const int32_t *slot_ids, void *ws,
                   size_t ws_bytes, void *stream);
+
+/* The persistent stack step (blog page "NemotronLabs VoiceChat 11B", "Key design decisions"
+ * item 2: the backbone is one deep stack of Mamba-2 layers with attention layers among them,
+ * stepped once per 80 ms frame). m2_stack_step with flags: M2_PERSISTENT runs every maximal
+ * run of consecutive mixer layers in ONE kernel launch (plus a one-wave launch that clears
+ * its barrier words) where the run applies: one session (batch 1), bf16 weights in every
+ * layer of the run, each layer within plan 2's shape limits (m2_step_plan), and two
+ * workgroups of the kernel resident on every CU of the device that was current at
+ * m2_stack_create (the kernel's occupancy is checked on the host before each launch).
+ * Inside the launch each layer is three phases with a grid-wide barrier after each:
+ * in_proj (the arithmetic of plan 0's GEMV) | the SSD update (plan 2's) | out_proj +
+ * residual (plan 2's); the residual stream between the run's layers, zx, v and the sums of
+ * squares live in per-layer buffers of the workspace, written once and read past the
+ * per-XCD caches. The results are bitwise those of calling m2_step with M2_PERSISTENT |
+ * M2_RESIDUAL layer by layer. Every barrier wait is bounded: should the grid not be
+ * resident, the launch still ends (its results are then undefined). Attention layers, and
+ * runs where the path does not apply, are stepped as by m2_stack_step. The workspace is
+ * m2_stack_workspace_flags bytes: the persistent area (barrier words and per-layer buffers)
+ * first, then m2_stack_workspace's. Errors as m2_stack_step, and M2_ERR_UNSUPPORTED for
+ * unknown flags; with flags 0 the call is m2_stack_step. */
+size_t m2_stack_workspace_flags(m2_stack s, int32_t batch, int32_t flags);
+int m2_stack_step_flags(m2_stack s, const float *x, float *y, int32_t batch, const int32_t *slot_ids,
+                        int32_t flags, void *ws, size_t ws_bytes, void *stream);
+/* How many persistent launches m2_stack_step_flags makes per step for `batch` sessions (0
+ * where the path does not apply; -1 for a NULL stack, batch <= 0 or unknown flags). */
+int m2_stack_persistent_runs(m2_stack s, int32_t batch, int32_t flags);
 
 #ifdef __cplusplus
 }

@@ -300,6 +300,19 @@ def test_stack_rejects_bad_tables_and_calls_without_launching():
     assert L.m2_stack_step(sh, FAKE + 4, FAKE * 2, 2, None, FAKE, need, None) == m2.M2_ERR_ALIGN
     assert L.m2_stack_step(None, FAKE, FAKE * 2, 2, None, FAKE, need, None) == m2.M2_ERR_NULL
     assert L.m2_stack_step(sh, FAKE, FAKE * 2, 2, None, FAKE + 4, need, None) == m2.M2_ERR_ALIGN
+    # the persistent stack step's entry points: its workspace puts the persistent area (a
+    # multiple of 256 bytes) before the layers' own; the same checks, and unknown flags
+    P = m2.M2_PERSISTENT
+    assert L.m2_stack_workspace_flags(sh, 2, 0) == need
+    need_p = L.m2_stack_workspace_flags(sh, 1, P)
+    assert need_p > L.m2_stack_workspace(sh, 1) and (need_p - L.m2_stack_workspace(sh, 1)) % 256 == 0
+    assert L.m2_stack_workspace_flags(sh, 1, 8) == 0 and L.m2_stack_workspace_flags(None, 1, P) == 0
+    assert L.m2_stack_step_flags(sh, FAKE, FAKE * 2, 1, None, 8, FAKE, need_p, None) == m2.M2_ERR_UNSUPPORTED
+    assert L.m2_stack_step_flags(sh, FAKE, FAKE * 2, 1, None, P, FAKE, need_p - 1, None) == m2.M2_ERR_WORKSPACE
+    assert L.m2_stack_step_flags(sh, FAKE, FAKE * 2, 3, None, P, FAKE, need_p, None) == m2.M2_ERR_SLOT
+    assert L.m2_stack_step_flags(None, FAKE, FAKE * 2, 1, None, P, FAKE, need_p, None) == m2.M2_ERR_NULL
+    assert L.m2_stack_persistent_runs(sh, 1, 8) == -1 and L.m2_stack_persistent_runs(None, 1, P) == -1
+    assert L.m2_stack_persistent_runs(sh, 2, P) == 0                    # one session only
     L.m2_stack_destroy(sh)
     L.m2_attn_destroy(ah)
     L.m2_attn_destroy(ah2)
