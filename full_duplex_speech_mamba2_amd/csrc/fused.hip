@@ -169,19 +169,37 @@ __device__ __forceinline__ float out_row_dot(int s0, int s1, int lane, const Out
 // STACK: inside the persistent stack kernel, where zx, the residual input and y are
 // written and read by other workgroups of the same launch: all of them go past the per-XCD
 // caches (zx and the residual input read, y stored). LDS: fused_lds_bytes; ctl initialised.
+// The workgroup's SSD item: which it is (without one of its own, a copy of the last, never
+// written), and its state tile's loads.
+struct FItem {
+  bool has;
+  int h, ps;
+};
+
+__device__ __forceinline__ FItem fused_item(const SsdArgs &sa, int items) {
+  FItem it;
+  it.has = (int)blockIdx.x < items;
+  const int item = it.has ? (int)blockIdx.x : items - 1;
+  it.h = item / sa.psplit;
+  it.ps = item - it.h * sa.psplit;
+  return it;
+}
+
+__device__ __forceinline__ void fused_tile_load(const SsdArgs &sa, const FItem &it, int wave, int lane,
+                                                SsdTile<kFMaxI> &tile) {
+  const int slot = sa.slots ? sa.slots[0] : 0;
+  ssd_load<kFWaves, kFMaxI>(sa, it.h, it.ps, slot, wave, lane, tile);
+}
+
 template <bool STACK>
-__device__ __forceinline__ void ssd_out_phase(const GemvArgs &go, const SsdArgs &sa, unsigned *bar, int items,
-                                              BarCtl *ctl, unsigned gen, float *lds, int tid, int lane, int wave) {
+__device__ __forceinline__ void ssd_out_phase(const GemvArgs &go, const SsdArgs &sa, unsigned *bar, const FItem &it,
+                                              SsdTile<kFMaxI> &tile, BarCtl *ctl, unsigned gen, float *lds, int tid,
+                                              int lane, int wave) {
   const int nwg = gridDim.x;
   const int slot = go.slots ? go.slots[0] : 0;          // the session's slot, read once
   const bool sok = slot >= 0 && slot < go.n_slots;
-
-  // the SSD item's state tile first, then the first two batches of out_proj rows
-  const bool has_item = (int)blockIdx.x < items;
-  const int item = has_item ? (int)blockIdx.x : items - 1;   // without one: a copy of the last, not written
-  const int h = item / sa.psplit, ps = item - h * sa.psplit;
-  SsdTile<kFMaxI> tile;
-  ssd_load<kFWaves, kFMaxI>(sa, h, ps, slot, wave, lane, tile);
+  const bool has_item = it.has;
+  const int h = it.h, ps = it.ps;
   const int r0 = (int)(((long)blockIdx.x * go.rows) / nwg);
   const int nr = (int)(((long)(blockIdx.x + 1) * go.rows) / nwg) - r0;
   const int NC = go.K / 8, per_w = (NC + kFWaves - 1) / kFWaves;
@@ -290,7 +308,11 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
     ctl.arrived = 0;
     ctl.go = 0;
   }
-  ssd_out_phase<false>(f.go, f.sa, f.bar, f.items, &ctl, 1, lds, tid, lane, wave);
+  // the SSD item's state tile first
+  const FItem it = fused_item(f.sa, f.items);
+  SsdTile<kFMaxI> tile;
+  fused_tile_load(f.sa, it, wave, lane, tile);
+  ssd_out_phase<false>(f.go, f.sa, f.bar, it, tile, &ctl, 1, lds, tid, lane, wave);
 }
 
 // ---------------------------------------------------------------------------
@@ -305,56 +327,62 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
 // in_proj of one session, as the three-kernel step's wave GEMV computes it: one wave per
 // row, lane l summing the row's 8-element chunks l, l + 64, ... in order, then the same
 // cross-lane tree and epilogue, so the results are bitwise that kernel's. Wave gw of the
-// grid's nw takes rows gw, gw + nw, ...; the next row's first loads go out before the
-// current row's reduction. x is staged into LDS and zx stored past the per-XCD caches.
-constexpr int kIU = 5;          // chunk loads in flight per lane
+// grid's nw takes rows gw, gw + nw, ... A row is at most kIJ chunks per lane (d_model <=
+// 4608), all requested at once; each register is refilled with the same chunk of the wave's
+// next row as soon as it has been used, so the wave keeps a row's loads in flight across its
+// reductions and epilogues, and the first row's loads are requested before the barrier the
+// phase starts after (weights do not depend on the data). Loads go through a buffer resource:
+// a chunk past the row or a row past the matrix reads zeros without a memory access, so no
+// load is conditional. x is staged into LDS and zx stored past the per-XCD caches.
+constexpr int kIJ = 9;          // chunks per lane of one row
 
-__device__ __forceinline__ void inproj_load(const GemvArgs &gi, int row, int NC, int cb, int lane, u32x4 (&w)[kIU]) {
-  const char *wr = static_cast<const char *>(gi.W) + (size_t)(row < gi.rows ? row : 0) * NC * 16;
-#pragma unroll
-  for (int u = 0; u < kIU; ++u) {
-    const int c = cb + 64 * u;
-    w[u] = (row < gi.rows && c < NC) ? load_chunk<M2_W_BF16, 1>(wr, c) : u32x4{};
-  }
+struct InRow {
+  u32x4 w[kIJ];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t inproj_rsrc(const GemvArgs &gi) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(gi.W), (short)0, gi.rows * (gi.K / 8) * 16, 0x00020000);
 }
 
-__device__ __forceinline__ void inproj_phase(const GemvArgs &gi, float *lds, int tid, int lane, int wave) {
+__device__ __forceinline__ u32x4 inproj_chunk(__amdgpu_buffer_rsrc_t wr, const GemvArgs &gi, int row, int j, int lane) {
+  const int NC = gi.K / 8, c = lane + 64 * j;
+  const int off = (row < gi.rows && c < NC) ? (row * NC + c) * 16 : kBufOutOfRange;
+  const f32x4b v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 2);     // nt
+  return u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+}
+
+// the first row of this wave, before the phase's barrier
+__device__ __forceinline__ void inproj_first(const GemvArgs &gi, int wave, int lane, InRow &r) {
+  const __amdgpu_buffer_rsrc_t wr = inproj_rsrc(gi);
+  const int row = blockIdx.x * kFWaves + wave;
+#pragma unroll
+  for (int j = 0; j < kIJ; ++j) r.w[j] = inproj_chunk(wr, gi, row, j, lane);
+}
+
+__device__ __forceinline__ void inproj_phase(const GemvArgs &gi, InRow &r, float *lds, int tid, int lane, int wave) {
   const int nw = gridDim.x * kFWaves;
   const int K = gi.K, NC = K / 8;
   const int slot = gi.slots ? gi.slots[0] : 0;
   const bool sok = slot >= 0 && slot < gi.n_slots;
-  int row = blockIdx.x * kFWaves + wave;
-  u32x4 w[kIU];
-  inproj_load(gi, row, NC, lane, lane, w);            // weights do not depend on x: first
+  const __amdgpu_buffer_rsrc_t wr = inproj_rsrc(gi);
   for (int i = tid; i < K; i += kFThreads) lds[i] = ldc<true>(gi.act + i);
   __syncthreads();
   const int dt0 = gi.d_inner + gi.conv_dim;
-  while (row < gi.rows) {                             // uniform over the wave
-    const char *wr = static_cast<const char *>(gi.W) + (size_t)row * NC * 16;
-    float acc = 0.0f;
-    for (int cb = lane;;) {
-#pragma unroll
-      for (int u = 0; u < kIU; ++u) {
-        const int c = cb + 64 * u;
-        if (c < NC) acc = chunk_acc<M2_W_BF16>(w[u], lds + c * 8, QScale{1.0f, 0.0f}, acc);
-      }
-      cb += 64 * kIU;
-      if (cb >= NC) break;
-#pragma unroll
-      for (int u = 0; u < kIU; ++u) {
-        const int c = cb + 64 * u;
-        w[u] = c < NC ? load_chunk<M2_W_BF16, 1>(wr, c) : u32x4{};
-      }
-    }
+  for (int row = blockIdx.x * kFWaves + wave; row < gi.rows; row += nw) {   // uniform over the wave
     const int next = row + nw;
-    inproj_load(gi, next, NC, lane, lane, w);
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kIJ; ++j) {
+      const int c = lane + 64 * j;
+      if (c < NC) acc = chunk_acc<M2_W_BF16>(r.w[j], lds + c * 8, QScale{1.0f, 0.0f}, acc);
+      r.w[j] = inproj_chunk(wr, gi, next, j, lane);
+    }
     acc = group_reduce<64>(acc);
     if (lane == 0) {
       float val = acc * gi.gamma;
       if (row >= dt0) val = softplus(val + gi.dt_bias[row - dt0]);
       stc<true>(gi.zx + row, sok ? val : __builtin_nanf(""));
     }
-    row = next;
   }
 }
 
@@ -388,6 +416,8 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
   unsigned *bar = reinterpret_cast<unsigned *>(a.area);
   unsigned gen = 0;
   const float *u = a.y;
+  InRow w;
+  inproj_first(a.tab[a.l0].gi, wave, lane, w);
   for (int l = a.l0; l < a.l1; ++l) {
     const StackRec &r = a.tab[l];
     float *zx = reinterpret_cast<float *>(a.area + r.zx_off);
@@ -399,14 +429,18 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
     gi.zx = zx;
     gi.slots = a.slots;
     gi.n_slots = a.n_slots;
-    inproj_phase(gi, lds, tid, lane, wave);
-    grid_barrier(bar, &ctl, ++gen, wave, lane, NoOp());
+    inproj_phase(gi, w, lds, tid, lane, wave);
+    // the SSD item's state tile (no phase of this launch writes it before) while waiting
     SsdArgs sa = r.sa;
     sa.zx = zx;
     sa.vw = v;
     sa.ss = ss;
     sa.slots = a.slots;
     sa.n_slots = a.n_slots;
+    const FItem it = fused_item(sa, r.items);
+    SsdTile<kFMaxI> tile;
+    fused_tile_load(sa, it, wave, lane, tile);
+    grid_barrier(bar, &ctl, ++gen, wave, lane, NoOp());
     GemvArgs go = r.go;
     go.act = v;
     go.ss = ss;
@@ -415,8 +449,11 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
     go.zx = zx;
     go.slots = a.slots;
     go.n_slots = a.n_slots;
-    ssd_out_phase<true>(go, sa, bar, r.items, &ctl, ++gen, lds, tid, lane, wave);
-    if (l + 1 < a.l1) grid_barrier(bar, &ctl, ++gen, wave, lane, NoOp());
+    ssd_out_phase<true>(go, sa, bar, it, tile, &ctl, ++gen, lds, tid, lane, wave);
+    if (l + 1 < a.l1) {
+      inproj_first(a.tab[l + 1].gi, wave, lane, w);   // the next layer's first row, while waiting
+      grid_barrier(bar, &ctl, ++gen, wave, lane, NoOp());
+    }
     u = uo;
   }
 }
@@ -626,7 +663,8 @@ int stack_grid(size_t lds) {
 }
 
 bool stack_fits(const m2_layer_s &L, int grid) {
-  return fused_fits(L, grid) && L.d_in_proj > 0 && (long)L.d_in_proj * (L.cfg.d_model / 8) * 16 < (1L << 40);
+  return fused_fits(L, grid) && L.cfg.d_model <= 8 * 64 * kIJ &&                // in_proj: one row per trip
+         (long)L.d_in_proj * (L.cfg.d_model / 8) * 16 < kBufOutOfRange;       // W_in within one resource
 }
 
 hipError_t launch_stack_run(const void *tab, int l0, int l1, size_t lds, void *area, float *y,
