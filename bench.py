@@ -10,10 +10,12 @@ single-session decode of a 9B-shaped layer (d_model 4480, 128 heads x 80,
 d_state 128, 8 groups, bf16 weights, fp32 state), 750 frames of 80 ms.
 
 The layer's weights are held in `--copies` identical device copies used in
-turn (default: enough copies for at least 590 MB, i.e. 2 for bf16 weights and 8
-for 4-bit codes), so the 256 MB last-level cache cannot serve a step from the
-weights of a recent step, as in a real stack where every other layer's weights
-stream through in between.
+turn (default: enough copies for at least 2.5 GB, about ten times the 256 MB
+last-level cache, i.e. 9 for bf16 weights and 30 for 4-bit codes), so that no
+step is served from the cache by the weights of a recent step, whatever each
+load's cache policy, as in a real stack where every other layer's weights
+stream through in between. (With two bf16 copies, the two W_out matrices, 184 MB,
+fit the cache when in_proj's loads bypass it.)
 
 Prints one JSON line. Besides steps/s it reports the step's algorithmic HBM
 bytes and bandwidth, per-kernel durations measured with HIP events on the
@@ -50,7 +52,7 @@ def parse():
                          "9 (hybrid stack of 27 Mamba-2 and 4 attention layers, one call per step, 1 session), "
                          "10 (attention layer, 32 sessions)")
     ap.add_argument("--copies", type=int, default=0,
-                    help="identical weight copies used in turn (0: enough for >= 590 MB)")
+                    help="identical weight copies used in turn (0: enough for >= 2.5 GB)")
     ap.add_argument("--no-graph", action="store_true", help="time plain launches only")
     ap.add_argument("--persistent", action="store_true",
                     help="single-layer decode workloads: plan 2 (the persistent SSD + out_proj kernel); "
@@ -71,6 +73,9 @@ def wbytes(dims):
 
 # phases of m2_step_timed (the same for both step plans of m2_step_plan)
 PHASES = ["gemv_in", "ssd_step", "gemv_out"]
+# Weight bytes the single-layer workloads rotate through (identical device copies used in
+# turn): about ten times the MI355X's 256 MB last-level cache.
+ROTATION_BYTES = 2_500_000_000
 
 
 def kernel_bytes(dims, B):
@@ -286,7 +291,7 @@ def main():
         ncopy = args.copies
         if ncopy <= 0:
             per = kernel_bytes(dims, 1)["gemv_in"] + kernel_bytes(dims, 1)["gemv_out"]
-            ncopy = max(2, -(-590_000_000 // per))
+            ncopy = max(2, -(-ROTATION_BYTES // per))
         layers = [m2.Layer(dims, w, dev) for _ in range(ncopy)]
         states = [m2.State(layers[0], B, torch.from_numpy(ssm0).to(dev), torch.from_numpy(conv0).to(dev))]
     else:
@@ -554,7 +559,7 @@ def bench_attn(args, wl):
     ncopy = args.copies
     if ncopy <= 0:
         per = attn_bytes(wl, 0)["qkv_gemv"] + attn_bytes(wl, 0)["o_gemv"]
-        ncopy = max(2, -(-590_000_000 // per))
+        ncopy = max(2, -(-ROTATION_BYTES // per))
     layers = [m2.Attn(d, w, dev) for _ in range(ncopy)]
     kc = torch.from_numpy(kc_np.view(np.int16)).to(dev)
     vc = torch.from_numpy(vc_np.view(np.int16)).to(dev)

@@ -456,6 +456,15 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(4, 4)
     }
     u = uo;
   }
+  // A barrier wait that ran out (the grid was not all resident) left the results undefined;
+  // every workgroup then sees the error word (it was raised before any workgroup passed that
+  // barrier) and writes NaN over its rows of the output, so the failure cannot pass unseen.
+  if (__hip_atomic_load(bar + kBarError * kBarStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+    const int rows = a.tab[a.l1 - 1].go.rows;
+    const int r0 = (int)(((long)blockIdx.x * rows) / gridDim.x);
+    const int r1 = (int)(((long)(blockIdx.x + 1) * rows) / gridDim.x);
+    if (r0 + tid < r1) stc<true>(a.y + r0 + tid, __builtin_nanf(""));
+  }
 }
 
 __global__ void bar_zero_kernel(unsigned *bar) {

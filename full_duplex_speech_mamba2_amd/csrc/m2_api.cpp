@@ -455,6 +455,7 @@ struct m2_stack_s {
   int n_slots;
   int d_model;
   void *dtab = nullptr;     // the persistent kernel's layer table, on the device current at create
+  int dev = -1;             // that device
   size_t area = 0;          // bytes of the persistent path's workspace area (a multiple of 256)
   ~m2_stack_s() {
     if (dtab) (void)hipFree(dtab);
@@ -512,7 +513,8 @@ int m2_stack_create(const m2_stack_layer *layers, int32_t n_layers, int32_t n_sl
   S->area = (off + 255) & ~(size_t)255;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0) {
-    hipError_t e = hipMalloc(&S->dtab, tab.size());
+    hipError_t e = hipGetDevice(&S->dev);
+    if (e == hipSuccess) e = hipMalloc(&S->dtab, tab.size());
     if (e == hipSuccess) e = hipMemcpy(S->dtab, tab.data(), tab.size(), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       delete S;
@@ -561,6 +563,8 @@ struct StackRun {
 std::vector<StackRun> stack_runs(const m2_stack_s &s, int batch, int flags) {
   std::vector<StackRun> runs;
   if (!(flags & M2_PERSISTENT) || batch != 1 || !s.dtab) return runs;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != s.dev) return runs;   // the table is on s.dev
   const int n = (int)s.layers.size();
   for (int i = 0; i < n;) {
     if (s.layers[i].kind != M2_LAYER_MIXER) {

@@ -362,9 +362,11 @@ int m2_stack_step(m2_stack s, const float *x, float *y, int32_t batch, const int
  * residual (plan 2's); the residual stream between the run's layers, zx, v and the sums of
  * squares live in per-layer buffers of the workspace, written once and read past the
  * per-XCD caches. The results are bitwise those of calling m2_step with M2_PERSISTENT |
- * M2_RESIDUAL layer by layer. Every barrier wait is bounded: should the grid not be
- * resident, the launch still ends (its results are then undefined). Attention layers, and
- * runs where the path does not apply, are stepped as by m2_stack_step. The workspace is
+ * M2_RESIDUAL layer by layer. Every barrier wait is bounded: should the grid not be all
+ * resident (another stream's kernels holding CUs; persistent steps on one device are best
+ * serialised), the launch still ends, writes NaN over its run's outputs and leaves the run's
+ * states undefined. Attention layers, runs where the path does not apply, and steps on a
+ * device other than the table's, are stepped as by m2_stack_step. The workspace is
  * m2_stack_workspace_flags bytes: the persistent area (barrier words and per-layer buffers)
  * first, then m2_stack_workspace's. Errors as m2_stack_step, and M2_ERR_UNSUPPORTED for
  * unknown flags; with flags 0 the call is m2_stack_step. */
