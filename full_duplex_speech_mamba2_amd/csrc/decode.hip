@@ -42,21 +42,32 @@ __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
   constexpr int CB = WTraits<WT>::CB;
   using chunk_t = typename WTraits<WT>::chunk_t;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int row = blockIdx.x * WPB + (tid >> 6);
+  const int row = blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool row_ok = row < a.rows;
   const int nb = min(BT, a.B);
   const int K = a.K;
   const int NC = K / EPC;
   const char *wr = static_cast<const char *>(a.W) + (size_t)(row_ok ? row : 0) * NC * CB;
   const void *srow = scale_row<WT>(a.S, (size_t)(row_ok ? row : 0), NC >> a.q_shift);
+  // 16-byte chunks are read through a buffer resource over the wave's row (none for a row
+  // past the matrix): a chunk past the row takes an offset past the resource and reads zeros
+  // without a memory access, so no weight load is conditional and each register can be
+  // refilled as soon as its chunk has been used (the compiler's wait counts stay exact)
+  constexpr bool BUF = CB == 16;
+  const __amdgpu_buffer_rsrc_t rr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(wr), (short)0, row_ok ? NC * CB : 0, 0x00020000);
+  auto ldw = [&](int c) -> chunk_t {
+    if constexpr (BUF) {
+      return __builtin_amdgcn_raw_buffer_load_b128(rr, c < NC ? c * 16 : kBufOutOfRange, 0, NT ? 2 : 0);   // 2: nt
+    } else {
+      return (row_ok && c < NC) ? load_chunk<WT, NT>(wr, c) : chunk_t{};
+    }
+  };
 
   // weights do not depend on the activations: put the first U loads in flight first
   chunk_t w[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c = lane + 64 * u;
-    w[u] = (row_ok && c < NC) ? load_chunk<WT, NT>(wr, c) : chunk_t{};
-  }
+  for (int u = 0; u < U; ++u) w[u] = ldw(lane + 64 * u);
   EpiIn epi{};
   if (row_ok && lane < nb) epi = epilogue_prefetch<EPI>(a, row, lane);
   if (EPI == EPI_INPROJ && a.bar_clear && blockIdx.x == 0 && tid < kBarWords) a.bar_clear[tid * kBarStride] = 0u;
@@ -78,23 +89,25 @@ __global__ __launch_bounds__(TPB) void gemv_wave_kernel(GemvArgs a) {
   float acc[BT];
 #pragma unroll
   for (int bb = 0; bb < BT; ++bb) acc[bb] = 0.0f;
+  // lane l adds its chunks l, l + 64, l + 128, ... in order (trip t holds chunks
+  // l + 64 (U t + u), u < U); with buffer loads each register takes the same chunk of the
+  // next trip right after its use, so U loads stay in flight through the whole row
   if (row_ok) {
-    for (int cb = lane;;) {
+    const int trips = (NC + 64 * U - 1) / (64 * U);
+    for (int t = 0; t < trips; ++t) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = cb + 64 * u;
+        const int c = lane + 64 * (U * t + u);
         if (c < NC) {
           const QScale qs = load_qscale<WT>(srow, c, a.q_shift);
 #pragma unroll
           for (int bb = 0; bb < BT; ++bb) acc[bb] = chunk_acc<WT>(w[u], act_s + bb * K + c * EPC, qs, acc[bb]);
         }
+        if constexpr (BUF) w[u] = ldw(c + 64 * U);
       }
-      cb += 64 * U;
-      if (cb >= NC) break;
+      if constexpr (!BUF) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = cb + 64 * u;
-        w[u] = c < NC ? load_chunk<WT, NT>(wr, c) : chunk_t{};
+        for (int u = 0; u < U; ++u) w[u] = ldw(lane + 64 * (U * (t + 1) + u));
       }
     }
   }
@@ -987,12 +1000,18 @@ hipError_t dispatch_bt(GemvArgs a, hipStream_t stream) {
   }
   constexpr int KS = EPI == EPI_INPROJ ? 1 : 4;
   const bool regs_ok = PRO != PRO_NORM || (a.K / 4 <= 512 * kNormF4PerThread && a.n_partials <= 512 && a.n_norm <= 512);
-  // Both projections stream their weights with nontemporal loads, 5 per lane in flight: such
-  // loads do not allocate in the last-level cache, and in a stack of layers no weight line is
-  // read again before it would be evicted anyway (measured on 8 distinct 9B layers: out_proj
-  // 19.8 us with 5 nontemporal loads in flight, 20.6 / 20.8 / 21.3 / 20.7 with 4 / 3 / 6 / 8,
-  // 21.9 with 8 cache-allocating ones, which only win when two layers' W_out fit the cache).
+  // Both projections stream their weights with nontemporal loads: such loads do not allocate
+  // in the last-level cache, and in a stack of layers no weight line is read again before it
+  // would be evicted anyway (measured on 8 distinct 9B layers: out_proj 19.8 us with 5
+  // nontemporal loads in flight per lane, 20.6 / 20.8 / 21.3 / 20.7 with 4 / 3 / 6 / 8, 21.9
+  // with 8 cache-allocating ones, which only win when two layers' W_out fit the cache).
+  // out_proj at one session runs 6 rows per workgroup (384 threads): its 40 KB of staged
+  // activations allow 3 workgroups per CU, and 4480 rows then make one even round of 747
+  // workgroups on 256 CUs (8 rows per workgroup leave 48 CUs with 3 and the rest with 2);
+  // with 8 loads in flight per lane: 17.4 us against 19.5 (5 in flight: 18.2-18.6; 256, 320
+  // and 448 threads: 23.0, 21.8 and 18.5).
   if (a.B <= 2 && regs_ok && wave_lds_bytes(a, a.B, PRO) <= kWaveLdsMax) {
+    if (EPI == EPI_OUT && PRO == PRO_NORM && a.B == 1) return launch_wave<WT, 1, 384, 8, 1, PRO, EPI>(a, stream);
     if (a.B == 1) return launch_wave<WT, 1, 512, 5, 1, PRO, EPI>(a, stream);
     return launch_wave<WT, 2, 512, 5, 1, PRO, EPI>(a, stream);
   }

@@ -386,10 +386,11 @@ __device__ __forceinline__ void rms_factors(const GemvArgs &a, int b0, int nb, f
 // partials; wave w reduces norm groups w, w + W, ... (each lane a strided part of the
 // group's partials, then a cross-lane tree: a fixed order) into their RMS factors, and after
 // one barrier every thread writes its float4s scaled by their group's factor.
-// LDS: act [BT][K] | rn [BT][n_norm]. K/4 <= TPB * kNormF4PerThread.
+// LDS: act [BT][K] | rn [BT][n_norm]. K/4 <= 512 * kNormF4PerThread (each thread holds
+// ceil(512 * kNormF4PerThread / TPB) float4s).
 template <int BT, int TPB>
 __device__ __forceinline__ void stage_norm_act(const GemvArgs &a, float *lds, int tid) {
-  constexpr int MAXF = kNormF4PerThread, W = TPB / 64;
+  constexpr int MAXF = (kNormF4PerThread * 512 + TPB - 1) / TPB, W = TPB / 64;   // K/4 <= 512 * kNormF4PerThread
   const int K = a.K, nb = min(BT, a.B), nf = K / 4;
   const int lane = tid & 63, wave = tid >> 6;
   float *act_s = lds;
