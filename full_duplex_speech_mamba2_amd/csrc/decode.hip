@@ -1008,10 +1008,12 @@ hipError_t dispatch_bt(GemvArgs a, hipStream_t stream) {
   // out_proj at one session runs 6 rows per workgroup (384 threads): its 40 KB of staged
   // activations allow 3 workgroups per CU, and 4480 rows then make one even round of 747
   // workgroups on 256 CUs (8 rows per workgroup leave 48 CUs with 3 and the rest with 2);
-  // with 8 loads in flight per lane: 17.4 us against 19.5 (5 in flight: 18.2-18.6; 256, 320
-  // and 448 threads: 23.0, 21.8 and 18.5).
+  // with 7 loads in flight per lane: 17.2 us against 19.5 (8 / 5 / 10 in flight: 17.5 /
+  // 18.2 / 21.2; 256, 320 and 448 threads: 23.0, 21.8 and 18.5). in_proj at one session keeps
+  // 3 loads per lane in flight (33.3 us against 33.55 with 5, 33.8 with 4, 34.7 with 6).
   if (a.B <= 2 && regs_ok && wave_lds_bytes(a, a.B, PRO) <= kWaveLdsMax) {
-    if (EPI == EPI_OUT && PRO == PRO_NORM && a.B == 1) return launch_wave<WT, 1, 384, 8, 1, PRO, EPI>(a, stream);
+    if (EPI == EPI_OUT && PRO == PRO_NORM && a.B == 1) return launch_wave<WT, 1, 384, 7, 1, PRO, EPI>(a, stream);
+    if (EPI == EPI_INPROJ && a.B == 1) return launch_wave<WT, 1, 512, 3, 1, PRO, EPI>(a, stream);
     if (a.B == 1) return launch_wave<WT, 1, 512, 5, 1, PRO, EPI>(a, stream);
     return launch_wave<WT, 2, 512, 5, 1, PRO, EPI>(a, stream);
   }
@@ -1473,7 +1475,7 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
     // in_proj as in plan 0 (it also zeroes the next kernel's barrier counter), then the
     // SSD and out_proj in one persistent kernel
     gi.bar_clear = ws.bar;
-    e = launch_wave<M2_W_BF16, 1, 512, 5, 1, PRO_PLAIN, EPI_INPROJ>(gi, stream);
+    e = launch_wave<M2_W_BF16, 1, 512, 3, 1, PRO_PLAIN, EPI_INPROJ>(gi, stream);
     if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess) e = launch_fused_step(L, S, x, y, slots, flags, ws, fused_grid(L), stream);
     for (int i = 2; i < 4 && e == hipSuccess; ++i) e = mark(i);
