@@ -1643,11 +1643,14 @@ hipError_t launch_gemv_plain(int wtype, const void *W, const void *S, int rows, 
     if (e != hipSuccess) return e;
     return launch_mfma_reduce<EPI_OUT>(a, p, part, stream);
   }
-  // 1-2 sessions, 2- and 4-byte weights: the in_proj configuration (5 nontemporal loads in
-  // flight); otherwise the decode step's choice for out_proj.
+  // 1-2 sessions, 2- and 4-byte weights: one wave per row, 5 nontemporal loads in flight;
+  // bf16 at one session with 6 rows per workgroup (384 threads): measured on the attention
+  // layer's projections (7168 x 4480 and 4480 x 5120, 23 rotating copies), 13.2 and 10.2 us
+  // against 13.9 and 11.0 with 8 rows (256 / 768 threads: 13.8 / 15.0 and 10.7 / 10.6; 3, 7
+  // or 8 loads in flight slower); otherwise the decode step's choice for out_proj.
   if (batch <= 2 && (wtype == M2_W_BF16 || wtype == M2_W_F32) && wave_lds_bytes(a, batch, PRO_PLAIN) <= kWaveLdsMax) {
     if (wtype == M2_W_BF16)
-      return batch == 1 ? launch_wave<M2_W_BF16, 1, 512, 5, 1, PRO_PLAIN, EPI_OUT>(a, stream)
+      return batch == 1 ? launch_wave<M2_W_BF16, 1, 384, 5, 1, PRO_PLAIN, EPI_OUT>(a, stream)
                         : launch_wave<M2_W_BF16, 2, 512, 5, 1, PRO_PLAIN, EPI_OUT>(a, stream);
     return batch == 1 ? launch_wave<M2_W_F32, 1, 512, 5, 1, PRO_PLAIN, EPI_OUT>(a, stream)
                       : launch_wave<M2_W_F32, 2, 512, 5, 1, PRO_PLAIN, EPI_OUT>(a, stream);
