@@ -434,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void gemv_tiled_kernel(GemvArgs a) {
 template <int NW, int MAXI>
 __global__ __launch_bounds__(NW * 64) void ssd_step_kernel(SsdArgs a) {
   __shared__ float wsum[NW];
-  __shared__ float cx[2 * 256 + 32];   // conv outputs: B [N] | C [N] | x rows [prange]
+  __shared__ float cx[2 * 256 + 64];   // conv outputs: B [N] | C [N] | x rows [prange <= 64]
   const int h = blockIdx.x / a.psplit, ps = blockIdx.x - h * a.psplit;
   ssd_item<NW, MAXI>(a, h, ps, blockIdx.y, threadIdx.x >> 6, threadIdx.x & 63, wsum, cx);
 }
@@ -1431,6 +1431,8 @@ hipError_t launch_ssd(const SsdArgs &sa, int items, int batch, hipStream_t strea
   const dim3 grid(items, batch);
   if (batch <= 2 && n_inst <= 16)
     hipLaunchKernelGGL((ssd_step_kernel<8, 2>), grid, dim3(512), 0, stream, sa);
+  else if (batch <= 2 && n_inst <= 24)
+    hipLaunchKernelGGL((ssd_step_kernel<8, 3>), grid, dim3(512), 0, stream, sa);
   else if (n_inst <= 10)
     hipLaunchKernelGGL((ssd_step_kernel<2, 5>), grid, dim3(128), 0, stream, sa);
   else if (n_inst <= 16)
@@ -1513,6 +1515,19 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   sa.n_partials = L.n_partials;
   sa.slots = slots;
   sa.n_slots = S.n_slots;
+  // One or two sessions: SSD items of twice the layer's row range where it still divides the
+  // head and the RMS group and fits the 8-wave item (measured on the 9B layer, 40 rows instead
+  // of 20: SSD 6.9 against 7.1 us, and out_proj sums half the partials; step +0.43 % on one
+  // box, three repeats each; two 20-row ranges per item with a partial each: +0.08 %). The
+  // partials then number half of the workspace's n_partials.
+  if (!mfma && batch <= 2) {
+    const int pr2 = 2 * L.prange, rpi = 64 / (c.d_state / 4);
+    if (L.psplit % 2 == 0 && L.ng % pr2 == 0 && pr2 <= 64 && (pr2 + rpi - 1) / rpi <= 24) {
+      sa.prange = pr2;
+      sa.psplit = L.psplit / 2;
+      sa.n_partials = L.n_partials / 2;
+    }
+  }
 
   // 3. RMSNorm + out_proj (+ residual)
   GemvArgs go{};
@@ -1526,7 +1541,7 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   go.B = batch;
   go.ss = ws.ss;
   go.ng = L.ng;
-  go.n_partials = L.n_partials;
+  go.n_partials = sa.n_partials;
   go.n_norm = L.n_norm;
   go.eps = c.norm_eps;
   go.y = y;
@@ -1539,7 +1554,7 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   go.conv_dim = L.conv_dim;
   go.d_conv = c.d_conv;
   go.conv_cache = S.conv;
-  e = launch_ssd(sa, c.n_heads * L.psplit, batch, stream);
+  e = launch_ssd(sa, c.n_heads * sa.psplit, batch, stream);
   if (e == hipSuccess) e = mark(2);
   if (e != hipSuccess) return e;
   if (mfma) {
