@@ -61,6 +61,23 @@ def test_ragged_shapes(wtype, variant, batch):
            residual=residual)
 
 
+@pytest.mark.parametrize("batch", [1, 2])
+@pytest.mark.parametrize("norm_group", [0, 20])
+def test_doubled_ssd_range(batch, norm_group):
+    """The 9B SSD item shape at one and two sessions: head_dim 80 gives 20-row ranges, which
+    the three-kernel plan doubles to 40-row items (8 waves x up to 3 state slices of a
+    128-wide state row) with one sum of squares each; with RMS groups of 20 channels a
+    doubled range would straddle two groups, so the layer's 20-row items stay. Slots and
+    the residual on; outputs, states and conv caches against the oracle."""
+    dims = synth.MixerDims(d_model=256, n_heads=4, head_dim=80, d_state=128, n_groups=2, wtype="bf16",
+                           norm_group=norm_group)
+    w = synth.make_layer_weights(dims, 91)
+    xs = synth.make_inputs(dims, 92, 7, batch)
+    ssm0, conv0 = synth.make_state(dims, 93, 4, 0.1)
+    slots = np.array([3, 1][:batch], np.int32)
+    _check("doubled-range-b%d-ng%s" % (batch, norm_group), dims, w, xs, ssm0, conv0, slot_ids=slots, residual=True)
+
+
 @pytest.mark.parametrize("batch", [1, 2, 5, 8, 17, 40])
 def test_batch_sizes_bf16(batch):
     """1-2 sessions: one-wave-per-row GEMVs; 3-32: MFMA GEMVs; 40: the tiled VALU GEMVs."""
