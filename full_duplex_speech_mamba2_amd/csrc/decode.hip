@@ -1429,8 +1429,13 @@ hipError_t launch_ssd(const SsdArgs &sa, int items, int batch, hipStream_t strea
   const int rpi = 64 / (sa.N / 4);
   const int n_inst = (sa.prange + rpi - 1) / rpi;
   const dim3 grid(items, batch);
+  // one or two sessions: items of 10 waves x 2 slices for 17-20 slice instructions (the 9B
+  // layer's 40-row items: step 18,440 against 18,389 steps/s with 8 x 3, 18,429 with 12 x 2,
+  // 18,226 with 5 x 4, same box, two repeats each)
   if (batch <= 2 && n_inst <= 16)
     hipLaunchKernelGGL((ssd_step_kernel<8, 2>), grid, dim3(512), 0, stream, sa);
+  else if (batch <= 2 && n_inst <= 20)
+    hipLaunchKernelGGL((ssd_step_kernel<10, 2>), grid, dim3(640), 0, stream, sa);
   else if (batch <= 2 && n_inst <= 24)
     hipLaunchKernelGGL((ssd_step_kernel<8, 3>), grid, dim3(512), 0, stream, sa);
   else if (n_inst <= 10)

@@ -65,8 +65,8 @@ def test_ragged_shapes(wtype, variant, batch):
 @pytest.mark.parametrize("norm_group", [0, 20])
 def test_doubled_ssd_range(batch, norm_group):
     """The 9B SSD item shape at one and two sessions: head_dim 80 gives 20-row ranges, which
-    the three-kernel plan doubles to 40-row items (8 waves x up to 3 state slices of a
-    128-wide state row) with one sum of squares each; with RMS groups of 20 channels a
+    the three-kernel plan doubles to 40-row items (10 waves x 2 state slices of a 128-wide
+    state row) with one sum of squares each; with RMS groups of 20 channels a
     doubled range would straddle two groups, so the layer's 20-row items stay. Slots and
     the residual on; outputs, states and conv caches against the oracle."""
     dims = synth.MixerDims(d_model=256, n_heads=4, head_dim=80, d_state=128, n_groups=2, wtype="bf16",
