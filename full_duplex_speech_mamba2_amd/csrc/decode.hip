@@ -1432,14 +1432,14 @@ hipError_t launch_ssd(const SsdArgs &sa, int items, int batch, hipStream_t strea
   // one or two sessions: items of 10 waves x 2 slices for 17-20 slice instructions (the 9B
   // layer's 40-row items: step 18,440 against 18,389 steps/s with 8 x 3, 18,429 with 12 x 2,
   // 18,226 with 5 x 4, same box, two repeats each)
-  // 3-8 sessions, 17-20 slice instructions (the 9B layer's 40-row items): 4 waves x 5 slices
-  // up to 4 sessions, 2 x 10 beyond (4 sessions: 15,340 / 15,006 steps/s with 4 x 5 / 2 x 10;
-  // 8 int8 sessions: 564 / 572 stack steps/s)
+  // 3 or more sessions, 17-20 slice instructions (the 9B layer's 40-row items): 4 waves x 5
+  // slices up to 4 sessions, 2 x 10 beyond (4 sessions: 15,340 / 15,006 steps/s with 4 x 5 /
+  // 2 x 10; 8 int8 sessions: 564 / 572 stack steps/s)
   if (batch > 2 && batch <= 4 && n_inst > 16 && n_inst <= 20) {
     hipLaunchKernelGGL((ssd_step_kernel<4, 5>), grid, dim3(256), 0, stream, sa);
     return hipGetLastError();
   }
-  if (batch > 4 && batch <= 8 && n_inst > 16 && n_inst <= 20) {
+  if (batch > 4 && n_inst > 16 && n_inst <= 20) {
     hipLaunchKernelGGL((ssd_step_kernel<2, 10>), grid, dim3(128), 0, stream, sa);
     return hipGetLastError();
   }
@@ -1531,13 +1531,13 @@ hipError_t launch_step(const m2_layer_s &L, const m2_state_s &S, const float *x,
   sa.n_partials = L.n_partials;
   sa.slots = slots;
   sa.n_slots = S.n_slots;
-  // Up to 8 sessions: SSD items of twice the layer's row range where it still divides the
-  // head and the RMS group and fits the items below (measured on the 9B layer, 40 rows instead
-  // of 20: at one session the SSD 6.9 against 7.1 us, and out_proj sums half the partials, step
-  // +0.43 % on one box, three repeats each, where two 20-row ranges per item with a partial
-  // each gave +0.08 %; 4 sessions +0.6 %, the 8-session int8 stack 558 -> 572 stack steps/s).
-  // The partials then number half of the workspace's n_partials.
-  if (batch <= 8) {
+  // SSD items of twice the layer's row range where it still divides the head and the RMS
+  // group and fits the items below (measured on the 9B layer, 40 rows instead of 20: at one
+  // session the SSD 6.9 against 7.1 us, and out_proj sums half the partials, step +0.43 % on
+  // one box, three repeats each, where two 20-row ranges per item with a partial each gave
+  // +0.08 %; 4 sessions +0.6 %, the 8-session int8 stack 558 -> 572 stack steps/s, 32 sessions
+  // 7,470 -> 7,563 steps/s). The partials then number half of the workspace's n_partials.
+  {
     const int pr2 = 2 * L.prange, rpi = 64 / (c.d_state / 4);
     if (L.psplit % 2 == 0 && L.ng % pr2 == 0 && pr2 <= 64 && (pr2 + rpi - 1) / rpi <= 24) {
       sa.prange = pr2;

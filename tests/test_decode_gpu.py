@@ -61,21 +61,21 @@ def test_ragged_shapes(wtype, variant, batch):
            residual=residual)
 
 
-@pytest.mark.parametrize("batch", [1, 2, 4, 8])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8, 17])
 @pytest.mark.parametrize("norm_group", [0, 20])
 def test_doubled_ssd_range(batch, norm_group):
-    """The 9B SSD item shape at 1-8 sessions: head_dim 80 gives 20-row ranges, which the step
-    doubles to 40-row items with one sum of squares each (10 waves x 2 state slices of a
-    128-wide state row at 1-2 sessions, 4 x 5 at 4 and 2 x 10 at 8, where the GEMVs are the
-    MFMA plan's); with RMS groups of 20 channels a doubled range would straddle two groups, so
+    """The 9B SSD item shape at 1-17 sessions: head_dim 80 gives 20-row ranges, which the
+    step doubles to 40-row items with one sum of squares each (10 waves x 2 state slices of a
+    128-wide state row at 1-2 sessions, 4 x 5 at 4 and 2 x 10 at 8 and 17, where the GEMVs
+    are the MFMA plan's); with RMS groups of 20 channels a doubled range would straddle two groups, so
     the layer's 20-row items stay. Slots and the residual on; outputs, states and conv caches
     against the oracle."""
     dims = synth.MixerDims(d_model=256, n_heads=4, head_dim=80, d_state=128, n_groups=2, wtype="bf16",
                            norm_group=norm_group)
     w = synth.make_layer_weights(dims, 91)
     xs = synth.make_inputs(dims, 92, 7, batch)
-    ssm0, conv0 = synth.make_state(dims, 93, 10, 0.1)
-    slots = np.array([3, 1, 9, 0, 5, 7, 2, 8][:batch], np.int32)
+    ssm0, conv0 = synth.make_state(dims, 93, 20, 0.1)
+    slots = np.array([3, 1, 9, 0, 5, 7, 2, 8, 19, 11, 4, 16, 6, 13, 10, 18, 12][:batch], np.int32)
     _check("doubled-range-b%d-ng%s" % (batch, norm_group), dims, w, xs, ssm0, conv0, slot_ids=slots, residual=True)
 
 
