@@ -205,7 +205,9 @@ int m2_step_noalloc(m2_layer layer, m2_state st, const float *x, float *y, int32
  *   2  only when asked for with M2_PERSISTENT (slower than plan 0 on MI355X), for one
  *      session with bf16 weights on a device where two workgroups of the persistent kernel
  *      fit on every CU (shapes up to d_model 2 x CUs x 9 = 4608 on 256 CUs, d_inner 12288,
- *      and n_heads x head_dim / prange no larger than 2 x CUs): the in_proj GEMV of plan 0,
+ *      and n_heads x head_dim / prange no larger than 2 x CUs, prange being the layer's SSD
+ *      row range: the largest multiple of 4 up to 32 dividing gcd(head_dim, norm_group)): the
+ *      in_proj GEMV of plan 0,
  *      then the SSD update and out_proj in one persistent kernel whose workgroups meet at
  *      one grid-wide barrier, out_proj's weights in flight across it.
  * m2_step_timed's events delimit the phases of plans 0 and 1; with plan 2, events[2] and
