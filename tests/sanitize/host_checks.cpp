@@ -164,6 +164,19 @@ int main() {
   tab[1].k_cache = fake(19);
   expect(m2_stack_create(tab, 2, 4, &sk), M2_OK, "stack: good");
   expect(m2_stack_step(sk, x, y, 0, nullptr, ws, 1u << 30, nullptr) < 0 ? 0 : 1, 0, "stack step: batch 0");
+  // the persistent stack step's entry points: workspace, run count and the checks before
+  // any launch (no GPU here, so the persistent path never applies)
+  const size_t need_p = m2_stack_workspace_flags(sk, 1, M2_PERSISTENT);
+  expect(need_p > m2_stack_workspace(sk, 1) ? 0 : 1, 0, "stack: persistent area in the workspace");
+  expect(m2_stack_workspace_flags(sk, 1, 8) == 0 ? 0 : 1, 0, "stack workspace: unknown flag");
+  expect(m2_stack_persistent_runs(sk, 1, M2_PERSISTENT), 0, "stack: no persistent run without a GPU");
+  expect(m2_stack_persistent_runs(nullptr, 1, M2_PERSISTENT), -1, "stack runs: NULL stack");
+  expect(m2_stack_step_flags(sk, x, y, 1, nullptr, 8, ws, need_p, nullptr), M2_ERR_UNSUPPORTED,
+         "stack step: unknown flag");
+  expect(m2_stack_step_flags(sk, x, y, 1, nullptr, M2_PERSISTENT, ws, need_p - 1, nullptr), M2_ERR_WORKSPACE,
+         "stack step: persistent workspace one byte short");
+  expect(m2_stack_step_flags(sk, x, y, 5, nullptr, M2_PERSISTENT, ws, need_p, nullptr), M2_ERR_SLOT,
+         "stack step: more sessions than slots");
   m2_stack_destroy(sk);
 
   m2_attn_destroy(at);
