@@ -154,6 +154,29 @@ def hold_ms(steps):
     return max(5.0, 0.04 * steps)
 
 
+def copy_bandwidth(dev, mib=512, reps=5):
+    """A device-to-device copy of `mib` MiB timed with events (median of `reps`), outside any
+    timed region: GB/s counting the bytes read and written (2 x the buffer), the box's own
+    read-plus-write reference next to the 8 TB/s peak."""
+    import numpy as np
+    import torch
+    src = torch.ones((mib << 20) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * (mib << 20) / (float(np.median(ms)) * 1e-3) / 1e9
+
+
 def eager_ms_per_step(run, t0, steps, before=None):
     """Median over REPEATS of the milliseconds per step of `steps` plain-launch steps, each
     repeat bracketed by events on torch's current stream (where the steps run), the GPU held
@@ -365,6 +388,7 @@ def main():
         for e in row:
             hip.hipEventDestroy(e)
     dom = max(names, key=lambda n: kb[n])
+    copy_gbps = copy_bandwidth(dev)
     achieved = kb[dom] / (dur_us[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -386,6 +410,9 @@ def main():
         "hbm_peak_frac": round(wl.layers * kb["step"] * steps_per_s / 1e9 / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": wl.layers * kb["step"],
         "session_tokens_per_s": round(B * steps_per_s, 1),
+        "realtime_sessions": round(B * steps_per_s * 0.08, 1),
+        "copy_GBps": round(copy_gbps, 1),
+        "copy_frac": round(wl.layers * kb["step"] * steps_per_s / 1e9 / copy_gbps, 4),
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
         "repeats_ms_per_step": {"eager": [round(v, 5) for v in rep_eager],
@@ -777,6 +804,7 @@ def bench_stack(args, wl):
         "hbm_peak_frac": round(step_bytes * sps / 1e9 / HBM_PEAK_GBPS, 4),
         "step_algorithmic_bytes": step_bytes,
         "frame_budget_ms": 80.0,
+        "realtime_sessions": round(B * sps * 0.08, 1),
         "ms_per_step_eager": round(ms_eager, 4),
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 4),
         "kernel_us_first_mixer": {n: round(v, 2) for n, v in dur_us.items()},
