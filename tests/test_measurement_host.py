@@ -78,3 +78,13 @@ def test_weight_rotation_exceeds_the_last_level_cache(config):
     copies = max(2, -(-bench.ROTATION_BYTES // per))
     assert copies * per >= 2.5e9
     assert copies * kb["gemv_out"] > 2 * 256 * 2 ** 20
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The library runs on one GPU: asked for several, the bench exits with status 2 and a
+    message saying so, before touching a device."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
